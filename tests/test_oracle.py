@@ -1,0 +1,302 @@
+"""Pins of the fp64 CPU oracle against facts fixed outside it.
+
+Each test checks the oracle against something it does not contain: closed-form
+values derived by hand (tests/golden/closed_forms.json), a library routine
+(torch's scaled_dot_product_attention on the CPU in fp64, numpy eigvalsh,
+scipy logsumexp), invariants of softmax attention, and brute force with scalar
+loops on tiny inputs.  A dropped term, a wrong sign or index, or a transposed
+operand in the oracle fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _eval(expr: str) -> float:
+    return float(eval(expr, {"__builtins__": {}}, {"cos": math.cos, "sin": math.sin}))
+
+
+# ------------------------------------------------------------------ ALiBi ----
+def test_alibi_slopes_closed_form():
+    g = _golden()["alibi_slopes_H8"]
+    np.testing.assert_array_equal(oracle.alibi_slopes(8), [_eval(e) for e in g["values_expr"]])
+    m12 = oracle.alibi_slopes(12)
+    assert m12[0] == pytest.approx(2.0 ** (-2.0 / 3.0), rel=1e-15)
+    assert m12[-1] == 2.0 ** -8          # the last head always gets 2^-8
+    assert np.all(np.diff(m12) < 0)
+
+
+def test_alibi_bias_closed_form_values():
+    g = _golden()["alibi_bias_examples"]
+    b = oracle.alibi_bias(oracle.alibi_slopes(g["H"]), 16)
+    for c in g["cases"]:
+        assert b[c["h"], c["i"], c["j"]] == _eval(c["value_expr"])
+
+
+def test_alibi_bias_structure():
+    m = oracle.alibi_slopes(12)
+    b = oracle.alibi_bias(m, 64)
+    assert np.all(np.diagonal(b, axis1=1, axis2=2) == 0)
+    np.testing.assert_array_equal(b, -np.swapaxes(b, 1, 2))      # antisymmetric
+    np.testing.assert_allclose(np.diff(b, axis=2), np.broadcast_to(m[:, None, None], (12, 64, 63)), rtol=0, atol=1e-13)
+    assert np.all(b[:, 0, 1] > 0)                                   # positive for j > i
+
+
+def test_alibi_factor_identity_1e12():
+    """phi_q phi_k^T reproduces m_h (j - i) to 1e-12 at the GPT-2 size (N = 2048)."""
+    m = oracle.alibi_slopes(12)
+    pq, pk = oracle.alibi_factors(m, 2048)
+    assert pq.shape == pk.shape == (12, 2048, 2)
+    err = np.abs(oracle.lowrank_bias(pq, pk) - oracle.alibi_bias(m, 2048)).max()
+    assert err <= 1e-12
+
+
+# --------------------------------------------------------------- Sandwich ----
+@pytest.mark.parametrize("key", ["sandwich_C4", "sandwich_C2"])
+def test_sandwich_closed_forms(key):
+    g = _golden()[key]
+    N = max(max(c["i"], c["j"]) for c in g["cases"]) + 1
+    b = oracle.sandwich_bias(N, g["C"])
+    for c in g["cases"]:
+        assert b[c["i"], c["j"]] == pytest.approx(_eval(c["value_expr"]), abs=1e-14)
+
+
+def test_sandwich_frequencies_closed_form():
+    w = oracle.sandwich_frequencies(4).astype(np.float64)
+    np.testing.assert_allclose(w, [1e-2, 1e-4], rtol=1e-15)
+    w64 = oracle.sandwich_frequencies(64).astype(np.float64)
+    assert w64[0] == pytest.approx(10000.0 ** (-1.0 / 32.0), rel=1e-15)   # highest frequency < 1
+    assert w64[-1] == pytest.approx(1e-4, rel=1e-15)
+
+
+def test_sandwich_structure():
+    C, N = 64, 300
+    b = oracle.sandwich_bias(N, C)
+    np.testing.assert_allclose(np.diagonal(b), C / 2, rtol=0, atol=1e-13)
+    np.testing.assert_array_equal(b, b.T)                                   # symmetric
+    np.testing.assert_array_equal(b[1:, 1:], b[:-1, :-1])                   # Toeplitz
+    ev = np.linalg.eigvalsh(b)
+    assert ev.min() > -1e-9                                                 # Gram matrix: PSD
+
+
+def test_sandwich_factor_identity_1e12():
+    """phi phi^T reproduces the cosine sum to 1e-12 at the Sandwich size (N = 4096, C = 64)."""
+    N, C = 4096, 64
+    phi = oracle.sandwich_factors(N, C)
+    assert phi.shape == (N, C)
+    np.testing.assert_allclose(phi[:, 0::2] ** 2 + phi[:, 1::2] ** 2, 1.0, rtol=0, atol=1e-15)
+    err = np.abs(oracle.lowrank_bias(phi, phi) - oracle.sandwich_bias(N, C)).max()
+    assert err <= 1e-12
+
+
+# --------------------------------------------------------------- attention ---
+def _sdpa(q, k, v, mask=None, scale=None, causal=False):
+    import torch
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))
+    m = None if mask is None else t(np.broadcast_to(mask, q.shape[:2] + (q.shape[2], k.shape[2])))
+    o = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=m, scale=scale,
+                                                         is_causal=causal)
+    return o.numpy()
+
+
+def _qkv(B, H, N, D, seed, std=1.0):
+    r = np.random.default_rng(seed)
+    return tuple(r.standard_normal((B, H, N, D)) * std for _ in range(3))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_no_bias_matches_library(causal):
+    q, k, v = _qkv(2, 3, 77, 32, 1)
+    o, _ = oracle.attention(q, k, v, causal=causal)
+    np.testing.assert_allclose(o, _sdpa(q, k, v, causal=causal), rtol=0, atol=1e-12)
+
+
+def test_attention_bias_matches_library():
+    """An asymmetric per-head bias passed as a float attn_mask: pins the bias sign,
+    its orientation (row = query) and the scale."""
+    q, k, v = _qkv(2, 3, 65, 16, 2)
+    r = np.random.default_rng(3)
+    bias = r.standard_normal((3, 65, 65)) * 2.0
+    for scale in (None, 0.3):
+        o, _ = oracle.attention(q, k, v, bias=bias, scale=scale)
+        np.testing.assert_allclose(o, _sdpa(q, k, v, mask=bias[None], scale=scale), rtol=0, atol=1e-12)
+
+
+def test_attention_causal_bias_matches_library():
+    q, k, v = _qkv(1, 2, 50, 8, 4)
+    m = oracle.alibi_slopes(2)
+    bias = oracle.alibi_bias(m, 50)
+    o, _ = oracle.attention(q, k, v, bias=bias, causal=True)
+    mask = np.where(np.arange(50)[None, :] > np.arange(50)[:, None], -np.inf, 0.0) + bias
+    np.testing.assert_allclose(o, _sdpa(q, k, v, mask=mask[None]), rtol=0, atol=1e-12)
+
+
+def _brute(q, k, v, bias, scale, causal):
+    """Scalar loops with math.fsum: O and LSE by the definition."""
+    B, H, N, D = q.shape
+    O = np.zeros((B, H, N, D))
+    LSE = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            for i in range(N):
+                js = [j for j in range(N) if not (causal and j > i)]
+                L = [scale * math.fsum(q[b, h, i, d] * k[b, h, j, d] for d in range(D)) + bias[h, i, j] for j in js]
+                mx = max(L)
+                p = [math.exp(x - mx) for x in L]
+                l = math.fsum(p)
+                LSE[b, h, i] = mx + math.log(l)
+                for d in range(D):
+                    O[b, h, i, d] = math.fsum(pj * v[b, h, j, d] for pj, j in zip(p, js)) / l
+    return O, LSE
+
+
+@pytest.mark.parametrize("N,causal", [(1, False), (5, True), (8, False), (8, True)])
+def test_attention_brute_force_tiny(N, causal):
+    q, k, v = _qkv(1, 2, N, 4, 10 + N)
+    bias = np.random.default_rng(N).standard_normal((2, N, N))
+    o, lse = oracle.attention(q, k, v, bias=bias, scale=0.7, causal=causal)
+    ob, lb = _brute(q, k, v, bias, 0.7, causal)
+    np.testing.assert_allclose(o, ob, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, lb, rtol=0, atol=1e-14)
+
+
+def test_lse_matches_logsumexp():
+    from scipy.special import logsumexp
+    q, k, v = _qkv(1, 1, 40, 8, 5)
+    bias = np.random.default_rng(6).standard_normal((40, 40))
+    _, lse = oracle.attention(q, k, v, bias=bias)
+    _, lse2 = oracle.attention(q, k, v, bias=bias - lse[0, 0][:, None])
+    np.testing.assert_allclose(lse2, 0.0, atol=1e-13)
+    # library check of the same quantity on the scores the SDPA pin fixed
+    s = 1 / math.sqrt(8)
+    np.testing.assert_allclose(lse[0, 0], logsumexp(s * q[0, 0] @ k[0, 0].T + bias, axis=1), rtol=0, atol=1e-12)
+
+
+def test_row_constant_invariance():
+    """Adding a per-row constant to b leaves O unchanged (ALiBi's -m_h*i is such a term)."""
+    q, k, v = _qkv(2, 2, 33, 16, 7)
+    bias = np.random.default_rng(8).standard_normal((2, 33, 33))
+    row_c = np.random.default_rng(9).standard_normal((2, 33, 1)) * 100
+    o1, l1 = oracle.attention(q, k, v, bias=bias, causal=True)
+    o2, l2 = oracle.attention(q, k, v, bias=bias + row_c, causal=True)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l2 - l1, np.broadcast_to(row_c[None, :, :, 0], l1.shape), rtol=0, atol=1e-10)
+
+
+def test_softmax_value_path_invariants():
+    q, k, v = _qkv(1, 1, 20, 8, 11)
+    # constant V rows -> O equals that constant
+    vc = np.broadcast_to(np.arange(8.0), v.shape).copy()
+    o, _ = oracle.attention(q, k, vc, bias=np.random.default_rng(1).standard_normal((20, 20)))
+    np.testing.assert_allclose(o, vc, rtol=0, atol=1e-13)
+    # one key with a +50 bias captures every row
+    bias = np.zeros((20, 20))
+    bias[:, 13] = 50.0
+    o, _ = oracle.attention(q, k, v, bias=bias)
+    np.testing.assert_allclose(o[0, 0], np.broadcast_to(v[0, 0, 13], (20, 8)), rtol=0, atol=1e-12)
+    # permuting keys (K, V and bias columns together) leaves O unchanged
+    bias = np.random.default_rng(2).standard_normal((20, 20))
+    perm = np.random.default_rng(3).permutation(20)
+    o1, _ = oracle.attention(q, k, v, bias=bias)
+    o2, _ = oracle.attention(q, k[:, :, perm], v[:, :, perm], bias=bias[:, perm])
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-13)
+
+
+def test_rows_subset_equals_full():
+    q, k, v = _qkv(2, 2, 30, 8, 12)
+    bias = np.random.default_rng(13).standard_normal((2, 30, 30))
+    rows = np.array([0, 7, 29, 3])
+    of, lf = oracle.attention(q, k, v, bias=bias, causal=True)
+    os_, ls = oracle.attention(q, k, v, bias=bias, causal=True, rows=rows)
+    np.testing.assert_array_equal(os_, of[:, :, rows])
+    np.testing.assert_array_equal(ls, lf[:, :, rows])
+
+
+def test_lowrank_bias_folds_into_contraction():
+    """softmax(s QK^T + phi_q phi_k^T) V equals plain attention on Q' = [Q s, phi_q], K' = [K, phi_k]
+    with unit scale -- the augmented contraction of the FlashBias recipe."""
+    q, k, v = _qkv(1, 2, 24, 8, 14)
+    r = np.random.default_rng(15)
+    pq, pk = r.standard_normal((2, 24, 3)), r.standard_normal((2, 24, 3))
+    s = 1 / math.sqrt(8)
+    o1, _ = oracle.attention(q, k, v, bias=oracle.lowrank_bias(pq, pk))
+    qa = np.concatenate([q * s, pq[None]], axis=-1)
+    ka = np.concatenate([k, pk[None]], axis=-1)
+    np.testing.assert_allclose(o1, _sdpa(qa, ka, v, scale=1.0), rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------- SVD ---
+def test_svd_singular_values_match_eigvalsh():
+    b = np.random.default_rng(16).standard_normal((60, 60))
+    f = oracle.truncated_svd(b, 5)
+    ref = np.sqrt(np.clip(np.linalg.eigvalsh(b.T @ b), 0, None))[::-1]
+    np.testing.assert_allclose(f["sigma"], ref, rtol=1e-9, atol=1e-9)
+
+
+@pytest.mark.parametrize("method", ["full", "arpack"])
+def test_svd_eckart_young(method):
+    r = np.random.default_rng(17)
+    b = r.standard_normal((80, 80)) @ np.diag(0.8 ** np.arange(80)) @ r.standard_normal((80, 80))
+    R = 6
+    f = oracle.truncated_svd(b, R, method=method)
+    s_all = np.linalg.svd(b, compute_uv=False)
+    err2 = np.linalg.norm(b - oracle.lowrank_bias(f["phi_q"], f["phi_k"])) ** 2
+    assert err2 == pytest.approx(np.sum(s_all[R:] ** 2), rel=1e-8)
+    assert f["energy"] == pytest.approx(np.sum(s_all[:R] ** 2) / np.sum(s_all ** 2), rel=1e-10)
+    np.testing.assert_allclose(f["sigma"][:R], s_all[:R], rtol=1e-9)
+
+
+def test_svd_exact_on_rank_r():
+    r = np.random.default_rng(18)
+    a, c = r.standard_normal((50, 4)), r.standard_normal((50, 4))
+    b = a @ c.T
+    f = oracle.truncated_svd(b, 4)
+    np.testing.assert_allclose(oracle.lowrank_bias(f["phi_q"], f["phi_k"]), b, rtol=0, atol=1e-12)
+    assert f["energy"] == pytest.approx(1.0, abs=1e-14)
+
+
+def test_svd_recovers_alibi_and_sandwich_rank():
+    """The exact biases have the rank their factors claim: 2 for ALiBi, C for Sandwich."""
+    b = oracle.alibi_bias(oracle.alibi_slopes(4), 64)[1]
+    f = oracle.truncated_svd(b, 2)
+    assert f["sigma"][2] < 1e-12 * f["sigma"][0]
+    sw = oracle.sandwich_bias(256, 4)
+    f = oracle.truncated_svd(sw, 4)
+    assert f["sigma"][4] < 1e-10 * f["sigma"][0]
+
+
+# ----------------------------------------------------------- synth inputs ----
+def test_synth_vision_bias_structure():
+    w = synth.workload("vision_svd", grid=8, B=1, H=2)
+    inp = synth.make_inputs(w)
+    b = inp["bias_src"]
+    assert b.shape == (2, 64, 64)
+    # b_ij depends only on (y_i - y_j, x_i - x_j): translating both tokens leaves it unchanged
+    G = 8
+    tok = lambda y, x: G * y + x
+    assert b[0, tok(1, 1), tok(2, 3)] == b[0, tok(4, 2), tok(5, 4)]
+    # the diagonal is t_h[0,0] = 4 + 0.05 * noise
+    assert np.allclose(np.diagonal(b[1]), np.diagonal(b[1])[0])
+    assert abs(np.diagonal(b[1])[0] - 4.0) < 0.5
+
+
+def test_synth_rounding_is_representable():
+    w = synth.workload("sandwich", B=1, H=1, N=64)
+    q, k, v = synth.draw_qkv(w, synth.rng_for(w))
+    np.testing.assert_array_equal(synth.round_to(q, "bf16"), q)
+    # bf16 keeps 8 significant bits: every value times 2^k is an integer below 2^8
+    m, _ = np.frexp(q[q != 0])
+    assert np.all(np.abs(m * 256) == np.round(np.abs(m * 256)))
