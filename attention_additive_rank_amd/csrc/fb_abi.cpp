@@ -1,0 +1,236 @@
+// C ABI of libflashbias: argument validation and dispatch.  Every check runs
+// before any launch; nothing here allocates device memory.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <new>
+
+#include "fb_internal.h"
+
+namespace fb {
+
+fb_status svd_factors(const double* A, int N, int R, uint64_t seed, double* phq, double* phk, double* sigma,
+                      double* energy);
+
+namespace {
+thread_local char g_err[512] = "";
+
+int esize(fb_dtype t) { return t == FB_F32 ? 4 : 2; }
+bool known_dtype(fb_dtype t) { return t == FB_F32 || t == FB_BF16 || t == FB_F16; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define FB_FAIL(code, ...)      \
+  do {                          \
+    set_error(__VA_ARGS__);     \
+    return code;                \
+  } while (0)
+
+// Strides of a [B][H][N][X] tensor whose rows start on 16-byte boundaries.
+bool rows_aligned(const int64_t s[3], int es) {
+  const int64_t ce = 16 / es;
+  return s[0] % ce == 0 && s[1] % ce == 0 && s[2] % ce == 0;
+}
+
+fb_status check_common(const fb_attn_args* a, const char* fn) {
+  if (!a) FB_FAIL(FB_EINVAL, "%s: null argument struct", fn);
+  if (a->B < 0 || a->H < 0 || a->N < 0) FB_FAIL(FB_EINVAL, "%s: negative size", fn);
+  if (!known_dtype(a->dt)) FB_FAIL(FB_EUNSUPPORTED, "%s: unknown dtype %d", fn, (int)a->dt);
+  if (a->D != 16 && a->D != 32 && a->D != 64 && a->D != 128)
+    FB_FAIL(FB_EUNSUPPORTED, "%s: head dim %d not in {16,32,64,128}", fn, a->D);
+  if ((int64_t)a->B * a->H * a->N == 0) return FB_OK;
+  if (!a->q || !a->k || !a->v || !a->o) FB_FAIL(FB_EINVAL, "%s: null q/k/v/o", fn);
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
+    FB_FAIL(FB_EINVAL, "%s: q/k/v/o must be 16-byte aligned", fn);
+  const int es = esize(a->dt);
+  const int64_t* st[4] = {a->sq, a->sk, a->sv, a->so};
+  const char* nm[4] = {"q", "k", "v", "o"};
+  for (int i = 0; i < 4; ++i) {
+    if (st[i][0] < 0 || st[i][1] < 0 || st[i][2] < 0) FB_FAIL(FB_EINVAL, "%s: negative %s stride", fn, nm[i]);
+    if (!rows_aligned(st[i], es)) FB_FAIL(FB_EINVAL, "%s: %s strides must be multiples of %d elements", fn, nm[i], 16 / es);
+    if (a->N > 1 && st[i][2] < a->D) FB_FAIL(FB_EINVAL, "%s: %s row stride < D", fn, nm[i]);
+  }
+  if (a->lse && ((uintptr_t)a->lse & 3u)) FB_FAIL(FB_EINVAL, "%s: lse must be 4-byte aligned", fn);
+  if (!std::isfinite(a->scale)) FB_FAIL(FB_EINVAL, "%s: scale must be finite", fn);
+  const int64_t nqb = (a->N + 127) / 128;
+  if (nqb * a->H * a->B > 0x7fffffffLL) FB_FAIL(FB_EUNSUPPORTED, "%s: grid too large", fn);
+  return FB_OK;
+}
+
+AttnParams base_params(const fb_attn_args* a) {
+  AttnParams p{};
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.o = a->o;
+  p.lse = a->lse;
+  for (int i = 0; i < 3; ++i) {
+    p.sq[i] = a->sq[i];
+    p.sk[i] = a->sk[i];
+    p.sv[i] = a->sv[i];
+    p.so[i] = a->so[i];
+  }
+  p.B = a->B;
+  p.H = a->H;
+  p.N = a->N;
+  p.causal = a->causal ? 1 : 0;
+  p.scale = a->scale;
+  p.nqb = (a->N + 127) / 128;
+  return p;
+}
+
+}  // namespace
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+}  // namespace fb
+
+using namespace fb;
+
+extern "C" {
+
+const char* fb_status_str(fb_status st) {
+  switch (st) {
+    case FB_OK: return "FB_OK";
+    case FB_EINVAL: return "FB_EINVAL: invalid argument";
+    case FB_EUNSUPPORTED: return "FB_EUNSUPPORTED: unsupported configuration";
+    case FB_EHIP: return "FB_EHIP: HIP runtime error";
+    case FB_ENOMEM: return "FB_ENOMEM: out of host memory";
+  }
+  return "unknown fb_status";
+}
+
+const char* fb_last_error(void) { return g_err; }
+
+fb_status fb_make_factors(fb_bias_kind kind, int H, int N, int C, const double* slopes_host, fb_dtype out_dt,
+                          int split, void* phi_q, void* phi_k, int R_pad, int* R_used, hipStream_t stream) {
+  const char* fn = "fb_make_factors";
+  if (kind != FB_ALIBI && kind != FB_SANDWICH) FB_FAIL(FB_EINVAL, "%s: unknown bias kind", fn);
+  if (!known_dtype(out_dt)) FB_FAIL(FB_EINVAL, "%s: unknown dtype", fn);
+  if (H < 1 || N < 1) FB_FAIL(FB_EINVAL, "%s: H and N must be >= 1", fn);
+  if (kind == FB_SANDWICH && (C < 2 || C % 2)) FB_FAIL(FB_EINVAL, "%s: Sandwich needs an even C >= 2", fn);
+  if (split < 1 || split > 3) FB_FAIL(FB_EINVAL, "%s: split must be 1, 2 or 3", fn);
+  if (kind == FB_ALIBI && slopes_host && H > kMaxSlopes)
+    FB_FAIL(FB_EUNSUPPORTED, "%s: explicit slopes limited to %d heads", fn, kMaxSlopes);
+  const int r_nat = kind == FB_ALIBI ? 2 : C;
+  const int used = r_nat * split * (split + 1) / 2;
+  if (R_used) *R_used = used;
+  if (R_pad < used) FB_FAIL(FB_EINVAL, "%s: R_pad %d < %d columns needed", fn, R_pad, used);
+  if (!phi_q || !phi_k) FB_FAIL(FB_EINVAL, "%s: null factor pointer", fn);
+  if (!aligned16(phi_q) || !aligned16(phi_k)) FB_FAIL(FB_EINVAL, "%s: factor pointers must be 16-byte aligned", fn);
+  if ((int64_t)H * N * R_pad > (int64_t)1 << 40) FB_FAIL(FB_EUNSUPPORTED, "%s: too large", fn);
+  return launch_make_factors(kind, H, N, C, kind == FB_ALIBI ? slopes_host : nullptr, out_dt, split, phi_q,
+                             phi_k, R_pad, r_nat, stream);
+}
+
+fb_status fb_make_dense_bias(fb_bias_kind kind, int H, int N, int C, const double* slopes_host, fb_dtype out_dt,
+                             void* bias, int64_t head_stride, int64_t row_stride, hipStream_t stream) {
+  const char* fn = "fb_make_dense_bias";
+  if (kind != FB_ALIBI && kind != FB_SANDWICH) FB_FAIL(FB_EINVAL, "%s: unknown bias kind", fn);
+  if (!known_dtype(out_dt)) FB_FAIL(FB_EINVAL, "%s: unknown dtype", fn);
+  if (H < 1 || N < 1) FB_FAIL(FB_EINVAL, "%s: H and N must be >= 1", fn);
+  if (kind == FB_SANDWICH && (C < 2 || C % 2)) FB_FAIL(FB_EINVAL, "%s: Sandwich needs an even C >= 2", fn);
+  if (!bias) FB_FAIL(FB_EINVAL, "%s: null bias", fn);
+  if (((uintptr_t)bias % esize(out_dt)) != 0) FB_FAIL(FB_EINVAL, "%s: misaligned bias", fn);
+  if (row_stride < N) FB_FAIL(FB_EINVAL, "%s: row_stride < N", fn);
+  if (H > 1 && head_stride < (int64_t)N * row_stride) FB_FAIL(FB_EINVAL, "%s: head_stride too small", fn);
+  if (kind == FB_ALIBI && slopes_host && H > kMaxSlopes)
+    FB_FAIL(FB_EUNSUPPORTED, "%s: explicit slopes limited to %d heads", fn, kMaxSlopes);
+  return launch_make_dense_bias(kind, H, N, C, kind == FB_ALIBI ? slopes_host : nullptr, out_dt, bias,
+                                head_stride, row_stride, stream);
+}
+
+fb_status fb_svd_factors(const double* bias, int N, int R, uint64_t seed, double* phi_q, double* phi_k,
+                         double* sigma, double* energy) {
+  const char* fn = "fb_svd_factors";
+  if (!bias || !phi_q || !phi_k) FB_FAIL(FB_EINVAL, "%s: null pointer", fn);
+  if (N < 1 || R < 1 || R > N) FB_FAIL(FB_EINVAL, "%s: need 1 <= R <= N", fn);
+  try {
+    return svd_factors(bias, N, R, seed, phi_q, phi_k, sigma, energy);
+  } catch (const std::bad_alloc&) {
+    FB_FAIL(FB_ENOMEM, "%s: out of host memory", fn);
+  } catch (...) {
+    FB_FAIL(FB_EINVAL, "%s: internal error", fn);
+  }
+}
+
+fb_status fb_attn_fwd_lowrank(const fb_attn_args* a, const void* phi_q, const void* phi_k, fb_dtype phi_dt,
+                              int R, const int64_t sphi_q[3], const int64_t sphi_k[3], hipStream_t stream) {
+  const char* fn = "fb_attn_fwd_lowrank";
+  fb_status st = check_common(a, fn);
+  if (st != FB_OK) return st;
+  if (R < 0) FB_FAIL(FB_EINVAL, "%s: negative R", fn);
+  const int maxR = a->dt == FB_F32 ? 32 : 128;
+  if (R > maxR) FB_FAIL(FB_EUNSUPPORTED, "%s: R = %d above the limit %d", fn, R, maxR);
+  if (R > 0) {
+    if (!known_dtype(phi_dt)) FB_FAIL(FB_EUNSUPPORTED, "%s: unknown factor dtype", fn);
+    if ((a->dt == FB_F32) != (phi_dt == FB_F32) || (a->dt == FB_F16 && phi_dt != FB_F16))
+      FB_FAIL(FB_EUNSUPPORTED, "%s: factor dtype does not match the q/k/v dtype", fn);
+  }
+  if ((int64_t)a->B * a->H * a->N == 0) return FB_OK;
+  AttnParams p = base_params(a);
+  int RP = 0;
+  if (R > 0) {
+    if (!phi_q || !phi_k || !sphi_q || !sphi_k) FB_FAIL(FB_EINVAL, "%s: null factor pointer or strides", fn);
+    for (int i = 0; i < 3; ++i)
+      if (sphi_q[i] < 0 || sphi_k[i] < 0) FB_FAIL(FB_EINVAL, "%s: negative factor stride", fn);
+    if (a->N > 1 && (sphi_q[2] < R || sphi_k[2] < R)) FB_FAIL(FB_EINVAL, "%s: factor row stride < R", fn);
+    const int es = esize(phi_dt);
+    if (((uintptr_t)phi_q % es) || ((uintptr_t)phi_k % es)) FB_FAIL(FB_EINVAL, "%s: misaligned factors", fn);
+    p.phq = phi_q;
+    p.phk = phi_k;
+    for (int i = 0; i < 3; ++i) {
+      p.spq[i] = sphi_q[i];
+      p.spk[i] = sphi_k[i];
+    }
+    p.R = R;
+    p.phq_vec = aligned16(phi_q) && rows_aligned(sphi_q, es);
+    p.phk_vec = aligned16(phi_k) && rows_aligned(sphi_k, es);
+    const int step = a->dt == FB_F32 ? 4 : 16;
+    RP = (R + step - 1) / step * step;
+    if (a->dt == FB_F32) { if (RP == 12) RP = 16; else if (RP > 16 && RP < 32) RP = 32; }
+    else { if (RP == 48) RP = 64; else if (RP > 64) RP = 128; }
+  }
+  const fb_dtype aux = R > 0 ? phi_dt : a->dt;
+  switch (a->D) {
+    case 16: st = launch_attention_d16(0, a->dt, aux, RP, p, stream); break;
+    case 32: st = launch_attention_d32(0, a->dt, aux, RP, p, stream); break;
+    case 64: st = launch_attention_d64(0, a->dt, aux, RP, p, stream); break;
+    default: st = launch_attention_d128(0, a->dt, aux, RP, p, stream); break;
+  }
+  if (st == FB_EUNSUPPORTED) set_error("%s: no kernel for this dtype / rank combination", fn);
+  return st;
+}
+
+fb_status fb_attn_fwd_densebias(const fb_attn_args* a, const void* bias, fb_dtype bias_dt, const int64_t sbias[3],
+                                hipStream_t stream) {
+  const char* fn = "fb_attn_fwd_densebias";
+  fb_status st = check_common(a, fn);
+  if (st != FB_OK) return st;
+  if (!known_dtype(bias_dt)) FB_FAIL(FB_EUNSUPPORTED, "%s: unknown bias dtype", fn);
+  if (bias_dt != a->dt) FB_FAIL(FB_EUNSUPPORTED, "%s: bias dtype must equal the q/k/v dtype", fn);
+  if ((int64_t)a->B * a->H * a->N == 0) return FB_OK;
+  if (!bias || !sbias) FB_FAIL(FB_EINVAL, "%s: null bias or strides", fn);
+  if (sbias[0] < 0 || sbias[1] < 0 || sbias[2] < 0) FB_FAIL(FB_EINVAL, "%s: negative bias stride", fn);
+  if (a->N > 1 && sbias[2] < a->N) FB_FAIL(FB_EINVAL, "%s: bias row stride < N", fn);
+  const int es = esize(bias_dt);
+  if ((uintptr_t)bias % es) FB_FAIL(FB_EINVAL, "%s: misaligned bias", fn);
+  AttnParams p = base_params(a);
+  p.bias = bias;
+  for (int i = 0; i < 3; ++i) p.sb[i] = sbias[i];
+  p.bias_vec = aligned16(bias) && rows_aligned(sbias, es);
+  switch (a->D) {
+    case 16: st = launch_attention_d16(1, a->dt, bias_dt, 0, p, stream); break;
+    case 32: st = launch_attention_d32(1, a->dt, bias_dt, 0, p, stream); break;
+    case 64: st = launch_attention_d64(1, a->dt, bias_dt, 0, p, stream); break;
+    default: st = launch_attention_d128(1, a->dt, bias_dt, 0, p, stream); break;
+  }
+  if (st == FB_EUNSUPPORTED) set_error("%s: no kernel for this dtype combination", fn);
+  return st;
+}
+
+}  // extern "C"

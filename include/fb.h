@@ -1,0 +1,206 @@
+/*
+ * fb.h -- C ABI of libflashbias: the forward pass of attention with an additive
+ * bias on AMD Instinct MI355X (gfx950), with the bias given either as a
+ * low-rank product b = phi_q phi_k^T (FlashBias) or as a dense N x N tensor.
+ *
+ * Source of the method: "FlashBias: Fast Computation of Attention with Bias"
+ * (Wu et al.; abstract and the authors' OpenReview rebuttal).
+ *
+ *   O = softmax(s * Q K^T + b) V,  b[i,j] = sum_r phi_q[i,r] * phi_k[j,r]
+ *
+ * Attention with bias adds a bias matrix to the query-key scores (abstract).
+ * When b has rank R, the factors are concatenated to the queries and keys,
+ * Q' = [Q*s, phi_q], K' = [K, phi_k], and the attention runs on Q', K' with no
+ * N x N bias read from HBM (rebuttal, answer to Reviewer UJUf, Q2: concatenate
+ * the decomposed factor functions with queries and keys and run FlashAttention;
+ * answer to Reviewer BRmd, Q3: factors of #heads x N x R instead of a
+ * #heads x N x N bias).
+ *
+ * Conventions shared by every entry point
+ *   - Every call returns fb_status; no C++ exception crosses the ABI.
+ *   - Device pointers are caller-allocated (e.g. by PyTorch) and stay owned by
+ *     the caller.  The library never allocates or frees device memory and
+ *     keeps no workspace.  Host buffers are read/written only during the call.
+ *   - Argument validation is synchronous and happens before any launch; on a
+ *     validation error nothing is launched and no output is touched.
+ *   - Kernels are launched asynchronously on the caller's `stream`
+ *     (NULL = the null stream); there is no implicit synchronisation.  A HIP
+ *     launch error is reported as FB_EHIP.  Errors raised later by the kernel
+ *     surface at the caller's next synchronisation.
+ *   - Strides are in ELEMENTS.  For a tensor "[B][H][N][X] with strides
+ *     s[3]", element (b,h,n,x) lives at base + b*s[0] + h*s[1] + n*s[2] + x: the
+ *     last axis is contiguous.  A stride of 0 broadcasts along that axis.
+ *   - NaN / Inf inputs are not checked; they propagate to the outputs.
+ *   - fb_last_error() returns a short, thread-local description of the last
+ *     non-FB_OK status raised in the calling thread.
+ *   - The library is stateless and thread-safe.
+ */
+#ifndef FLASHBIAS_FB_H
+#define FLASHBIAS_FB_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum {
+  FB_OK = 0,
+  FB_EINVAL = 1,        /* null pointer, bad size, misalignment, bad stride */
+  FB_EUNSUPPORTED = 2,  /* valid request outside what the kernels implement */
+  FB_EHIP = 3,          /* a HIP runtime call or launch failed */
+  FB_ENOMEM = 4         /* host allocation failed (fb_svd_factors only) */
+} fb_status;
+
+typedef enum { FB_F32 = 0, FB_BF16 = 1, FB_F16 = 2 } fb_dtype;
+
+typedef enum {
+  FB_ALIBI = 0,     /* b[h,i,j] = m_h (j - i); rank 2 */
+  FB_SANDWICH = 1   /* b[i,j] = sum_{k=1}^{C/2} cos((i-j) / 10000^(2k/C)); rank C */
+} fb_bias_kind;
+
+/* Human-readable name of a status code (static string). */
+const char* fb_status_str(fb_status st);
+
+/* Thread-local description of the last error raised in this thread ("" if none). */
+const char* fb_last_error(void);
+
+/*
+ * fb_make_factors -- exact factors of a closed-form bias, generated on the GPU.
+ *
+ * ALiBi (rebuttal, answer to Reviewer BRmd, Q2: slopes of shape #heads; the
+ * factor tiles are Block_q x 2 and Block_k x 2): phi_q(i) = [1, i],
+ * phi_k(j) = [m_h * j, -m_h], so phi_q phi_k^T = m_h (j - i).
+ * Sandwich (rebuttal, answer to Reviewer UJUf, Q1 (1)-(2)):
+ * phi(i) = [cos(i w_1), sin(i w_1), ..., cos(i w_{C/2}), sin(i w_{C/2})],
+ * w_k = 10000^(-2k/C), phi_q = phi_k = phi; phi phi^T is the Sandwich bias.
+ *
+ *   kind        FB_ALIBI or FB_SANDWICH
+ *   H, N        heads and sequence length (>= 1)
+ *   C           Sandwich channel count (even, >= 2); ignored for ALiBi
+ *   slopes_host ALiBi: host array [H] of slopes, or NULL for m_h = 2^(-8(h+1)/H);
+ *               ignored for Sandwich
+ *   out_dt      element type of phi_q / phi_k
+ *   split       1, 2 or 3: each factor value x is written as `split` pieces of
+ *               out_dt, x ~ x_0 + x_1 + ..., x_0 = rn(x), x_1 = rn(x - x_0), ...
+ *               Each natural column c becomes the columns of the piece pairs
+ *               (a, b) with a + b < split (phi_q gets piece a, phi_k piece b),
+ *               in the order (0,0), (0,1), (1,0), (0,2), (1,1), (2,0); so
+ *               phi_q' phi_k'^T equals phi_q phi_k^T up to the dropped
+ *               higher-order piece products.  split = 1 is plain rounding.
+ *   phi_q,phi_k device, caller-allocated, [H][N][R_pad] of out_dt, contiguous
+ *   R_pad       row length; must be >= R_used.  Columns R_used..R_pad-1 are
+ *               written as zero.
+ *   R_used      host out (may be NULL): natural rank x split(split+1)/2
+ *               (ALiBi 2, Sandwich C, times 1, 3 or 6)
+ * The values are computed in fp64 on the device and rounded to nearest even.
+ * Errors: FB_EINVAL (null pointers, H or N < 1, odd or < 2 C for Sandwich,
+ * split outside 1..3, R_pad < R_used, 16-byte-misaligned phi pointers);
+ * FB_EHIP.
+ */
+fb_status fb_make_factors(fb_bias_kind kind, int H, int N, int C, const double* slopes_host,
+                          fb_dtype out_dt, int split, void* phi_q, void* phi_k, int R_pad,
+                          int* R_used, hipStream_t stream);
+
+/*
+ * fb_make_dense_bias -- the same closed-form biases, materialised as a dense
+ * [H][N][N] tensor (the input of the dense-bias baseline, fb_attn_fwd_densebias).
+ * Computed in fp64 from the defining formula (ALiBi m_h (j - i); Sandwich the
+ * sum of C/2 cosines), rounded to nearest even into out_dt.
+ *   bias        device, [H][N][N] with element strides head_stride, row_stride
+ *               (last axis contiguous)
+ * Errors: FB_EINVAL (null bias, H or N < 1, C odd or < 2 for Sandwich,
+ * row_stride < N, head_stride < N*row_stride when H > 1); FB_EHIP.
+ */
+fb_status fb_make_dense_bias(fb_bias_kind kind, int H, int N, int C, const double* slopes_host,
+                             fb_dtype out_dt, void* bias, int64_t head_stride, int64_t row_stride,
+                             hipStream_t stream);
+
+/*
+ * fb_svd_factors -- truncated SVD factors of one general (e.g. learned) bias,
+ * computed on the host; the pages do this offline, once per layer and head
+ * (rebuttal, answer to Reviewer xU4x, Q6; abstract: fast-accurate
+ * approximation for general biases).
+ *
+ *   bias        host, [N][N] fp64, row-major (read only)
+ *   N, R        1 <= R <= N
+ *   seed        seed of the randomized range finder (results are deterministic
+ *               for a given seed)
+ *   phi_q,phi_k host out, [N][R] fp64: U_R sqrt(S_R) and V_R sqrt(S_R), so that
+ *               phi_q phi_k^T is the best rank-R approximation of bias
+ *   sigma       host out [R] or NULL: the R largest singular values, descending
+ *   energy      host out or NULL: sum_{r<R} sigma_r^2 / ||bias||_F^2, the
+ *               retained energy (rebuttal, answer to Reviewer Bp2x, Q2: heads
+ *               are chosen to keep 95% energy)
+ * Method: randomized subspace iteration (Halko, Martinsson, Tropp 2011) with
+ * Householder QR re-orthonormalisation, iterated until the top-R singular
+ * values settle, followed by a one-sided Jacobi SVD of the small projected
+ * matrix.  Temporary host memory is freed before return.
+ * Errors: FB_EINVAL (null pointers, N < 1, R < 1 or R > N); FB_ENOMEM.
+ */
+fb_status fb_svd_factors(const double* bias, int N, int R, uint64_t seed, double* phi_q,
+                         double* phi_k, double* sigma, double* energy);
+
+/* Arguments shared by both attention entry points. */
+typedef struct {
+  int B, H, N, D;      /* batch, heads, sequence length (queries = keys), head dim */
+  fb_dtype dt;         /* element type of Q, K, V and O: FB_F32, FB_BF16 or FB_F16 */
+  int causal;          /* nonzero: query i attends to keys j <= i */
+  float scale;         /* s, the score scale (callers usually pass 1/sqrt(D)) */
+  const void* q;       /* device [B][H][N][D], strides sq */
+  const void* k;       /* device [B][H][N][D], strides sk */
+  const void* v;       /* device [B][H][N][D], strides sv */
+  void* o;             /* device [B][H][N][D], strides so (output) */
+  int64_t sq[3], sk[3], sv[3], so[3];
+  float* lse;          /* device [B][H][N] contiguous fp32, or NULL: m + ln(l), the
+                          natural log-sum-exp of each row's biased scores */
+} fb_attn_args;
+
+/*
+ * fb_attn_fwd_lowrank -- O = softmax(s Q K^T + phi_q phi_k^T) V in one fused
+ * kernel: the augmented contraction [Q*s, phi_q] [K, phi_k]^T feeds an online
+ * softmax and the P V product, tile by tile; the N x N bias is never formed.
+ *
+ *   a            shared arguments (see fb_attn_args)
+ *   phi_q, phi_k device [B][H][N][R] (strides sphi_q / sphi_k; 0 broadcasts a
+ *                factor over batch and/or heads).  May be NULL when R == 0.
+ *   phi_dt       FB_F32 when a->dt is FB_F32; FB_BF16 or FB_F16 when a->dt is
+ *                FB_BF16 or FB_F16 (the factor columns then run through their own
+ *                matrix-core chain in phi_dt, accumulating into the same fp32 scores)
+ *   R            number of factor columns, 0 <= R <= 128 (16-bit) or <= 32 (fp32);
+ *                R == 0 is plain attention.  Columns are zero-padded internally to
+ *                the matrix-core step (16 for 16-bit types, 4 for fp32).
+ * Numerics: fp32 accumulation; Q*s is rounded once to dt; the probabilities P
+ * are rounded to dt (RNE) before the P V product; O is written in dt.
+ * Alignment: q, k, v, o 16-byte aligned and their strides multiples of
+ * 16 bytes / element size.  phi rows may be unaligned (slower loads).
+ * Errors: FB_EINVAL (null pointers, negative sizes, misalignment, row strides
+ * too small); FB_EUNSUPPORTED (D not in {16,32,64,128}, R above the limit, a
+ * dtype pair not listed above); FB_EHIP.  B*H*N == 0 is a no-op returning FB_OK.
+ */
+fb_status fb_attn_fwd_lowrank(const fb_attn_args* a, const void* phi_q, const void* phi_k,
+                              fb_dtype phi_dt, int R, const int64_t sphi_q[3],
+                              const int64_t sphi_k[3], hipStream_t stream);
+
+/*
+ * fb_attn_fwd_densebias -- O = softmax(s Q K^T + b) V with b read as a dense
+ * tensor: each (query-tile, key-tile) pair streams its bias tile from HBM, the
+ * quadratic IO of attention with bias (abstract; rebuttal, answer to Reviewer
+ * BRmd, Q3).  The in-house baseline the low-rank kernel is measured against.
+ *
+ *   bias     device [B][H][N][N] with strides sbias (b, h, i); the last axis (j)
+ *            contiguous; sbias[0] and/or sbias[1] may be 0 (shared bias)
+ *   bias_dt  FB_F32 when a->dt is FB_F32; FB_BF16 or FB_F16 otherwise
+ * Numerics and alignment as fb_attn_fwd_lowrank; the bias is added in fp32.
+ * Errors: as fb_attn_fwd_lowrank; FB_EINVAL for a null bias or sbias[2] < N.
+ */
+fb_status fb_attn_fwd_densebias(const fb_attn_args* a, const void* bias, fb_dtype bias_dt,
+                                const int64_t sbias[3], hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FLASHBIAS_FB_H */

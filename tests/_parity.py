@@ -1,0 +1,167 @@
+"""Helpers shared by the GPU parity tests and smoke(): run one workload through the
+HIP path (libflashbias) and through the fp64 oracle on the same seeded inputs."""
+from __future__ import annotations
+
+import math
+import sys
+from typing import Optional
+
+import numpy as np
+
+import oracle
+import synth
+
+# (max-abs, relative L2) bars of the parity contract
+TOL = {"f32": (1e-4, 1e-4), "bf16": (2e-2, 5e-3), "f16": (2e-2, 5e-3)}
+
+
+def say(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def tdtype(name: str):
+    import torch
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[name]
+
+
+def round_exact(x: np.ndarray, dtype: str) -> np.ndarray:
+    """fp64 -> dtype with a single round-to-nearest-even (torch's fp64 casts go through fp32
+    and can round twice).  Values are returned as fp64."""
+    prec, emin = {"f32": (24, -126), "bf16": (8, -126), "f16": (11, -14)}[dtype]
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    ex = np.maximum(e - 1, emin)
+    q = np.ldexp(1.0, ex - prec + 1)
+    return np.where(x == 0, x, np.rint(x / q) * q)
+
+
+def to_dev(x: np.ndarray, dtype: str, device="cuda:0"):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).to(tdtype(dtype)).to(device)
+
+
+def to_np(t) -> np.ndarray:
+    return t.detach().to("cpu").double().numpy()
+
+
+def errors(got: np.ndarray, ref: np.ndarray):
+    d = got - ref
+    return float(np.abs(d).max()), float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-300))
+
+
+def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    ma, rl = errors(got, ref)
+    amax, rmax = TOL[dtype]
+    say(f"  {what}: max-abs {ma:.3e} (<= {amax}), rel-L2 {rl:.3e} (<= {rmax})")
+    assert ma <= amax and rl <= rmax, f"{what}: max-abs {ma:.3e}, rel-L2 {rl:.3e}"
+    return ma, rl
+
+
+# ------------------------------------------------------------------ factors --
+def factor_plan(w: synth.Workload):
+    """Factor dtype and split used for each exact-bias workload on the GPU path.
+
+    ALiBi in 16-bit: the factor m_h*j reaches ~1300 at N=2048, so one f16 value
+    loses ~0.5 absolute; two f16 pieces per value (split=2) keep 22 bits.
+    Sandwich: f16 factors (|phi| <= 1, 11 bits).  fp32 workloads: fp32 factors."""
+    if w.dtype == "f32":
+        return "f32", 1
+    if w.bias == "alibi":
+        return "f16", 2
+    return "f16", 1
+
+
+def exact_bias_oracle(w: synth.Workload):
+    """Callable (b, h) -> [N, N] fp64 closed-form bias, from the oracle."""
+    if w.bias == "alibi":
+        m = oracle.alibi_slopes(w.H)
+        cache = {}
+
+        def f(b, h):
+            if h not in cache:
+                cache.clear()
+                cache[h] = oracle.alibi_bias(m[h:h + 1], w.N)[0]
+            return cache[h]
+        return f
+    if w.bias == "sandwich":
+        bb = oracle.sandwich_bias(w.N, w.C)
+        return lambda b, h: bb
+    raise ValueError(w.bias)
+
+
+def device_exact_factors(w: synth.Workload, device="cuda:0"):
+    """fb_make_factors on the GPU for an exact-bias workload; returns (phi_q, phi_k) views
+    broadcastable to [B, H, N, R]."""
+    import attention_additive_rank_amd as fb
+    dt, split = factor_plan(w)
+    if w.bias == "alibi":
+        pq, pk, r = fb.fb_make_factors("alibi", w.H, w.N, dtype=tdtype(dt), split=split, device=device)
+        return pq, pk
+    pq, pk, r = fb.fb_make_factors("sandwich", 1, w.N, C=w.C, dtype=tdtype(dt), split=split, device=device)
+    return pq, pk
+
+
+def oracle_svd_factors(w: synth.Workload, bias_src: np.ndarray, phi_dtype: str = "f16"):
+    """Per-head truncated-SVD factors from the oracle, rounded to the factor dtype
+    (the kernel and the oracle then use the very same factor values)."""
+    method = "full" if w.N <= 1024 else "arpack"
+    pq = np.empty((w.H, w.N, w.R))
+    pk = np.empty((w.H, w.N, w.R))
+    energy = []
+    for h in range(w.H):
+        f = oracle.truncated_svd(bias_src[h], w.R, method=method)
+        pq[h], pk[h] = f["phi_q"], f["phi_k"]
+        energy.append(f["energy"])
+    return synth.round_to(pq, phi_dtype), synth.round_to(pk, phi_dtype), energy
+
+
+# ---------------------------------------------------------------- workloads --
+class Case:
+    """One workload prepared for both sides."""
+
+    def __init__(self, w: synth.Workload, device="cuda:0", rows: Optional[np.ndarray] = None):
+        self.w = w
+        self.device = device
+        self.rows = rows
+        inp = synth.make_inputs(w)
+        self.q, self.k, self.v = inp["q"], inp["k"], inp["v"]
+        self.qd, self.kd, self.vd = (to_dev(x, w.dtype, device) for x in (self.q, self.k, self.v))
+        if w.bias in ("alibi", "sandwich"):
+            self.bias_ref = exact_bias_oracle(w)
+            self.phq, self.phk = device_exact_factors(w, device)
+            self.energy = None
+        else:
+            pq, pk, self.energy = oracle_svd_factors(w, inp["bias_src"], "f16")
+            self.bias_full = inp["bias_src"]
+            self.pq_np, self.pk_np = pq, pk
+            self.bias_ref = lambda b, h: oracle.lowrank_bias(pq[h], pk[h])
+            self.phq, self.phk = to_dev(pq, "f16", device), to_dev(pk, "f16", device)
+
+    def run_lowrank(self, **kw):
+        import attention_additive_rank_amd as fb
+        return fb.fb_attn_fwd_lowrank(self.qd, self.kd, self.vd, self.phq, self.phk, causal=self.w.causal, **kw)
+
+    def reference(self, rows=None, bh=None):
+        """Oracle output for all (b, h) or the listed pairs, restricted to `rows`."""
+        w = self.w
+        rows = self.rows if rows is None else rows
+        if bh is None:
+            o, lse = oracle.attention(self.q, self.k, self.v, bias=self.bias_ref, causal=w.causal, rows=rows)
+            return o, lse
+        outs, lses = [], []
+        for (b, h) in bh:
+            o, l = oracle.attention(self.q[b:b + 1, h:h + 1], self.k[b:b + 1, h:h + 1], self.v[b:b + 1, h:h + 1],
+                                    bias=lambda _b, _h: self.bias_ref(b, h), causal=w.causal, rows=rows)
+            outs.append(o[0, 0])
+            lses.append(l[0, 0])
+        return np.stack(outs), np.stack(lses)
+
+
+def sample_rows(N: int, n: int, seed: int = 0) -> np.ndarray:
+    """A fixed sample of query rows: the first and last rows, tile edges and random rows."""
+    r = np.random.default_rng(seed)
+    fixed = [0, 1, 31, 32, 63, 64, 127, 128, N // 2, N - 2, N - 1]
+    extra = r.choice(N, size=min(N, n), replace=False)
+    return np.unique(np.clip(np.concatenate([fixed, extra]), 0, N - 1))

@@ -1,0 +1,217 @@
+"""CPU checks of the C-ABI library: it loads, exports every entry point that
+include/fb.h declares, rejects bad arguments before any launch, and its host
+SVD agrees with the oracle's.  No GPU kernel is launched here: every call below
+either fails validation (which runs before any HIP call) or is host-only."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import attention_additive_rank_amd as fb
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "fb.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fb_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for n in ["fb_make_factors", "fb_attn_fwd_lowrank", "fb_attn_fwd_densebias", "fb_svd_factors",
+              "fb_status_str", "fb_make_dense_bias", "fb_last_error"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fb.load()
+    for n in _declared_functions():
+        assert hasattr(lib, n), n
+    out = os.popen(f"nm -D --defined-only {fb.library_path}").read()
+    for n in _declared_functions():
+        assert re.search(rf"\bT {n}\b", out), n
+
+
+def test_status_strings():
+    assert fb.fb_status_str(0) == "FB_OK"
+    for s in range(1, 5):
+        assert fb.fb_status_str(s).startswith("FB_E")
+
+
+# ------------------------------------------------------- validation paths ----
+FAKE = 0x10000          # 16-byte-aligned address never dereferenced: validation fails first
+
+
+def _args(**kw):
+    a = fb._AttnArgs()
+    a.B, a.H, a.N, a.D = kw.get("B", 1), kw.get("H", 1), kw.get("N", 64), kw.get("D", 64)
+    a.dt = kw.get("dt", fb.FB_BF16)
+    a.causal = 0
+    a.scale = kw.get("scale", 0.125)
+    a.q = kw.get("q", FAKE)
+    a.k = kw.get("k", FAKE)
+    a.v = kw.get("v", FAKE)
+    a.o = kw.get("o", FAKE)
+    D = a.D
+    st = kw.get("strides", (a.H * a.N * D, a.N * D, D))
+    a.sq = fb._I64x3(*st)
+    a.sk = fb._I64x3(*st)
+    a.sv = fb._I64x3(*st)
+    a.so = fb._I64x3(*kw.get("so", st))
+    a.lse = kw.get("lse", None)
+    return a
+
+
+def _lowrank(a, R=0, phi_dt=fb.FB_BF16, pq=FAKE, pk=FAKE, s=(0, 0, 64)):
+    sp = fb._I64x3(*s)
+    return fb.load().fb_attn_fwd_lowrank(ctypes.byref(a), pq, pk, phi_dt, R, ctypes.byref(sp), ctypes.byref(sp), None)
+
+
+def _dense(a, bias=FAKE, bdt=fb.FB_BF16, s=(0, 0, 64)):
+    sb = fb._I64x3(*s)
+    return fb.load().fb_attn_fwd_densebias(ctypes.byref(a), bias, bdt, ctypes.byref(sb), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=48), fb.FB_EUNSUPPORTED),
+    (dict(D=256), fb.FB_EUNSUPPORTED),
+    (dict(dt=7), fb.FB_EUNSUPPORTED),
+    (dict(q=None), fb.FB_EINVAL),
+    (dict(o=None), fb.FB_EINVAL),
+    (dict(q=FAKE + 8), fb.FB_EINVAL),                       # misaligned
+    (dict(strides=(4096, 64, 68)), fb.FB_EINVAL),           # row stride not a multiple of 8 elements
+    (dict(strides=(4096, 64, 32)), fb.FB_EINVAL),           # row stride < D
+    (dict(strides=(4096, -64, 64)), fb.FB_EINVAL),
+    (dict(B=-1), fb.FB_EINVAL),
+    (dict(lse=FAKE + 2), fb.FB_EINVAL),
+    (dict(scale=float("nan")), fb.FB_EINVAL),
+])
+def test_attention_validation(kw, code):
+    assert _lowrank(_args(**kw)) == code
+    assert fb.fb_last_error() != ""
+    if kw.get("dt") is None:
+        assert _dense(_args(**kw)) == code
+
+
+def test_empty_inputs_are_noops():
+    # B*H*N == 0 returns before any pointer is looked at, so no launch happens
+    assert _lowrank(_args(N=0, q=None, k=None, v=None, o=None)) == fb.FB_OK
+    assert _dense(_args(B=0, q=None, k=None, v=None, o=None), bias=None) == fb.FB_OK
+
+
+@pytest.mark.parametrize("R,phi_dt,kw,code", [
+    (-1, fb.FB_BF16, {}, fb.FB_EINVAL),
+    (129, fb.FB_BF16, {}, fb.FB_EUNSUPPORTED),
+    (8, fb.FB_F32, {}, fb.FB_EUNSUPPORTED),                  # fp32 factors with bf16 q/k/v
+    (8, fb.FB_BF16, dict(pq=None), fb.FB_EINVAL),
+    (8, fb.FB_BF16, dict(s=(0, 0, 4)), fb.FB_EINVAL),       # factor row stride < R
+    (8, fb.FB_BF16, dict(pq=FAKE + 1), fb.FB_EINVAL),       # not element aligned
+])
+def test_lowrank_factor_validation(R, phi_dt, kw, code):
+    assert _lowrank(_args(), R=R, phi_dt=phi_dt, **kw) == code
+
+
+def test_lowrank_fp32_limits():
+    a = _args(dt=fb.FB_F32, D=32, strides=(2048, 1024, 32))
+    assert _lowrank(a, R=33, phi_dt=fb.FB_F32) == fb.FB_EUNSUPPORTED
+    assert _lowrank(a, R=4, phi_dt=fb.FB_BF16) == fb.FB_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("bdt,kw,code", [
+    (fb.FB_F16, {}, fb.FB_EUNSUPPORTED),                    # bias dtype must match q/k/v
+    (fb.FB_BF16, dict(bias=None), fb.FB_EINVAL),
+    (fb.FB_BF16, dict(s=(0, 0, 32)), fb.FB_EINVAL),         # row stride < N
+    (fb.FB_BF16, dict(bias=FAKE + 1), fb.FB_EINVAL),
+])
+def test_densebias_validation(bdt, kw, code):
+    assert _dense(_args(), bdt=bdt, **kw) == code
+
+
+def test_make_factors_validation():
+    lib = fb.load()
+    r = ctypes.c_int(0)
+    call = lambda kind=0, H=2, N=16, C=0, dt=fb.FB_F16, split=1, pq=FAKE, pk=FAKE, R_pad=16: \
+        lib.fb_make_factors(kind, H, N, C, None, dt, split, pq, pk, R_pad, ctypes.byref(r), None)
+    assert call(kind=5) == fb.FB_EINVAL
+    assert call(H=0) == fb.FB_EINVAL
+    assert call(kind=1, C=3) == fb.FB_EINVAL
+    assert call(split=4) == fb.FB_EINVAL
+    assert call(R_pad=1) == fb.FB_EINVAL and r.value == 2
+    assert call(split=2, R_pad=4) == fb.FB_EINVAL and r.value == 6
+    assert call(kind=1, C=64, R_pad=32) == fb.FB_EINVAL and r.value == 64
+    assert call(pq=None) == fb.FB_EINVAL
+    assert call(pq=FAKE + 2) == fb.FB_EINVAL
+
+
+def test_make_dense_bias_validation():
+    lib = fb.load()
+    call = lambda kind=0, H=2, N=16, C=0, bias=FAKE, hs=256, rs=16: \
+        lib.fb_make_dense_bias(kind, H, N, C, None, fb.FB_BF16, bias, hs, rs, None)
+    assert call(bias=None) == fb.FB_EINVAL
+    assert call(rs=8) == fb.FB_EINVAL
+    assert call(hs=100) == fb.FB_EINVAL
+    assert call(kind=1, C=0) == fb.FB_EINVAL
+
+
+def test_svd_validation():
+    lib = fb.load()
+    a = np.zeros((4, 4))
+    p = a.ctypes.data_as(fb._DP)
+    assert lib.fb_svd_factors(None, 4, 2, 0, p, p, None, None) == fb.FB_EINVAL
+    assert lib.fb_svd_factors(p, 4, 5, 0, p, p, None, None) == fb.FB_EINVAL
+    assert lib.fb_svd_factors(p, 4, 0, 0, p, p, None, None) == fb.FB_EINVAL
+
+
+# ------------------------------------------------------------- host SVD ----
+def test_host_svd_matches_oracle_on_random_decay():
+    r = np.random.default_rng(3)
+    N, R = 200, 8
+    b = r.standard_normal((N, N)) @ np.diag(0.85 ** np.arange(N)) @ r.standard_normal((N, N))
+    got = fb.fb_svd_factors(b, R, seed=1)
+    ref = oracle.truncated_svd(b, R)
+    np.testing.assert_allclose(got["sigma"], ref["sigma"][:R], rtol=1e-9)
+    assert got["energy"] == pytest.approx(ref["energy"], rel=1e-10)
+    err2 = np.linalg.norm(b - oracle.lowrank_bias(got["phi_q"], got["phi_k"])) ** 2
+    assert err2 == pytest.approx(np.sum(ref["sigma"][R:] ** 2), rel=1e-7)
+
+
+def test_host_svd_exact_rank():
+    r = np.random.default_rng(4)
+    a, c = r.standard_normal((96, 5)), r.standard_normal((96, 5))
+    b = a @ c.T
+    got = fb.fb_svd_factors(b, 5, seed=2)
+    np.testing.assert_allclose(oracle.lowrank_bias(got["phi_q"], got["phi_k"]), b, rtol=0, atol=1e-10)
+    assert got["energy"] == pytest.approx(1.0, abs=1e-12)
+
+
+@pytest.mark.parametrize("kind", ["vision", "pairformer"])
+def test_host_svd_on_workload_biases(kind):
+    """Small versions of the vision (spatial) and pair-rep biases: the host SVD
+    reaches the optimal rank-R error and the oracle's singular values."""
+    if kind == "vision":
+        w = synth.workload("vision_svd", grid=12, B=1, H=2)
+    else:
+        w = synth.workload("pairformer_svd", N=96, B=1, H=2)
+    b = synth.make_inputs(w)["bias_src"]
+    for h in range(b.shape[0]):
+        got = fb.fb_svd_factors(b[h], w.R, seed=h)
+        ref = oracle.truncated_svd(b[h], w.R)
+        np.testing.assert_allclose(got["sigma"], ref["sigma"][:w.R], rtol=1e-9)
+        opt = np.sum(ref["sigma"][w.R:] ** 2)
+        err2 = np.linalg.norm(b[h] - oracle.lowrank_bias(got["phi_q"], got["phi_k"])) ** 2
+        assert err2 == pytest.approx(opt, rel=1e-6)
+
+
+def test_round_exact_helper_matches_numpy_half():
+    """The test-side single-rounding helper agrees with numpy's direct fp64 -> fp16 cast."""
+    from _parity import round_exact
+    x = np.random.default_rng(5).standard_normal(100000) * np.exp(np.random.default_rng(6).uniform(-12, 12, 100000))
+    x = x[np.abs(x) < 60000]
+    np.testing.assert_array_equal(round_exact(x, "f16"), x.astype(np.float16).astype(np.float64))
+    np.testing.assert_array_equal(round_exact(x, "f32"), x.astype(np.float32).astype(np.float64))
