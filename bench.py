@@ -1,0 +1,235 @@
+"""Benchmark of the biased-attention forward hot path on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input, inputs already
+resident in HBM:
+  1. exact factor generation on the GPU (fb_make_factors), and
+  2. the fused low-rank-biased attention forward (fb_attn_fwd_lowrank).
+Default workload: Sandwich-bias attention, B=4, H=8, N=4096, D=64, C=R=64, bf16
+(Q'/K' width 128), the configuration the N=4096, D=64 MFMA target is quoted on.
+
+Prints ONE JSON line (rank 0): metric/value (whole-step TFLOP/s with
+F = 4*B*H*N^2*(D + R/2)), the dominant kernel's roofline (HIP-event timed, against
+the bf16 dense MFMA peak), the in-house dense-bias kernel on the same inputs
+(speedup), and the fp64 CPU oracle timed on a bounded sample of the same work.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # MI355X dense matrix peaks
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["attention_additive_rank_amd/csrc/fb_attn_kernel.h",
+                  "attention_additive_rank_amd/csrc/fb_attn_inst.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def flops(w) -> float:
+    pairs = w.N * (w.N + 1) / 2 if w.causal else float(w.N) ** 2
+    return 4.0 * w.B * w.H * pairs * (w.D + w.R / 2.0)
+
+
+def algorithmic_bytes(w, es: int, phi_es: int, phi_shared_over_heads: bool) -> float:
+    """Q, K, V read and O written once, plus the factors (read once)."""
+    qkvo = 4.0 * w.B * w.H * w.N * w.D * es
+    phi_rows = w.N if phi_shared_over_heads else w.H * w.N
+    return qkvo + 2.0 * phi_rows * w.R * phi_es
+
+
+def cpu_oracle_baseline(w, budget_s: float):
+    """Time the fp64 oracle (numpy) on (b, h) pairs of the same workload until the budget is used."""
+    import numpy as np
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    inp = synth.make_inputs(w, with_bias_source=False)
+    t0 = time.time()
+    if w.bias == "sandwich":
+        bias = oracle.sandwich_bias(w.N, w.C)
+        bias_fn = lambda b, h: bias
+    else:
+        slopes = oracle.alibi_slopes(w.H)
+        bias_fn = lambda b, h: oracle.alibi_bias(slopes[h:h + 1], w.N)[0]
+    t_bias = time.time() - t0
+    done, t_attn = 0, 0.0
+    for b in range(w.B):
+        for h in range(w.H):
+            s = time.time()
+            oracle.attention(inp["q"][b:b + 1, h:h + 1], inp["k"][b:b + 1, h:h + 1], inp["v"][b:b + 1, h:h + 1],
+                             bias=lambda _b, _h: bias_fn(b, h), causal=w.causal)
+            t_attn += time.time() - s
+            done += 1
+            if t_attn >= budget_s:
+                break
+        if t_attn >= budget_s:
+            break
+    f = flops(w) * done / (w.B * w.H)
+    return {"value": round(f / t_attn / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} of {w.B * w.H} (batch, head) pairs, all {w.N} rows, fp64 numpy; "
+                      f"bias materialisation {t_bias:.2f}s not included", "seconds": round(t_attn, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="sandwich", choices=["sandwich", "gpt2_alibi_causal"])
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of CPU oracle work (0 = skip)")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense-bias baseline")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after timing, run one device copy of this many MiB (HBM counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; multi-GPU runs are not provided "
+                                   "(every (batch, head) pair is independent: see DESIGN.md for how it would shard)"}))
+        sys.exit(2)
+
+    import torch
+    import attention_additive_rank_amd as fb
+    import synth
+
+    fb.load()
+    dev = torch.device("cuda:0")
+    w = synth.workload(args.workload)
+    inp = synth.make_inputs(w, with_bias_source=False)
+    dt = {"bf16": torch.bfloat16, "f32": torch.float32}[w.dtype]
+    q, k, v = (torch.from_numpy(inp[n]).to(dt).to(dev) for n in "qkv")
+    del inp
+    out = torch.empty_like(q)
+    phi_dt = torch.float16 if w.dtype != "f32" else torch.float32
+    split = 2 if (w.bias == "alibi" and w.dtype != "f32") else 1
+    if w.bias == "sandwich":
+        fH, fC, R_used = 1, w.C, w.C * split * (split + 1) // 2
+    else:
+        fH, fC, R_used = w.H, 0, 2 * split * (split + 1) // 2
+    pq = torch.empty((fH, w.N, R_used), dtype=phi_dt, device=dev)
+    pk = torch.empty_like(pq)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fb.fb_make_factors(w.bias, fH, w.N, C=fC, dtype=phi_dt, split=split, phi_q=pq, phi_k=pk)
+        fb.fb_attn_fwd_lowrank(q, k, v, pq, pk, causal=w.causal, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(K):
+        fb.fb_make_factors(w.bias, fH, w.N, C=fC, dtype=phi_dt, split=split, phi_q=pq, phi_k=pk)
+        ev[i][0].record(stream)
+        fb.fb_attn_fwd_lowrank(q, k, v, pq, pk, causal=w.causal, out=out)
+        ev[i][1].record(stream)
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    step_ms = t_start.elapsed_time(t_stop) / K
+    kern_ms = sum(a.elapsed_time(b) for a, b in ev) / K
+
+    F = flops(w)
+    value = F / (step_ms * 1e-3) / 1e12
+    kern_tflops = F / (kern_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+
+    # dense-bias baseline on the same inputs (shared [N,N] bias for Sandwich, per-head for ALiBi)
+    dense = None
+    if not args.no_dense:
+        if w.bias == "sandwich":
+            bias = fb.fb_make_dense_bias("sandwich", 1, w.N, C=w.C, dtype=dt)
+        else:
+            bias = fb.fb_make_dense_bias("alibi", w.H, w.N, dtype=dt)
+        for _ in range(args.warmup):
+            fb.fb_attn_fwd_densebias(q, k, v, bias, causal=w.causal, out=out)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(K):
+            fb.fb_attn_fwd_densebias(q, k, v, bias, causal=w.causal, out=out)
+        b.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = a.elapsed_time(b) / K
+        dense = {"ms": round(dense_ms, 4), "tflops": round(F / (dense_ms * 1e-3) / 1e12, 2),
+                 "bias_shape": list(bias.shape), "bias_bytes_unique": bias.numel() * bias.element_size()}
+        del bias
+
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        x = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        y = torch.empty_like(x)
+        torch.cuda.synchronize()
+        y.copy_(x)
+        torch.cuda.synchronize()
+        del x, y
+
+    # HBM traffic from rocprofv3 counters, only while they describe this kernel source
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_hash") == kernel_source_hash():
+            traffic = tr.get("bytes_per_launch")
+
+    cpu = None
+    if args.cpu_budget > 0:
+        cpu = cpu_oracle_baseline(w, args.cpu_budget)
+
+    es = 2 if w.dtype != "f32" else 4
+    rec = {
+        "metric": "biased-attention fwd TFLOP/s + % MFMA peak; speedup vs dense-bias kernel",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D, "R": w.R, "causal": w.causal,
+                   "factor_dtype": "f16" if phi_dt == torch.float16 else "f32", "factor_split": split,
+                   "flops_per_step": F},
+        "pct_mfma_peak": round(100.0 * value / peak, 2),
+        "kernel_ms": round(kern_ms, 4),
+        "kernel_tflops": round(kern_tflops, 2),
+        "densebias": dense,
+        "speedup_vs_densebias": round(dense["ms"] / step_ms, 3) if dense else None,
+        "roofline": {"bound": "mfma", "achieved": round(kern_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(kern_tflops / peak, 4), "traffic": traffic,
+                     "algorithmic_bytes": algorithmic_bytes(w, es, 2 if phi_dt == torch.float16 else 4,
+                                                            w.bias == "sandwich"),
+                     "kernel": "attn_fwd_kernel (fb_attn_fwd_lowrank)"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
