@@ -31,12 +31,19 @@ bool rows_aligned(const int64_t s[3], int es) {
   return s[0] % ce == 0 && s[1] % ce == 0 && s[2] % ce == 0;
 }
 
+// Element strides and the extent of one (b, h) slice must fit in 32-bit offsets.
+bool strides_fit32(const int64_t s[3], int N) {
+  const int64_t lim = 0x7fffffffLL;
+  return s[0] <= lim && s[1] <= lim && s[2] <= lim && (int64_t)N * s[2] <= lim;
+}
+
 fb_status check_common(const fb_attn_args* a, const char* fn) {
   if (!a) FB_FAIL(FB_EINVAL, "%s: null argument struct", fn);
   if (a->B < 0 || a->H < 0 || a->N < 0) FB_FAIL(FB_EINVAL, "%s: negative size", fn);
   if (!known_dtype(a->dt)) FB_FAIL(FB_EUNSUPPORTED, "%s: unknown dtype %d", fn, (int)a->dt);
   if (a->D != 16 && a->D != 32 && a->D != 64 && a->D != 128)
     FB_FAIL(FB_EUNSUPPORTED, "%s: head dim %d not in {16,32,64,128}", fn, a->D);
+  if (a->dt == FB_F32 && a->D > 64) FB_FAIL(FB_EUNSUPPORTED, "%s: fp32 supports head dims <= 64", fn);
   if ((int64_t)a->B * a->H * a->N == 0) return FB_OK;
   if (!a->q || !a->k || !a->v || !a->o) FB_FAIL(FB_EINVAL, "%s: null q/k/v/o", fn);
   if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
@@ -53,7 +60,26 @@ fb_status check_common(const fb_attn_args* a, const char* fn) {
   if (!std::isfinite(a->scale)) FB_FAIL(FB_EINVAL, "%s: scale must be finite", fn);
   const int64_t nqb = (a->N + 127) / 128;
   if (nqb * a->H * a->B > 0x7fffffffLL) FB_FAIL(FB_EUNSUPPORTED, "%s: grid too large", fn);
+  for (int i = 0; i < 4; ++i)
+    if (!strides_fit32(st[i], a->N)) FB_FAIL(FB_EUNSUPPORTED, "%s: %s strides exceed 32 bits", fn, nm[i]);
   return FB_OK;
+}
+
+fb_status dispatch_attention(int mode, fb_dtype dt, fb_dtype aux, int D, int RP, const AttnParams& p,
+                             hipStream_t s) {
+#define FB_DISPATCH_D(d)                                                   \
+  case d:                                                                  \
+    if (dt == FB_BF16) return launch_attention_d##d##_bf16(mode, aux, RP, p, s); \
+    if (dt == FB_F16) return launch_attention_d##d##_f16(mode, aux, RP, p, s);   \
+    return launch_attention_d##d##_f32(mode, aux, RP, p, s);
+  switch (D) {
+    FB_DISPATCH_D(16)
+    FB_DISPATCH_D(32)
+    FB_DISPATCH_D(64)
+    FB_DISPATCH_D(128)
+  }
+#undef FB_DISPATCH_D
+  return FB_EUNSUPPORTED;
 }
 
 AttnParams base_params(const fb_attn_args* a) {
@@ -64,15 +90,15 @@ AttnParams base_params(const fb_attn_args* a) {
   p.o = a->o;
   p.lse = a->lse;
   for (int i = 0; i < 3; ++i) {
-    p.sq[i] = a->sq[i];
-    p.sk[i] = a->sk[i];
-    p.sv[i] = a->sv[i];
-    p.so[i] = a->so[i];
+    p.sq[i] = (int)a->sq[i];
+    p.sk[i] = (int)a->sk[i];
+    p.sv[i] = (int)a->sv[i];
+    p.so[i] = (int)a->so[i];
   }
   p.B = a->B;
   p.H = a->H;
   p.N = a->N;
-  p.causal = a->causal ? 1 : 0;
+  p.flags = a->causal ? FLAG_CAUSAL : 0;
   p.scale = a->scale;
   p.nqb = (a->N + 127) / 128;
   return p;
@@ -178,30 +204,27 @@ fb_status fb_attn_fwd_lowrank(const fb_attn_args* a, const void* phi_q, const vo
     if (!phi_q || !phi_k || !sphi_q || !sphi_k) FB_FAIL(FB_EINVAL, "%s: null factor pointer or strides", fn);
     for (int i = 0; i < 3; ++i)
       if (sphi_q[i] < 0 || sphi_k[i] < 0) FB_FAIL(FB_EINVAL, "%s: negative factor stride", fn);
+    if (!strides_fit32(sphi_q, a->N) || !strides_fit32(sphi_k, a->N))
+      FB_FAIL(FB_EUNSUPPORTED, "%s: factor strides exceed 32 bits", fn);
     if (a->N > 1 && (sphi_q[2] < R || sphi_k[2] < R)) FB_FAIL(FB_EINVAL, "%s: factor row stride < R", fn);
     const int es = esize(phi_dt);
     if (((uintptr_t)phi_q % es) || ((uintptr_t)phi_k % es)) FB_FAIL(FB_EINVAL, "%s: misaligned factors", fn);
     p.phq = phi_q;
     p.phk = phi_k;
     for (int i = 0; i < 3; ++i) {
-      p.spq[i] = sphi_q[i];
-      p.spk[i] = sphi_k[i];
+      p.spq[i] = (int)sphi_q[i];
+      p.spk[i] = (int)sphi_k[i];
     }
     p.R = R;
-    p.phq_vec = aligned16(phi_q) && rows_aligned(sphi_q, es);
-    p.phk_vec = aligned16(phi_k) && rows_aligned(sphi_k, es);
+    if (aligned16(phi_q) && rows_aligned(sphi_q, es)) p.flags |= FLAG_PHQ_VEC;
+    if (aligned16(phi_k) && rows_aligned(sphi_k, es)) p.flags |= FLAG_PHK_VEC;
     const int step = a->dt == FB_F32 ? 4 : 16;
     RP = (R + step - 1) / step * step;
     if (a->dt == FB_F32) { if (RP == 12) RP = 16; else if (RP > 16 && RP < 32) RP = 32; }
     else { if (RP == 48) RP = 64; else if (RP > 64) RP = 128; }
   }
   const fb_dtype aux = R > 0 ? phi_dt : a->dt;
-  switch (a->D) {
-    case 16: st = launch_attention_d16(0, a->dt, aux, RP, p, stream); break;
-    case 32: st = launch_attention_d32(0, a->dt, aux, RP, p, stream); break;
-    case 64: st = launch_attention_d64(0, a->dt, aux, RP, p, stream); break;
-    default: st = launch_attention_d128(0, a->dt, aux, RP, p, stream); break;
-  }
+  st = dispatch_attention(0, a->dt, aux, a->D, RP, p, stream);
   if (st == FB_EUNSUPPORTED) set_error("%s: no kernel for this dtype / rank combination", fn);
   return st;
 }
@@ -219,16 +242,12 @@ fb_status fb_attn_fwd_densebias(const fb_attn_args* a, const void* bias, fb_dtyp
   if (a->N > 1 && sbias[2] < a->N) FB_FAIL(FB_EINVAL, "%s: bias row stride < N", fn);
   const int es = esize(bias_dt);
   if ((uintptr_t)bias % es) FB_FAIL(FB_EINVAL, "%s: misaligned bias", fn);
+  if (!strides_fit32(sbias, a->N)) FB_FAIL(FB_EUNSUPPORTED, "%s: bias strides exceed 32 bits", fn);
   AttnParams p = base_params(a);
   p.bias = bias;
-  for (int i = 0; i < 3; ++i) p.sb[i] = sbias[i];
-  p.bias_vec = aligned16(bias) && rows_aligned(sbias, es);
-  switch (a->D) {
-    case 16: st = launch_attention_d16(1, a->dt, bias_dt, 0, p, stream); break;
-    case 32: st = launch_attention_d32(1, a->dt, bias_dt, 0, p, stream); break;
-    case 64: st = launch_attention_d64(1, a->dt, bias_dt, 0, p, stream); break;
-    default: st = launch_attention_d128(1, a->dt, bias_dt, 0, p, stream); break;
-  }
+  for (int i = 0; i < 3; ++i) p.sb[i] = (int)sbias[i];
+  if (aligned16(bias) && rows_aligned(sbias, es)) p.flags |= FLAG_BIAS_VEC;
+  st = dispatch_attention(1, a->dt, bias_dt, a->D, 0, p, stream);
   if (st == FB_EUNSUPPORTED) set_error("%s: no kernel for this dtype combination", fn);
   return st;
 }

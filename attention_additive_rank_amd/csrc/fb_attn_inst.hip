@@ -1,10 +1,11 @@
-// Kernel instances of the fused attention forward for one head dimension.
-// This file is compiled once per head dimension with -DFB_ATTN_D=<16|32|64|128>
-// so that the instances build in parallel.
+// Kernel instances of the fused attention forward for one head dimension and one
+// Q/K/V element type.  Compiled once per (head dim, type) pair with
+// -DFB_ATTN_D=<16|32|64|128> -DFB_ATTN_QT=<0 bf16 | 1 f16 | 2 fp32> so that the
+// instances build in parallel.
 #include "fb_attn_kernel.h"
 
-#ifndef FB_ATTN_D
-#error "compile with -DFB_ATTN_D=<head dim>"
+#if !defined(FB_ATTN_D) || !defined(FB_ATTN_QT)
+#error "compile with -DFB_ATTN_D=<head dim> -DFB_ATTN_QT=<0|1|2>"
 #endif
 
 namespace fb {
@@ -13,7 +14,10 @@ namespace attn {
 template <typename QT, typename PT, int D, int RP, int MODE, typename BT>
 static fb_status launch_one(const AttnParams& p, hipStream_t stream) {
   const int64_t grid = (int64_t)p.nqb * p.H * p.B;
-  hipLaunchKernelGGL((attn_fwd_kernel<QT, PT, D, RP, MODE, BT>), dim3((unsigned)grid), dim3(NT), 0, stream, p);
+  if (p.flags & FLAG_CAUSAL)
+    hipLaunchKernelGGL((attn_fwd_kernel<QT, PT, D, RP, MODE, BT, true>), dim3((unsigned)grid), dim3(NT), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<QT, PT, D, RP, MODE, BT, false>), dim3((unsigned)grid), dim3(NT), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_error("attention launch failed: %s", hipGetErrorString(e));
@@ -44,31 +48,49 @@ static fb_status lowrank_rp(int RP, const AttnParams& p, hipStream_t s) {
 
 }  // namespace attn
 
-#define FB_CAT2(a, b) a##b
-#define FB_CAT(a, b) FB_CAT2(a, b)
+#define FB_CAT3_(a, b, c) a##b##c
+#define FB_CAT3(a, b, c) FB_CAT3_(a, b, c)
+#if FB_ATTN_QT == 0
+#define FB_QT_NAME _bf16
+#elif FB_ATTN_QT == 1
+#define FB_QT_NAME _f16
+#else
+#define FB_QT_NAME _f32
+#endif
 
 // mode 0: low rank (RP = padded factor width, 0 = plain attention); mode 1: dense bias.
-fb_status FB_CAT(launch_attention_d, FB_ATTN_D)(int mode, fb_dtype dt, fb_dtype aux_dt, int RP,
-                                                 const AttnParams& p, hipStream_t s) {
+fb_status FB_CAT3(launch_attention_d, FB_ATTN_D, FB_QT_NAME)(int mode, fb_dtype aux_dt, int RP,
+                                                              const AttnParams& p, hipStream_t s) {
   using namespace attn;
   constexpr int D = FB_ATTN_D;
-  if (mode == 1) {
-    if (dt == FB_BF16 && aux_dt == FB_BF16) return launch_one<bf16_t, bf16_t, D, 0, 1, bf16_t>(p, s);
-    if (dt == FB_F16 && aux_dt == FB_F16) return launch_one<f16_t, f16_t, D, 0, 1, f16_t>(p, s);
-    if (dt == FB_F32 && aux_dt == FB_F32) return launch_one<float, float, D, 0, 1, float>(p, s);
-    return FB_EUNSUPPORTED;
-  }
-  if (RP == 0) {
-    if (dt == FB_BF16) return launch_one<bf16_t, bf16_t, D, 0, 0, bf16_t>(p, s);
-    if (dt == FB_F16) return launch_one<f16_t, f16_t, D, 0, 0, f16_t>(p, s);
-    if (dt == FB_F32) return launch_one<float, float, D, 0, 0, float>(p, s);
-    return FB_EUNSUPPORTED;
-  }
-  if (dt == FB_BF16 && aux_dt == FB_BF16) return lowrank_rp<bf16_t, bf16_t, D>(RP, p, s);
-  if (dt == FB_BF16 && aux_dt == FB_F16) return lowrank_rp<bf16_t, f16_t, D>(RP, p, s);
-  if (dt == FB_F16 && aux_dt == FB_F16) return lowrank_rp<f16_t, f16_t, D>(RP, p, s);
-  if (dt == FB_F32 && aux_dt == FB_F32) return lowrank_rp<float, float, D>(RP, p, s);
+#if FB_ATTN_QT == 2 && FB_ATTN_D > 64
+  // fp32 Q/K/V is limited to head dims <= 64 (the fp32 matrix-core path is for small checks)
+  (void)mode; (void)aux_dt; (void)RP; (void)p; (void)s;
   return FB_EUNSUPPORTED;
+#else
+#if FB_ATTN_QT == 0
+  typedef bf16_t QT;
+  constexpr fb_dtype qdt = FB_BF16;
+#elif FB_ATTN_QT == 1
+  typedef f16_t QT;
+  constexpr fb_dtype qdt = FB_F16;
+#else
+  typedef float QT;
+  constexpr fb_dtype qdt = FB_F32;
+#endif
+  if (mode == 1) {
+    if (aux_dt == qdt) return launch_one<QT, QT, D, 0, 1, QT>(p, s);
+    return FB_EUNSUPPORTED;
+  }
+  if (RP == 0) return launch_one<QT, QT, D, 0, 0, QT>(p, s);
+#if FB_ATTN_QT == 0
+  if (aux_dt == FB_BF16) return lowrank_rp<QT, bf16_t, D>(RP, p, s);
+  if (aux_dt == FB_F16) return lowrank_rp<QT, f16_t, D>(RP, p, s);
+#else
+  if (aux_dt == qdt) return lowrank_rp<QT, QT, D>(RP, p, s);
+#endif
+  return FB_EUNSUPPORTED;
+#endif
 }
 
 }  // namespace fb

@@ -7,19 +7,28 @@
 // Reviewer UJUf, Q2: concatenate the factor functions with queries and keys,
 // then run FlashAttention).  MODE 1 (dense bias, the baseline): the contraction
 // is Q*s K^T and a bias tile is read from HBM for every (query, key) tile pair,
-// the quadratic IO the abstract and Fig. 1(c) describe.
+// the quadratic IO of the abstract and Fig. 1(c).
 //
 // Work decomposition
 //   * One workgroup = 4 wavefronts = 128 query rows of one (batch, head); each
 //     wavefront owns 32 query rows for the whole key loop.
-//   * Key tiles of 64 keys are staged in LDS once per workgroup: K' rows
-//     (K then phi_k, zero-padded to RP columns) and V transposed (Vt[d][key]).
+//   * Key tiles of 64 keys are staged in LDS (double-buffered) once per
+//     workgroup: K' rows (K then phi_k, zero-padded to RP columns) and V
+//     transposed (Vt[d][key]).  Global loads for tile t+2 are in flight while
+//     tile t is computed; no bounds branches inside the loop (rows past N are
+//     clamped on load and masked in the scores).
 //   * Scores are computed transposed, S^T = K' Q'^T, with 32x32 MFMAs
 //     (32x32x16 bf16/f16, 32x32x2 fp32).  With that orientation every lane owns
 //     ONE query (lane % 32) and 16 keys per 32-key block, so the row max / row
 //     sum of the online softmax are in-lane reductions plus a single exchange
 //     between the two half-waves, and P^T is already in the B-operand layout of
 //     the next product O^T = Vt P^T: P never leaves registers.
+//   * Software pipeline: the MFMAs of S(t+1) are independent of the softmax of
+//     tile t, so both are issued in the same stretch of code and the compiler
+//     interleaves matrix-core and vector work within each wavefront.
+//   * Lazy rescaling: the running row max only moves (and O, l are rescaled)
+//     when a tile's max exceeds it by more than 2^8 in exp2 units, so most
+//     tiles skip the O rescale; P then stays <= 2^8, exact in range for bf16.
 //   * K' rows and Vt rows are permuted in LDS so that lane half h holds keys
 //     16h..16h+15 of each 32-key block (and, in the output, head dims
 //     16h..16h+15 of each 32-dim block): bias reads, the causal mask and the
@@ -43,14 +52,17 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int NW = 4;          // wavefronts per workgroup
 constexpr int NT = NW * 64;    // threads per workgroup
 constexpr int BM = 32 * NW;    // query rows per workgroup
 constexpr int BN = 64;         // keys per LDS tile
+constexpr int NKB = BN / 32;   // 32-key blocks per tile
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float RESCALE_GAP = 8.0f / LOG2E;   // 2^8 in exp2 units, as a natural-log gap
 
 template <typename T> struct Elem;
 template <> struct Elem<bf16_t> { typedef u32x4 Frag; static constexpr int KW = 8; };
@@ -92,7 +104,7 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
 // Position inside a 32-row MFMA block that holds logical index k (key or head dim):
 // MFMA row m = 8a + 4h + c carries index 16h + 4a + c, so that output register r
 // of lane half h corresponds to index 16h + r.
-__device__ __forceinline__ int perm_row(int k) {
+__host__ __device__ constexpr int perm_row(int k) {
   return (k & ~31) | (((k & 15) >> 2) << 3) | (((k >> 4) & 1) << 2) | (k & 3);
 }
 
@@ -111,19 +123,49 @@ __device__ __forceinline__ typename Elem<T>::Frag scale_frag(typename Elem<T>::F
   }
 }
 
-// One 16-byte chunk of a factor row (CE elements starting at column c0), zero past R.
+// All ones when i < lim, else zero (branch-free: no per-element lane masks).
+__device__ __forceinline__ uint32_t below_mask(int i, int lim) { return (uint32_t)((i - lim) >> 31); }
+
+// CE elements of row[c0..] (row has `len` valid elements), zero past len; element loads
+// are clamped into the row and the excess is zeroed arithmetically.
 template <typename T>
-__device__ __forceinline__ u32x4 load_phi_chunk(const T* row, int c0, int R, int vec) {
+__device__ __forceinline__ u32x4 load_partial_chunk(const T* row, int c0, int len) {
   constexpr int CE = 16 / (int)sizeof(T);
-  if (vec && c0 + CE <= R) return ld16(row + c0);
-  ChunkV<T> v;
+  u32x4 r;
+  if constexpr (sizeof(T) == 2) {
+    const uint16_t* src = (const uint16_t*)row;
 #pragma unroll
-  for (int e = 0; e < CE; ++e) v[e] = (c0 + e < R) ? row[c0 + e] : from_f32<T>(0.f);
-  return __builtin_bit_cast(u32x4, v);
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t lo = src[min(c0 + 2 * w, len - 1)] & below_mask(c0 + 2 * w, len);
+      const uint32_t hi = src[min(c0 + 2 * w + 1, len - 1)] & below_mask(c0 + 2 * w + 1, len);
+      r[w] = lo | (hi << 16);
+    }
+  } else {
+    const uint32_t* src = (const uint32_t*)row;
+#pragma unroll
+    for (int w = 0; w < CE; ++w) r[w] = src[min(c0 + w, len - 1)] & below_mask(c0 + w, len);
+  }
+  return r;
 }
 
-template <typename QT, typename PT, int D, int RP, int MODE, typename BT>
-__global__ __launch_bounds__(NT) void attn_fwd_kernel(AttnParams p) {
+// One 16-byte chunk of a factor row (CE elements starting at column c0), zero past R.
+template <typename T>
+__device__ __forceinline__ u32x4 load_phi_chunk(const T* row, int c0, int R, bool vec) {
+  if (vec) return ld16(row + c0);
+  return load_partial_chunk<T>(row, c0, R);
+}
+
+// max / sum of a value over the two half-waves (lanes l and l ^ 32), via ds_bpermute
+__device__ __forceinline__ float halves_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+__device__ __forceinline__ float halves_sum(float x) { return x + __shfl_xor(x, 32); }
+
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int SG_VALU = 0x002 | 0x400;   // vector ALU incl. transcendental
+constexpr int SG_MFMA = 0x008;
+constexpr int SG_DS_READ = 0x100;
+
+template <typename QT, typename PT, int D, int RP, int MODE, typename BT, bool CAUSAL>
+__global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnParams p) {
   typedef typename Elem<QT>::Frag QFrag;
   typedef typename Elem<PT>::Frag PFrag;
   constexpr int ES = (int)sizeof(QT);
@@ -139,14 +181,21 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(AttnParams p) {
   constexpr int DB = DP / 32;             // 32-wide head-dim blocks of the output
   constexpr int QSTEPS = D / KS;
   constexpr int PSTEPS = RP / KS;
+  constexpr int NMMA_QK = NKB * (QSTEPS + PSTEPS);
   constexpr int KCH = D / CE;             // chunks per K / V row
   constexpr int PCH = RP / CE;            // chunks per phi_k row
-  constexpr int KPT = (BN * KCH + NT - 1) / NT;
-  constexpr int PPT = PCH > 0 ? (BN * PCH + NT - 1) / NT : 0;
+  constexpr int K_TOT = BN * KCH;         // K chunks per tile
+  constexpr int P_TOT = BN * PCH;         // phi_k chunks per tile
+  constexpr int V_TOT = (BN / 2) * KCH;   // V tasks per tile: one chunk column of a key pair
+  constexpr int KPT = (K_TOT + NT - 1) / NT;
+  constexpr int PPT = P_TOT > 0 ? (P_TOT + NT - 1) / NT : 0;
+  constexpr int VPT = (V_TOT + NT - 1) / NT;
+  constexpr int SK_BYTES = BN * PITCH_K;
+  constexpr int SV_BYTES = DP * PITCH_V;
   static_assert(D % KS == 0 && RP % KS == 0 && D % CE == 0 && RP % CE == 0, "bad tile widths");
 
-  __shared__ __attribute__((aligned(16))) unsigned char sK[BN * PITCH_K];
-  __shared__ __attribute__((aligned(16))) unsigned char sV[DP * PITCH_V];
+  __shared__ __attribute__((aligned(16))) unsigned char sK[2 * SK_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char sV[2 * SV_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -162,35 +211,37 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(AttnParams p) {
   const int L = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
   int qb = L % p.nqb;
   const int bh = L / p.nqb;
-  if (p.causal) qb = p.nqb - 1 - qb;
+  if (CAUSAL) qb = p.nqb - 1 - qb;
   const int hh = bh % p.H;
   const int bb = bh / p.H;
   const int N = p.N;
 
-  const QT* Qp = (const QT*)p.q + bb * p.sq[0] + hh * p.sq[1];
-  const QT* Kp = (const QT*)p.k + bb * p.sk[0] + hh * p.sk[1];
-  const QT* Vp = (const QT*)p.v + bb * p.sv[0] + hh * p.sv[1];
-  QT* Op = (QT*)p.o + bb * p.so[0] + hh * p.so[1];
+  const QT* Qp = (const QT*)p.q + ((int64_t)bb * p.sq[0] + (int64_t)hh * p.sq[1]);
+  const QT* Kp = (const QT*)p.k + ((int64_t)bb * p.sk[0] + (int64_t)hh * p.sk[1]);
+  const QT* Vp = (const QT*)p.v + ((int64_t)bb * p.sv[0] + (int64_t)hh * p.sv[1]);
+  QT* Op = (QT*)p.o + ((int64_t)bb * p.so[0] + (int64_t)hh * p.so[1]);
   const PT* PQp = nullptr;
   const PT* PKp = nullptr;
   if constexpr (RP > 0) {
-    PQp = (const PT*)p.phq + bb * p.spq[0] + hh * p.spq[1];
-    PKp = (const PT*)p.phk + bb * p.spk[0] + hh * p.spk[1];
+    PQp = (const PT*)p.phq + ((int64_t)bb * p.spq[0] + (int64_t)hh * p.spq[1]);
+    PKp = (const PT*)p.phk + ((int64_t)bb * p.spk[0] + (int64_t)hh * p.spk[1]);
   }
   const BT* Bp = nullptr;
-  if constexpr (MODE == 1) Bp = (const BT*)p.bias + bb * p.sb[0] + hh * p.sb[1];
+  if constexpr (MODE == 1) Bp = (const BT*)p.bias + ((int64_t)bb * p.sb[0] + (int64_t)hh * p.sb[1]);
 
   const int q0 = qb * BM;
   const int q0w = q0 + wave * 32;
   const int qrow = q0w + ln;
   const bool qvalid = qrow < N;
+  const int qclamp = qvalid ? qrow : N - 1;
 
   // Vt rows of head dims >= D (only when D < 32) are never written by the tile
-  // stores: clear them once so that the discarded output rows stay finite.
+  // stores: clear them once in both buffers so the discarded output rows stay finite.
   if constexpr (D < DP) {
-    for (int i = tid; i < (DP - D) * BN; i += NT) {
-      const int d = D + i / BN, key = i % BN;
-      unsigned char* dst = sV + perm_row(d) * PITCH_V + key * ES;
+    for (int i = tid; i < 2 * (DP - D) * BN; i += NT) {
+      const int buf = i / ((DP - D) * BN), r = i % ((DP - D) * BN);
+      const int d = D + r / BN, key = r % BN;
+      unsigned char* dst = sV + buf * SV_BYTES + perm_row(d) * PITCH_V + key * ES;
       if constexpr (ES == 2) *(uint16_t*)dst = 0; else *(uint32_t*)dst = 0;
     }
   }
@@ -200,25 +251,162 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(AttnParams p) {
   PFrag pf[PSTEPS > 0 ? PSTEPS : 1];
 #pragma unroll
   for (int t = 0; t < QSTEPS; ++t) {
-    if (qvalid) {
-      if constexpr (KW == 1) qf[t] = scale_frag<QT>(Qp[qrow * p.sq[2] + KS * t + hf], p.scale);
-      else qf[t] = scale_frag<QT>(ld16(Qp + qrow * p.sq[2] + KS * t + KW * hf), p.scale);
-    } else {
-      qf[t] = QFrag{};
-    }
+    if constexpr (KW == 1) qf[t] = scale_frag<QT>(Qp[qclamp * p.sq[2] + KS * t + hf], p.scale);
+    else qf[t] = scale_frag<QT>(ld16(Qp + qclamp * p.sq[2] + KS * t + KW * hf), p.scale);
   }
   if constexpr (RP > 0) {
-    const PT* prow = PQp + (int64_t)(qvalid ? qrow : 0) * p.spq[2];
+    const PT* prow = PQp + qclamp * p.spq[2];
 #pragma unroll
     for (int t = 0; t < PSTEPS; ++t) {
       const int c0 = KS * t + KW * hf;
-      if constexpr (KW == 1) {
-        pf[t] = (qvalid && c0 < p.R) ? prow[c0] : 0.f;
-      } else {
-        pf[t] = qvalid ? load_phi_chunk<PT>(prow, c0, p.R, p.phq_vec) : u32x4{};
-      }
+      if constexpr (KW == 1) pf[t] = c0 < p.R ? prow[c0] : 0.f;
+      else pf[t] = load_phi_chunk<PT>(prow, c0, p.R, (p.flags & FLAG_PHQ_VEC) && c0 + KW <= p.R);
     }
   }
+
+  // ---- per-thread staging assignment (loop invariant) ------------------------
+  // K chunk i covers row c / KCH, chunk column c % KCH of the tile (c = tid + i*NT).
+  const QT* k_ptr[KPT];
+  int k_row[KPT], k_lds[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int c = tid + i * NT;
+    const int cc = c < K_TOT ? c : 0;
+    k_row[i] = cc / KCH;
+    k_ptr[i] = Kp + k_row[i] * p.sk[2] + (cc % KCH) * CE;
+    k_lds[i] = perm_row(k_row[i]) * PITCH_K + (cc % KCH) * 16;
+  }
+  const PT* p_ptr[PPT > 0 ? PPT : 1];
+  int p_row[PPT > 0 ? PPT : 1], p_col[PPT > 0 ? PPT : 1], p_lds[PPT > 0 ? PPT : 1];
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) {
+    const int c = tid + i * NT;
+    const int cc = c < P_TOT ? c : 0;
+    p_row[i] = cc / PCH;
+    p_col[i] = (cc % PCH) * CE;
+    p_ptr[i] = PKp + p_row[i] * p.spk[2];
+    p_lds[i] = perm_row(p_row[i]) * PITCH_K + D * ES + (cc % PCH) * 16;
+  }
+  // factor rows: 16-byte vector loads when every chunk is either full or past R
+  const bool phk_fast = (RP == 0) || ((p.flags & FLAG_PHK_VEC) && p.R % CE == 0);
+  // V task i: key pair pr (keys 2pr, 2pr+1), chunk column vc; pairs run fastest
+  // across lanes so that each 32-bit LDS write of a wavefront hits distinct banks.
+  const QT* v_ptr[VPT];
+  int v_pair[VPT], v_col[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int c = tid + i * NT;
+    const int cc = c < V_TOT ? c : 0;
+    v_pair[i] = cc % (BN / 2);
+    v_col[i] = cc / (BN / 2);
+    v_ptr[i] = Vp + (2 * v_pair[i]) * p.sv[2] + v_col[i] * CE;
+  }
+
+  u32x4 kr[KPT], vr0[VPT], vr1[VPT];
+  u32x4 pr[PPT > 0 ? PPT : 1];
+
+  auto load_tile = [&](int kb) {
+    if (kb + BN <= N) {           // whole tile inside the sequence: plain strided loads
+      const int ko = kb * p.sk[2], vo = kb * p.sv[2];
+#pragma unroll
+      for (int i = 0; i < KPT; ++i)
+        if (K_TOT % NT == 0 || tid + i * NT < K_TOT) kr[i] = ld16(k_ptr[i] + ko);
+#pragma unroll
+      for (int i = 0; i < VPT; ++i)
+        if (V_TOT % NT == 0 || tid + i * NT < V_TOT) {
+          vr0[i] = ld16(v_ptr[i] + vo);
+          vr1[i] = ld16(v_ptr[i] + vo + p.sv[2]);
+        }
+    } else {                      // tail tile: rows past N are clamped (and masked later)
+#pragma unroll
+      for (int i = 0; i < KPT; ++i)
+        if (K_TOT % NT == 0 || tid + i * NT < K_TOT) {
+          const int key = min(kb + k_row[i], N - 1);
+          kr[i] = ld16(k_ptr[i] + (key - k_row[i]) * p.sk[2]);
+        }
+#pragma unroll
+      for (int i = 0; i < VPT; ++i)
+        if (V_TOT % NT == 0 || tid + i * NT < V_TOT) {
+          const int k0 = min(kb + 2 * v_pair[i], N - 1), k1 = min(kb + 2 * v_pair[i] + 1, N - 1);
+          vr0[i] = ld16(v_ptr[i] + (k0 - 2 * v_pair[i]) * p.sv[2]);
+          vr1[i] = ld16(v_ptr[i] + (k1 - 2 * v_pair[i]) * p.sv[2]);
+        }
+    }
+    if constexpr (PPT > 0) {
+#pragma unroll
+      for (int i = 0; i < PPT; ++i) {
+        if (P_TOT % NT == 0 || tid + i * NT < P_TOT) {
+          const int key = min(kb + p_row[i], N - 1);
+          const PT* row = p_ptr[i] + (key - p_row[i]) * p.spk[2];
+          if (phk_fast) pr[i] = p_col[i] < p.R ? ld16(row + p_col[i]) : u32x4{};
+          else pr[i] = load_partial_chunk<PT>(row, p_col[i], p.R);
+        }
+      }
+    }
+  };
+
+  auto store_tile = [&](int buf) {
+    unsigned char* k_base = sK + buf * SK_BYTES;
+    unsigned char* v_base = sV + buf * SV_BYTES;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+      if (K_TOT % NT == 0 || tid + i * NT < K_TOT) st16(k_base + k_lds[i], kr[i]);
+    if constexpr (PPT > 0) {
+#pragma unroll
+      for (int i = 0; i < PPT; ++i)
+        if (P_TOT % NT == 0 || tid + i * NT < P_TOT) st16(k_base + p_lds[i], pr[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      if (V_TOT % NT == 0 || tid + i * NT < V_TOT) {
+        unsigned char* dst = v_base + 2 * v_pair[i] * ES;
+        const int d0 = v_col[i] * CE;
+        if constexpr (ES == 2) {
+          // element j of both keys -> one 32-bit word (key 2pr low, key 2pr+1 high)
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const uint32_t lo = __builtin_amdgcn_perm(vr1[i][m], vr0[i][m], 0x05040100u);
+            const uint32_t hi = __builtin_amdgcn_perm(vr1[i][m], vr0[i][m], 0x07060302u);
+            *(uint32_t*)(dst + perm_row(d0 + 2 * m) * PITCH_V) = lo;
+            *(uint32_t*)(dst + perm_row(d0 + 2 * m + 1) * PITCH_V) = hi;
+          }
+        } else {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            u32x2 w2 = {vr0[i][m], vr1[i][m]};
+            *(u32x2*)(dst + perm_row(d0 + m) * PITCH_V) = w2;
+          }
+        }
+      }
+    }
+  };
+
+  // ---- S^T = K' Q'^T of one tile from LDS buffer `buf` -----------------------
+  auto qk_tile = [&](int buf, f32x16 (&sacc)[NKB]) {
+    const unsigned char* k_base = sK + buf * SK_BYTES + ln * PITCH_K;
+#pragma unroll
+    for (int kb2 = 0; kb2 < NKB; ++kb2) sacc[kb2] = f32x16{};
+#pragma unroll
+    for (int t = 0; t < QSTEPS; ++t) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < NKB; ++kb2) {
+        const unsigned char* a = k_base + 32 * kb2 * PITCH_K + (KS * t + KW * hf) * ES;
+        if constexpr (KW == 1) sacc[kb2] = Mma<QT>::run(*(const float*)a, qf[t], sacc[kb2]);
+        else sacc[kb2] = Mma<QT>::run(ld16(a), qf[t], sacc[kb2]);
+      }
+    }
+    if constexpr (RP > 0) {
+#pragma unroll
+      for (int t = 0; t < PSTEPS; ++t) {
+#pragma unroll
+        for (int kb2 = 0; kb2 < NKB; ++kb2) {
+          const unsigned char* a = k_base + 32 * kb2 * PITCH_K + (D + KS * t + KW * hf) * ES;
+          if constexpr (KW == 1) sacc[kb2] = Mma<PT>::run(*(const float*)a, pf[t], sacc[kb2]);
+          else sacc[kb2] = Mma<PT>::run(ld16(a), pf[t], sacc[kb2]);
+        }
+      }
+    }
+  };
 
   f32x16 oacc[DB];
 #pragma unroll
@@ -226,216 +414,194 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(AttnParams p) {
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  const int kend = p.causal ? min(N, q0 + BM) : N;
+  const int kend = CAUSAL ? min(N, q0 + BM) : N;
   const int nkt = (kend + BN - 1) / BN;
 
-  // ---- cooperative tile loads: global -> registers -> LDS ------------------
-  u32x4 kr[KPT], vr[KPT];
-  u32x4 pr[PPT > 0 ? PPT : 1];
-
-  auto load_tile = [&](int kb) {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int c = tid + i * NT;
-      if ((BN * KCH) % NT == 0 || c < BN * KCH) {
-        const int row = c / KCH, col = c % KCH, key = kb + row;
-        if (key < N) {
-          kr[i] = ld16(Kp + (int64_t)key * p.sk[2] + col * CE);
-          vr[i] = ld16(Vp + (int64_t)key * p.sv[2] + col * CE);
-        } else {
-          kr[i] = u32x4{};
-          vr[i] = u32x4{};
-        }
-      }
-    }
-    if constexpr (PPT > 0) {
-#pragma unroll
-      for (int i = 0; i < PPT; ++i) {
-        const int c = tid + i * NT;
-        if ((BN * PCH) % NT == 0 || c < BN * PCH) {
-          const int row = c / PCH, col = c % PCH, key = kb + row;
-          pr[i] = key < N ? load_phi_chunk<PT>(PKp + (int64_t)key * p.spk[2], col * CE, p.R, p.phk_vec)
-                          : u32x4{};
-        }
-      }
-    }
-  };
-
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int c = tid + i * NT;
-      if ((BN * KCH) % NT == 0 || c < BN * KCH) {
-        const int row = c / KCH, col = c % KCH;
-        st16(sK + perm_row(row) * PITCH_K + col * 16, kr[i]);
-        // V goes in transposed: Vt[d][key]
-        if constexpr (ES == 2) {
-          const u16x8 e = __builtin_bit_cast(u16x8, vr[i]);
-#pragma unroll
-          for (int j = 0; j < CE; ++j)
-            *(uint16_t*)(sV + perm_row(col * CE + j) * PITCH_V + row * ES) = e[j];
-        } else {
-#pragma unroll
-          for (int j = 0; j < CE; ++j)
-            *(uint32_t*)(sV + perm_row(col * CE + j) * PITCH_V + row * ES) = vr[i][j];
-        }
-      }
-    }
-    if constexpr (PPT > 0) {
-#pragma unroll
-      for (int i = 0; i < PPT; ++i) {
-        const int c = tid + i * NT;
-        if ((BN * PCH) % NT == 0 || c < BN * PCH) {
-          const int row = c / PCH, col = c % PCH;
-          st16(sK + perm_row(row) * PITCH_K + D * ES + col * 16, pr[i]);
-        }
-      }
-    }
-  };
-
-  if (nkt > 0) {
-    load_tile(0);
-    store_tile();
-  }
-  __syncthreads();
-
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int kb = kt * BN;
-    const bool has_next = kt + 1 < nkt;
-    if (has_next) load_tile(kb + BN);
-
-    // dense bias of this lane's row and keys kb + 32*kb2 + 16*hf + [0, 16)
-    float bias_v[MODE == 1 ? 2 : 1][16];
+  // dense bias of this lane's row, keys kb + 32*kb2 + 16*hf + [0, 16), kept raw
+  constexpr int BES = MODE == 1 ? (int)sizeof(BT) : 2;
+  constexpr int BCH = BES;                  // 16-byte chunks per 16 keys
+  constexpr int NBR = MODE == 1 ? NKB * BCH : 1;
+  auto load_bias = [&](int kb, u32x4 (&raw)[NBR]) {
     if constexpr (MODE == 1) {
-      const BT* brow = Bp + (int64_t)(qvalid ? qrow : 0) * p.sb[2];
+      const BT* brow = Bp + qclamp * p.sb[2];
+      constexpr int BCE = 16 / BES;
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
+      for (int kb2 = 0; kb2 < NKB; ++kb2) {
         const int j0 = kb + 32 * kb2 + 16 * hf;
-        if (p.bias_vec && qvalid && j0 + 16 <= N) {
-          constexpr int BCE = 16 / (int)sizeof(BT);
+        if ((p.flags & FLAG_BIAS_VEC) && j0 + 16 <= N) {
 #pragma unroll
-          for (int c = 0; c < 16 / BCE; ++c) {
-            const ChunkV<BT> e = __builtin_bit_cast(ChunkV<BT>, ld16(brow + j0 + c * BCE));
-#pragma unroll
-            for (int j = 0; j < BCE; ++j) bias_v[kb2][c * BCE + j] = to_f32<BT>(e[j]);
-          }
+          for (int c = 0; c < BCH; ++c) raw[kb2 * BCH + c] = ld16(brow + j0 + c * BCE);
         } else {
 #pragma unroll
-          for (int j = 0; j < 16; ++j)
-            bias_v[kb2][j] = (qvalid && j0 + j < N) ? to_f32<BT>(brow[j0 + j]) : 0.f;
+          for (int c = 0; c < BCH; ++c) raw[kb2 * BCH + c] = load_partial_chunk<BT>(brow, j0 + c * BCE, N);
         }
       }
     }
+  };
 
-    // A wavefront whose queries all precede this key tile has nothing to do here.
-    const bool active = !p.causal || kb <= q0w + 31;
+  // One key tile.  Block A: bias add, mask, row max, rare rescale.  Block B: the
+  // MFMAs of S(t+1) interleaved with the exponentials of tile t.  Block C: O += Vt P^T.
+  // Then the LDS buffer just consumed is refilled with tile t+2.
+  auto iteration = [&](int kt, f32x16 (&s_cur)[NKB], f32x16 (&s_nxt)[NKB], u32x4 (&b_cur)[NBR],
+                       u32x4 (&b_nxt)[NBR]) {
+    const int kb = kt * BN;
+    const int buf = kt & 1;
+    // A wavefront whose queries all precede a key tile has nothing to do there
+    // (nor in any later tile).
+    const bool active = !CAUSAL || kb <= q0w + 31;
     if (active) {
-      // ---- S^T = K' Q'^T for two 32-key blocks ----------------------------
-      f32x16 sacc[2];
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        const unsigned char* arow = sK + (32 * kb2 + ln) * PITCH_K;
-        f32x16 acc = f32x16{};
-#pragma unroll
-        for (int t = 0; t < QSTEPS; ++t) {
-          if constexpr (KW == 1) acc = Mma<QT>::run(*(const float*)(arow + (KS * t + hf) * ES), qf[t], acc);
-          else acc = Mma<QT>::run(ld16(arow + (KS * t + KW * hf) * ES), qf[t], acc);
-        }
-        if constexpr (RP > 0) {
-#pragma unroll
-          for (int t = 0; t < PSTEPS; ++t) {
-            if constexpr (KW == 1)
-              acc = Mma<PT>::run(*(const float*)(arow + (D + KS * t + hf) * ES), pf[t], acc);
-            else
-              acc = Mma<PT>::run(ld16(arow + (D + KS * t + KW * hf) * ES), pf[t], acc);
-          }
-        }
-        sacc[kb2] = acc;
-      }
       if constexpr (MODE == 1) {
+        if (kt + 1 < nkt) load_bias(kb + BN, b_nxt);
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
+        for (int kb2 = 0; kb2 < NKB; ++kb2)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[kb2][r] += bias_v[kb2][r];
+          for (int c = 0; c < BCH; ++c) {
+            const ChunkV<BT> e = __builtin_bit_cast(ChunkV<BT>, b_cur[kb2 * BCH + c]);
+#pragma unroll
+            for (int j = 0; j < 16 / BES; ++j) s_cur[kb2][c * (16 / BES) + j] += to_f32<BT>(e[j]);
+          }
       }
-      // ---- mask: keys past N, and keys after the query when causal -----------
-      const bool need_mask = (kb + BN > N) || (p.causal && kb + BN - 1 > q0w);
+      // ---- mask: keys past N, and keys after the query when causal ------------
+      const bool need_mask = (kb + BN > N) || (CAUSAL && kb + BN - 1 > q0w);
       if (need_mask) {
+        // keys j visible to this row: j < N and (causal) j <= qrow; the rest -> -inf
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
+        for (int kb2 = 0; kb2 < NKB; ++kb2) {
+          const int j0 = kb + 32 * kb2 + 16 * hf;
+          int lim = N - j0;
+          if constexpr (CAUSAL) lim = min(lim, qrow + 1 - j0);
+          // One compare-select at a time: the scheduling fence keeps the compiler from
+          // hoisting all compares into simultaneously live scalar lane masks.
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int j = kb + 32 * kb2 + 16 * hf + r;
-            if (j >= N || (p.causal && j > qrow)) sacc[kb2][r] = -INFINITY;
+            s_cur[kb2][r] = r < lim ? s_cur[kb2][r] : -INFINITY;
+            __builtin_amdgcn_sched_barrier(0);
           }
+        }
       }
-      // ---- online softmax (row = this lane's query) ---------------------------
+      // ---- online softmax with lazy rescaling (row = this lane's query) -------
       float mx = -INFINITY;
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int kb2 = 0; kb2 < NKB; ++kb2)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb2][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * LOG2E);
-      const float ms = m_use * LOG2E;
-      float lsum = 0.f;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kb2][r]);
+      mx = halves_max(mx);
+      const bool grow = mx > m_run + RESCALE_GAP;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - mx) * LOG2E) : 1.f;  // 0 on the first tile
+        l_run *= alpha;
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb2][r], LOG2E, -ms));
-          sacc[kb2][r] = e;
-          lsum += e;
-        }
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+        m_run = grow ? mx : m_run;
+      }
+      const float ms = (m_run == -INFINITY ? 0.f : m_run) * LOG2E;
 
-      // ---- O^T += Vt P^T ----------------------------------------------------
+      // ---- block B: S(t+1) on the matrix cores, exp of tile t on the VALU ----
+      qk_tile(buf ^ 1, s_nxt);
+      u32x4 pfrag[KW == 1 ? 1 : NKB * 2];
+      if constexpr (KW == 1) {
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        if constexpr (KW == 1) {
+        for (int kb2 = 0; kb2 < NKB; ++kb2)
 #pragma unroll
-          for (int u = 0; u < 16; ++u) {
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-              const float a = *(const float*)(sV + (32 * db + ln) * PITCH_V + (32 * kb2 + 16 * hf + u) * ES);
-              oacc[db] = Mma<QT>::run(a, sacc[kb2][u], oacc[db]);
-            }
+          for (int r = 0; r < 16; ++r) {
+            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb2][r], LOG2E, -ms));
+            s_cur[kb2][r] = e;
+            l_run += e;
           }
-        } else {
+      } else {
+        typedef QT T8 __attribute__((ext_vector_type(8)));
+        typedef QT T2 __attribute__((ext_vector_type(2)));
+        float lsum = 0.f;
+#pragma unroll
+        for (int kb2 = 0; kb2 < NKB; ++kb2)
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            typedef QT T8 __attribute__((ext_vector_type(8)));
             T8 pb;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) pb[j] = from_f32<QT>(sacc[kb2][8 * u + j]);
-            const u32x4 bfrag = __builtin_bit_cast(u32x4, pb);
+            for (int j = 0; j < 8; ++j)
+              pb[j] = from_f32<QT>(__builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb2][8 * u + j], LOG2E, -ms)));
+            pfrag[kb2 * 2 + u] = __builtin_bit_cast(u32x4, pb);
+            // row sum of the rounded probabilities (what the P V product uses)
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-              const u32x4 a = ld16(sV + (32 * db + ln) * PITCH_V + (32 * kb2 + 16 * hf + 8 * u) * ES);
-              oacc[db] = Mma<QT>::run(a, bfrag, oacc[db]);
+            for (int m = 0; m < 4; ++m) {
+              const T2 two = {pb[2 * m], pb[2 * m + 1]};
+              const T2 one = {from_f32<QT>(1.f), from_f32<QT>(1.f)};
+              if constexpr (sizeof(QT) == 2 && __is_same(QT, bf16_t))
+                lsum = __builtin_amdgcn_fdot2_f32_bf16(two, one, lsum, false);
+              else
+                lsum = __builtin_amdgcn_fdot2(two, one, lsum, false);
             }
           }
+        l_run += lsum;
+      }
+      // interleave: a few K' reads up front, then per MFMA one read and ~6 VALU ops
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 4, 0);
+#pragma unroll
+      for (int i = 0; i < NMMA_QK; ++i) {
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_VALU, 6, 0);
+      }
+
+      // ---- block C: O^T += Vt P^T -----------------------------------------------
+      const unsigned char* v_base = sV + buf * SV_BYTES + ln * PITCH_V + 16 * hf * ES;
+#pragma unroll
+      for (int kb2 = 0; kb2 < NKB; ++kb2) {
+        if constexpr (KW == 1) {
+#pragma unroll
+          for (int u = 0; u < 16; ++u)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+              const float a = *(const float*)(v_base + 32 * db * PITCH_V + (32 * kb2 + u) * ES);
+              oacc[db] = Mma<QT>::run(a, s_cur[kb2][u], oacc[db]);
+            }
+        } else {
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+              const u32x4 a = ld16(v_base + 32 * db * PITCH_V + (32 * kb2 + 8 * u) * ES);
+              oacc[db] = Mma<QT>::run(a, pfrag[kb2 * 2 + u], oacc[db]);
+            }
         }
       }
     }
 
+    // ---- refill the buffer just consumed with tile t+2; start loading t+3 ----
     __syncthreads();
-    if (has_next) {
-      store_tile();
-      __syncthreads();
+    if (kt + 2 < nkt) {
+      store_tile(buf);
+      if (kt + 3 < nkt) load_tile(kb + 3 * BN);
     }
+    __syncthreads();
+  };
+
+  // ---- prologue: tiles 0 and 1 into LDS, tile 2 in flight, S(0) ------------
+  load_tile(0);
+  store_tile(0);
+  if (nkt > 1) {
+    load_tile(BN);
+    store_tile(1);
   }
+  if (nkt > 2) load_tile(2 * BN);
+  u32x4 braw_a[NBR], braw_b[NBR];
+  load_bias(0, braw_a);
+  __syncthreads();
+
+  f32x16 s_a[NKB], s_b[NKB];
+  qk_tile(0, s_a);
+  int kt = 0;
+  for (; kt + 1 < nkt; kt += 2) {
+    iteration(kt, s_a, s_b, braw_a, braw_b);
+    iteration(kt + 1, s_b, s_a, braw_b, braw_a);
+  }
+  if (kt < nkt) iteration(kt, s_a, s_b, braw_a, braw_b);
 
   // ---- epilogue: O = O / l, LSE = m + ln l -----------------------------------
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = halves_sum(l_run);
   if (qvalid) {
     const float inv = 1.f / l_tot;
-    QT* orow = Op + (int64_t)qrow * p.so[2];
+    QT* orow = Op + qrow * p.so[2];
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int d0 = 32 * db + 16 * hf;

@@ -9,36 +9,47 @@
 namespace fb {
 
 // Everything one fused attention launch needs (passed by value as the kernel argument).
+// Strides are in elements and fit in 32 bits (checked by the C-ABI layer); the
+// per-(batch, head) base offsets are formed in 64 bits inside the kernel.
 struct AttnParams {
   const void* q;
   const void* k;
   const void* v;
   void* o;
   float* lse;
-  int64_t sq[3], sk[3], sv[3], so[3];
-  // low-rank factors (R columns, zero-padded to the template's RP)
-  const void* phq;
+  const void* phq;        // low-rank factors (R columns, zero-padded to the template's RP)
   const void* phk;
-  int64_t spq[3], spk[3];
+  const void* bias;       // dense bias
+  int sq[3], sk[3], sv[3], so[3];
+  int spq[3], spk[3];
+  int sb[3];
   int R;
-  int phq_vec, phk_vec;   // 1: rows are 16-byte aligned and R fills whole chunks -> vector loads
-  // dense bias
-  const void* bias;
-  int64_t sb[3];
-  int bias_vec;           // 1: rows 16-byte aligned -> vector loads
+  int flags;              // FLAG_* below
   int B, H, N;
-  int causal;
   float scale;
   int nqb;                // number of query blocks per (b, h)
 };
+constexpr int FLAG_CAUSAL = 1;
+constexpr int FLAG_PHQ_VEC = 2;   // phi_q rows 16-byte aligned -> vector loads
+constexpr int FLAG_PHK_VEC = 4;   // phi_k rows 16-byte aligned -> vector loads
+constexpr int FLAG_BIAS_VEC = 8;  // bias rows 16-byte aligned -> vector loads
 
-// Launch one fused attention forward for head dim 16/32/64/128.  mode 0: low-rank
-// factors padded to RP columns (0 = plain attention); mode 1: dense bias (RP = 0).
-// aux_dt is the factor or bias dtype.  FB_EUNSUPPORTED when no kernel instance matches.
-fb_status launch_attention_d16(int mode, fb_dtype dt, fb_dtype aux_dt, int RP, const AttnParams& p, hipStream_t s);
-fb_status launch_attention_d32(int mode, fb_dtype dt, fb_dtype aux_dt, int RP, const AttnParams& p, hipStream_t s);
-fb_status launch_attention_d64(int mode, fb_dtype dt, fb_dtype aux_dt, int RP, const AttnParams& p, hipStream_t s);
-fb_status launch_attention_d128(int mode, fb_dtype dt, fb_dtype aux_dt, int RP, const AttnParams& p, hipStream_t s);
+// Launch one fused attention forward; one function per head dim (16/32/64/128) and Q/K/V
+// element type.  mode 0: low-rank factors padded to RP columns (0 = plain attention);
+// mode 1: dense bias (RP = 0).  aux_dt is the factor or bias dtype.  FB_EUNSUPPORTED when
+// no kernel instance matches.
+fb_status launch_attention_d16_bf16(int mode, fb_dtype aux_dt, int RP, const AttnParams& p, hipStream_t s);
+fb_status launch_attention_d16_f16(int mode, fb_dtype aux_dt, int RP, const AttnParams& p, hipStream_t s);
+fb_status launch_attention_d16_f32(int mode, fb_dtype aux_dt, int RP, const AttnParams& p, hipStream_t s);
+fb_status launch_attention_d32_bf16(int mode, fb_dtype aux_dt, int RP, const AttnParams& p, hipStream_t s);
+fb_status launch_attention_d32_f16(int mode, fb_dtype aux_dt, int RP, const AttnParams& p, hipStream_t s);
+fb_status launch_attention_d32_f32(int mode, fb_dtype aux_dt, int RP, const AttnParams& p, hipStream_t s);
+fb_status launch_attention_d64_bf16(int mode, fb_dtype aux_dt, int RP, const AttnParams& p, hipStream_t s);
+fb_status launch_attention_d64_f16(int mode, fb_dtype aux_dt, int RP, const AttnParams& p, hipStream_t s);
+fb_status launch_attention_d64_f32(int mode, fb_dtype aux_dt, int RP, const AttnParams& p, hipStream_t s);
+fb_status launch_attention_d128_bf16(int mode, fb_dtype aux_dt, int RP, const AttnParams& p, hipStream_t s);
+fb_status launch_attention_d128_f16(int mode, fb_dtype aux_dt, int RP, const AttnParams& p, hipStream_t s);
+fb_status launch_attention_d128_f32(int mode, fb_dtype aux_dt, int RP, const AttnParams& p, hipStream_t s);
 
 // Exact closed-form factors / dense bias.  slopes_host: [H] (H <= kMaxSlopes) or NULL.
 constexpr int kMaxSlopes = 256;

@@ -178,8 +178,10 @@ typedef struct {
  * Alignment: q, k, v, o 16-byte aligned and their strides multiples of
  * 16 bytes / element size.  phi rows may be unaligned (slower loads).
  * Errors: FB_EINVAL (null pointers, negative sizes, misalignment, row strides
- * too small); FB_EUNSUPPORTED (D not in {16,32,64,128}, R above the limit, a
- * dtype pair not listed above); FB_EHIP.  B*H*N == 0 is a no-op returning FB_OK.
+ * too small); FB_EUNSUPPORTED (D not in {16,32,64,128}, or D = 128 with fp32
+ * Q/K/V; R above the limit; a dtype pair not listed above; element strides or
+ * N * row stride of any operand above 2^31 - 1); FB_EHIP.  B*H*N == 0 is a
+ * no-op returning FB_OK.
  */
 fb_status fb_attn_fwd_lowrank(const fb_attn_args* a, const void* phi_q, const void* phi_k,
                               fb_dtype phi_dt, int R, const int64_t sphi_q[3],

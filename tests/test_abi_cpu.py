@@ -215,3 +215,10 @@ def test_round_exact_helper_matches_numpy_half():
     x = x[np.abs(x) < 60000]
     np.testing.assert_array_equal(round_exact(x, "f16"), x.astype(np.float16).astype(np.float64))
     np.testing.assert_array_equal(round_exact(x, "f32"), x.astype(np.float32).astype(np.float64))
+
+
+def test_fp32_head_dim_limit_and_stride_limit():
+    a = _args(dt=fb.FB_F32, D=128, strides=(128 * 64, 128 * 64, 128))
+    assert _lowrank(a) == fb.FB_EUNSUPPORTED
+    big = _args(N=64, strides=(1 << 33, 4096, 64))           # batch stride beyond 32 bits
+    assert _lowrank(big) == fb.FB_EUNSUPPORTED
