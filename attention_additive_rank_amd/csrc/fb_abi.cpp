@@ -58,7 +58,7 @@ fb_status check_common(const fb_attn_args* a, const char* fn) {
   }
   if (a->lse && ((uintptr_t)a->lse & 3u)) FB_FAIL(FB_EINVAL, "%s: lse must be 4-byte aligned", fn);
   if (!std::isfinite(a->scale)) FB_FAIL(FB_EINVAL, "%s: scale must be finite", fn);
-  const int64_t nqb = (a->N + 127) / 128;
+  const int64_t nqb = (a->N + kAttnBlockM - 1) / kAttnBlockM;
   if (nqb * a->H * a->B > 0x7fffffffLL) FB_FAIL(FB_EUNSUPPORTED, "%s: grid too large", fn);
   for (int i = 0; i < 4; ++i)
     if (!strides_fit32(st[i], a->N)) FB_FAIL(FB_EUNSUPPORTED, "%s: %s strides exceed 32 bits", fn, nm[i]);
@@ -100,7 +100,7 @@ AttnParams base_params(const fb_attn_args* a) {
   p.N = a->N;
   p.flags = a->causal ? FLAG_CAUSAL : 0;
   p.scale = a->scale;
-  p.nqb = (a->N + 127) / 128;
+  p.nqb = (a->N + kAttnBlockM - 1) / kAttnBlockM;
   return p;
 }
 

@@ -10,22 +10,25 @@
 // the quadratic IO of the abstract and Fig. 1(c).
 //
 // Work decomposition
-//   * One workgroup = 4 wavefronts = 128 query rows of one (batch, head); each
-//     wavefront owns 32 query rows for the whole key loop.
-//   * Key tiles of 64 keys are staged in LDS (double-buffered) once per
-//     workgroup: K' rows (K then phi_k, zero-padded to RP columns) and V
-//     transposed (Vt[d][key]).  Global loads for tile t+2 are in flight while
-//     tile t is computed; no bounds branches inside the loop (rows past N are
-//     clamped on load and masked in the scores).
+//   * One workgroup = 8 wavefronts = 256 query rows of one (batch, head); each
+//     wavefront owns 32 query rows for the whole key loop.  Waves w and w+4 run
+//     on the same SIMD, so the two groups {0..3} and {4..7} pair up per SIMD.
+//   * Ping-pong schedule: per key tile each wavefront has a matrix phase
+//     (S(t+1) = K'(t+1) Q'^T and O += Vt(t) P(t)^T on the MFMA units) and a
+//     vector phase (online softmax of S(t+1)); the two groups run opposite
+//     phases between workgroup barriers, so on every SIMD one wave keeps the
+//     matrix core busy while the other does exp2/max/sum on the VALU.  The
+//     group in its vector phase also refills LDS for later tiles (group 1 the
+//     K' rows, group 0 the V rows), from registers loaded two phases earlier.
+//   * Key tiles of 64 keys are double-buffered in LDS: K' rows (K then phi_k,
+//     zero-padded to RP columns) and V transposed (Vt[d][key]).  Rows past N
+//     are clamped on load and masked in the scores (no bounds branches).
 //   * Scores are computed transposed, S^T = K' Q'^T, with 32x32 MFMAs
 //     (32x32x16 bf16/f16, 32x32x2 fp32).  With that orientation every lane owns
 //     ONE query (lane % 32) and 16 keys per 32-key block, so the row max / row
 //     sum of the online softmax are in-lane reductions plus a single exchange
 //     between the two half-waves, and P^T is already in the B-operand layout of
 //     the next product O^T = Vt P^T: P never leaves registers.
-//   * Software pipeline: the MFMAs of S(t+1) are independent of the softmax of
-//     tile t, so both are issued in the same stretch of code and the compiler
-//     interleaves matrix-core and vector work within each wavefront.
 //   * Lazy rescaling: the running row max only moves (and O, l are rescaled)
 //     when a tile's max exceeds it by more than 2^8 in exp2 units, so most
 //     tiles skip the O rescale; P then stays <= 2^8, exact in range for bf16.
@@ -56,9 +59,11 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int NW = 4;          // wavefronts per workgroup
+constexpr int NW = 8;          // wavefronts per workgroup: two groups of four
 constexpr int NT = NW * 64;    // threads per workgroup
+constexpr int GT = NT / 2;     // threads per group
 constexpr int BM = 32 * NW;    // query rows per workgroup
+static_assert(BM == kAttnBlockM, "host and kernel block sizes differ");
 constexpr int BN = 64;         // keys per LDS tile
 constexpr int NKB = BN / 32;   // 32-key blocks per tile
 constexpr float LOG2E = 1.4426950408889634f;
@@ -155,17 +160,25 @@ __device__ __forceinline__ u32x4 load_phi_chunk(const T* row, int c0, int R, boo
   return load_partial_chunk<T>(row, c0, R);
 }
 
-// max / sum of a value over the two half-waves (lanes l and l ^ 32), via ds_bpermute
-__device__ __forceinline__ float halves_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
-__device__ __forceinline__ float halves_sum(float x) { return x + __shfl_xor(x, 32); }
-
-// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int SG_VALU = 0x002 | 0x400;   // vector ALU incl. transcendental
-constexpr int SG_MFMA = 0x008;
-constexpr int SG_DS_READ = 0x100;
+// max / sum of a value over the two half-waves (lanes l and l ^ 32).  v_permlane32_swap
+// exchanges the upper half of one register with the lower half of the other, so after
+// swapping two copies of x every lane holds x and x of lane l ^ 32 in (a, b).  Written as
+// asm: the compiler's intrinsic folds the swap of two equal values into a no-op, and the
+// portable shuffle goes through ds_bpermute (an LDS round trip).  s_nop 1 covers the
+// VALU-write -> permlane-read hazard.
+__device__ __forceinline__ float halves_max(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return a + b;
+}
 
 template <typename QT, typename PT, int D, int RP, int MODE, typename BT, bool CAUSAL>
-__global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnParams p) {
+__global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   typedef typename Elem<QT>::Frag QFrag;
   typedef typename Elem<PT>::Frag PFrag;
   constexpr int ES = (int)sizeof(QT);
@@ -181,15 +194,14 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnParams p) {
   constexpr int DB = DP / 32;             // 32-wide head-dim blocks of the output
   constexpr int QSTEPS = D / KS;
   constexpr int PSTEPS = RP / KS;
-  constexpr int NMMA_QK = NKB * (QSTEPS + PSTEPS);
   constexpr int KCH = D / CE;             // chunks per K / V row
   constexpr int PCH = RP / CE;            // chunks per phi_k row
   constexpr int K_TOT = BN * KCH;         // K chunks per tile
   constexpr int P_TOT = BN * PCH;         // phi_k chunks per tile
   constexpr int V_TOT = (BN / 2) * KCH;   // V tasks per tile: one chunk column of a key pair
-  constexpr int KPT = (K_TOT + NT - 1) / NT;
-  constexpr int PPT = P_TOT > 0 ? (P_TOT + NT - 1) / NT : 0;
-  constexpr int VPT = (V_TOT + NT - 1) / NT;
+  constexpr int KPT = (K_TOT + GT - 1) / GT;
+  constexpr int PPT = P_TOT > 0 ? (P_TOT + GT - 1) / GT : 0;
+  constexpr int VPT = (V_TOT + GT - 1) / GT;
   constexpr int SK_BYTES = BN * PITCH_K;
   constexpr int SV_BYTES = DP * PITCH_V;
   static_assert(D % KS == 0 && RP % KS == 0 && D % CE == 0 && RP % CE == 0, "bad tile widths");
@@ -200,6 +212,8 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int grp = wave >> 2;     // waves w and w+4 share a SIMD: one of each group per SIMD
+  const int gtid = tid & (GT - 1);
   const int ln = lane & 31;
   const int hf = lane >> 5;
 
@@ -234,6 +248,8 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnParams p) {
   const int qrow = q0w + ln;
   const bool qvalid = qrow < N;
   const int qclamp = qvalid ? qrow : N - 1;
+  const int kend = CAUSAL ? min(N, q0 + BM) : N;
+  const int nkt = (kend + BN - 1) / BN;
 
   // Vt rows of head dims >= D (only when D < 32) are never written by the tile
   // stores: clear them once in both buffers so the discarded output rows stay finite.
@@ -264,13 +280,13 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnParams p) {
     }
   }
 
-  // ---- per-thread staging assignment (loop invariant) ------------------------
-  // K chunk i covers row c / KCH, chunk column c % KCH of the tile (c = tid + i*NT).
+  // ---- staging: group 1 streams K' tiles (K then phi_k), group 0 V tiles ----
+  // K chunk i of a group-1 thread covers row c / KCH, chunk column c % KCH (c = gtid + i*GT).
   const QT* k_ptr[KPT];
   int k_row[KPT], k_lds[KPT];
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
-    const int c = tid + i * NT;
+    const int c = gtid + i * GT;
     const int cc = c < K_TOT ? c : 0;
     k_row[i] = cc / KCH;
     k_ptr[i] = Kp + k_row[i] * p.sk[2] + (cc % KCH) * CE;
@@ -280,7 +296,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnParams p) {
   int p_row[PPT > 0 ? PPT : 1], p_col[PPT > 0 ? PPT : 1], p_lds[PPT > 0 ? PPT : 1];
 #pragma unroll
   for (int i = 0; i < PPT; ++i) {
-    const int c = tid + i * NT;
+    const int c = gtid + i * GT;
     const int cc = c < P_TOT ? c : 0;
     p_row[i] = cc / PCH;
     p_col[i] = (cc % PCH) * CE;
@@ -289,13 +305,13 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnParams p) {
   }
   // factor rows: 16-byte vector loads when every chunk is either full or past R
   const bool phk_fast = (RP == 0) || ((p.flags & FLAG_PHK_VEC) && p.R % CE == 0);
-  // V task i: key pair pr (keys 2pr, 2pr+1), chunk column vc; pairs run fastest
-  // across lanes so that each 32-bit LDS write of a wavefront hits distinct banks.
+  // V task i of a group-0 thread: key pair pr (keys 2pr, 2pr+1), chunk column vc;
+  // pairs run fastest across lanes so each 32-bit LDS write hits distinct banks.
   const QT* v_ptr[VPT];
   int v_pair[VPT], v_col[VPT];
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
-    const int c = tid + i * NT;
+    const int c = gtid + i * GT;
     const int cc = c < V_TOT ? c : 0;
     v_pair[i] = cc % (BN / 2);
     v_col[i] = cc / (BN / 2);
@@ -305,61 +321,53 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnParams p) {
   u32x4 kr[KPT], vr0[VPT], vr1[VPT];
   u32x4 pr[PPT > 0 ? PPT : 1];
 
-  auto load_tile = [&](int kb) {
-    if (kb + BN <= N) {           // whole tile inside the sequence: plain strided loads
-      const int ko = kb * p.sk[2], vo = kb * p.sv[2];
+  auto load_k = [&](int kb) {          // group 1: K' rows of the tile starting at key kb
+    const bool full = kb + BN <= N;
 #pragma unroll
-      for (int i = 0; i < KPT; ++i)
-        if (K_TOT % NT == 0 || tid + i * NT < K_TOT) kr[i] = ld16(k_ptr[i] + ko);
-#pragma unroll
-      for (int i = 0; i < VPT; ++i)
-        if (V_TOT % NT == 0 || tid + i * NT < V_TOT) {
-          vr0[i] = ld16(v_ptr[i] + vo);
-          vr1[i] = ld16(v_ptr[i] + vo + p.sv[2]);
-        }
-    } else {                      // tail tile: rows past N are clamped (and masked later)
-#pragma unroll
-      for (int i = 0; i < KPT; ++i)
-        if (K_TOT % NT == 0 || tid + i * NT < K_TOT) {
-          const int key = min(kb + k_row[i], N - 1);
-          kr[i] = ld16(k_ptr[i] + (key - k_row[i]) * p.sk[2]);
-        }
-#pragma unroll
-      for (int i = 0; i < VPT; ++i)
-        if (V_TOT % NT == 0 || tid + i * NT < V_TOT) {
-          const int k0 = min(kb + 2 * v_pair[i], N - 1), k1 = min(kb + 2 * v_pair[i] + 1, N - 1);
-          vr0[i] = ld16(v_ptr[i] + (k0 - 2 * v_pair[i]) * p.sv[2]);
-          vr1[i] = ld16(v_ptr[i] + (k1 - 2 * v_pair[i]) * p.sv[2]);
-        }
-    }
+    for (int i = 0; i < KPT; ++i)
+      if (K_TOT % GT == 0 || gtid + i * GT < K_TOT) {
+        const int key = full ? kb + k_row[i] : min(kb + k_row[i], N - 1);
+        kr[i] = ld16(k_ptr[i] + (key - k_row[i]) * p.sk[2]);
+      }
     if constexpr (PPT > 0) {
 #pragma unroll
-      for (int i = 0; i < PPT; ++i) {
-        if (P_TOT % NT == 0 || tid + i * NT < P_TOT) {
+      for (int i = 0; i < PPT; ++i)
+        if (P_TOT % GT == 0 || gtid + i * GT < P_TOT) {
           const int key = min(kb + p_row[i], N - 1);
           const PT* row = p_ptr[i] + (key - p_row[i]) * p.spk[2];
           if (phk_fast) pr[i] = p_col[i] < p.R ? ld16(row + p_col[i]) : u32x4{};
           else pr[i] = load_partial_chunk<PT>(row, p_col[i], p.R);
         }
-      }
     }
   };
-
-  auto store_tile = [&](int buf) {
-    unsigned char* k_base = sK + buf * SK_BYTES;
-    unsigned char* v_base = sV + buf * SV_BYTES;
+  auto store_k = [&](int buf) {
+    unsigned char* base = sK + buf * SK_BYTES;
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
-      if (K_TOT % NT == 0 || tid + i * NT < K_TOT) st16(k_base + k_lds[i], kr[i]);
+      if (K_TOT % GT == 0 || gtid + i * GT < K_TOT) st16(base + k_lds[i], kr[i]);
     if constexpr (PPT > 0) {
 #pragma unroll
       for (int i = 0; i < PPT; ++i)
-        if (P_TOT % NT == 0 || tid + i * NT < P_TOT) st16(k_base + p_lds[i], pr[i]);
+        if (P_TOT % GT == 0 || gtid + i * GT < P_TOT) st16(base + p_lds[i], pr[i]);
     }
+  };
+  auto load_v = [&](int kb) {          // group 0: V rows of the tile starting at key kb
+    const bool full = kb + BN <= N;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+      if (V_TOT % GT == 0 || gtid + i * GT < V_TOT) {
+        const int k0 = full ? kb + 2 * v_pair[i] : min(kb + 2 * v_pair[i], N - 1);
+        const int k1 = full ? k0 + 1 : min(kb + 2 * v_pair[i] + 1, N - 1);
+        vr0[i] = ld16(v_ptr[i] + (k0 - 2 * v_pair[i]) * p.sv[2]);
+        vr1[i] = ld16(v_ptr[i] + (k1 - 2 * v_pair[i]) * p.sv[2]);
+      }
+  };
+  auto store_v = [&](int buf) {        // transposed: Vt[d][key]
+    unsigned char* base = sV + buf * SV_BYTES;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      if (V_TOT % NT == 0 || tid + i * NT < V_TOT) {
-        unsigned char* dst = v_base + 2 * v_pair[i] * ES;
+      if (V_TOT % GT == 0 || gtid + i * GT < V_TOT) {
+        unsigned char* dst = base + 2 * v_pair[i] * ES;
         const int d0 = v_col[i] * CE;
         if constexpr (ES == 2) {
           // element j of both keys -> one 32-bit word (key 2pr low, key 2pr+1 high)
@@ -381,8 +389,44 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnParams p) {
     }
   };
 
-  // ---- S^T = K' Q'^T of one tile from LDS buffer `buf` -----------------------
-  auto qk_tile = [&](int buf, f32x16 (&sacc)[NKB]) {
+  // ---- per-wave state ----------------------------------------------------------
+  f32x16 sacc[NKB];                    // S^T of the tile being processed
+  u32x4 pfrag[KW == 1 ? 1 : NKB * 2];  // P^T (16-bit), B operand of the P V product
+  float p32[KW == 1 ? NKB : 1][16];    // P^T (fp32 path)
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  // dense bias of this lane's row, keys kb + 32*kb2 + 16*hf + [0, 16), loaded one tile ahead
+  constexpr int BES = MODE == 1 ? (int)sizeof(BT) : 2;
+  constexpr int BCH = BES;                  // 16-byte chunks per 16 keys
+  constexpr int NBR = MODE == 1 ? NKB * BCH : 1;
+  u32x4 braw[NBR];
+  auto load_bias = [&](int kb) {
+    if constexpr (MODE == 1) {
+      const BT* brow = Bp + qclamp * p.sb[2];
+      constexpr int BCE = 16 / BES;
+#pragma unroll
+      for (int kb2 = 0; kb2 < NKB; ++kb2) {
+        const int j0 = kb + 32 * kb2 + 16 * hf;
+        if ((p.flags & FLAG_BIAS_VEC) && j0 + 16 <= N) {
+#pragma unroll
+          for (int c = 0; c < BCH; ++c) braw[kb2 * BCH + c] = ld16(brow + j0 + c * BCE);
+        } else {
+#pragma unroll
+          for (int c = 0; c < BCH; ++c) braw[kb2 * BCH + c] = load_partial_chunk<BT>(brow, j0 + c * BCE, N);
+        }
+      }
+    }
+  };
+
+  // A wavefront whose queries all precede a key tile has nothing to do there.
+  auto active = [&](int t) { return !CAUSAL || t * BN <= q0w + 31; };
+
+  // S^T = K'(t) Q'^T from LDS buffer `buf`
+  auto qk = [&](int buf) {
     const unsigned char* k_base = sK + buf * SK_BYTES + ln * PITCH_K;
 #pragma unroll
     for (int kb2 = 0; kb2 < NKB; ++kb2) sacc[kb2] = f32x16{};
@@ -408,194 +452,169 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnParams p) {
     }
   };
 
-  f32x16 oacc[DB];
+  // O^T += Vt(t) P(t)^T from LDS buffer `buf`
+  auto pv = [&](int buf) {
+    const unsigned char* v_base = sV + buf * SV_BYTES + ln * PITCH_V + 16 * hf * ES;
 #pragma unroll
-  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-
-  const int kend = CAUSAL ? min(N, q0 + BM) : N;
-  const int nkt = (kend + BN - 1) / BN;
-
-  // dense bias of this lane's row, keys kb + 32*kb2 + 16*hf + [0, 16), kept raw
-  constexpr int BES = MODE == 1 ? (int)sizeof(BT) : 2;
-  constexpr int BCH = BES;                  // 16-byte chunks per 16 keys
-  constexpr int NBR = MODE == 1 ? NKB * BCH : 1;
-  auto load_bias = [&](int kb, u32x4 (&raw)[NBR]) {
-    if constexpr (MODE == 1) {
-      const BT* brow = Bp + qclamp * p.sb[2];
-      constexpr int BCE = 16 / BES;
+    for (int kb2 = 0; kb2 < NKB; ++kb2) {
+      if constexpr (KW == 1) {
 #pragma unroll
-      for (int kb2 = 0; kb2 < NKB; ++kb2) {
-        const int j0 = kb + 32 * kb2 + 16 * hf;
-        if ((p.flags & FLAG_BIAS_VEC) && j0 + 16 <= N) {
+        for (int u = 0; u < 16; ++u)
 #pragma unroll
-          for (int c = 0; c < BCH; ++c) raw[kb2 * BCH + c] = ld16(brow + j0 + c * BCE);
-        } else {
+          for (int db = 0; db < DB; ++db) {
+            const float a = *(const float*)(v_base + 32 * db * PITCH_V + (32 * kb2 + u) * ES);
+            oacc[db] = Mma<QT>::run(a, p32[kb2][u], oacc[db]);
+          }
+      } else {
 #pragma unroll
-          for (int c = 0; c < BCH; ++c) raw[kb2 * BCH + c] = load_partial_chunk<BT>(brow, j0 + c * BCE, N);
-        }
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const u32x4 a = ld16(v_base + 32 * db * PITCH_V + (32 * kb2 + 8 * u) * ES);
+            oacc[db] = Mma<QT>::run(a, pfrag[kb2 * 2 + u], oacc[db]);
+          }
       }
     }
   };
 
-  // One key tile.  Block A: bias add, mask, row max, rare rescale.  Block B: the
-  // MFMAs of S(t+1) interleaved with the exponentials of tile t.  Block C: O += Vt P^T.
-  // Then the LDS buffer just consumed is refilled with tile t+2.
-  auto iteration = [&](int kt, f32x16 (&s_cur)[NKB], f32x16 (&s_nxt)[NKB], u32x4 (&b_cur)[NBR],
-                       u32x4 (&b_nxt)[NBR]) {
-    const int kb = kt * BN;
-    const int buf = kt & 1;
-    // A wavefront whose queries all precede a key tile has nothing to do there
-    // (nor in any later tile).
-    const bool active = !CAUSAL || kb <= q0w + 31;
-    if (active) {
-      if constexpr (MODE == 1) {
-        if (kt + 1 < nkt) load_bias(kb + BN, b_nxt);
-#pragma unroll
-        for (int kb2 = 0; kb2 < NKB; ++kb2)
-#pragma unroll
-          for (int c = 0; c < BCH; ++c) {
-            const ChunkV<BT> e = __builtin_bit_cast(ChunkV<BT>, b_cur[kb2 * BCH + c]);
-#pragma unroll
-            for (int j = 0; j < 16 / BES; ++j) s_cur[kb2][c * (16 / BES) + j] += to_f32<BT>(e[j]);
-          }
-      }
-      // ---- mask: keys past N, and keys after the query when causal ------------
-      const bool need_mask = (kb + BN > N) || (CAUSAL && kb + BN - 1 > q0w);
-      if (need_mask) {
-        // keys j visible to this row: j < N and (causal) j <= qrow; the rest -> -inf
-#pragma unroll
-        for (int kb2 = 0; kb2 < NKB; ++kb2) {
-          const int j0 = kb + 32 * kb2 + 16 * hf;
-          int lim = N - j0;
-          if constexpr (CAUSAL) lim = min(lim, qrow + 1 - j0);
-          // One compare-select at a time: the scheduling fence keeps the compiler from
-          // hoisting all compares into simultaneously live scalar lane masks.
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            s_cur[kb2][r] = r < lim ? s_cur[kb2][r] : -INFINITY;
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }
-      }
-      // ---- online softmax with lazy rescaling (row = this lane's query) -------
-      float mx = -INFINITY;
+  // online softmax of tile t (scores in sacc) -> P(t); lazy rescaling of O and l
+  auto softmax = [&](int t) {
+    const int kb = t * BN;
+    if constexpr (MODE == 1) {
 #pragma unroll
       for (int kb2 = 0; kb2 < NKB; ++kb2)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kb2][r]);
-      mx = halves_max(mx);
-      const bool grow = mx > m_run + RESCALE_GAP;
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-        const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - mx) * LOG2E) : 1.f;  // 0 on the first tile
-        l_run *= alpha;
+        for (int c = 0; c < BCH; ++c) {
+          const ChunkV<BT> e = __builtin_bit_cast(ChunkV<BT>, braw[kb2 * BCH + c]);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-        m_run = grow ? mx : m_run;
-      }
-      const float ms = (m_run == -INFINITY ? 0.f : m_run) * LOG2E;
-
-      // ---- block B: S(t+1) on the matrix cores, exp of tile t on the VALU ----
-      qk_tile(buf ^ 1, s_nxt);
-      u32x4 pfrag[KW == 1 ? 1 : NKB * 2];
-      if constexpr (KW == 1) {
-#pragma unroll
-        for (int kb2 = 0; kb2 < NKB; ++kb2)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb2][r], LOG2E, -ms));
-            s_cur[kb2][r] = e;
-            l_run += e;
-          }
-      } else {
-        typedef QT T8 __attribute__((ext_vector_type(8)));
-        typedef QT T2 __attribute__((ext_vector_type(2)));
-        float lsum = 0.f;
-#pragma unroll
-        for (int kb2 = 0; kb2 < NKB; ++kb2)
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            T8 pb;
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-              pb[j] = from_f32<QT>(__builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb2][8 * u + j], LOG2E, -ms)));
-            pfrag[kb2 * 2 + u] = __builtin_bit_cast(u32x4, pb);
-            // row sum of the rounded probabilities (what the P V product uses)
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-              const T2 two = {pb[2 * m], pb[2 * m + 1]};
-              const T2 one = {from_f32<QT>(1.f), from_f32<QT>(1.f)};
-              if constexpr (sizeof(QT) == 2 && __is_same(QT, bf16_t))
-                lsum = __builtin_amdgcn_fdot2_f32_bf16(two, one, lsum, false);
-              else
-                lsum = __builtin_amdgcn_fdot2(two, one, lsum, false);
-            }
-          }
-        l_run += lsum;
-      }
-      // interleave: a few K' reads up front, then per MFMA one read and ~6 VALU ops
-      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 4, 0);
-#pragma unroll
-      for (int i = 0; i < NMMA_QK; ++i) {
-        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(SG_VALU, 6, 0);
-      }
-
-      // ---- block C: O^T += Vt P^T -----------------------------------------------
-      const unsigned char* v_base = sV + buf * SV_BYTES + ln * PITCH_V + 16 * hf * ES;
+          for (int j = 0; j < 16 / BES; ++j) sacc[kb2][c * (16 / BES) + j] += to_f32<BT>(e[j]);
+        }
+      if (t + 1 < nkt) load_bias(kb + BN);
+    }
+    // mask: keys past N, and keys after the query when causal
+    const bool need_mask = (kb + BN > N) || (CAUSAL && kb + BN - 1 > q0w);
+    if (need_mask) {
 #pragma unroll
       for (int kb2 = 0; kb2 < NKB; ++kb2) {
-        if constexpr (KW == 1) {
+        const int j0 = kb + 32 * kb2 + 16 * hf;
+        int lim = N - j0;
+        if constexpr (CAUSAL) lim = min(lim, qrow + 1 - j0);
+        // One compare-select at a time: the scheduling fence keeps the compiler from
+        // hoisting all compares into simultaneously live scalar lane masks.
 #pragma unroll
-          for (int u = 0; u < 16; ++u)
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-              const float a = *(const float*)(v_base + 32 * db * PITCH_V + (32 * kb2 + u) * ES);
-              oacc[db] = Mma<QT>::run(a, s_cur[kb2][u], oacc[db]);
-            }
-        } else {
-#pragma unroll
-          for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-              const u32x4 a = ld16(v_base + 32 * db * PITCH_V + (32 * kb2 + 8 * u) * ES);
-              oacc[db] = Mma<QT>::run(a, pfrag[kb2 * 2 + u], oacc[db]);
-            }
+        for (int r = 0; r < 16; ++r) {
+          sacc[kb2][r] = r < lim ? sacc[kb2][r] : -INFINITY;
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
-
-    // ---- refill the buffer just consumed with tile t+2; start loading t+3 ----
-    __syncthreads();
-    if (kt + 2 < nkt) {
-      store_tile(buf);
-      if (kt + 3 < nkt) load_tile(kb + 3 * BN);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb2][r]);
+    mx = halves_max(mx);
+    const bool grow = mx > m_run + RESCALE_GAP;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - mx) * LOG2E) : 1.f;  // 0 on the first tile
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      m_run = grow ? mx : m_run;
     }
-    __syncthreads();
+    const float ms = (m_run == -INFINITY ? 0.f : m_run) * LOG2E;
+    if constexpr (KW == 1) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb2][r], LOG2E, -ms));
+          p32[kb2][r] = e;
+          l_run += e;
+        }
+    } else {
+      typedef QT T8 __attribute__((ext_vector_type(8)));
+      typedef QT T2 __attribute__((ext_vector_type(2)));
+      float lsum = 0.f;
+#pragma unroll
+      for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          T8 pb;
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            pb[j] = from_f32<QT>(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb2][8 * u + j], LOG2E, -ms)));
+          pfrag[kb2 * 2 + u] = __builtin_bit_cast(u32x4, pb);
+          // row sum of the rounded probabilities (what the P V product uses)
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const T2 two = {pb[2 * m], pb[2 * m + 1]};
+            const T2 one = {from_f32<QT>(1.f), from_f32<QT>(1.f)};
+            if constexpr (__is_same(QT, bf16_t))
+              lsum = __builtin_amdgcn_fdot2_f32_bf16(two, one, lsum, false);
+            else
+              lsum = __builtin_amdgcn_fdot2(two, one, lsum, false);
+          }
+        }
+      l_run += lsum;
+    }
   };
 
-  // ---- prologue: tiles 0 and 1 into LDS, tile 2 in flight, S(0) ------------
-  load_tile(0);
-  store_tile(0);
-  if (nkt > 1) {
-    load_tile(BN);
-    store_tile(1);
+  // Matrix phase of tile t: S(t+1) = K'(t+1) Q'^T and O += Vt(t) P(t)^T.
+  auto mma_phase = [&](int t) {
+    if (t + 1 < nkt && active(t + 1)) qk((t + 1) & 1);
+    if (active(t)) pv(t & 1);
+  };
+
+  // ---- prologue: K'(0), K'(1), V(0) in LDS; K'(2), V(1) in flight; P(0) -------
+  if (grp == 1) {
+    load_k(0);
+    store_k(0);
+    if (nkt > 1) {
+      load_k(BN);
+      store_k(1);
+    }
+    if (nkt > 2) load_k(2 * BN);
+  } else {
+    load_v(0);
+    store_v(0);
+    if (nkt > 1) load_v(BN);
   }
-  if (nkt > 2) load_tile(2 * BN);
-  u32x4 braw_a[NBR], braw_b[NBR];
-  load_bias(0, braw_a);
+  load_bias(0);
+  __syncthreads();
+  qk(0);
+  softmax(0);
   __syncthreads();
 
-  f32x16 s_a[NKB], s_b[NKB];
-  qk_tile(0, s_a);
-  int kt = 0;
-  for (; kt + 1 < nkt; kt += 2) {
-    iteration(kt, s_a, s_b, braw_a, braw_b);
-    iteration(kt + 1, s_b, s_a, braw_b, braw_a);
+  // ---- ping-pong: per SIMD, one wave multiplies while the other does softmax ----
+  // group 0: phase A = MFMA(t) [S(t+1) = K'(t+1) Q'^T, O += Vt(t) P(t)], phase B = softmax(t+1)
+  // group 1: phase A = softmax(t) (t > 0),                               phase B = MFMA(t)
+  // The softmax group also refills LDS: group 1 K'(t+2) in phase A, group 0 V(t+1) in phase B.
+  for (int t = 0; t < nkt; ++t) {
+    const int kb = t * BN;
+    // ---- phase A ----
+    if (grp == 0) {
+      mma_phase(t);
+    } else {
+      if (t + 2 < nkt) {
+        store_k(t & 1);
+        if (t + 3 < nkt) load_k(kb + 3 * BN);
+      }
+      if (t > 0 && active(t)) softmax(t);
+    }
+    __syncthreads();
+    // ---- phase B ----
+    if (grp == 0) {
+      if (t + 1 < nkt) {
+        store_v((t + 1) & 1);
+        if (t + 2 < nkt) load_v(kb + 2 * BN);
+      }
+      if (t + 1 < nkt && active(t + 1)) softmax(t + 1);
+    } else {
+      mma_phase(t);
+    }
+    __syncthreads();
   }
-  if (kt < nkt) iteration(kt, s_a, s_b, braw_a, braw_b);
 
   // ---- epilogue: O = O / l, LSE = m + ln l -----------------------------------
   const float l_tot = halves_sum(l_run);
