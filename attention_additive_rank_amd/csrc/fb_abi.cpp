@@ -37,6 +37,9 @@ bool strides_fit32(const int64_t s[3], int N) {
   return s[0] <= lim && s[1] <= lim && s[2] <= lim && (int64_t)N * s[2] <= lim;
 }
 
+// A key tile of rows with this element stride spans fewer than 2^31 bytes.
+bool tile_fits32(int64_t row_stride, int es) { return (int64_t)kAttnKeyTile * row_stride * es <= 0x7fffffffLL; }
+
 fb_status check_common(const fb_attn_args* a, const char* fn) {
   if (!a) FB_FAIL(FB_EINVAL, "%s: null argument struct", fn);
   if (a->B < 0 || a->H < 0 || a->N < 0) FB_FAIL(FB_EINVAL, "%s: negative size", fn);
@@ -62,6 +65,9 @@ fb_status check_common(const fb_attn_args* a, const char* fn) {
   if (nqb * a->H * a->B > 0x7fffffffLL) FB_FAIL(FB_EUNSUPPORTED, "%s: grid too large", fn);
   for (int i = 0; i < 4; ++i)
     if (!strides_fit32(st[i], a->N)) FB_FAIL(FB_EUNSUPPORTED, "%s: %s strides exceed 32 bits", fn, nm[i]);
+  // key rows are addressed by 32-bit byte offsets within one key tile
+  if (!tile_fits32(a->sk[2], es) || !tile_fits32(a->sv[2], es))
+    FB_FAIL(FB_EUNSUPPORTED, "%s: k/v row strides too large", fn);
   return FB_OK;
 }
 
@@ -204,7 +210,7 @@ fb_status fb_attn_fwd_lowrank(const fb_attn_args* a, const void* phi_q, const vo
     if (!phi_q || !phi_k || !sphi_q || !sphi_k) FB_FAIL(FB_EINVAL, "%s: null factor pointer or strides", fn);
     for (int i = 0; i < 3; ++i)
       if (sphi_q[i] < 0 || sphi_k[i] < 0) FB_FAIL(FB_EINVAL, "%s: negative factor stride", fn);
-    if (!strides_fit32(sphi_q, a->N) || !strides_fit32(sphi_k, a->N))
+    if (!strides_fit32(sphi_q, a->N) || !strides_fit32(sphi_k, a->N) || !tile_fits32(sphi_k[2], esize(phi_dt)))
       FB_FAIL(FB_EUNSUPPORTED, "%s: factor strides exceed 32 bits", fn);
     if (a->N > 1 && (sphi_q[2] < R || sphi_k[2] < R)) FB_FAIL(FB_EINVAL, "%s: factor row stride < R", fn);
     const int es = esize(phi_dt);
@@ -218,9 +224,9 @@ fb_status fb_attn_fwd_lowrank(const fb_attn_args* a, const void* phi_q, const vo
     p.R = R;
     if (aligned16(phi_q) && rows_aligned(sphi_q, es)) p.flags |= FLAG_PHQ_VEC;
     if (aligned16(phi_k) && rows_aligned(sphi_k, es)) p.flags |= FLAG_PHK_VEC;
-    const int step = a->dt == FB_F32 ? 4 : 16;
+    const int step = a->dt == FB_F32 ? 8 : 16;
     RP = (R + step - 1) / step * step;
-    if (a->dt == FB_F32) { if (RP == 12) RP = 16; else if (RP > 16 && RP < 32) RP = 32; }
+    if (a->dt == FB_F32) { if (RP == 24) RP = 32; }
     else { if (RP == 48) RP = 64; else if (RP > 64) RP = 128; }
   }
   const fb_dtype aux = R > 0 ? phi_dt : a->dt;

@@ -11,19 +11,33 @@
 namespace fb {
 namespace attn {
 
-template <typename QT, typename PT, int D, int RP, int MODE, typename BT>
-static fb_status launch_one(const AttnParams& p, hipStream_t stream) {
+template <typename QT, typename PT, int D, int RP, int MODE, typename BT, bool PHI_DMA>
+static fb_status launch_kernel(const AttnParams& p, hipStream_t stream) {
   const int64_t grid = (int64_t)p.nqb * p.H * p.B;
   if (p.flags & FLAG_CAUSAL)
-    hipLaunchKernelGGL((attn_fwd_kernel<QT, PT, D, RP, MODE, BT, true>), dim3((unsigned)grid), dim3(NT), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<QT, PT, D, RP, MODE, BT, true, PHI_DMA>), dim3((unsigned)grid), dim3(NT), 0,
+                       stream, p);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<QT, PT, D, RP, MODE, BT, false>), dim3((unsigned)grid), dim3(NT), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<QT, PT, D, RP, MODE, BT, false, PHI_DMA>), dim3((unsigned)grid), dim3(NT), 0,
+                       stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_error("attention launch failed: %s", hipGetErrorString(e));
     return FB_EHIP;
   }
   return FB_OK;
+}
+
+// phi_k goes to LDS by direct 16-byte loads when its rows are 16-byte aligned and R is a
+// multiple of a chunk; otherwise through registers.
+template <typename QT, typename PT, int D, int RP, int MODE, typename BT>
+static fb_status launch_one(const AttnParams& p, hipStream_t stream) {
+  if constexpr (RP > 0) {
+    constexpr int CE = 16 / (int)sizeof(PT);
+    if (!((p.flags & FLAG_PHK_VEC) && p.R % CE == 0))
+      return launch_kernel<QT, PT, D, RP, MODE, BT, false>(p, stream);
+  }
+  return launch_kernel<QT, PT, D, RP, MODE, BT, true>(p, stream);
 }
 
 template <typename QT, typename PT, int D>
@@ -37,7 +51,6 @@ static fb_status lowrank_rp(int RP, const AttnParams& p, hipStream_t s) {
     }
   } else {
     switch (RP) {
-      case 4: return launch_one<QT, PT, D, 4, 0, QT>(p, s);
       case 8: return launch_one<QT, PT, D, 8, 0, QT>(p, s);
       case 16: return launch_one<QT, PT, D, 16, 0, QT>(p, s);
       case 32: return launch_one<QT, PT, D, 32, 0, QT>(p, s);

@@ -14,28 +14,28 @@
 //     wavefront owns 32 query rows for the whole key loop.  Waves w and w+4 run
 //     on the same SIMD, so the two groups {0..3} and {4..7} pair up per SIMD.
 //   * Ping-pong schedule: per key tile each wavefront has a matrix phase
-//     (S(t+1) = K'(t+1) Q'^T and O += Vt(t) P(t)^T on the MFMA units) and a
+//     (S(t+1) = K'(t+1) Q'^T and O += V(t)^T P(t)^T on the MFMA units) and a
 //     vector phase (online softmax of S(t+1)); the two groups run opposite
 //     phases between workgroup barriers, so on every SIMD one wave keeps the
-//     matrix core busy while the other does exp2/max/sum on the VALU.  The
-//     group in its vector phase also refills LDS for later tiles (group 1 the
-//     K' rows, group 0 the V rows), from registers loaded two phases earlier.
+//     matrix core busy while the other does exp2/max/sum on the VALU.
 //   * Key tiles of 64 keys are double-buffered in LDS: K' rows (K then phi_k,
-//     zero-padded to RP columns) and V transposed (Vt[d][key]).  Rows past N
+//     zero-padded to RP columns) and V rows.  The group in its matrix phase
+//     fills them with direct global->LDS loads (16 bytes per lane, no register
+//     round trip, no VALU), two tiles ahead for K' and one for V.  Rows past N
 //     are clamped on load and masked in the scores (no bounds branches).
+//   * V stays row-major in LDS; the A operand of O^T = V^T P^T comes from
+//     64-bit transpose reads (ds_read_b64_tr_b16), four keys per read.
 //   * Scores are computed transposed, S^T = K' Q'^T, with 32x32 MFMAs
 //     (32x32x16 bf16/f16, 32x32x2 fp32).  With that orientation every lane owns
 //     ONE query (lane % 32) and 16 keys per 32-key block, so the row max / row
 //     sum of the online softmax are in-lane reductions plus a single exchange
 //     between the two half-waves, and P^T is already in the B-operand layout of
-//     the next product O^T = Vt P^T: P never leaves registers.
+//     the next product O^T = V^T P^T: P never leaves registers.
 //   * Lazy rescaling: the running row max only moves (and O, l are rescaled)
 //     when a tile's max exceeds it by more than 2^8 in exp2 units, so most
 //     tiles skip the O rescale; P then stays <= 2^8, exact in range for bf16.
-//   * K' rows and Vt rows are permuted in LDS so that lane half h holds keys
-//     16h..16h+15 of each 32-key block (and, in the output, head dims
-//     16h..16h+15 of each 32-dim block): bias reads, the causal mask and the
-//     O stores then touch contiguous runs.
+//   * K' rows are permuted in LDS so that lane half h holds keys 16h..16h+15
+//     of each 32-key block: bias reads and the causal mask touch contiguous runs.
 //   * The factor columns of K' / Q' go through their own MFMA chain in the
 //     factor dtype (PT), accumulating into the same fp32 score tile.
 //   * Workgroup ids are remapped so that the query blocks of one (b, h) run on
@@ -112,6 +112,10 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
 __host__ __device__ constexpr int perm_row(int k) {
   return (k & ~31) | (((k & 15) >> 2) << 3) | (((k >> 4) & 1) << 2) | (k & 3);
 }
+// The inverse: the logical index held by MFMA row r.
+__host__ __device__ constexpr int inv_perm_row(int r) {
+  return (r & ~31) | (((r >> 2) & 1) << 4) | (((r & 31) >> 3) << 2) | (r & 3);
+}
 
 // Scale the KW query elements of one fragment by s and round them back to T.
 template <typename T>
@@ -177,7 +181,23 @@ __device__ __forceinline__ float halves_sum(float x) {
   return a + b;
 }
 
-template <typename QT, typename PT, int D, int RP, int MODE, typename BT, bool CAUSAL>
+typedef __attribute__((address_space(1))) void global_void;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// 16 bytes global -> LDS without a register round trip: lane l of the wavefront writes
+// lds_base + 16 * l (lds_base must be the same for the whole wavefront).
+__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)lds_base, 16, 0, 0);
+}
+
+// 64-bit transpose read of 16-bit elements (ds_read_b64_tr_b16): within each group of
+// 16 lanes, value j of output lane 4a + c is element c of the 64-bit row read by lane 4j + a.
+__device__ __forceinline__ s16x4 lds_read_tr16(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+}
+
+template <typename QT, typename PT, int D, int RP, int MODE, typename BT, bool CAUSAL, bool PHI_DMA>
 __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   typedef typename Elem<QT>::Frag QFrag;
   typedef typename Elem<PT>::Frag PFrag;
@@ -187,33 +207,40 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   constexpr int KW = Elem<QT>::KW;        // k elements per lane per MFMA
   constexpr int KS = 2 * KW;              // k per MFMA
   constexpr int CE = 16 / ES;             // elements per 16-byte chunk
-  constexpr int W = D + RP;               // width of the augmented contraction
-  constexpr int PITCH_K = W * ES + 16;    // LDS bytes per K' row (+16: conflict-free 128-bit reads)
-  constexpr int DP = D < 32 ? 32 : D;     // Vt rows, padded to one 32-row MFMA block
-  constexpr int PITCH_V = BN * ES + 16;
+  constexpr int DP = D < 32 ? 32 : D;     // V width in LDS, at least one 32-wide MFMA block
   constexpr int DB = DP / 32;             // 32-wide head-dim blocks of the output
   constexpr int QSTEPS = D / KS;
   constexpr int PSTEPS = RP / KS;
   constexpr int KCH = D / CE;             // chunks per K / V row
-  constexpr int PCH = RP / CE;            // chunks per phi_k row
-  constexpr int K_TOT = BN * KCH;         // K chunks per tile
-  constexpr int P_TOT = BN * PCH;         // phi_k chunks per tile
-  constexpr int V_TOT = (BN / 2) * KCH;   // V tasks per tile: one chunk column of a key pair
-  constexpr int KPT = (K_TOT + GT - 1) / GT;
-  constexpr int PPT = P_TOT > 0 ? (P_TOT + GT - 1) / GT : 0;
-  constexpr int VPT = (V_TOT + GT - 1) / GT;
-  constexpr int SK_BYTES = BN * PITCH_K;
-  constexpr int SV_BYTES = DP * PITCH_V;
+  constexpr int PCH = RP / CE;            // chunks per (padded) phi_k row
+  // Both tiles are stored chunk-column-major: column c holds 16-byte chunk c of the 64
+  // rows of the tile, row r at byte 16 r.  K' columns are 1024 bytes apart: a 128-bit
+  // read of rows 32 kb2 + lane is then contiguous per half-wave.  V columns are padded
+  // so that the reads of the P V product hit distinct banks: 64 bytes for the transpose
+  // reads (two adjacent columns, four rows each), 16 bytes for the fp32 reads (eight
+  // columns, one row).
+  constexpr int CBK = BN * 16;
+  constexpr int CBV = BN * 16 + (ES == 2 ? 64 : 16);
+  constexpr int SK_BYTES = (KCH + PCH) * CBK;
+  constexpr int SV_BYTES = (DP / CE) * CBV;
+  constexpr int NDMA = KCH + PCH + KCH;   // 64-row chunk columns per tile: K, phi_k, V
+  constexpr int DPW = (NDMA + 3) / 4;     // column loads per wavefront of the issuing group
+  static_assert(BN == 64 && BN == kAttnKeyTile, "one direct load fills one 64-row chunk column");
   static_assert(D % KS == 0 && RP % KS == 0 && D % CE == 0 && RP % CE == 0, "bad tile widths");
+  static_assert(KW > 1 || (D % 8 == 0 && RP % 8 == 0), "fp32 k order pairs chunk columns");
 
-  __shared__ __attribute__((aligned(16))) unsigned char sK[2 * SK_BYTES];
-  __shared__ __attribute__((aligned(16))) unsigned char sV[2 * SV_BYTES];
+  // Four separate LDS objects rather than two double buffers: with the key loop unrolled by
+  // two every access names its buffer statically, so the compiler can tell that a direct
+  // load in flight never writes the buffer being read, and does not wait for it.
+  __shared__ __attribute__((aligned(16))) unsigned char sK0[SK_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char sK1[SK_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char sV0[SV_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char sV1[SV_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2;     // waves w and w+4 share a SIMD: one of each group per SIMD
-  const int gtid = tid & (GT - 1);
   const int ln = lane & 31;
   const int hf = lane >> 5;
 
@@ -251,143 +278,110 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   const int kend = CAUSAL ? min(N, q0 + BM) : N;
   const int nkt = (kend + BN - 1) / BN;
 
-  // Vt rows of head dims >= D (only when D < 32) are never written by the tile
-  // stores: clear them once in both buffers so the discarded output rows stay finite.
-  if constexpr (D < DP) {
-    for (int i = tid; i < 2 * (DP - D) * BN; i += NT) {
-      const int buf = i / ((DP - D) * BN), r = i % ((DP - D) * BN);
-      const int d = D + r / BN, key = r % BN;
-      unsigned char* dst = sV + buf * SV_BYTES + perm_row(d) * PITCH_V + key * ES;
-      if constexpr (ES == 2) *(uint16_t*)dst = 0; else *(uint32_t*)dst = 0;
-    }
-  }
-
   // ---- Q' fragments (B operand of S^T = K' Q'^T), resident for the whole loop
+  // 16-bit: k-step t of lane half h covers chunk 2t + h.  fp32 (one element per lane and
+  // k-step): k-step t of half h takes element 4 (t % 4) ... of chunk 2 (t / 4) + h, i.e.
+  // column 8 (t / 4) + 4 h + t % 4, so one 128-bit read of K' serves four k-steps.
   QFrag qf[QSTEPS];
   PFrag pf[PSTEPS > 0 ? PSTEPS : 1];
+  auto col32 = [&](int t) __attribute__((always_inline)) { return 8 * (t >> 2) + 4 * hf + (t & 3); };
 #pragma unroll
   for (int t = 0; t < QSTEPS; ++t) {
-    if constexpr (KW == 1) qf[t] = scale_frag<QT>(Qp[qclamp * p.sq[2] + KS * t + hf], p.scale);
+    if constexpr (KW == 1) qf[t] = scale_frag<QT>(Qp[qclamp * p.sq[2] + col32(t)], p.scale);
     else qf[t] = scale_frag<QT>(ld16(Qp + qclamp * p.sq[2] + KS * t + KW * hf), p.scale);
   }
   if constexpr (RP > 0) {
     const PT* prow = PQp + qclamp * p.spq[2];
 #pragma unroll
     for (int t = 0; t < PSTEPS; ++t) {
-      const int c0 = KS * t + KW * hf;
-      if constexpr (KW == 1) pf[t] = c0 < p.R ? prow[c0] : 0.f;
-      else pf[t] = load_phi_chunk<PT>(prow, c0, p.R, (p.flags & FLAG_PHQ_VEC) && c0 + KW <= p.R);
-    }
-  }
-
-  // ---- staging: group 1 streams K' tiles (K then phi_k), group 0 V tiles ----
-  // K chunk i of a group-1 thread covers row c / KCH, chunk column c % KCH (c = gtid + i*GT).
-  const QT* k_ptr[KPT];
-  int k_row[KPT], k_lds[KPT];
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const int c = gtid + i * GT;
-    const int cc = c < K_TOT ? c : 0;
-    k_row[i] = cc / KCH;
-    k_ptr[i] = Kp + k_row[i] * p.sk[2] + (cc % KCH) * CE;
-    k_lds[i] = perm_row(k_row[i]) * PITCH_K + (cc % KCH) * 16;
-  }
-  const PT* p_ptr[PPT > 0 ? PPT : 1];
-  int p_row[PPT > 0 ? PPT : 1], p_col[PPT > 0 ? PPT : 1], p_lds[PPT > 0 ? PPT : 1];
-#pragma unroll
-  for (int i = 0; i < PPT; ++i) {
-    const int c = gtid + i * GT;
-    const int cc = c < P_TOT ? c : 0;
-    p_row[i] = cc / PCH;
-    p_col[i] = (cc % PCH) * CE;
-    p_ptr[i] = PKp + p_row[i] * p.spk[2];
-    p_lds[i] = perm_row(p_row[i]) * PITCH_K + D * ES + (cc % PCH) * 16;
-  }
-  // factor rows: 16-byte vector loads when every chunk is either full or past R
-  const bool phk_fast = (RP == 0) || ((p.flags & FLAG_PHK_VEC) && p.R % CE == 0);
-  // V task i of a group-0 thread: key pair pr (keys 2pr, 2pr+1), chunk column vc;
-  // pairs run fastest across lanes so each 32-bit LDS write hits distinct banks.
-  const QT* v_ptr[VPT];
-  int v_pair[VPT], v_col[VPT];
-#pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const int c = gtid + i * GT;
-    const int cc = c < V_TOT ? c : 0;
-    v_pair[i] = cc % (BN / 2);
-    v_col[i] = cc / (BN / 2);
-    v_ptr[i] = Vp + (2 * v_pair[i]) * p.sv[2] + v_col[i] * CE;
-  }
-
-  u32x4 kr[KPT], vr0[VPT], vr1[VPT];
-  u32x4 pr[PPT > 0 ? PPT : 1];
-
-  auto load_k = [&](int kb) {          // group 1: K' rows of the tile starting at key kb
-    const bool full = kb + BN <= N;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i)
-      if (K_TOT % GT == 0 || gtid + i * GT < K_TOT) {
-        const int key = full ? kb + k_row[i] : min(kb + k_row[i], N - 1);
-        kr[i] = ld16(k_ptr[i] + (key - k_row[i]) * p.sk[2]);
+      if constexpr (KW == 1) {
+        const int c = col32(t);
+        pf[t] = c < p.R ? prow[c] : 0.f;
+      } else {
+        const int c0 = KS * t + KW * hf;
+        pf[t] = load_phi_chunk<PT>(prow, c0, p.R, (p.flags & FLAG_PHQ_VEC) && c0 + KW <= p.R);
       }
-    if constexpr (PPT > 0) {
-#pragma unroll
-      for (int i = 0; i < PPT; ++i)
-        if (P_TOT % GT == 0 || gtid + i * GT < P_TOT) {
-          const int key = min(kb + p_row[i], N - 1);
-          const PT* row = p_ptr[i] + (key - p_row[i]) * p.spk[2];
-          if (phk_fast) pr[i] = p_col[i] < p.R ? ld16(row + p_col[i]) : u32x4{};
-          else pr[i] = load_partial_chunk<PT>(row, p_col[i], p.R);
-        }
     }
-  };
-  auto store_k = [&](int buf) {
-    unsigned char* base = sK + buf * SK_BYTES;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i)
-      if (K_TOT % GT == 0 || gtid + i * GT < K_TOT) st16(base + k_lds[i], kr[i]);
-    if constexpr (PPT > 0) {
-#pragma unroll
-      for (int i = 0; i < PPT; ++i)
-        if (P_TOT % GT == 0 || gtid + i * GT < P_TOT) st16(base + p_lds[i], pr[i]);
-    }
-  };
-  auto load_v = [&](int kb) {          // group 0: V rows of the tile starting at key kb
+  }
+
+  // ---- tile staging by direct global -> LDS loads ---------------------------
+  // Column load n of a tile: n < KCH is K chunk n, n < KCH + PCH is phi_k chunk n - KCH,
+  // the rest V chunk n - KCH - PCH.  Lane l loads row l: key inv_perm_row(l) for K' (so
+  // that lane half h of the scores holds keys 16h..16h+15), key l for V.  Wavefront w of
+  // the issuing group takes loads w, w+4, w+8, ...
+  // With PHI_DMA false (phi_k rows not 16-byte loadable: unaligned, or R not a multiple of
+  // a chunk) the phi_k columns are staged through registers instead (phi_load / phi_store).
+  constexpr bool phk_fast = PHI_DMA;
+  const int npch = phk_fast ? p.R / CE : 0;     // phi_k columns that the direct path loads
+  const int gw = wave & 3;
+  const int keyk = inv_perm_row(lane);
+  const uint32_t offk = (uint32_t)(min(keyk, N - 1) * p.sk[2] * ES);
+  const uint32_t offp = RP > 0 ? (uint32_t)(min(keyk, N - 1) * p.spk[2] * ES) : 0u;
+  const uint32_t offv = (uint32_t)(min(lane, N - 1) * p.sv[2] * ES);
+  // issue the loads of tile kb: K' into dK (do_k), V into dV (do_v)
+  auto dma_tile = [&](int kb, unsigned char* dK, unsigned char* dV, bool do_k, bool do_v) __attribute__((always_inline)) {
     const bool full = kb + BN <= N;
+    // byte offset of this lane's row: rows past N repeat row N-1 (finite; masked scores)
+    auto row_off = [&](uint32_t off_full, int key, int stride) __attribute__((always_inline)) {
+      return full ? off_full : (uint32_t)((min(kb + key, N - 1) - kb) * (stride * ES));
+    };
 #pragma unroll
-    for (int i = 0; i < VPT; ++i)
-      if (V_TOT % GT == 0 || gtid + i * GT < V_TOT) {
-        const int k0 = full ? kb + 2 * v_pair[i] : min(kb + 2 * v_pair[i], N - 1);
-        const int k1 = full ? k0 + 1 : min(kb + 2 * v_pair[i] + 1, N - 1);
-        vr0[i] = ld16(v_ptr[i] + (k0 - 2 * v_pair[i]) * p.sv[2]);
-        vr1[i] = ld16(v_ptr[i] + (k1 - 2 * v_pair[i]) * p.sv[2]);
+    for (int i = 0; i < DPW; ++i) {
+      const int n = gw + 4 * i;
+      if (n < KCH) {
+        if (do_k)
+          dma16((const char*)(Kp + (int64_t)kb * p.sk[2] + n * CE) + row_off(offk, keyk, p.sk[2]),
+                dK + n * CBK);
+      } else if (n < KCH + PCH) {
+        if (do_k && n - KCH < npch)
+          dma16((const char*)(PKp + (int64_t)kb * p.spk[2] + (n - KCH) * CE) + row_off(offp, keyk, p.spk[2]),
+                dK + n * CBK);
+      } else if (n < NDMA) {
+        const int c = n - KCH - PCH;
+        if (do_v)
+          dma16((const char*)(Vp + (int64_t)kb * p.sv[2] + c * CE) + row_off(offv, lane, p.sv[2]),
+                dV + c * CBV);
       }
+    }
   };
-  auto store_v = [&](int buf) {        // transposed: Vt[d][key]
-    unsigned char* base = sV + buf * SV_BYTES;
+  // phi_k columns of K' tiles through registers: the softmax group loads tile t+3 while
+  // it stores tile t+2.  Chunk s of a tile is column s / BN, row s % BN, zero beyond R.
+  constexpr int NPS = (BN * (PCH > 0 ? PCH : 1) + GT - 1) / GT;
+  u32x4 phreg[NPS];
+  const int gtid = tid & (GT - 1);
+  auto phi_load = [&](int kb) __attribute__((always_inline)) {
+    if constexpr (PCH > 0 && !phk_fast) {
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      if (V_TOT % GT == 0 || gtid + i * GT < V_TOT) {
-        unsigned char* dst = base + 2 * v_pair[i] * ES;
-        const int d0 = v_col[i] * CE;
-        if constexpr (ES == 2) {
-          // element j of both keys -> one 32-bit word (key 2pr low, key 2pr+1 high)
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const uint32_t lo = __builtin_amdgcn_perm(vr1[i][m], vr0[i][m], 0x05040100u);
-            const uint32_t hi = __builtin_amdgcn_perm(vr1[i][m], vr0[i][m], 0x07060302u);
-            *(uint32_t*)(dst + perm_row(d0 + 2 * m) * PITCH_V) = lo;
-            *(uint32_t*)(dst + perm_row(d0 + 2 * m + 1) * PITCH_V) = hi;
-          }
-        } else {
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            u32x2 w2 = {vr0[i][m], vr1[i][m]};
-            *(u32x2*)(dst + perm_row(d0 + m) * PITCH_V) = w2;
-          }
+      for (int i = 0; i < NPS; ++i) {
+        int s = gtid + GT * i;
+        // opaque to loop-invariant code motion: otherwise every element offset of the
+        // chunk is precomputed and held in registers for the whole key loop
+        asm volatile("" : "+v"(s));
+        if (s < BN * PCH) {
+          const int key = min(kb + inv_perm_row(s % BN), N - 1);
+          phreg[i] = load_partial_chunk<PT>(PKp + key * p.spk[2], (s / BN) * CE, p.R);
         }
       }
     }
   };
+  auto phi_store = [&](unsigned char* dK) __attribute__((always_inline)) {
+    if constexpr (PCH > 0 && !phk_fast) {
+#pragma unroll
+      for (int i = 0; i < NPS; ++i) {
+        const int s = gtid + GT * i;
+        if (s < BN * PCH) st16(dK + KCH * CBK + s * 16, phreg[i]);
+      }
+    }
+  };
+  // On the direct path phi_k columns at or beyond R are never loaded: zero them once.
+  if constexpr (RP > 0 && phk_fast) {
+    for (int s = tid; s < BN * PCH; s += NT) {
+      if (s / BN >= npch) {
+        st16(sK0 + KCH * CBK + s * 16, u32x4{0, 0, 0, 0});
+        st16(sK1 + KCH * CBK + s * 16, u32x4{0, 0, 0, 0});
+      }
+    }
+  }
 
   // ---- per-wave state ----------------------------------------------------------
   f32x16 sacc[NKB];                    // S^T of the tile being processed
@@ -404,7 +398,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   constexpr int BCH = BES;                  // 16-byte chunks per 16 keys
   constexpr int NBR = MODE == 1 ? NKB * BCH : 1;
   u32x4 braw[NBR];
-  auto load_bias = [&](int kb) {
+  auto load_bias = [&](int kb) __attribute__((always_inline)) {
     if constexpr (MODE == 1) {
       const BT* brow = Bp + qclamp * p.sb[2];
       constexpr int BCE = 16 / BES;
@@ -423,46 +417,65 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   };
 
   // A wavefront whose queries all precede a key tile has nothing to do there.
-  auto active = [&](int t) { return !CAUSAL || t * BN <= q0w + 31; };
+  auto active = [&](int t) __attribute__((always_inline)) { return !CAUSAL || t * BN <= q0w + 31; };
 
-  // S^T = K'(t) Q'^T from LDS buffer `buf`
-  auto qk = [&](int buf) {
-    const unsigned char* k_base = sK + buf * SK_BYTES + ln * PITCH_K;
+  // S^T = K'(t) Q'^T from the K' tile at sKt: lane (ln, h) reads row 32 kb2 + ln of chunk
+  // column 2t + h (16-bit) or 2 (t / 4) + h (fp32, four k-steps per read).
+  auto qk = [&](const unsigned char* sKt) __attribute__((always_inline)) {
+    const unsigned char* k_base = sKt + ln * 16 + hf * CBK;
 #pragma unroll
     for (int kb2 = 0; kb2 < NKB; ++kb2) sacc[kb2] = f32x16{};
+    if constexpr (KW == 1) {
 #pragma unroll
-    for (int t = 0; t < QSTEPS; ++t) {
-#pragma unroll
-      for (int kb2 = 0; kb2 < NKB; ++kb2) {
-        const unsigned char* a = k_base + 32 * kb2 * PITCH_K + (KS * t + KW * hf) * ES;
-        if constexpr (KW == 1) sacc[kb2] = Mma<QT>::run(*(const float*)a, qf[t], sacc[kb2]);
-        else sacc[kb2] = Mma<QT>::run(ld16(a), qf[t], sacc[kb2]);
-      }
-    }
-    if constexpr (RP > 0) {
-#pragma unroll
-      for (int t = 0; t < PSTEPS; ++t) {
+      for (int t4 = 0; t4 < QSTEPS / 4; ++t4)
 #pragma unroll
         for (int kb2 = 0; kb2 < NKB; ++kb2) {
-          const unsigned char* a = k_base + 32 * kb2 * PITCH_K + (D + KS * t + KW * hf) * ES;
-          if constexpr (KW == 1) sacc[kb2] = Mma<PT>::run(*(const float*)a, pf[t], sacc[kb2]);
-          else sacc[kb2] = Mma<PT>::run(ld16(a), pf[t], sacc[kb2]);
+          const f32x4 a = __builtin_bit_cast(f32x4, ld16(k_base + 2 * t4 * CBK + 32 * kb2 * 16));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sacc[kb2] = Mma<QT>::run(a[e], qf[4 * t4 + e], sacc[kb2]);
         }
-      }
+#pragma unroll
+      for (int t4 = 0; t4 < PSTEPS / 4; ++t4)
+#pragma unroll
+        for (int kb2 = 0; kb2 < NKB; ++kb2) {
+          const f32x4 a = __builtin_bit_cast(f32x4, ld16(k_base + (KCH + 2 * t4) * CBK + 32 * kb2 * 16));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sacc[kb2] = Mma<PT>::run(a[e], pf[4 * t4 + e], sacc[kb2]);
+        }
+    } else {
+#pragma unroll
+      for (int t = 0; t < QSTEPS; ++t)
+#pragma unroll
+        for (int kb2 = 0; kb2 < NKB; ++kb2)
+          sacc[kb2] = Mma<QT>::run(ld16(k_base + 2 * t * CBK + 32 * kb2 * 16), qf[t], sacc[kb2]);
+#pragma unroll
+      for (int t = 0; t < PSTEPS; ++t)
+#pragma unroll
+        for (int kb2 = 0; kb2 < NKB; ++kb2)
+          sacc[kb2] = Mma<PT>::run(ld16(k_base + (KCH + 2 * t) * CBK + 32 * kb2 * 16), pf[t], sacc[kb2]);
     }
   };
 
-  // O^T += Vt(t) P(t)^T from LDS buffer `buf`
-  auto pv = [&](int buf) {
-    const unsigned char* v_base = sV + buf * SV_BYTES + ln * PITCH_V + 16 * hf * ES;
+  // O^T += V(t)^T P(t)^T from the V tile at sVt.  MFMA row m of head-dim
+  // block db is head dim 32 db + m; k-slot j of lane half h in k-step u of key block kb2
+  // is key 32 kb2 + 16 h + 8 u + j, matching the registers of P.
+  // 16-bit: each A fragment is two transpose reads of four keys.  Lane 4 jj + a of a
+  // 16-lane group g reads key (16 h + 8 u + 4 q + jj), head dims 16 (g & 1) + 4 a .. + 3,
+  // so output lane 4 a + c receives head dim 16 (g & 1) + 4 a + c = lane % 32 for four
+  // consecutive keys.
+  const int tr_l = lane & 15, tr_a = tr_l & 3;
+  const int tr_off = (2 * ((lane >> 4) & 1) + (tr_a >> 1)) * CBV + (16 * hf + (tr_l >> 2)) * 16 + 8 * (tr_a & 1);
+  auto pv = [&](const unsigned char* sVt) __attribute__((always_inline)) {
+    const unsigned char* v_base = sVt;
 #pragma unroll
     for (int kb2 = 0; kb2 < NKB; ++kb2) {
       if constexpr (KW == 1) {
+        const unsigned char* vb = v_base + (ln >> 2) * CBV + (ln & 3) * 4 + (32 * kb2 + 16 * hf) * 16;
 #pragma unroll
         for (int u = 0; u < 16; ++u)
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const float a = *(const float*)(v_base + 32 * db * PITCH_V + (32 * kb2 + u) * ES);
+            const float a = *(const float*)(vb + u * 16 + 8 * db * CBV);
             oacc[db] = Mma<QT>::run(a, p32[kb2][u], oacc[db]);
           }
       } else {
@@ -470,15 +483,18 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
         for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const u32x4 a = ld16(v_base + 32 * db * PITCH_V + (32 * kb2 + 8 * u) * ES);
-            oacc[db] = Mma<QT>::run(a, pfrag[kb2 * 2 + u], oacc[db]);
+            const unsigned char* r0 = v_base + tr_off + (32 * kb2 + 8 * u) * 16 + 4 * db * CBV;
+            const s16x4 lo = lds_read_tr16(r0);
+            const s16x4 hi = lds_read_tr16(r0 + 4 * 16);
+            const s16x4 a[2] = {lo, hi};
+            oacc[db] = Mma<QT>::run(__builtin_bit_cast(u32x4, a), pfrag[kb2 * 2 + u], oacc[db]);
           }
       }
     }
   };
 
   // online softmax of tile t (scores in sacc) -> P(t); lazy rescaling of O and l
-  auto softmax = [&](int t) {
+  auto softmax = [&](int t) __attribute__((always_inline)) {
     const int kb = t * BN;
     if constexpr (MODE == 1) {
 #pragma unroll
@@ -534,106 +550,105 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
         }
     } else {
       typedef QT T8 __attribute__((ext_vector_type(8)));
-      typedef QT T2 __attribute__((ext_vector_type(2)));
-      float lsum = 0.f;
+      // Row sum in fp32 from the unrounded exponentials with plain adds (four partial
+      // sums): the dot-product instructions that could sum the packed probabilities run
+      // on the matrix pipeline and would stall behind the other wavefront's MFMAs.
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb2 = 0; kb2 < NKB; ++kb2)
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           T8 pb;
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            pb[j] = from_f32<QT>(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb2][8 * u + j], LOG2E, -ms)));
-          pfrag[kb2 * 2 + u] = __builtin_bit_cast(u32x4, pb);
-          // row sum of the rounded probabilities (what the P V product uses)
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const T2 two = {pb[2 * m], pb[2 * m + 1]};
-            const T2 one = {from_f32<QT>(1.f), from_f32<QT>(1.f)};
-            if constexpr (__is_same(QT, bf16_t))
-              lsum = __builtin_amdgcn_fdot2_f32_bf16(two, one, lsum, false);
-            else
-              lsum = __builtin_amdgcn_fdot2(two, one, lsum, false);
+          for (int j = 0; j < 8; ++j) {
+            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb2][8 * u + j], LOG2E, -ms));
+            pb[j] = from_f32<QT>(e);
+            ls[j & 3] += e;
           }
+          pfrag[kb2 * 2 + u] = __builtin_bit_cast(u32x4, pb);
         }
-      l_run += lsum;
+      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
     }
   };
 
-  // Matrix phase of tile t: S(t+1) = K'(t+1) Q'^T and O += Vt(t) P(t)^T.
-  auto mma_phase = [&](int t) {
-    if (t + 1 < nkt && active(t + 1)) qk((t + 1) & 1);
-    if (active(t)) pv(t & 1);
-  };
-
-  // ---- prologue: K'(0), K'(1), V(0) in LDS; K'(2), V(1) in flight; P(0) -------
-  if (grp == 1) {
-    load_k(0);
-    store_k(0);
+  // ---- prologue: K'(0), K'(1), V(0) in LDS; P(0) ------------------------------
+  if (grp == 0) {
+    dma_tile(0, sK0, sV0, true, true);
+    if (nkt > 1) dma_tile(BN, sK1, sV1, true, false);
+  } else if (!phk_fast) {
+    phi_load(0);
+    phi_store(sK0);
     if (nkt > 1) {
-      load_k(BN);
-      store_k(1);
+      phi_load(BN);
+      phi_store(sK1);
     }
-    if (nkt > 2) load_k(2 * BN);
-  } else {
-    load_v(0);
-    store_v(0);
-    if (nkt > 1) load_v(BN);
   }
   load_bias(0);
   __syncthreads();
-  qk(0);
+  qk(sK0);
   softmax(0);
   __syncthreads();
 
-  // ---- ping-pong: per SIMD, one wave multiplies while the other does softmax ----
-  // group 0: phase A = MFMA(t) [S(t+1) = K'(t+1) Q'^T, O += Vt(t) P(t)], phase B = softmax(t+1)
-  // group 1: phase A = softmax(t) (t > 0),                               phase B = MFMA(t)
-  // The softmax group also refills LDS: group 1 K'(t+2) in phase A, group 0 V(t+1) in phase B.
-  for (int t = 0; t < nkt; ++t) {
+  // ---- ping-pong: per SIMD, one wavefront multiplies while the other does softmax ----
+  // Every wavefront runs the same sequence  MFMA(t) | softmax(t+1) | MFMA(t+1) | ...  with
+  // MFMA(t) = {S(t+1) = K'(t+1) Q'^T, O += V(t)^T P(t)}, one phase per barrier; group 1
+  // starts one phase late, so on each SIMD the two wavefronts are always in opposite
+  // phases.  (One code path for both groups: branching on the group around the
+  // accumulators makes the compiler copy them at every join.)
+  // At the start of its MFMA(t), group 0 issues the direct loads of K'(t+2) and V(t+1)
+  // into the buffers that tile t-1 released; they complete behind both phases, and its
+  // next barrier (which ends tile t for both groups) waits for them.  With phi_k staged
+  // through registers, group 1 loads and stores the phi_k columns of tile t+3 during its
+  // softmax(t+1) (which follows its MFMA(t)); its next barrier waits for the stores.
+  // kt / kn: K' buffers of tiles t / t+1; vt / vn: V buffers of tiles t / t+1.
+  auto step = [&](int t, unsigned char* kt, unsigned char* kn, unsigned char* vt,
+                  unsigned char* vn) __attribute__((always_inline)) {
     const int kb = t * BN;
-    // ---- phase A ----
     if (grp == 0) {
-      mma_phase(t);
-    } else {
-      if (t + 2 < nkt) {
-        store_k(t & 1);
-        if (t + 3 < nkt) load_k(kb + 3 * BN);
-      }
-      if (t > 0 && active(t)) softmax(t);
+      dma_tile(kb + 2 * BN, kt, vn, t + 2 < nkt, false);
+      dma_tile(kb + BN, kt, vn, false, t + 1 < nkt);
     }
+    if (t + 1 < nkt && active(t + 1)) qk(kn);
+    if (active(t)) pv(vt);
+    __builtin_amdgcn_s_barrier();
+    if (!phk_fast && grp == 1 && t + 3 < nkt) phi_load(kb + 3 * BN);
+    if (t + 1 < nkt && active(t + 1)) softmax(t + 1);
+    if (!phk_fast && grp == 1 && t + 3 < nkt) phi_store(kn);
     __syncthreads();
-    // ---- phase B ----
-    if (grp == 0) {
-      if (t + 1 < nkt) {
-        store_v((t + 1) & 1);
-        if (t + 2 < nkt) load_v(kb + 2 * BN);
-      }
-      if (t + 1 < nkt && active(t + 1)) softmax(t + 1);
-    } else {
-      mma_phase(t);
+  };
+  if (grp == 1) {
+    // group 1's first phase: the phi_k columns of tile 2 (into K'(0)'s buffer, free now)
+    if (!phk_fast && nkt > 2) {
+      phi_load(2 * BN);
+      phi_store(sK0);
     }
     __syncthreads();
   }
+  for (int t = 0; t < nkt; t += 2) {
+    step(t, sK0, sK1, sV0, sV1);
+    if (t + 1 < nkt) step(t + 1, sK1, sK0, sV1, sV0);
+  }
+  if (grp == 0) __builtin_amdgcn_s_barrier();   // matches group 1's extra first phase
 
   // ---- epilogue: O = O / l, LSE = m + ln l -----------------------------------
+  // register r of lane half hf in head-dim block db holds head dim 32 db + 8 (r / 4) + 4 hf + r % 4
   const float l_tot = halves_sum(l_run);
   if (qvalid) {
     const float inv = 1.f / l_tot;
     QT* orow = Op + qrow * p.so[2];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int d0 = 32 * db + 16 * hf;
-      if (d0 < D) {
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int c = 0; c < 16 / CE; ++c) {
-          ChunkV<QT> v;
+      for (int c = 0; c < 4; ++c) {
+        const int d0 = 32 * db + 8 * c + 4 * hf;
+        if (d0 < D) {
+          typedef QT T4 __attribute__((ext_vector_type(4)));
+          T4 v;
 #pragma unroll
-          for (int j = 0; j < CE; ++j) v[j] = from_f32<QT>(oacc[db][c * CE + j] * inv);
-          st16(orow + d0 + c * CE, __builtin_bit_cast(u32x4, v));
+          for (int j = 0; j < 4; ++j) v[j] = from_f32<QT>(oacc[db][4 * c + j] * inv);
+          *(T4*)(orow + d0) = v;
         }
       }
-    }
     if (p.lse && hf == 0) p.lse[((int64_t)bb * p.H + hh) * N + qrow] = m_run + logf(l_tot);
   }
 }

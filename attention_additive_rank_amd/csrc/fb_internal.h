@@ -30,6 +30,7 @@ struct AttnParams {
   int nqb;                // number of query blocks per (b, h)
 };
 constexpr int kAttnBlockM = 256;   // query rows per attention workgroup
+constexpr int kAttnKeyTile = 64;   // keys per LDS tile of the attention kernels
 constexpr int FLAG_CAUSAL = 1;
 constexpr int FLAG_PHQ_VEC = 2;   // phi_q rows 16-byte aligned -> vector loads
 constexpr int FLAG_PHK_VEC = 4;   // phi_k rows 16-byte aligned -> vector loads

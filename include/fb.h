@@ -172,16 +172,20 @@ typedef struct {
  *                matrix-core chain in phi_dt, accumulating into the same fp32 scores)
  *   R            number of factor columns, 0 <= R <= 128 (16-bit) or <= 32 (fp32);
  *                R == 0 is plain attention.  Columns are zero-padded internally to
- *                the matrix-core step (16 for 16-bit types, 4 for fp32).
+ *                the matrix-core step (16 for 16-bit types, 8 for fp32).
  * Numerics: fp32 accumulation; Q*s is rounded once to dt; the probabilities P
- * are rounded to dt (RNE) before the P V product; O is written in dt.
+ * are rounded to dt (RNE) before the P V product, their row sum is taken in
+ * fp32 before that rounding; O is written in dt.
  * Alignment: q, k, v, o 16-byte aligned and their strides multiples of
- * 16 bytes / element size.  phi rows may be unaligned (slower loads).
+ * 16 bytes / element size.  phi rows may be unaligned; phi_k is fastest with
+ * 16-byte aligned rows and R a multiple of 16 bytes / element size (it is then
+ * copied straight into on-chip memory, otherwise staged through registers).
  * Errors: FB_EINVAL (null pointers, negative sizes, misalignment, row strides
  * too small); FB_EUNSUPPORTED (D not in {16,32,64,128}, or D = 128 with fp32
  * Q/K/V; R above the limit; a dtype pair not listed above; element strides or
- * N * row stride of any operand above 2^31 - 1); FB_EHIP.  B*H*N == 0 is a
- * no-op returning FB_OK.
+ * N * row stride of any operand above 2^31 - 1; a k, v or phi_k row stride
+ * whose 64 rows span 2^31 bytes or more); FB_EHIP.  B*H*N == 0 is a no-op
+ * returning FB_OK.
  */
 fb_status fb_attn_fwd_lowrank(const fb_attn_args* a, const void* phi_q, const void* phi_k,
                               fb_dtype phi_dt, int R, const int64_t sphi_q[3],
