@@ -124,7 +124,11 @@ def main():
         fH, fC, R_used = 1, w.C, w.C * split * (split + 1) // 2
     else:
         fH, fC, R_used = w.H, 0, 2 * split * (split + 1) // 2
-    pq = torch.empty((fH, w.N, R_used), dtype=phi_dt, device=dev)
+    # factor rows padded with zero columns to a whole 16-byte chunk: the kernel then copies
+    # phi_k rows with 16-byte loads (the zero columns add nothing to phi_q phi_k^T)
+    ce = 16 // (2 if phi_dt == torch.float16 else 4)
+    R_cols = (R_used + ce - 1) // ce * ce
+    pq = torch.empty((fH, w.N, R_cols), dtype=phi_dt, device=dev)
     pk = torch.empty_like(pq)
     stream = torch.cuda.current_stream(dev)
 
@@ -215,6 +219,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D, "R": w.R, "causal": w.causal,
                    "factor_dtype": "f16" if phi_dt == torch.float16 else "f32", "factor_split": split,
+                   "factor_columns": R_used, "factor_columns_padded": R_cols,
                    "flops_per_step": F},
         "pct_mfma_peak": round(100.0 * value / peak, 2),
         "kernel_ms": round(kern_ms, 4),
