@@ -19,12 +19,20 @@
 //     phases between workgroup barriers, so on every SIMD one wave keeps the
 //     matrix core busy while the other does exp2/max/sum on the VALU.
 //   * Key tiles of 64 keys are double-buffered in LDS: K' rows (K then phi_k,
-//     zero-padded to RP columns) and V rows.  The group in its matrix phase
-//     fills them with direct global->LDS loads (16 bytes per lane, no register
-//     round trip, no VALU), two tiles ahead for K' and one for V.  Rows past N
-//     are clamped on load and masked in the scores (no bounds branches).
+//     zero-padded to RP columns) and V rows, each region row-major with a
+//     per-row XOR swizzle of its 16-byte chunks (conflict-free MFMA operand
+//     reads, whole rows per copy).  Tiles arrive by direct global->LDS loads
+//     (16 bytes per lane, no register round trip, no VALU), two tiles ahead for
+//     K' and one for V; each load fills 1 KB of consecutive rows, so its lanes
+//     read whole row segments.  For bf16/fp16 operands four more wavefronts
+//     (one per SIMD) issue every copy, keeping the matrix and softmax waves
+//     free of the address unit's stalls; otherwise the softmax phase issues
+//     them.  Rows past N are not loaded and are masked in the scores.
 //   * V stays row-major in LDS; the A operand of O^T = V^T P^T comes from
 //     64-bit transpose reads (ds_read_b64_tr_b16), four keys per read.
+//   * The softmax row sum (16-bit operands) is one more MFMA per P V k-step with
+//     an all-ones A row, so it costs matrix-core cycles instead of VALU adds and
+//     is rescaled together with O.
 //   * Scores are computed transposed, S^T = K' Q'^T, with 32x32 MFMAs
 //     (32x32x16 bf16/f16, 32x32x2 fp32).  With that orientation every lane owns
 //     ONE query (lane % 32) and 16 keys per 32-key block, so the row max / row
@@ -63,6 +71,7 @@ constexpr int NW = 8;          // wavefronts per workgroup: two groups of four
 constexpr int NT = NW * 64;    // threads per workgroup
 constexpr int GT = NT / 2;     // threads per group
 constexpr int BM = 32 * NW;    // query rows per workgroup
+constexpr int NLW = 4;         // loader wavefronts (kernels with a loader)
 static_assert(BM == kAttnBlockM, "host and kernel block sizes differ");
 constexpr int BN = 64;         // keys per LDS tile
 constexpr int NKB = BN / 32;   // 32-key blocks per tile
@@ -188,7 +197,25 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 // 16 bytes global -> LDS without a register round trip: lane l of the wavefront writes
 // lds_base + 16 * l (lds_base must be the same for the whole wavefront).
 __device__ __forceinline__ void dma16(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)lds_base, 16, 0, 0);
+  // The low 32 bits of a generic pointer into LDS are its LDS address (the shared aperture
+  // sits in the high half); going through the integer avoids the generic-to-LDS null
+  // check, which the compiler mis-encodes in some contexts.
+  lds_void* dst = (lds_void*)(uint32_t)(uintptr_t)lds_base;
+  __builtin_amdgcn_global_load_lds((global_void*)src, dst, 16, 0, 0);
+}
+
+// Swizzled row-major tiles.  A region of 64 rows x cpr 16-byte chunks (cpr a power of
+// two) stores chunk c of row r at chunk position c ^ swz(r), which keeps every row's
+// chunks inside the row while spreading the rows over the LDS banks:
+//   swz_rows: eight consecutive rows read at one chunk (the score MFMA operands) hit
+//             eight different 16-byte bank groups;
+//   swz_quad: four consecutive rows read at two adjacent chunks (the 64-bit transpose
+//             reads of V) hit eight different groups.
+__host__ __device__ constexpr int swz_rows(int cpr, int r) {
+  return cpr >= 8 ? (r & 7) : cpr == 4 ? ((r >> 1) & 3) : cpr == 2 ? ((r >> 2) & 1) : 0;
+}
+__host__ __device__ constexpr int swz_quad(int cpr, int r) {
+  return cpr >= 8 ? 2 * (r & 3) : cpr == 4 ? 2 * ((r >> 1) & 1) : 0;
 }
 
 // 64-bit transpose read of 16-bit elements (ds_read_b64_tr_b16): within each group of
@@ -197,8 +224,9 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const unsigned char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
 }
 
-template <typename QT, typename PT, int D, int RP, int MODE, typename BT, bool CAUSAL, bool PHI_DMA>
-__global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
+// LOADER: NLW more wavefronts (one per SIMD) issue every tile copy (see the key loop).
+template <typename QT, typename PT, int D, int RP, int MODE, typename BT, bool CAUSAL, bool PHI_DMA, bool LOADER>
+__global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kernel(AttnParams p) {
   typedef typename Elem<QT>::Frag QFrag;
   typedef typename Elem<PT>::Frag PFrag;
   constexpr int ES = (int)sizeof(QT);
@@ -211,27 +239,29 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   constexpr int DB = DP / 32;             // 32-wide head-dim blocks of the output
   constexpr int QSTEPS = D / KS;
   constexpr int PSTEPS = RP / KS;
-  constexpr int KCH = D / CE;             // chunks per K / V row
+  constexpr int KCH = D / CE;             // chunks per K row (and data chunks per V row)
   constexpr int PCH = RP / CE;            // chunks per (padded) phi_k row
-  // Both tiles are stored chunk-column-major: column c holds 16-byte chunk c of the 64
-  // rows of the tile, row r at byte 16 r.  K' columns are 1024 bytes apart: a 128-bit
-  // read of rows 32 kb2 + lane is then contiguous per half-wave.  V columns are padded
-  // so that the reads of the P V product hit distinct banks: 64 bytes for the transpose
-  // reads (two adjacent columns, four rows each), 16 bytes for the fp32 reads (eight
-  // columns, one row).
-  constexpr int CBK = BN * 16;
-  constexpr int CBV = BN * 16 + (ES == 2 ? 64 : 16);
-  constexpr int SK_BYTES = (KCH + PCH) * CBK;
-  constexpr int SV_BYTES = (DP / CE) * CBV;
-  constexpr int NDMA = KCH + PCH + KCH;   // 64-row chunk columns per tile: K, phi_k, V
-  constexpr int DPW = (NDMA + 3) / 4;     // column loads per wavefront of the issuing group
-  static_assert(BN == 64 && BN == kAttnKeyTile, "one direct load fills one 64-row chunk column");
+  constexpr int VCH = DP / CE;            // chunks per V row in LDS
+  // A K' tile is two swizzled row-major regions, K (64 x KCH chunks) then phi_k
+  // (64 x PCH chunks); LDS row r holds key inv_perm_row(r), so that lane half h of the
+  // scores holds keys 16h..16h+15 of each 32-key block.  A V tile is one region of
+  // 64 x VCH chunks, row = key.  Chunk c of row r sits at position c ^ swz(r).
+  constexpr int KREG = BN * KCH * 16;
+  constexpr int SK_BYTES = KREG + BN * PCH * 16;
+  constexpr int SV_BYTES = BN * VCH * 16;
+  // Tile copies: one direct load fills 1 KB = 64 consecutive chunk slots of a region
+  // (whole rows), so its 64 lanes read whole row segments from global memory.
+  constexpr int NDMA = KCH + PCH + VCH;   // loads per tile: K, phi_k, V
+  constexpr int DPW = (NDMA + NW - 1) / NW;   // loads per compute wavefront and tile
+  static_assert(BN == 64 && BN == kAttnKeyTile, "one direct load per 1 KB of a 64-row tile");
   static_assert(D % KS == 0 && RP % KS == 0 && D % CE == 0 && RP % CE == 0, "bad tile widths");
-  static_assert(KW > 1 || (D % 8 == 0 && RP % 8 == 0), "fp32 k order pairs chunk columns");
+  static_assert(KW > 1 || (D % 8 == 0 && RP % 8 == 0), "fp32 k order pairs chunks");
+  static_assert((KCH & (KCH - 1)) == 0 && (PCH & (PCH - 1)) == 0 && (VCH & (VCH - 1)) == 0 && VCH >= 4,
+                "tile rows must be a power-of-two number of chunks");
 
-  // Four separate LDS objects rather than two double buffers: with the key loop unrolled by
-  // two every access names its buffer statically, so the compiler can tell that a direct
-  // load in flight never writes the buffer being read, and does not wait for it.
+  // Four LDS objects, with the key loop unrolled by two: every access names its buffer
+  // statically, so the compiler can tell that a direct load in flight never writes the
+  // buffer being read, and does not wait for it.
   __shared__ __attribute__((aligned(16))) unsigned char sK0[SK_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char sK1[SK_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char sV0[SV_BYTES];
@@ -271,16 +301,130 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   if constexpr (MODE == 1) Bp = (const BT*)p.bias + ((int64_t)bb * p.sb[0] + (int64_t)hh * p.sb[1]);
 
   const int q0 = qb * BM;
+  const int kend = CAUSAL ? min(N, q0 + BM) : N;
+  const int nkt = (kend + BN - 1) / BN;
+
+  // ---- tile copies -----------------------------------------------------------------
+  // Load n of a tile: n < KCH fills K-region bytes [1024 n, 1024 (n+1)), then the
+  // phi_k region, then V.  Lane l of a load writes chunk slot l of its 1 KB: row
+  // n' (64 / cpr) + l / cpr, chunk position l % cpr, i.e. logical chunk (l % cpr) ^ swz(row).
+  // Chunks that are never loaded (phi_k at or beyond R, V past D) hold zeros.
+  // With PHI_DMA false (phi_k rows not 16-byte loadable: unaligned, or R not a multiple of
+  // a chunk) the phi_k region is staged through registers instead (phi_load / phi_store).
+  constexpr bool phk_fast = PHI_DMA;
+  const int npch = phk_fast ? p.R / CE : 0;     // phi_k chunks that the direct path loads
+  struct Slot { int region, cpr, row, c; };
+  auto slot_of = [&](int n) __attribute__((always_inline)) {
+    Slot d;
+    int nr = n;
+    if (n < KCH) { d.region = 0; d.cpr = KCH; }
+    else if (n < KCH + PCH) { d.region = 1; d.cpr = PCH; nr = n - KCH; }
+    else { d.region = 2; d.cpr = VCH; nr = n - KCH - PCH; }
+    d.row = nr * (64 / d.cpr) + lane / d.cpr;
+    d.c = (lane % d.cpr) ^ (d.region == 2 ? swz_quad(d.cpr, d.row) : swz_rows(d.cpr, d.row));
+    return d;
+  };
+  // source byte offset of this lane's chunk of load n relative to the tile's first row, ~0
+  // for a chunk that is not loaded
+  auto src_offset = [&](int n) __attribute__((always_inline)) {
+    const Slot d = slot_of(n);
+    const int key = d.region == 2 ? d.row : inv_perm_row(d.row);
+    const int stride = d.region == 0 ? p.sk[2] : d.region == 1 ? p.spk[2] : p.sv[2];
+    const bool ok = d.region == 0 || (d.region == 1 ? d.c < npch : d.c < KCH);
+    return ok ? (uint32_t)(key * (stride * ES) + d.c * 16) : ~0u;
+  };
+  // issue load n of K'(kbk) (into dK) or V(kbv) (into dV), given its offset; rows past N
+  // are not loaded (their scores are masked; V rows keep finite data)
+  auto dma_load = [&](int n, uint32_t off, int kbk, int kbv, unsigned char* dK, unsigned char* dV) __attribute__((always_inline)) {
+    const int region = n < KCH ? 0 : n < KCH + PCH ? 1 : 2;
+    const int kb = region == 2 ? kbv : kbk;
+    const char* base = region == 0 ? (const char*)(Kp + (int64_t)kb * p.sk[2])
+                     : region == 1 ? (const char*)(PKp + (int64_t)kb * p.spk[2])
+                                   : (const char*)(Vp + (int64_t)kb * p.sv[2]);
+    unsigned char* dst = region == 2 ? dV + (n - KCH - PCH) * 1024 : dK + n * 1024;
+    bool ok = off != ~0u;
+    if (kb + BN > N) {
+      const Slot d = slot_of(n);
+      ok = ok && (region == 2 ? d.row : inv_perm_row(d.row)) < N - kb;
+    }
+    if (ok) dma16(base + off, dst);
+  };
+  // Chunks that are never loaded must hold finite values: the V buffers start zeroed (a
+  // first tile may have rows past N) and so do the phi_k chunks at or beyond R.
+#pragma unroll
+  for (int i = 0; i < (SV_BYTES / 16 + NT - 1) / NT; ++i) {
+    const int s = tid + NT * i;
+    if (s < SV_BYTES / 16) {
+      st16(sV0 + 16 * s, u32x4{0, 0, 0, 0});
+      st16(sV1 + 16 * s, u32x4{0, 0, 0, 0});
+    }
+  }
+  if constexpr (RP > 0) {
+    for (int s = tid; s < BN * PCH; s += NT) {
+      const int r = s / PCH, c = s % PCH;
+      if (c >= npch) {
+        const int o = KREG + (r * PCH + (c ^ swz_rows(PCH, r))) * 16;
+        st16(sK0 + o, u32x4{0, 0, 0, 0});
+        st16(sK1 + o, u32x4{0, 0, 0, 0});
+      }
+    }
+  }
+  __syncthreads();   // the zero fills land before any direct load into those buffers
+
+  // ---- the loader wavefronts ------------------------------------------------------
+  // A direct load holds the wavefront that issues it until the address unit takes it.
+  // With LOADER, NLW more wavefronts (one per SIMD, doing nothing else) issue them all,
+  // so no compute wavefront stalls on them.  They keep the compute wavefronts' barrier
+  // sequence: two prologue barriers, then per tile t the barrier that ends phase A and
+  // the one that ends phase B (group 0's MFMA / group 1's softmax, then the reverse), and
+  // the final one.  During tile t they copy K'(t+2) and V(t+1) into the buffers that tile
+  // t-1 released, half of each wavefront's share in each phase, and wait for them before
+  // the barrier that ends the tile.
+  if constexpr (LOADER) {
+    static_assert(PHI_DMA, "the loaders copy phi_k directly");
+    if (wave >= NW) {
+      constexpr int PER = (NDMA + NLW - 1) / NLW;   // loads per loader wavefront and tile
+      const int lw = wave - NW;
+      uint32_t off[PER];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) off[i] = lw + NLW * i < NDMA ? src_offset(lw + NLW * i) : ~0u;
+      auto loads = [&](int i0, int i1, int kbk, int kbv, unsigned char* dK, unsigned char* dV) __attribute__((always_inline)) {
+        // tiles past the last are replaced by the last one: their copies go to buffers
+        // that nothing reads again
+        kbk = min(kbk, (nkt - 1) * BN);
+        kbv = min(kbv, (nkt - 1) * BN);
+#pragma unroll
+        for (int i = i0; i < i1; ++i)
+          if (lw + NLW * i < NDMA) dma_load(lw + NLW * i, off[i], kbk, kbv, dK, dV);
+      };
+      loads(0, PER, 0, 0, sK0, sV0);
+      loads(0, PER, BN, BN, sK1, sV1);   // V(1) into sV1 as well, harmlessly early
+      __syncthreads();
+      __builtin_amdgcn_s_barrier();
+      auto lstep = [&](int t, unsigned char* kt, unsigned char* vn) __attribute__((always_inline)) {
+        const int kb = t * BN;
+        loads(0, PER / 2, kb + 2 * BN, kb + BN, kt, vn);
+        __builtin_amdgcn_s_barrier();
+        loads(PER / 2, PER, kb + 2 * BN, kb + BN, kt, vn);
+        __syncthreads();
+      };
+      for (int t = 0; t < nkt; t += 2) {
+        lstep(t, sK0, sV1);
+        if (t + 1 < nkt) lstep(t + 1, sK1, sV0);
+      }
+      __builtin_amdgcn_s_barrier();
+      return;
+    }
+  }
+
   const int q0w = q0 + wave * 32;
   const int qrow = q0w + ln;
   const bool qvalid = qrow < N;
   const int qclamp = qvalid ? qrow : N - 1;
-  const int kend = CAUSAL ? min(N, q0 + BM) : N;
-  const int nkt = (kend + BN - 1) / BN;
 
   // ---- Q' fragments (B operand of S^T = K' Q'^T), resident for the whole loop
   // 16-bit: k-step t of lane half h covers chunk 2t + h.  fp32 (one element per lane and
-  // k-step): k-step t of half h takes element 4 (t % 4) ... of chunk 2 (t / 4) + h, i.e.
+  // k-step): k-step t of half h takes element t % 4 of chunk 2 (t / 4) + h, i.e.
   // column 8 (t / 4) + 4 h + t % 4, so one 128-bit read of K' serves four k-steps.
   QFrag qf[QSTEPS];
   PFrag pf[PSTEPS > 0 ? PSTEPS : 1];
@@ -304,48 +448,25 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
     }
   }
 
-  // ---- tile staging by direct global -> LDS loads ---------------------------
-  // Column load n of a tile: n < KCH is K chunk n, n < KCH + PCH is phi_k chunk n - KCH,
-  // the rest V chunk n - KCH - PCH.  Lane l loads row l: key inv_perm_row(l) for K' (so
-  // that lane half h of the scores holds keys 16h..16h+15), key l for V.  Wavefront w of
-  // the issuing group takes loads w, w+4, w+8, ...
-  // With PHI_DMA false (phi_k rows not 16-byte loadable: unaligned, or R not a multiple of
-  // a chunk) the phi_k columns are staged through registers instead (phi_load / phi_store).
-  constexpr bool phk_fast = PHI_DMA;
-  const int npch = phk_fast ? p.R / CE : 0;     // phi_k columns that the direct path loads
-  const int gw = wave & 3;
-  const int keyk = inv_perm_row(lane);
-  const uint32_t offk = (uint32_t)(min(keyk, N - 1) * p.sk[2] * ES);
-  const uint32_t offp = RP > 0 ? (uint32_t)(min(keyk, N - 1) * p.spk[2] * ES) : 0u;
-  const uint32_t offv = (uint32_t)(min(lane, N - 1) * p.sv[2] * ES);
-  // issue the loads of tile kb: K' into dK (do_k), V into dV (do_v)
-  auto dma_tile = [&](int kb, unsigned char* dK, unsigned char* dV, bool do_k, bool do_v) __attribute__((always_inline)) {
-    const bool full = kb + BN <= N;
-    // byte offset of this lane's row: rows past N repeat row N-1 (finite; masked scores)
-    auto row_off = [&](uint32_t off_full, int key, int stride) __attribute__((always_inline)) {
-      return full ? off_full : (uint32_t)((min(kb + key, N - 1) - kb) * (stride * ES));
-    };
+  // tile copies by the compute wavefronts (no loader): wavefront w issues loads w, w+8, ...
+  uint32_t coff[LOADER ? 1 : DPW];
+  if constexpr (!LOADER) {
 #pragma unroll
-    for (int i = 0; i < DPW; ++i) {
-      const int n = gw + 4 * i;
-      if (n < KCH) {
-        if (do_k)
-          dma16((const char*)(Kp + (int64_t)kb * p.sk[2] + n * CE) + row_off(offk, keyk, p.sk[2]),
-                dK + n * CBK);
-      } else if (n < KCH + PCH) {
-        if (do_k && n - KCH < npch)
-          dma16((const char*)(PKp + (int64_t)kb * p.spk[2] + (n - KCH) * CE) + row_off(offp, keyk, p.spk[2]),
-                dK + n * CBK);
-      } else if (n < NDMA) {
-        const int c = n - KCH - PCH;
-        if (do_v)
-          dma16((const char*)(Vp + (int64_t)kb * p.sv[2] + c * CE) + row_off(offv, lane, p.sv[2]),
-                dV + c * CBV);
+    for (int i = 0; i < DPW; ++i) coff[i] = wave + NW * i < NDMA ? src_offset(wave + NW * i) : ~0u;
+  }
+  auto dma_tile = [&](int kbk, int kbv, unsigned char* dK, unsigned char* dV, bool do_k, bool do_v) __attribute__((always_inline)) {
+    if constexpr (!LOADER) {
+#pragma unroll
+      for (int i = 0; i < DPW; ++i) {
+        const int n = wave + NW * i;
+        const bool is_k = n < KCH + PCH;
+        if (n < NDMA && (is_k ? do_k : do_v)) dma_load(n, coff[i], kbk, kbv, dK, dV);
       }
     }
   };
-  // phi_k columns of K' tiles through registers: the softmax group loads tile t+3 while
-  // it stores tile t+2.  Chunk s of a tile is column s / BN, row s % BN, zero beyond R.
+  // phi_k region through registers (PHI_DMA false): group 1 loads and stores tile t+3
+  // during its softmax(t+1).  Chunk s of a tile: row s / PCH, logical chunk s % PCH, zero
+  // beyond R.
   constexpr int NPS = (BN * (PCH > 0 ? PCH : 1) + GT - 1) / GT;
   u32x4 phreg[NPS];
   const int gtid = tid & (GT - 1);
@@ -358,8 +479,8 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
         // chunk is precomputed and held in registers for the whole key loop
         asm volatile("" : "+v"(s));
         if (s < BN * PCH) {
-          const int key = min(kb + inv_perm_row(s % BN), N - 1);
-          phreg[i] = load_partial_chunk<PT>(PKp + key * p.spk[2], (s / BN) * CE, p.R);
+          const int key = min(kb + inv_perm_row(s / PCH), N - 1);
+          phreg[i] = load_partial_chunk<PT>(PKp + key * p.spk[2], (s % PCH) * CE, p.R);
         }
       }
     }
@@ -369,19 +490,11 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
       for (int i = 0; i < NPS; ++i) {
         const int s = gtid + GT * i;
-        if (s < BN * PCH) st16(dK + KCH * CBK + s * 16, phreg[i]);
+        const int r = s / PCH, c = s % PCH;
+        if (s < BN * PCH) st16(dK + KREG + (r * PCH + (c ^ swz_rows(PCH, r))) * 16, phreg[i]);
       }
     }
   };
-  // On the direct path phi_k columns at or beyond R are never loaded: zero them once.
-  if constexpr (RP > 0 && phk_fast) {
-    for (int s = tid; s < BN * PCH; s += NT) {
-      if (s / BN >= npch) {
-        st16(sK0 + KCH * CBK + s * 16, u32x4{0, 0, 0, 0});
-        st16(sK1 + KCH * CBK + s * 16, u32x4{0, 0, 0, 0});
-      }
-    }
-  }
 
   // ---- per-wave state ----------------------------------------------------------
   f32x16 sacc[NKB];                    // S^T of the tile being processed
@@ -391,7 +504,14 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   float m_run = -INFINITY;
-  float l_run = 0.f;
+  float l_run = 0.f;      // row sum (fp32 path)
+  // 16-bit path: the row sum of P rides on the matrix core as one more MFMA per k-step,
+  // with an A operand whose row 0 is all ones (lane 0 of each half) and rows 1..31 zero:
+  // row 0 of lacc (register 0 of the lanes of half 0) is then sum_k P[k][query], and the
+  // rescaling of O scales it too.  This takes 32 adds per tile off the vector unit.
+  f32x16 lacc = f32x16{};
+  const uint32_t one2 = __is_same(QT, bf16_t) ? 0x3F803F80u : 0x3C003C00u;   // two 1.0 values of QT
+  const u32x4 ones = ln == 0 ? u32x4{one2, one2, one2, one2} : u32x4{0u, 0u, 0u, 0u};
 
   // dense bias of this lane's row, keys kb + 32*kb2 + 16*hf + [0, 16), loaded one tile ahead
   constexpr int BES = MODE == 1 ? (int)sizeof(BT) : 2;
@@ -419,10 +539,57 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   // A wavefront whose queries all precede a key tile has nothing to do there.
   auto active = [&](int t) __attribute__((always_inline)) { return !CAUSAL || t * BN <= q0w + 31; };
 
-  // S^T = K'(t) Q'^T from the K' tile at sKt: lane (ln, h) reads row 32 kb2 + ln of chunk
-  // column 2t + h (16-bit) or 2 (t / 4) + h (fp32, four k-steps per read).
+  // ---- LDS operand addresses ------------------------------------------------------
+  // Score MFMA operand of k-step t (fp32: of 4-step group t), key block kb2: row
+  // 32 kb2 + ln, logical chunk c = 2t + hf of the K region (or of the phi_k region for the
+  // factor steps).  The row swizzle depends on ln only and flips the low three bits of c,
+  // so per lane there are four distinct addresses (t mod 4); the rest is an immediate.
+  auto kaddr = [&](int cpr, int j) __attribute__((always_inline)) {
+    const int c = (2 * j + hf) & (cpr - 1);
+    return ln * cpr * 16 + 16 * (c ^ swz_rows(cpr, ln));
+  };
+  int ka_k[4], ka_p[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    ka_k[j] = kaddr(KCH, j);
+    ka_p[j] = KREG + (PCH > 0 ? kaddr(PCH, j) : 0);
+  }
+  auto kread = [&](const unsigned char* sKt, bool phi, int t, int kb2) __attribute__((always_inline)) {
+    const int cpr = phi ? PCH : KCH;
+    const int* a = phi ? ka_p : ka_k;
+    return ld16(sKt + a[t & 3] + 128 * (t >> 2) + 32 * kb2 * cpr * 16);
+  };
+  // P V operand (16-bit), key block kb2, k-step u, head-dim block db: two transpose reads,
+  // rows 32 kb2 + 16 hf + 8 u + 4 q + jj (q = 0, 1), where lane 4 jj + a of a 16-lane group
+  // g reads head dims 32 db + 16 (g & 1) + 4 a .. + 3: logical chunk
+  // 4 db + 2 (g & 1) + (a >> 1), byte 8 (a & 1).  The quad swizzle of those rows depends on
+  // jj only, so per lane there are two addresses (db even / odd).  Value j of output lane
+  // 4 a + c of a transpose read is element c of lane 4 j + a's row: head dim
+  // 32 db + lane % 32 for four consecutive keys.
+  const int tr_a = lane & 3, tr_jj = (lane >> 2) & 3, tr_gg = (lane >> 4) & 1;
+  int va[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int r = 16 * hf + tr_jj;
+    const int c = (4 * e + 2 * tr_gg + (tr_a >> 1)) & (VCH - 1);
+    va[e] = r * VCH * 16 + 16 * (c ^ swz_quad(VCH, r)) + 8 * (tr_a & 1);
+  }
+  auto vread_tr = [&](const unsigned char* sVt, int kb2, int u, int db) __attribute__((always_inline)) {
+    const unsigned char* r0 = sVt + va[db & 1] + 128 * (db >> 1) + (32 * kb2 + 8 * u) * VCH * 16;
+    const s16x4 a[2] = {lds_read_tr16(r0), lds_read_tr16(r0 + 4 * VCH * 16)};
+    return __builtin_bit_cast(u32x4, a);
+  };
+  // fp32 P V operand: V[32 kb2 + 16 hf + u][32 db + ln]; the quad swizzle of row u depends
+  // on u mod 4.
+  int vf[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 16 * hf + j;
+    vf[j] = r * VCH * 16 + 16 * ((ln >> 2) ^ swz_quad(VCH, r)) + 4 * (ln & 3);
+  }
+
+  // S^T = K'(t) Q'^T from the K' tile at sKt
   auto qk = [&](const unsigned char* sKt) __attribute__((always_inline)) {
-    const unsigned char* k_base = sKt + ln * 16 + hf * CBK;
 #pragma unroll
     for (int kb2 = 0; kb2 < NKB; ++kb2) sacc[kb2] = f32x16{};
     if constexpr (KW == 1) {
@@ -430,7 +597,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
       for (int t4 = 0; t4 < QSTEPS / 4; ++t4)
 #pragma unroll
         for (int kb2 = 0; kb2 < NKB; ++kb2) {
-          const f32x4 a = __builtin_bit_cast(f32x4, ld16(k_base + 2 * t4 * CBK + 32 * kb2 * 16));
+          const f32x4 a = __builtin_bit_cast(f32x4, kread(sKt, false, t4, kb2));
 #pragma unroll
           for (int e = 0; e < 4; ++e) sacc[kb2] = Mma<QT>::run(a[e], qf[4 * t4 + e], sacc[kb2]);
         }
@@ -438,7 +605,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
       for (int t4 = 0; t4 < PSTEPS / 4; ++t4)
 #pragma unroll
         for (int kb2 = 0; kb2 < NKB; ++kb2) {
-          const f32x4 a = __builtin_bit_cast(f32x4, ld16(k_base + (KCH + 2 * t4) * CBK + 32 * kb2 * 16));
+          const f32x4 a = __builtin_bit_cast(f32x4, kread(sKt, true, t4, kb2));
 #pragma unroll
           for (int e = 0; e < 4; ++e) sacc[kb2] = Mma<PT>::run(a[e], pf[4 * t4 + e], sacc[kb2]);
         }
@@ -446,52 +613,39 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
       for (int t = 0; t < QSTEPS; ++t)
 #pragma unroll
-        for (int kb2 = 0; kb2 < NKB; ++kb2)
-          sacc[kb2] = Mma<QT>::run(ld16(k_base + 2 * t * CBK + 32 * kb2 * 16), qf[t], sacc[kb2]);
+        for (int kb2 = 0; kb2 < NKB; ++kb2) sacc[kb2] = Mma<QT>::run(kread(sKt, false, t, kb2), qf[t], sacc[kb2]);
 #pragma unroll
       for (int t = 0; t < PSTEPS; ++t)
 #pragma unroll
-        for (int kb2 = 0; kb2 < NKB; ++kb2)
-          sacc[kb2] = Mma<PT>::run(ld16(k_base + (KCH + 2 * t) * CBK + 32 * kb2 * 16), pf[t], sacc[kb2]);
+        for (int kb2 = 0; kb2 < NKB; ++kb2) sacc[kb2] = Mma<PT>::run(kread(sKt, true, t, kb2), pf[t], sacc[kb2]);
     }
   };
 
-  // O^T += V(t)^T P(t)^T from the V tile at sVt.  MFMA row m of head-dim
-  // block db is head dim 32 db + m; k-slot j of lane half h in k-step u of key block kb2
-  // is key 32 kb2 + 16 h + 8 u + j, matching the registers of P.
-  // 16-bit: each A fragment is two transpose reads of four keys.  Lane 4 jj + a of a
-  // 16-lane group g reads key (16 h + 8 u + 4 q + jj), head dims 16 (g & 1) + 4 a .. + 3,
-  // so output lane 4 a + c receives head dim 16 (g & 1) + 4 a + c = lane % 32 for four
-  // consecutive keys.
-  const int tr_l = lane & 15, tr_a = tr_l & 3;
-  const int tr_off = (2 * ((lane >> 4) & 1) + (tr_a >> 1)) * CBV + (16 * hf + (tr_l >> 2)) * 16 + 8 * (tr_a & 1);
+  // O^T += V(t)^T P(t)^T from the V tile at sVt.  MFMA row m of head-dim block db is head
+  // dim 32 db + m; k-slot j of lane half h in k-step u of key block kb2 is key
+  // 32 kb2 + 16 h + 8 u + j, matching the registers of P.
   auto pv = [&](const unsigned char* sVt) __attribute__((always_inline)) {
-    const unsigned char* v_base = sVt;
 #pragma unroll
     for (int kb2 = 0; kb2 < NKB; ++kb2) {
       if constexpr (KW == 1) {
-        const unsigned char* vb = v_base + (ln >> 2) * CBV + (ln & 3) * 4 + (32 * kb2 + 16 * hf) * 16;
 #pragma unroll
         for (int u = 0; u < 16; ++u)
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const float a = *(const float*)(vb + u * 16 + 8 * db * CBV);
+            const float a = *(const float*)(sVt + vf[u & 3] + (32 * kb2 + (u & ~3)) * VCH * 16 + 128 * db);
             oacc[db] = Mma<QT>::run(a, p32[kb2][u], oacc[db]);
           }
       } else {
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int u = 0; u < 2; ++u) {
 #pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const unsigned char* r0 = v_base + tr_off + (32 * kb2 + 8 * u) * 16 + 4 * db * CBV;
-            const s16x4 lo = lds_read_tr16(r0);
-            const s16x4 hi = lds_read_tr16(r0 + 4 * 16);
-            const s16x4 a[2] = {lo, hi};
-            oacc[db] = Mma<QT>::run(__builtin_bit_cast(u32x4, a), pfrag[kb2 * 2 + u], oacc[db]);
-          }
+          for (int db = 0; db < DB; ++db) oacc[db] = Mma<QT>::run(vread_tr(sVt, kb2, u, db), pfrag[kb2 * 2 + u], oacc[db]);
+          lacc = Mma<QT>::run(ones, pfrag[kb2 * 2 + u], lacc);
+        }
       }
     }
   };
+
 
   // online softmax of tile t (scores in sacc) -> P(t); lazy rescaling of O and l
   auto softmax = [&](int t) __attribute__((always_inline)) {
@@ -536,6 +690,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      lacc *= alpha;
       m_run = grow ? mx : m_run;
     }
     const float ms = (m_run == -INFINITY ? 0.f : m_run) * LOG2E;
@@ -550,10 +705,6 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
         }
     } else {
       typedef QT T8 __attribute__((ext_vector_type(8)));
-      // Row sum in fp32 from the unrounded exponentials with plain adds (four partial
-      // sums): the dot-product instructions that could sum the packed probabilities run
-      // on the matrix pipeline and would stall behind the other wavefront's MFMAs.
-      float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb2 = 0; kb2 < NKB; ++kb2)
 #pragma unroll
@@ -561,21 +712,17 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
           T8 pb;
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb2][8 * u + j], LOG2E, -ms));
-            pb[j] = from_f32<QT>(e);
-            ls[j & 3] += e;
+            pb[j] = from_f32<QT>(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb2][8 * u + j], LOG2E, -ms)));
           }
           pfrag[kb2 * 2 + u] = __builtin_bit_cast(u32x4, pb);
         }
-      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
     }
   };
 
   // ---- prologue: K'(0), K'(1), V(0) in LDS; P(0) ------------------------------
-  if (grp == 0) {
-    dma_tile(0, sK0, sV0, true, true);
-    if (nkt > 1) dma_tile(BN, sK1, sV1, true, false);
-  } else if (!phk_fast) {
+  dma_tile(0, 0, sK0, sV0, true, true);
+  dma_tile(BN, BN, sK1, sV1, nkt > 1, false);
+  if (!phk_fast && grp == 1) {
     phi_load(0);
     phi_store(sK0);
     if (nkt > 1) {
@@ -595,29 +742,35 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   // starts one phase late, so on each SIMD the two wavefronts are always in opposite
   // phases.  (One code path for both groups: branching on the group around the
   // accumulators makes the compiler copy them at every join.)
-  // At the start of its MFMA(t), group 0 issues the direct loads of K'(t+2) and V(t+1)
-  // into the buffers that tile t-1 released; they complete behind both phases, and its
-  // next barrier (which ends tile t for both groups) waits for them.  With phi_k staged
-  // through registers, group 1 loads and stores the phi_k columns of tile t+3 during its
-  // softmax(t+1) (which follows its MFMA(t)); its next barrier waits for the stores.
+  // Without loader wavefronts the tile copies go out from the softmax phases, which read
+  // nothing from LDS (the compiler cannot order LDS reads after an outstanding direct load
+  // by the counter, and would wait for all of them), split between the groups: group 0,
+  // in its softmax(t+1) (tile t's second phase), issues its loads of K'(t+2) and V(t+1)
+  // into the buffers that tile t-1 released; group 1, in its softmax(t+1) (tile t+1's
+  // first phase), its loads of K'(t+3) and V(t+2), into the buffers that K'(t+1) and V(t)
+  // have just released.  The barrier that closes each softmax phase waits for them.  With
+  // phi_k staged through registers, group 1 also loads and stores the phi_k region of
+  // tile t+3 there.
   // kt / kn: K' buffers of tiles t / t+1; vt / vn: V buffers of tiles t / t+1.
   auto step = [&](int t, unsigned char* kt, unsigned char* kn, unsigned char* vt,
                   unsigned char* vn) __attribute__((always_inline)) {
     const int kb = t * BN;
-    if (grp == 0) {
-      dma_tile(kb + 2 * BN, kt, vn, t + 2 < nkt, false);
-      dma_tile(kb + BN, kt, vn, false, t + 1 < nkt);
-    }
     if (t + 1 < nkt && active(t + 1)) qk(kn);
     if (active(t)) pv(vt);
     __builtin_amdgcn_s_barrier();
+    if constexpr (!LOADER) {
+      const int kbk = kb + (2 + grp) * BN, kbv = kb + (1 + grp) * BN;
+      dma_tile(kbk, kbv, grp ? kn : kt, grp ? vt : vn, kbk < nkt * BN, kbv < nkt * BN);
+    }
     if (!phk_fast && grp == 1 && t + 3 < nkt) phi_load(kb + 3 * BN);
     if (t + 1 < nkt && active(t + 1)) softmax(t + 1);
     if (!phk_fast && grp == 1 && t + 3 < nkt) phi_store(kn);
     __syncthreads();
   };
   if (grp == 1) {
-    // group 1's first phase: the phi_k columns of tile 2 (into K'(0)'s buffer, free now)
+    // group 1's first phase: its loads of K'(2) (into K'(0)'s buffer, free now) and V(1),
+    // and the phi_k region of tile 2
+    dma_tile(2 * BN, BN, sK0, sV1, 2 < nkt, 1 < nkt);
     if (!phk_fast && nkt > 2) {
       phi_load(2 * BN);
       phi_store(sK0);
@@ -632,7 +785,8 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
 
   // ---- epilogue: O = O / l, LSE = m + ln l -----------------------------------
   // register r of lane half hf in head-dim block db holds head dim 32 db + 8 (r / 4) + 4 hf + r % 4
-  const float l_tot = halves_sum(l_run);
+  // (register 0 of lacc is row 0 in half 0 and row 4, all zeros, in half 1)
+  const float l_tot = halves_sum(KW > 1 ? lacc[0] : l_run);
   if (qvalid) {
     const float inv = 1.f / l_tot;
     QT* orow = Op + qrow * p.so[2];

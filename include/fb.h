@@ -174,8 +174,9 @@ typedef struct {
  *                R == 0 is plain attention.  Columns are zero-padded internally to
  *                the matrix-core step (16 for 16-bit types, 8 for fp32).
  * Numerics: fp32 accumulation; Q*s is rounded once to dt; the probabilities P
- * are rounded to dt (RNE) before the P V product, their row sum is taken in
- * fp32 before that rounding; O is written in dt.
+ * are rounded to dt (RNE) before the P V product and their row sum is taken
+ * from the same rounded values (fp32 accumulation; fp32 Q/K/V: unrounded);
+ * O is written in dt.
  * Alignment: q, k, v, o 16-byte aligned and their strides multiples of
  * 16 bytes / element size.  phi rows may be unaligned; phi_k is fastest with
  * 16-byte aligned rows and R a multiple of 16 bytes / element size (it is then
