@@ -204,19 +204,38 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_base) {
   __builtin_amdgcn_global_load_lds((global_void*)src, dst, 16, 0, 0);
 }
 
+// Scheduling-group pins of the matrix phase (see mma_phase): for group G, its MFMAs
+// (DB + 1 in a P V group, NKB in a score group), then the LDS reads of group G + 2
+// (two transpose reads per head-dim block, or one 128-bit read per key block).
+// 0x008 selects MFMA instructions and 0x100 LDS reads.
+template <int G, int NG, int NPV, int DB, int NKB>
+__device__ __forceinline__ void mma_pins() {
+  if constexpr (G < NG) {
+    __builtin_amdgcn_sched_group_barrier(0x008, G < NPV ? DB + 1 : NKB, 0);
+    if constexpr (G + 2 < NG) __builtin_amdgcn_sched_group_barrier(0x100, G + 2 < NPV ? 2 * DB : NKB, 0);
+    mma_pins<G + 1, NG, NPV, DB, NKB>();
+  }
+}
+
 // Swizzled row-major tiles.  A region of 64 rows x cpr 16-byte chunks (cpr a power of
 // two) stores chunk c of row r at chunk position c ^ swz(r), which keeps every row's
-// chunks inside the row while spreading the rows over the LDS banks:
-//   swz_rows: eight consecutive rows read at one chunk (the score MFMA operands) hit
-//             eight different 16-byte bank groups;
-//   swz_quad: four consecutive rows read at two adjacent chunks (the 64-bit transpose
-//             reads of V) hit eight different groups.
+// chunks inside the row while spreading the rows over the LDS banks.  The LDS serves a
+// 128-bit read in passes of 16 lanes over 64 four-byte banks (256 bytes), so the lanes of
+// a pass must touch 16 different 16-byte bank groups, i.e. distinct (row * cpr + position)
+// mod 16:
+//   swz_rows: 16 consecutive rows read at one chunk (the score MFMA operands);
+//   swz_quad: four consecutive rows read at four adjacent chunks (the 64-bit transpose
+//             reads of V, 32 lanes of 8 bytes per pass).
 __host__ __device__ constexpr int swz_rows(int cpr, int r) {
-  return cpr >= 8 ? (r & 7) : cpr == 4 ? ((r >> 1) & 3) : cpr == 2 ? ((r >> 2) & 1) : 0;
+  return cpr >= 16 ? (r & 15) : cpr == 8 ? ((r >> 1) & 7) : cpr == 4 ? ((r >> 2) & 3) : cpr == 2 ? ((r >> 2) & 1) : 0;
 }
 __host__ __device__ constexpr int swz_quad(int cpr, int r) {
   return cpr >= 8 ? 2 * (r & 3) : cpr == 4 ? 2 * ((r >> 1) & 1) : 0;
 }
+// K and phi_k rows are stored in key order but read by the score MFMA in the order
+// of perm_row (lane ln of a 32-key block reads key inv_perm_row(ln)), so their swizzle
+// follows the reading lane: eight lanes that read together still hit eight groups.
+__host__ __device__ constexpr int swz_key(int cpr, int key) { return swz_rows(cpr, perm_row(key)); }
 
 // 64-bit transpose read of 16-bit elements (ds_read_b64_tr_b16): within each group of
 // 16 lanes, value j of output lane 4a + c is element c of the 64-bit row read by lane 4j + a.
@@ -243,9 +262,10 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   constexpr int PCH = RP / CE;            // chunks per (padded) phi_k row
   constexpr int VCH = DP / CE;            // chunks per V row in LDS
   // A K' tile is two swizzled row-major regions, K (64 x KCH chunks) then phi_k
-  // (64 x PCH chunks); LDS row r holds key inv_perm_row(r), so that lane half h of the
-  // scores holds keys 16h..16h+15 of each 32-key block.  A V tile is one region of
-  // 64 x VCH chunks, row = key.  Chunk c of row r sits at position c ^ swz(r).
+  // (64 x PCH chunks), a V tile one region of 64 x VCH chunks; row = key, and chunk c of
+  // key row r sits at position c ^ swz_key(r) (K, phi_k) or c ^ swz_quad(r) (V).  The
+  // score MFMA reads key inv_perm_row(ln) in lane ln of a 32-key block, so that lane
+  // half h of the scores holds keys 16h..16h+15.
   constexpr int KREG = BN * KCH * 16;
   constexpr int SK_BYTES = KREG + BN * PCH * 16;
   constexpr int SV_BYTES = BN * VCH * 16;
@@ -266,6 +286,9 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   __shared__ __attribute__((aligned(16))) unsigned char sK1[SK_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char sV0[SV_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char sV1[SV_BYTES];
+  // third stage of the loader pipeline
+  __shared__ __attribute__((aligned(16))) unsigned char sK2[LOADER ? SK_BYTES : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char sV2[LOADER ? SV_BYTES : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -308,6 +331,8 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   // Load n of a tile: n < KCH fills K-region bytes [1024 n, 1024 (n+1)), then the
   // phi_k region, then V.  Lane l of a load writes chunk slot l of its 1 KB: row
   // n' (64 / cpr) + l / cpr, chunk position l % cpr, i.e. logical chunk (l % cpr) ^ swz(row).
+  // One load thus reads 1 KB of consecutive rows from global memory (the concurrent
+  // workgroups of a head read the same tiles: scattered rows there cost L2 throughput).
   // Chunks that are never loaded (phi_k at or beyond R, V past D) hold zeros.
   // With PHI_DMA false (phi_k rows not 16-byte loadable: unaligned, or R not a multiple of
   // a chunk) the phi_k region is staged through registers instead (phi_load / phi_store).
@@ -321,14 +346,14 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
     else if (n < KCH + PCH) { d.region = 1; d.cpr = PCH; nr = n - KCH; }
     else { d.region = 2; d.cpr = VCH; nr = n - KCH - PCH; }
     d.row = nr * (64 / d.cpr) + lane / d.cpr;
-    d.c = (lane % d.cpr) ^ (d.region == 2 ? swz_quad(d.cpr, d.row) : swz_rows(d.cpr, d.row));
+    d.c = (lane % d.cpr) ^ (d.region == 2 ? swz_quad(d.cpr, d.row) : swz_key(d.cpr, d.row));
     return d;
   };
   // source byte offset of this lane's chunk of load n relative to the tile's first row, ~0
   // for a chunk that is not loaded
   auto src_offset = [&](int n) __attribute__((always_inline)) {
     const Slot d = slot_of(n);
-    const int key = d.region == 2 ? d.row : inv_perm_row(d.row);
+    const int key = d.row;
     const int stride = d.region == 0 ? p.sk[2] : d.region == 1 ? p.spk[2] : p.sv[2];
     const bool ok = d.region == 0 || (d.region == 1 ? d.c < npch : d.c < KCH);
     return ok ? (uint32_t)(key * (stride * ES) + d.c * 16) : ~0u;
@@ -345,25 +370,28 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
     bool ok = off != ~0u;
     if (kb + BN > N) {
       const Slot d = slot_of(n);
-      ok = ok && (region == 2 ? d.row : inv_perm_row(d.row)) < N - kb;
+      ok = ok && d.row < N - kb;
     }
     if (ok) dma16(base + off, dst);
   };
   // Chunks that are never loaded must hold finite values: the V buffers start zeroed (a
-  // first tile may have rows past N) and so do the phi_k chunks at or beyond R.
+  // first tile may have rows past N) and so do the phi_k chunks at or beyond R.  (The
+  // loader wavefronts fill every chunk slot instead.)
+  if constexpr (!LOADER) {
 #pragma unroll
-  for (int i = 0; i < (SV_BYTES / 16 + NT - 1) / NT; ++i) {
-    const int s = tid + NT * i;
-    if (s < SV_BYTES / 16) {
-      st16(sV0 + 16 * s, u32x4{0, 0, 0, 0});
-      st16(sV1 + 16 * s, u32x4{0, 0, 0, 0});
+    for (int i = 0; i < (SV_BYTES / 16 + NT - 1) / NT; ++i) {
+      const int s = tid + NT * i;
+      if (s < SV_BYTES / 16) {
+        st16(sV0 + 16 * s, u32x4{0, 0, 0, 0});
+        st16(sV1 + 16 * s, u32x4{0, 0, 0, 0});
+      }
     }
   }
-  if constexpr (RP > 0) {
+  if constexpr (RP > 0 && !LOADER) {
     for (int s = tid; s < BN * PCH; s += NT) {
       const int r = s / PCH, c = s % PCH;
       if (c >= npch) {
-        const int o = KREG + (r * PCH + (c ^ swz_rows(PCH, r))) * 16;
+        const int o = KREG + (r * PCH + (c ^ swz_key(PCH, r))) * 16;
         st16(sK0 + o, u32x4{0, 0, 0, 0});
         st16(sK1 + o, u32x4{0, 0, 0, 0});
       }
@@ -374,44 +402,84 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   // ---- the loader wavefronts ------------------------------------------------------
   // A direct load holds the wavefront that issues it until the address unit takes it.
   // With LOADER, NLW more wavefronts (one per SIMD, doing nothing else) issue them all,
-  // so no compute wavefront stalls on them.  They keep the compute wavefronts' barrier
-  // sequence: two prologue barriers, then per tile t the barrier that ends phase A and
-  // the one that ends phase B (group 0's MFMA / group 1's softmax, then the reverse), and
-  // the final one.  During tile t they copy K'(t+2) and V(t+1) into the buffers that tile
-  // t-1 released, half of each wavefront's share in each phase, and wait for them before
-  // the barrier that ends the tile.
+  // so no compute wavefront stalls on them, into three stages of K' and V buffers.  They
+  // keep the compute wavefronts' barrier sequence: two prologue barriers, then per tile t
+  // the barrier that ends phase A and the one that ends phase B (group 0's MFMA / group
+  // 1's softmax, then the reverse), and the final one.  During tile t they copy K'(t+3)
+  // into K'(t)'s buffer and V(t+2) into V(t-1)'s, half of each wavefront's share in each
+  // phase; before the barrier that ends tile t they wait only for the copies issued
+  // before tile t (K'(t+2), V(t+1), needed from tile t+1 on), so copies stay in flight
+  // across barriers instead of draining every tile.  That wait counts this wavefront's
+  // outstanding loads, so every load is issued with all lanes active: a lane whose chunk
+  // is not wanted (a row past N, a phi_k chunk at or beyond R) copies a finite stand-in
+  // (the last row's chunk, the row's first chunk) that the scores mask or that meets zero
+  // phi_q columns.
   if constexpr (LOADER) {
     static_assert(PHI_DMA, "the loaders copy phi_k directly");
     if (wave >= NW) {
-      constexpr int PER = (NDMA + NLW - 1) / NLW;   // loads per loader wavefront and tile
+      constexpr int PER = (NDMA + NLW - 1) / NLW;   // most loads per loader wavefront and tile
+      constexpr int PMIN = NDMA / NLW;              // fewest
+      static_assert(PMIN >= 1 && PMIN <= 15, "loads per wavefront and tile");
       const int lw = wave - NW;
+      int rowi[PER], cbyte[PER];
       uint32_t off[PER];
 #pragma unroll
-      for (int i = 0; i < PER; ++i) off[i] = lw + NLW * i < NDMA ? src_offset(lw + NLW * i) : ~0u;
-      auto loads = [&](int i0, int i1, int kbk, int kbv, unsigned char* dK, unsigned char* dV) __attribute__((always_inline)) {
-        // tiles past the last are replaced by the last one: their copies go to buffers
-        // that nothing reads again
+      for (int i = 0; i < PER; ++i) {
+        const int n = lw + NLW * i;
+        rowi[i] = cbyte[i] = 0;
+        off[i] = 0;
+        if (n < NDMA) {
+          const Slot d = slot_of(n);
+          rowi[i] = d.row;
+          cbyte[i] = d.region == 1 && d.c >= npch ? 0 : d.c * 16;
+          const int stride = d.region == 0 ? p.sk[2] : d.region == 1 ? p.spk[2] : p.sv[2];
+          off[i] = (uint32_t)(d.row * stride * ES + cbyte[i]);
+        }
+      }
+      // loads [i0, i1) of this wavefront for K'(kbk) into dK and V(kbv) into dV; tiles past
+      // the last are replaced by the last one (their copies land in buffers that nothing
+      // reads again)
+      auto loads = [&](int i0, int i1, int kbk, int kbv, unsigned char* dK, unsigned char* dV, bool do_k, bool do_v)
+          __attribute__((always_inline)) {
         kbk = min(kbk, (nkt - 1) * BN);
         kbv = min(kbv, (nkt - 1) * BN);
 #pragma unroll
-        for (int i = i0; i < i1; ++i)
-          if (lw + NLW * i < NDMA) dma_load(lw + NLW * i, off[i], kbk, kbv, dK, dV);
+        for (int i = i0; i < i1; ++i) {
+          const int n = lw + NLW * i;
+          const int region = n < KCH ? 0 : n < KCH + PCH ? 1 : 2;
+          if (n < NDMA && (region == 2 ? do_v : do_k)) {
+            const int kb = region == 2 ? kbv : kbk;
+            const int stride = region == 0 ? p.sk[2] : region == 1 ? p.spk[2] : p.sv[2];
+            const char* base = region == 0 ? (const char*)(Kp + (int64_t)kb * p.sk[2])
+                             : region == 1 ? (const char*)(PKp + (int64_t)kb * p.spk[2])
+                                           : (const char*)(Vp + (int64_t)kb * p.sv[2]);
+            unsigned char* dst = region == 2 ? dV + (n - KCH - PCH) * 1024 : dK + n * 1024;
+            uint32_t o = off[i];
+            if (kb + BN > N) o = (uint32_t)(min(rowi[i], N - 1 - kb) * stride * ES + cbyte[i]);
+            dma16(base + o, dst);
+          }
+        }
       };
-      loads(0, PER, 0, 0, sK0, sV0);
-      loads(0, PER, BN, BN, sK1, sV1);   // V(1) into sV1 as well, harmlessly early
-      __syncthreads();
+      loads(0, PER, 0, 0, sK0, sV0, true, true);          // K'(0), V(0)
+      loads(0, PER, BN, 0, sK1, sV0, true, false);        // K'(1)
+      __syncthreads();                                    // (waits for them)
+      loads(0, PER, 2 * BN, BN, sK2, sV1, true, true);    // K'(2), V(1)
       __builtin_amdgcn_s_barrier();
-      auto lstep = [&](int t, unsigned char* kt, unsigned char* vn) __attribute__((always_inline)) {
+      auto lstep = [&](int t, unsigned char* kd, unsigned char* vd) __attribute__((always_inline)) {
         const int kb = t * BN;
-        loads(0, PER / 2, kb + 2 * BN, kb + BN, kt, vn);
+        loads(0, PER / 2, kb + 3 * BN, kb + 2 * BN, kd, vd, true, true);
         __builtin_amdgcn_s_barrier();
-        loads(PER / 2, PER, kb + 2 * BN, kb + BN, kt, vn);
-        __syncthreads();
+        loads(PER / 2, PER, kb + 3 * BN, kb + 2 * BN, kd, vd, true, true);
+        // vmcnt(PMIN): at most PMIN loads outstanding, so all of the previous tile's are done
+        __builtin_amdgcn_s_waitcnt(PMIN | 0x0F70);
+        __builtin_amdgcn_s_barrier();
       };
-      for (int t = 0; t < nkt; t += 2) {
-        lstep(t, sK0, sV1);
+      for (int t = 0; t < nkt; t += 3) {
+        lstep(t, sK0, sV2);
         if (t + 1 < nkt) lstep(t + 1, sK1, sV0);
+        if (t + 2 < nkt) lstep(t + 2, sK2, sV1);
       }
+      __builtin_amdgcn_s_waitcnt(0);   // no copy outlives the workgroup
       __builtin_amdgcn_s_barrier();
       return;
     }
@@ -479,7 +547,7 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
         // chunk is precomputed and held in registers for the whole key loop
         asm volatile("" : "+v"(s));
         if (s < BN * PCH) {
-          const int key = min(kb + inv_perm_row(s / PCH), N - 1);
+          const int key = min(kb + s / PCH, N - 1);
           phreg[i] = load_partial_chunk<PT>(PKp + key * p.spk[2], (s % PCH) * CE, p.R);
         }
       }
@@ -491,7 +559,7 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
       for (int i = 0; i < NPS; ++i) {
         const int s = gtid + GT * i;
         const int r = s / PCH, c = s % PCH;
-        if (s < BN * PCH) st16(dK + KREG + (r * PCH + (c ^ swz_rows(PCH, r))) * 16, phreg[i]);
+        if (s < BN * PCH) st16(dK + KREG + (r * PCH + (c ^ swz_key(PCH, r))) * 16, phreg[i]);
       }
     }
   };
@@ -540,24 +608,26 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   auto active = [&](int t) __attribute__((always_inline)) { return !CAUSAL || t * BN <= q0w + 31; };
 
   // ---- LDS operand addresses ------------------------------------------------------
-  // Score MFMA operand of k-step t (fp32: of 4-step group t), key block kb2: row
-  // 32 kb2 + ln, logical chunk c = 2t + hf of the K region (or of the phi_k region for the
-  // factor steps).  The row swizzle depends on ln only and flips the low three bits of c,
-  // so per lane there are four distinct addresses (t mod 4); the rest is an immediate.
+  // Score MFMA operand of k-step t (fp32: of 4-step group t), key block kb2: key row
+  // 32 kb2 + inv_perm_row(ln), logical chunk c = 2t + hf of the K region (or of the phi_k
+  // region for the factor steps).  The row swizzle depends on ln only and flips the low
+  // three bits of c (four with 16-chunk rows), so per lane there are four (eight)
+  // distinct addresses, t mod 4 (8); the rest is an immediate.
   auto kaddr = [&](int cpr, int j) __attribute__((always_inline)) {
     const int c = (2 * j + hf) & (cpr - 1);
-    return ln * cpr * 16 + 16 * (c ^ swz_rows(cpr, ln));
+    return inv_perm_row(ln) * cpr * 16 + 16 * (c ^ swz_key(cpr, inv_perm_row(ln)));
   };
-  int ka_k[4], ka_p[4];
+  constexpr int KA = KCH >= 16 ? 8 : 4, PA = PCH >= 16 ? 8 : 4;
+  int ka_k[KA], ka_p[PA];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    ka_k[j] = kaddr(KCH, j);
-    ka_p[j] = KREG + (PCH > 0 ? kaddr(PCH, j) : 0);
-  }
+  for (int j = 0; j < KA; ++j) ka_k[j] = kaddr(KCH, j);
+#pragma unroll
+  for (int j = 0; j < PA; ++j) ka_p[j] = KREG + (PCH > 0 ? kaddr(PCH, j) : 0);
   auto kread = [&](const unsigned char* sKt, bool phi, int t, int kb2) __attribute__((always_inline)) {
     const int cpr = phi ? PCH : KCH;
+    const int na = phi ? PA : KA;
     const int* a = phi ? ka_p : ka_k;
-    return ld16(sKt + a[t & 3] + 128 * (t >> 2) + 32 * kb2 * cpr * 16);
+    return ld16(sKt + a[t % na] + 32 * na * (t / na) + 32 * kb2 * cpr * 16);
   };
   // P V operand (16-bit), key block kb2, k-step u, head-dim block db: two transpose reads,
   // rows 32 kb2 + 16 hf + 8 u + 4 q + jj (q = 0, 1), where lane 4 jj + a of a 16-lane group
@@ -646,6 +716,54 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
     }
   };
 
+
+  // The whole matrix phase of a non-causal 16-bit tile in one scheduling region:
+  // O += V(t)^T P(t)^T first (P dies, its registers take the new scores), then
+  // S(t+1) = K'(t+1) Q'^T.  Operands are read two MFMA groups ahead of their use
+  // (group = the MFMAs of one k-step), so the LDS latency hides behind the matrix
+  // core instead of stalling it; the scheduling-group pins below keep that order.
+  auto mma_phase = [&](const unsigned char* sKn, const unsigned char* sVt) __attribute__((always_inline)) {
+    if constexpr (KW > 1) {
+      constexpr int NPV = NKB * 2;              // P V groups (kb2, u): DB reads-pairs + DB+1 MFMAs
+      constexpr int NQK = QSTEPS + PSTEPS;      // score groups: NKB reads + NKB MFMAs
+      constexpr int NG = NPV + NQK;
+      u32x4 opnd[NG][NKB > DB ? NKB : DB];
+      auto issue = [&](int g) __attribute__((always_inline)) {
+        if (g < NPV) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) opnd[g][db] = vread_tr(sVt, g >> 1, g & 1, db);
+        } else {
+          const int t = g - NPV;
+#pragma unroll
+          for (int kb2 = 0; kb2 < NKB; ++kb2)
+            opnd[g][kb2] = t < QSTEPS ? kread(sKn, false, t, kb2) : kread(sKn, true, t - QSTEPS, kb2);
+        }
+      };
+#pragma unroll
+      for (int kb2 = 0; kb2 < NKB; ++kb2) sacc[kb2] = f32x16{};
+      issue(0);
+      issue(1);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        if (g + 2 < NG) issue(g + 2);
+        if (g < NPV) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) oacc[db] = Mma<QT>::run(opnd[g][db], pfrag[g], oacc[db]);
+          lacc = Mma<QT>::run(ones, pfrag[g], lacc);
+        } else {
+          const int t = g - NPV;
+#pragma unroll
+          for (int kb2 = 0; kb2 < NKB; ++kb2)
+            sacc[kb2] = t < QSTEPS ? Mma<QT>::run(opnd[g][kb2], qf[t], sacc[kb2])
+                                   : Mma<PT>::run(opnd[g][kb2], pf[t - QSTEPS], sacc[kb2]);
+        }
+      }
+      // pins: reads of groups 0 and 1; then per group g its MFMAs and the reads of g + 2
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * DB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * DB, 0);
+      mma_pins<0, NG, NPV, DB, NKB>();
+    }
+  };
 
   // online softmax of tile t (scores in sacc) -> P(t); lazy rescaling of O and l
   auto softmax = [&](int t) __attribute__((always_inline)) {
@@ -755,8 +873,13 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   auto step = [&](int t, unsigned char* kt, unsigned char* kn, unsigned char* vt,
                   unsigned char* vn) __attribute__((always_inline)) {
     const int kb = t * BN;
-    if (t + 1 < nkt && active(t + 1)) qk(kn);
-    if (active(t)) pv(vt);
+    if constexpr (!CAUSAL && KW > 1) {
+      // past the last tile the scores of a stale buffer are computed and never used
+      mma_phase(kn, vt);
+    } else {
+      if (t + 1 < nkt && active(t + 1)) qk(kn);
+      if (active(t)) pv(vt);
+    }
     __builtin_amdgcn_s_barrier();
     if constexpr (!LOADER) {
       const int kbk = kb + (2 + grp) * BN, kbv = kb + (1 + grp) * BN;
@@ -777,9 +900,17 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
     }
     __syncthreads();
   }
-  for (int t = 0; t < nkt; t += 2) {
-    step(t, sK0, sK1, sV0, sV1);
-    if (t + 1 < nkt) step(t + 1, sK1, sK0, sV1, sV0);
+  if constexpr (LOADER) {
+    for (int t = 0; t < nkt; t += 3) {
+      step(t, sK0, sK1, sV0, sV1);
+      if (t + 1 < nkt) step(t + 1, sK1, sK2, sV1, sV2);
+      if (t + 2 < nkt) step(t + 2, sK2, sK0, sV2, sV0);
+    }
+  } else {
+    for (int t = 0; t < nkt; t += 2) {
+      step(t, sK0, sK1, sV0, sV1);
+      if (t + 1 < nkt) step(t + 1, sK1, sK0, sV1, sV0);
+    }
   }
   if (grp == 0) __builtin_amdgcn_s_barrier();   // matches group 1's extra first phase
 
