@@ -15,7 +15,7 @@ template <typename QT, typename PT, int D, int RP, int MODE, typename BT, bool P
 static fb_status launch_kernel(const AttnParams& p, hipStream_t stream) {
   const int64_t grid = (int64_t)p.nqb * p.H * p.B;
   // loader wavefronts where their register budget (three wavefronts on one SIMD) holds
-  constexpr bool LOADER = PHI_DMA && sizeof(QT) == 2 && D <= 64 && RP <= 64 && MODE == 0;
+  constexpr bool LOADER = PHI_DMA && sizeof(QT) == 2 && D <= 64 && RP <= 64 && (MODE == 0 || sizeof(BT) == 2);
   const dim3 block(LOADER ? NT + NLW * 64 : NT);
   if (p.flags & FLAG_CAUSAL)
     hipLaunchKernelGGL((attn_fwd_kernel<QT, PT, D, RP, MODE, BT, true, PHI_DMA, LOADER>), dim3((unsigned)grid), block, 0,

@@ -205,15 +205,15 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_base) {
 }
 
 // Scheduling-group pins of the matrix phase (see mma_phase): for group G, its MFMAs
-// (DB + 1 in a P V group, NKB in a score group), then the LDS reads of group G + 2
+// (MPV in a P V group, NKB in a score group), then the LDS reads of group G + 2
 // (two transpose reads per head-dim block, or one 128-bit read per key block).
 // 0x008 selects MFMA instructions and 0x100 LDS reads.
-template <int G, int NG, int NPV, int DB, int NKB>
+template <int G, int NG, int NPV, int DB, int NKB, int MPV>
 __device__ __forceinline__ void mma_pins() {
   if constexpr (G < NG) {
-    __builtin_amdgcn_sched_group_barrier(0x008, G < NPV ? DB + 1 : NKB, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, G < NPV ? MPV : NKB, 0);
     if constexpr (G + 2 < NG) __builtin_amdgcn_sched_group_barrier(0x100, G + 2 < NPV ? 2 * DB : NKB, 0);
-    mma_pins<G + 1, NG, NPV, DB, NKB>();
+    mma_pins<G + 1, NG, NPV, DB, NKB, MPV>();
   }
 }
 
@@ -572,11 +572,13 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   float m_run = -INFINITY;
-  float l_run = 0.f;      // row sum (fp32 path)
-  // 16-bit path: the row sum of P rides on the matrix core as one more MFMA per k-step,
-  // with an A operand whose row 0 is all ones (lane 0 of each half) and rows 1..31 zero:
-  // row 0 of lacc (register 0 of the lanes of half 0) is then sum_k P[k][query], and the
-  // rescaling of O scales it too.  This takes 32 adds per tile off the vector unit.
+  float l_run = 0.f;      // row sum (vector-unit path)
+  // Low-rank mode, 16-bit: the row sum of P rides on the matrix core as one more MFMA per
+  // k-step, with an A operand whose row 0 is all ones (lane 0 of each half) and rows 1..31
+  // zero: row 0 of lacc (register 0 of the lanes of half 0) is then sum_k P[k][query], and
+  // the rescaling of O scales it too.  This takes 32 adds per tile off the vector unit.
+  // (Dense-bias mode keeps the adds: its bias registers leave no room for lacc.)
+  constexpr bool MROW = KW > 1 && MODE == 0;
   f32x16 lacc = f32x16{};
   const uint32_t one2 = __is_same(QT, bf16_t) ? 0x3F803F80u : 0x3C003C00u;   // two 1.0 values of QT
   const u32x4 ones = ln == 0 ? u32x4{one2, one2, one2, one2} : u32x4{0u, 0u, 0u, 0u};
@@ -710,7 +712,7 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
         for (int u = 0; u < 2; ++u) {
 #pragma unroll
           for (int db = 0; db < DB; ++db) oacc[db] = Mma<QT>::run(vread_tr(sVt, kb2, u, db), pfrag[kb2 * 2 + u], oacc[db]);
-          lacc = Mma<QT>::run(ones, pfrag[kb2 * 2 + u], lacc);
+          if constexpr (MROW) lacc = Mma<QT>::run(ones, pfrag[kb2 * 2 + u], lacc);
         }
       }
     }
@@ -724,7 +726,7 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   // core instead of stalling it; the scheduling-group pins below keep that order.
   auto mma_phase = [&](const unsigned char* sKn, const unsigned char* sVt) __attribute__((always_inline)) {
     if constexpr (KW > 1) {
-      constexpr int NPV = NKB * 2;              // P V groups (kb2, u): DB reads-pairs + DB+1 MFMAs
+      constexpr int NPV = NKB * 2;              // P V groups (kb2, u): 2 DB reads, DB (+1) MFMAs
       constexpr int NQK = QSTEPS + PSTEPS;      // score groups: NKB reads + NKB MFMAs
       constexpr int NG = NPV + NQK;
       u32x4 opnd[NG][NKB > DB ? NKB : DB];
@@ -749,7 +751,7 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
         if (g < NPV) {
 #pragma unroll
           for (int db = 0; db < DB; ++db) oacc[db] = Mma<QT>::run(opnd[g][db], pfrag[g], oacc[db]);
-          lacc = Mma<QT>::run(ones, pfrag[g], lacc);
+          if constexpr (MROW) lacc = Mma<QT>::run(ones, pfrag[g], lacc);
         } else {
           const int t = g - NPV;
 #pragma unroll
@@ -761,7 +763,7 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
       // pins: reads of groups 0 and 1; then per group g its MFMAs and the reads of g + 2
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * DB, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * DB, 0);
-      mma_pins<0, NG, NPV, DB, NKB>();
+      mma_pins<0, NG, NPV, DB, NKB, DB + (MROW ? 1 : 0)>();
     }
   };
 
@@ -808,7 +810,7 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-      lacc *= alpha;
+      if constexpr (MROW) lacc *= alpha;
       m_run = grow ? mx : m_run;
     }
     const float ms = (m_run == -INFINITY ? 0.f : m_run) * LOG2E;
@@ -830,7 +832,9 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
           T8 pb;
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            pb[j] = from_f32<QT>(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb2][8 * u + j], LOG2E, -ms)));
+            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb2][8 * u + j], LOG2E, -ms));
+            pb[j] = from_f32<QT>(e);
+            if constexpr (!MROW) l_run += e;
           }
           pfrag[kb2 * 2 + u] = __builtin_bit_cast(u32x4, pb);
         }
@@ -917,7 +921,7 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   // ---- epilogue: O = O / l, LSE = m + ln l -----------------------------------
   // register r of lane half hf in head-dim block db holds head dim 32 db + 8 (r / 4) + 4 hf + r % 4
   // (register 0 of lacc is row 0 in half 0 and row 4, all zeros, in half 1)
-  const float l_tot = halves_sum(KW > 1 ? lacc[0] : l_run);
+  const float l_tot = halves_sum(MROW ? lacc[0] : l_run);
   if (qvalid) {
     const float inv = 1.f / l_tot;
     QT* orow = Op + qrow * p.so[2];

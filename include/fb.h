@@ -201,7 +201,8 @@ fb_status fb_attn_fwd_lowrank(const fb_attn_args* a, const void* phi_q, const vo
  *   bias     device [B][H][N][N] with strides sbias (b, h, i); the last axis (j)
  *            contiguous; sbias[0] and/or sbias[1] may be 0 (shared bias)
  *   bias_dt  FB_F32 when a->dt is FB_F32; FB_BF16 or FB_F16 otherwise
- * Numerics and alignment as fb_attn_fwd_lowrank; the bias is added in fp32.
+ * Numerics and alignment as fb_attn_fwd_lowrank, except that the row sum of P
+ * is taken in fp32 before P is rounded to dt; the bias is added in fp32.
  * Errors: as fb_attn_fwd_lowrank; FB_EINVAL for a null bias or sbias[2] < N.
  */
 fb_status fb_attn_fwd_densebias(const fb_attn_args* a, const void* bias, fb_dtype bias_dt,

@@ -199,7 +199,12 @@ def test_rank0_equals_densebias_zero(fb):
     zero = torch.zeros((w.N, w.N), dtype=torch.bfloat16, device="cuda:0")
     o2 = fb.fb_attn_fwd_densebias(c.qd, c.kd, c.vd, zero)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(to_np(o1), to_np(o2))
+    # Same scores and the same rounded P; the two modes form the softmax denominator
+    # differently (low rank: sum of the rounded P on the matrix core; dense bias: fp32 sum
+    # before rounding), a relative difference far below bf16 resolution, so the outputs
+    # agree to one bf16 ulp.
+    a, b = to_np(o1).astype(np.float64), to_np(o2).astype(np.float64)
+    assert np.all(np.abs(a - b) <= _ulp(np.maximum(np.abs(a), np.abs(b)), "bf16"))
     ro, _ = oracle.attention(c.q, c.k, c.v)
     assert_close(to_np(o1), ro, "bf16", "R=0")
 
