@@ -82,6 +82,9 @@ def load():
                                            ctypes.c_void_p]
         lib.fb_svd_factors.restype = ctypes.c_int
         lib.fb_svd_factors.argtypes = [_DP, ctypes.c_int, ctypes.c_int, ctypes.c_uint64, _DP, _DP, _DP, _DP]
+        lib.fb_svd_rank_for_energy.restype = ctypes.c_int
+        lib.fb_svd_rank_for_energy.argtypes = [_DP, ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_uint64,
+                                               ctypes.POINTER(ctypes.c_int), _DP, ctypes.POINTER(ctypes.c_int)]
         lib.fb_attn_fwd_lowrank.restype = ctypes.c_int
         lib.fb_attn_fwd_lowrank.argtypes = [ctypes.POINTER(_AttnArgs), ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_int, ctypes.c_int, ctypes.POINTER(_I64x3),
@@ -198,6 +201,23 @@ def fb_svd_factors(bias: np.ndarray, R: int, seed: int = 0):
                                sig.ctypes.data_as(_DP), ctypes.byref(en))
     _check(st)
     return {"phi_q": pq, "phi_k": pk, "sigma": sig, "energy": en.value}
+
+
+def fb_svd_rank_for_energy(bias: np.ndarray, target: float = 0.95, R_max: Optional[int] = None, seed: int = 0):
+    """Smallest rank whose truncated SVD keeps ``target`` of the bias energy (host).
+    Returns a dict with ``R``, ``energy`` (kept by ``R``) and ``reached`` (bool)."""
+    a = np.ascontiguousarray(np.asarray(bias, dtype=np.float64))
+    if a.ndim != 2 or a.shape[0] != a.shape[1]:
+        raise ValueError("bias must be a square [N, N] matrix")
+    N = a.shape[0]
+    R_max = min(N, 64) if R_max is None else int(R_max)
+    r = ctypes.c_int(0)
+    en = ctypes.c_double(0.0)
+    ok = ctypes.c_int(0)
+    st = load().fb_svd_rank_for_energy(a.ctypes.data_as(_DP), N, R_max, float(target), seed, ctypes.byref(r),
+                                       ctypes.byref(en), ctypes.byref(ok))
+    _check(st)
+    return {"R": r.value, "energy": en.value, "reached": bool(ok.value)}
 
 
 def _attn_args(q, k, v, out, lse, causal, scale):

@@ -4,6 +4,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <new>
+#include <vector>
+#include <algorithm>
 
 #include "fb_internal.h"
 
@@ -183,6 +185,42 @@ fb_status fb_svd_factors(const double* bias, int N, int R, uint64_t seed, double
   if (N < 1 || R < 1 || R > N) FB_FAIL(FB_EINVAL, "%s: need 1 <= R <= N", fn);
   try {
     return svd_factors(bias, N, R, seed, phi_q, phi_k, sigma, energy);
+  } catch (const std::bad_alloc&) {
+    FB_FAIL(FB_ENOMEM, "%s: out of host memory", fn);
+  } catch (...) {
+    FB_FAIL(FB_EINVAL, "%s: internal error", fn);
+  }
+}
+
+fb_status fb_svd_rank_for_energy(const double* bias, int N, int R_max, double target, uint64_t seed,
+                                 int* R_out, double* energy_out, int* reached) {
+  const char* fn = "fb_svd_rank_for_energy";
+  if (!bias || !R_out) FB_FAIL(FB_EINVAL, "%s: null pointer", fn);
+  if (N < 1 || R_max < 1 || R_max > N) FB_FAIL(FB_EINVAL, "%s: need 1 <= R_max <= N", fn);
+  if (!(target > 0.0 && target <= 1.0)) FB_FAIL(FB_EINVAL, "%s: need 0 < target <= 1", fn);
+  try {
+    std::vector<double> phq((size_t)N * R_max), phk((size_t)N * R_max), sig(R_max);
+    const fb_status st = svd_factors(bias, N, R_max, seed, phq.data(), phk.data(), sig.data(), nullptr);
+    if (st != FB_OK) return st;
+    double total = 0.0;
+    for (int64_t t = 0; t < (int64_t)N * N; ++t) total += bias[t] * bias[t];
+    int R = R_max;
+    double kept = 0.0, kept_at_R = 0.0;
+    bool ok = false;
+    for (int r = 0; r < R_max; ++r) {
+      kept += sig[r] * sig[r];
+      if (total <= 0.0 || kept >= target * total) {
+        R = r + 1;
+        kept_at_R = kept;
+        ok = true;
+        break;
+      }
+    }
+    if (!ok) kept_at_R = kept;
+    if (energy_out) *energy_out = total > 0.0 ? std::min(1.0, kept_at_R / total) : 1.0;
+    if (reached) *reached = ok ? 1 : 0;
+    *R_out = R;
+    return FB_OK;
   } catch (const std::bad_alloc&) {
     FB_FAIL(FB_ENOMEM, "%s: out of host memory", fn);
   } catch (...) {

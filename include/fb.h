@@ -144,6 +144,30 @@ fb_status fb_make_dense_bias(fb_bias_kind kind, int H, int N, int C, const doubl
 fb_status fb_svd_factors(const double* bias, int N, int R, uint64_t seed, double* phi_q,
                          double* phi_k, double* sigma, double* energy);
 
+/*
+ * fb_svd_rank_for_energy -- the smallest rank whose truncated SVD keeps a target share
+ * of a bias's energy.  The pages apply the low-rank path only where a rank-R factorisation
+ * keeps 95% of a head's bias energy (rebuttal, answer to Reviewer Bp2x, Q2, with the
+ * SwinV2 study of different R); this is that test for one head.
+ *
+ *   bias        host, [N][N] fp64, row-major (read only)
+ *   N, R_max    1 <= R_max <= N: the largest rank considered
+ *   target      0 < target <= 1, e.g. 0.95
+ *   seed        seed of the randomized range finder (as fb_svd_factors)
+ *   R_out       host out: the smallest R <= R_max with
+ *               sum_{r<R} sigma_r^2 >= target * ||bias||_F^2, or R_max when no R
+ *               reaches the target (the caller then keeps the dense bias for the head)
+ *   energy_out  host out or NULL: the energy kept by R_out
+ *   reached     host out or NULL: 1 if R_out reaches the target, else 0
+ * An all-zero bias needs rank 1 (energy 1).  The singular values come from the same
+ * randomized subspace iteration as fb_svd_factors run at rank R_max; call fb_svd_factors
+ * with R_out for the factors.
+ * Errors: FB_EINVAL (null pointers, N < 1, R_max out of range, target out of range);
+ * FB_ENOMEM.
+ */
+fb_status fb_svd_rank_for_energy(const double* bias, int N, int R_max, double target, uint64_t seed,
+                                 int* R_out, double* energy_out, int* reached);
+
 /* Arguments shared by both attention entry points. */
 typedef struct {
   int B, H, N, D;      /* batch, heads, sequence length (queries = keys), head dim */

@@ -41,7 +41,7 @@ import numpy as np
 __all__ = [
     "alibi_slopes", "alibi_bias", "alibi_factors",
     "sandwich_frequencies", "sandwich_bias", "sandwich_factors",
-    "lowrank_bias", "attention", "truncated_svd", "bias_energy",
+    "lowrank_bias", "attention", "truncated_svd", "bias_energy", "rank_for_energy",
 ]
 
 BiasLike = Union[None, np.ndarray, Callable[[int, int], np.ndarray]]
@@ -208,3 +208,24 @@ def bias_energy(bias: np.ndarray, phi_q: np.ndarray, phi_k: np.ndarray) -> dict:
     diff = np.asarray(bias, dtype=np.float64) - lowrank_bias(phi_q, phi_k)
     return {"rel_fro": float(np.linalg.norm(diff) / np.linalg.norm(bias)),
             "max_abs": float(np.abs(diff).max())}
+
+
+def rank_for_energy(bias: np.ndarray, target: float = 0.95, R_max: Optional[int] = None) -> dict:
+    """Smallest rank R whose truncated SVD keeps ``target`` of the energy of one ``[N,N]``
+    bias: sum_{r<R} s_r^2 >= target * ||b||_F^2 (the 95%-energy criterion of the rebuttal,
+    answer to Reviewer Bp2x, Q2).  Every singular value from ``numpy.linalg.svd``; the search
+    stops at ``R_max`` (default N), returning R_max with ``reached`` False if the target is
+    not met.  An all-zero bias needs rank 1."""
+    bias = np.asarray(bias, dtype=np.float64)
+    N = bias.shape[0]
+    R_max = N if R_max is None else int(R_max)
+    sigma = np.linalg.svd(bias, compute_uv=False)
+    total = float(np.sum(bias * bias))
+    if total == 0.0:
+        return {"R": 1, "energy": 1.0, "reached": True}
+    kept = np.cumsum(sigma[:R_max] ** 2)
+    hit = np.nonzero(kept >= target * total)[0]
+    if len(hit):
+        R = int(hit[0]) + 1
+        return {"R": R, "energy": float(kept[R - 1] / total), "reached": True}
+    return {"R": R_max, "energy": float(kept[-1] / total), "reached": False}

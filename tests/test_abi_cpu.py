@@ -208,6 +208,38 @@ def test_host_svd_on_workload_biases(kind):
         assert err2 == pytest.approx(opt, rel=1e-6)
 
 
+@pytest.mark.parametrize("kind", ["vision", "pairformer"])
+@pytest.mark.parametrize("target", [0.9, 0.95, 0.99])
+def test_rank_for_energy_matches_oracle(kind, target):
+    """Rank selection by retained energy (the pages keep heads at 95%): the library's
+    randomized singular values pick the same rank as the oracle's full SVD."""
+    if kind == "vision":
+        w = synth.workload("vision_svd", grid=12, B=1, H=2)
+    else:
+        w = synth.workload("pairformer_svd", N=96, B=1, H=2)
+    b = synth.make_inputs(w)["bias_src"]
+    for h in range(b.shape[0]):
+        got = fb.fb_svd_rank_for_energy(b[h], target, R_max=40, seed=h)
+        ref = oracle.rank_for_energy(b[h], target, R_max=40)
+        assert got["R"] == ref["R"] and got["reached"] == ref["reached"]
+        assert got["energy"] == pytest.approx(ref["energy"], rel=1e-9)
+
+
+def test_rank_for_energy_validation():
+    lib = fb.load()
+    a = np.ones((4, 4))
+    p = a.ctypes.data_as(fb._DP)
+    r = ctypes.c_int(0)
+    assert lib.fb_svd_rank_for_energy(None, 4, 2, 0.95, 0, ctypes.byref(r), None, None) == fb.FB_EINVAL
+    assert lib.fb_svd_rank_for_energy(p, 4, 5, 0.95, 0, ctypes.byref(r), None, None) == fb.FB_EINVAL
+    assert lib.fb_svd_rank_for_energy(p, 4, 2, 0.0, 0, ctypes.byref(r), None, None) == fb.FB_EINVAL
+    assert lib.fb_svd_rank_for_energy(p, 4, 2, 1.5, 0, ctypes.byref(r), None, None) == fb.FB_EINVAL
+    assert lib.fb_svd_rank_for_energy(p, 4, 2, 0.95, 0, None, None, None) == fb.FB_EINVAL
+    assert lib.fb_svd_rank_for_energy(p, 4, 2, 0.95, 0, ctypes.byref(r), None, None) == fb.FB_OK and r.value == 1
+    z = fb.fb_svd_rank_for_energy(np.zeros((6, 6)), 0.95, R_max=3)
+    assert z == {"R": 1, "energy": 1.0, "reached": True}
+
+
 def test_round_exact_helper_matches_numpy_half():
     """The test-side single-rounding helper agrees with numpy's direct fp64 -> fp16 cast."""
     from _parity import round_exact

@@ -258,6 +258,53 @@ def test_ranks_fp32(fb, R):
     assert_close(to_np(o), ro, "f32", f"fp32 R={R}")
 
 
+def test_per_batch_dynamic_factors(fb):
+    """Factors that change with the batch element but are shared by the heads ([B,1,N,R],
+    head stride 0): the shape a per-sample factor network would feed."""
+    import torch
+    r = np.random.default_rng(31)
+    B, H, N, D, R = 3, 4, 200, 64, 24
+    q, k, v = (synth.round_to(r.standard_normal((B, H, N, D)) * 0.5, "bf16") for _ in range(3))
+    pq = synth.round_to(r.standard_normal((B, 1, N, R)) * 0.4, "f16")
+    pk = synth.round_to(r.standard_normal((B, 1, N, R)) * 0.4, "f16")
+    o = fb.fb_attn_fwd_lowrank(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"),
+                               to_dev(pq, "f16"), to_dev(pk, "f16"))
+    torch.cuda.synchronize()
+    ro, _ = oracle.attention(q, k, v, bias=oracle.lowrank_bias(pq, pk))
+    assert_close(to_np(o), ro, "bf16", "per-batch factors")
+
+
+def test_energy_selected_ranks_per_head(fb):
+    """Per-head rank chosen for 95% energy on the host, factors from the host SVD at that
+    rank, zero-padded to the largest rank of the call; the kernel matches the oracle run on
+    the same factors, and the approximation error against the full bias is reported."""
+    import torch
+    w = synth.workload("vision_svd", grid=16, B=1, H=3)
+    inp = synth.make_inputs(w)
+    bias = inp["bias_src"]                                     # [H, N, N] fp64
+    H, N = bias.shape[0], bias.shape[1]
+    sel = [fb.fb_svd_rank_for_energy(bias[h], 0.95, R_max=48, seed=h) for h in range(H)]
+    Rp = max(x["R"] for x in sel)
+    pq = np.zeros((H, N, Rp))
+    pk = np.zeros((H, N, Rp))
+    for h in range(H):
+        f = fb.fb_svd_factors(bias[h], sel[h]["R"], seed=h)
+        pq[h, :, :sel[h]["R"]] = f["phi_q"]
+        pk[h, :, :sel[h]["R"]] = f["phi_k"]
+    pq, pk = synth.round_to(pq, "f16"), synth.round_to(pk, "f16")
+    r = np.random.default_rng(32)
+    q, k, v = (synth.round_to(r.standard_normal((1, H, N, w.D)) * 0.5, "bf16") for _ in range(3))
+    o = fb.fb_attn_fwd_lowrank(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"),
+                               to_dev(pq, "f16"), to_dev(pk, "f16"))
+    torch.cuda.synchronize()
+    ro, _ = oracle.attention(q, k, v, bias=oracle.lowrank_bias(pq, pk))
+    assert_close(to_np(o), ro, "bf16", f"energy-selected ranks {[x['R'] for x in sel]}")
+    rf, _ = oracle.attention(q, k, v, bias=bias)
+    say(f"ranks {[x['R'] for x in sel]} energy {[round(x['energy'], 4) for x in sel]}: "
+        f"output vs full bias max-abs {np.abs(to_np(o) - rf).max():.3e}")
+    assert all(x["reached"] and x["energy"] >= 0.95 for x in sel)
+
+
 def test_strided_inputs_and_broadcast_factors(fb):
     """Q/K/V as views into wider / permuted buffers; factors broadcast over batch and heads."""
     import torch

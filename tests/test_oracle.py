@@ -300,3 +300,39 @@ def test_synth_rounding_is_representable():
     # bf16 keeps 8 significant bits: every value times 2^k is an integer below 2^8
     m, _ = np.frexp(q[q != 0])
     assert np.all(np.abs(m * 256) == np.round(np.abs(m * 256)))
+
+
+# --------------------------------------------------- rank for a target energy ---
+def _with_singular_values(sig, N, seed):
+    r = np.random.default_rng(seed)
+    U, _ = np.linalg.qr(r.standard_normal((N, N)))
+    V, _ = np.linalg.qr(r.standard_normal((N, N)))
+    s = np.zeros(N)
+    s[:len(sig)] = sig
+    return (U * s) @ V.T
+
+
+def test_rank_for_energy_closed_form():
+    # singular values 4, 2, 1, 1/2: energies 16, 4, 1, 1/4 of 21.25 -> cumulative shares
+    # 0.753, 0.941, 0.988, 1: 95% needs rank 3, 99% rank 4, 75% rank 1
+    b = _with_singular_values([4.0, 2.0, 1.0, 0.5], 12, 1)
+    assert oracle.rank_for_energy(b, 0.95)["R"] == 3
+    assert oracle.rank_for_energy(b, 0.99)["R"] == 4
+    assert oracle.rank_for_energy(b, 0.75)["R"] == 1
+    e = oracle.rank_for_energy(b, 0.95)["energy"]
+    assert abs(e - 21.0 / 21.25) < 1e-12
+    miss = oracle.rank_for_energy(b, 0.99, R_max=2)
+    assert miss == {"R": 2, "energy": miss["energy"], "reached": False} and abs(miss["energy"] - 20 / 21.25) < 1e-12
+
+
+def test_rank_for_energy_exact_biases():
+    # ALiBi has rank 2, Sandwich rank C: full energy at exactly that rank
+    N = 96
+    alibi = oracle.alibi_bias(oracle.alibi_slopes(4), N)[1]
+    assert oracle.rank_for_energy(alibi, 1 - 1e-9)["R"] == 2
+    # Sandwich has rank C, but its low-frequency terms are nearly collinear at small N, so
+    # high energy shares come earlier; rank C keeps all of it
+    sw = oracle.sandwich_bias(N, 16)
+    full = oracle.rank_for_energy(sw, 1 - 1e-12, R_max=16)
+    assert full["reached"] and full["R"] <= 16
+    assert oracle.rank_for_energy(np.zeros((5, 5)), 0.95)["R"] == 1
