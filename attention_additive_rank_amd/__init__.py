@@ -89,6 +89,15 @@ def load():
         lib.fb_attn_fwd_lowrank.argtypes = [ctypes.POINTER(_AttnArgs), ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_int, ctypes.c_int, ctypes.POINTER(_I64x3),
                                             ctypes.POINTER(_I64x3), ctypes.c_void_p]
+        lib.fb_attn_fwd_mulbias.restype = ctypes.c_int
+        lib.fb_attn_fwd_mulbias.argtypes = [ctypes.POINTER(_AttnArgs), ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_int, ctypes.c_int, ctypes.POINTER(_I64x3),
+                                            ctypes.POINTER(_I64x3), ctypes.c_void_p, ctypes.c_size_t,
+                                            ctypes.c_void_p]
+        lib.fb_mulbias_expand.restype = ctypes.c_int
+        lib.fb_mulbias_expand.argtypes = lib.fb_attn_fwd_mulbias.argtypes
+        lib.fb_mulbias_workspace_bytes.restype = ctypes.c_size_t
+        lib.fb_mulbias_workspace_bytes.argtypes = [ctypes.POINTER(_AttnArgs), ctypes.c_int]
         lib.fb_attn_fwd_densebias.restype = ctypes.c_int
         lib.fb_attn_fwd_densebias.argtypes = [ctypes.POINTER(_AttnArgs), ctypes.c_void_p, ctypes.c_int,
                                               ctypes.POINTER(_I64x3), ctypes.c_void_p]
@@ -309,3 +318,79 @@ def fb_attn_fwd_densebias(q, k, v, bias, *, causal: bool = False, scale: Optiona
                                       _stream_ptr(q.device, stream))
     _check(st)
     return out
+
+
+def fb_mulbias_workspace_bytes(q, R: int) -> int:
+    """Device workspace (bytes) that fb_attn_fwd_mulbias needs for q's shape and rank R."""
+    a = _AttnArgs()
+    a.B, a.H, a.N, a.D = q.shape
+    a.dt = _dt_code(q.dtype)
+    return int(load().fb_mulbias_workspace_bytes(ctypes.byref(a), int(R)))
+
+
+def fb_attn_fwd_mulbias(q, k, v, phi_q, phi_k, *, causal: bool = False, scale: Optional[float] = None, out=None,
+                        lse=None, workspace=None, stream=None):
+    """O = softmax((scale * Q K^T) * (phi_q phi_k^T)) V: attention with a multiplicative
+    rank-R bias, through operand expansion to width D R and the fused low-rank kernel.
+
+    ``phi_q, phi_k``: ``[..., N, R]`` broadcastable to ``[B, H, N, R]`` (fp32 / bf16 / fp16).
+    ``workspace``: optional uint8 device tensor of at least fb_mulbias_workspace_bytes(q, R)
+    bytes (allocated here when None)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    a = _attn_args(q, k, v, out, lse, causal, scale)
+    B, H, N, _ = q.shape
+    if phi_q.shape[-1] != phi_k.shape[-1]:
+        raise ValueError("phi_q and phi_k need the same rank")
+    if phi_q.dtype != phi_k.dtype or phi_q.device != q.device or phi_k.device != q.device:
+        raise ValueError("phi_q / phi_k dtype or device mismatch")
+    R = phi_q.shape[-1]
+    need = fb_mulbias_workspace_bytes(q, R)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1) + 256, dtype=torch.uint8, device=q.device)
+    base = workspace.data_ptr()
+    off = (-base) % 256
+    eq, sq = _bhn_strides(phi_q, B, H, N, "phi_q")
+    ek, sk = _bhn_strides(phi_k, B, H, N, "phi_k")
+    st = load().fb_attn_fwd_mulbias(ctypes.byref(a), eq.data_ptr(), ek.data_ptr(), _dt_code(phi_q.dtype), R,
+                                    ctypes.byref(sq), ctypes.byref(sk), base + off, workspace.numel() - off,
+                                    _stream_ptr(q.device, stream))
+    _check(st)
+    return out
+
+
+def fb_mulbias_expand(q, k, phi_q, phi_k, *, scale: Optional[float] = None, workspace=None, stream=None):
+    """The expansion stage of fb_attn_fwd_mulbias alone.  Returns a dict of views into the
+    workspace: ``q1`` (= scale * q * phi_q[..., 0]) and ``k1`` (``[B, H, N, D]``), ``phi_q`` and
+    ``phi_k`` (``[B, H, N, (R - 1) D]``, the remaining expanded columns, None for R = 1), and the
+    ``workspace`` tensor; fb_attn_fwd_lowrank(q1, k1, v, phi_q, phi_k, scale=1) then gives the
+    same output as fb_attn_fwd_mulbias."""
+    torch = _torch()
+    B, H, N, D = q.shape
+    R = phi_q.shape[-1]
+    need = fb_mulbias_workspace_bytes(q, R)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1) + 256, dtype=torch.uint8, device=q.device)
+    off = (-workspace.data_ptr()) % 256
+    dummy_out = q  # never written by the expansion
+    a = _attn_args(q, k, k, dummy_out, None, False, scale)
+    eq, sq = _bhn_strides(phi_q, B, H, N, "phi_q")
+    ek, sk = _bhn_strides(phi_k, B, H, N, "phi_k")
+    st = load().fb_mulbias_expand(ctypes.byref(a), eq.data_ptr(), ek.data_ptr(), _dt_code(phi_q.dtype), R,
+                                  ctypes.byref(sq), ctypes.byref(sk), workspace.data_ptr() + off,
+                                  workspace.numel() - off, _stream_ptr(q.device, stream))
+    _check(st)
+    es = q.element_size()
+    up = lambda x: (x + 255) // 256 * 256
+    E = B * H * N
+    A = up(E * D * es)
+    W = (R - 1) * D
+
+    def view(byte_off, cols):
+        if cols == 0:
+            return None
+        n = E * cols
+        return workspace[off + byte_off: off + byte_off + n * es].view(q.dtype).view(B, H, N, cols)
+    return {"q1": view(0, D), "k1": view(A, D), "phi_q": view(2 * A, W), "phi_k": view(2 * A + up(E * W * es), W),
+            "workspace": workspace}

@@ -273,6 +273,108 @@ fb_status fb_attn_fwd_lowrank(const fb_attn_args* a, const void* phi_q, const vo
   return st;
 }
 
+size_t fb_mulbias_workspace_bytes(const fb_attn_args* a, int R) {
+  if (!a || R < 1 || a->B < 0 || a->H < 0 || a->N < 0 || a->D < 1) return 0;
+  const size_t rows = (size_t)a->B * a->H * a->N;
+  const size_t es = esize(a->dt);
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t first = up(rows * a->D * es), rest = up(rows * (size_t)(R - 1) * a->D * es);
+  return rows == 0 ? 0 : 2 * first + 2 * rest;
+}
+
+}  // extern "C"
+
+namespace {
+
+struct MulbiasParts {
+  void *q1, *k1, *pq, *pk;
+};
+
+// Validation shared by both multiplicative-bias entry points; on success, *parts locates
+// the expanded operands in the workspace (nothing to do when the inputs are empty).
+fb_status mulbias_check(const char* fn, const fb_attn_args* a, const void* phi_q, const void* phi_k,
+                        fb_dtype phi_dt, int R, const int64_t sphi_q[3], const int64_t sphi_k[3],
+                        void* workspace, size_t workspace_bytes, MulbiasParts* parts) {
+  fb_status st = check_common(a, fn);
+  if (st != FB_OK) return st;
+  if (a->dt != FB_BF16 && a->dt != FB_F16) FB_FAIL(FB_EUNSUPPORTED, "%s: q/k/v must be bf16 or f16", fn);
+  if (R < 1) FB_FAIL(FB_EINVAL, "%s: need R >= 1", fn);
+  if ((int64_t)(R - 1) * a->D > 128) FB_FAIL(FB_EUNSUPPORTED, "%s: (R - 1) * D = %d above 128", fn, (R - 1) * a->D);
+  if (!known_dtype(phi_dt)) FB_FAIL(FB_EUNSUPPORTED, "%s: unknown factor dtype", fn);
+  parts->q1 = parts->k1 = parts->pq = parts->pk = nullptr;
+  if ((int64_t)a->B * a->H * a->N == 0) return FB_OK;
+  if (!phi_q || !phi_k || !sphi_q || !sphi_k) FB_FAIL(FB_EINVAL, "%s: null factor pointer or strides", fn);
+  for (int i = 0; i < 3; ++i)
+    if (sphi_q[i] < 0 || sphi_k[i] < 0) FB_FAIL(FB_EINVAL, "%s: negative factor stride", fn);
+  if (a->N > 1 && (sphi_q[2] < R || sphi_k[2] < R)) FB_FAIL(FB_EINVAL, "%s: factor row stride < R", fn);
+  if (((uintptr_t)phi_q % esize(phi_dt)) || ((uintptr_t)phi_k % esize(phi_dt)))
+    FB_FAIL(FB_EINVAL, "%s: misaligned factors", fn);
+  const size_t need = fb_mulbias_workspace_bytes(a, R);
+  if (!workspace) FB_FAIL(FB_EINVAL, "%s: null workspace", fn);
+  if ((uintptr_t)workspace & 255u) FB_FAIL(FB_EINVAL, "%s: workspace must be 256-byte aligned", fn);
+  if (workspace_bytes < need) FB_FAIL(FB_EINVAL, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes, need);
+  const size_t rows = (size_t)a->B * a->H * a->N, es = esize(a->dt);
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  char* w = (char*)workspace;
+  parts->q1 = w;
+  parts->k1 = w + up(rows * a->D * es);
+  parts->pq = w + 2 * up(rows * a->D * es);
+  parts->pk = (char*)parts->pq + up(rows * (size_t)(R - 1) * a->D * es);
+  return FB_OK;
+}
+
+fb_status mulbias_expand(const fb_attn_args* a, const void* phi_q, const void* phi_k, fb_dtype phi_dt, int R,
+                         const int64_t sphi_q[3], const int64_t sphi_k[3], const MulbiasParts& w, hipStream_t s) {
+  fb_status st = launch_mulbias_expand(a->dt, phi_dt, a->q, a->sq, phi_q, sphi_q, a->B, a->H, a->N, a->D, R,
+                                       a->scale, w.q1, R > 1 ? w.pq : nullptr, s);
+  if (st != FB_OK) return st;
+  return launch_mulbias_expand(a->dt, phi_dt, a->k, a->sk, phi_k, sphi_k, a->B, a->H, a->N, a->D, R, 1.0f, w.k1,
+                               R > 1 ? w.pk : nullptr, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+fb_status fb_mulbias_expand(const fb_attn_args* a, const void* phi_q, const void* phi_k, fb_dtype phi_dt, int R,
+                            const int64_t sphi_q[3], const int64_t sphi_k[3], void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  MulbiasParts w;
+  fb_status st = mulbias_check("fb_mulbias_expand", a, phi_q, phi_k, phi_dt, R, sphi_q, sphi_k, workspace,
+                               workspace_bytes, &w);
+  if (st != FB_OK || (int64_t)a->B * a->H * a->N == 0) return st;
+  return mulbias_expand(a, phi_q, phi_k, phi_dt, R, sphi_q, sphi_k, w, stream);
+}
+
+fb_status fb_attn_fwd_mulbias(const fb_attn_args* a, const void* phi_q, const void* phi_k, fb_dtype phi_dt, int R,
+                              const int64_t sphi_q[3], const int64_t sphi_k[3], void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "fb_attn_fwd_mulbias";
+  MulbiasParts w;
+  fb_status st = mulbias_check(fn, a, phi_q, phi_k, phi_dt, R, sphi_q, sphi_k, workspace, workspace_bytes, &w);
+  if (st != FB_OK || (int64_t)a->B * a->H * a->N == 0) return st;
+  st = mulbias_expand(a, phi_q, phi_k, phi_dt, R, sphi_q, sphi_k, w, stream);
+  if (st != FB_OK) return st;
+  fb_attn_args e = *a;
+  e.q = w.q1;
+  e.k = w.k1;
+  e.scale = 1.0f;
+  const int64_t sx[3] = {(int64_t)a->H * a->N * a->D, (int64_t)a->N * a->D, a->D};
+  for (int i = 0; i < 3; ++i) {
+    e.sq[i] = sx[i];
+    e.sk[i] = sx[i];
+  }
+  const int64_t W = (int64_t)(R - 1) * a->D;
+  const int64_t sf[3] = {(int64_t)a->H * a->N * W, (int64_t)a->N * W, W};
+  st = fb_attn_fwd_lowrank(&e, R > 1 ? w.pq : nullptr, R > 1 ? w.pk : nullptr, a->dt, (int)W, sf, sf, stream);
+  if (st != FB_OK) {
+    char msg[512];
+    snprintf(msg, sizeof(msg), "%s", g_err);
+    set_error("%s: %s", fn, msg);
+  }
+  return st;
+}
+
 fb_status fb_attn_fwd_densebias(const fb_attn_args* a, const void* bias, fb_dtype bias_dt, const int64_t sbias[3],
                                 hipStream_t stream) {
   const char* fn = "fb_attn_fwd_densebias";

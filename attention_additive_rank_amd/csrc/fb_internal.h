@@ -63,6 +63,13 @@ fb_status launch_make_dense_bias(fb_bias_kind kind, int H, int N, int C, const d
                                  fb_dtype out_dt, void* bias, int64_t head_stride, int64_t row_stride,
                                  hipStream_t stream);
 
+// Multiplicative low-rank bias: writes first = [x phi_1] * scale ([B][H][N][D], contiguous)
+// and rest = [x phi_2, ..., x phi_R] * scale ([B][H][N][(R-1) D], contiguous) for x with
+// row strides sx and 16-byte aligned rows; dt is FB_BF16 or FB_F16.
+fb_status launch_mulbias_expand(fb_dtype dt, fb_dtype phi_dt, const void* x, const int64_t sx[3], const void* phi,
+                                const int64_t sphi[3], int B, int H, int N, int D, int R, float scale, void* first,
+                                void* rest, hipStream_t stream);
+
 void set_error(const char* fmt, ...);
 
 }  // namespace fb

@@ -4,6 +4,8 @@ One step = the whole hot path over one batch of synthetic input, inputs already
 resident in HBM:
   1. exact factor generation on the GPU (fb_make_factors), and
   2. the fused low-rank-biased attention forward (fb_attn_fwd_lowrank).
+(--workload mulbias_cos, the multiplicative bias b_ij = cos(i - j) of rank 2: 1. the
+operand expansion fb_mulbias_expand, 2. the same fused kernel on the expanded operands.)
 Default workload: Sandwich-bias attention, B=4, H=8, N=4096, D=64, C=R=64, bf16
 (Q'/K' width 128), the configuration the N=4096, D=64 MFMA target is quoted on.
 
@@ -40,7 +42,11 @@ def kernel_source_hash() -> str:
 
 
 def flops(w) -> float:
+    """4 B H pairs (D + R/2); for the multiplicative bias the score contraction is D R wide
+    (2 B H pairs (D R + D) in all)."""
     pairs = w.N * (w.N + 1) / 2 if w.causal else float(w.N) ** 2
+    if w.bias == "mulbias_cos":
+        return 2.0 * w.B * w.H * pairs * (w.D * w.R + w.D)
     return 4.0 * w.B * w.H * pairs * (w.D + w.R / 2.0)
 
 
@@ -63,7 +69,13 @@ def cpu_oracle_baseline(w, budget_s: float):
         cores = len(os.sched_getaffinity(0))
     inp = synth.make_inputs(w, with_bias_source=False)
     t0 = time.time()
-    if w.bias == "sandwich":
+    attn = oracle.attention
+    if w.bias == "mulbias_cos":
+        phi = oracle.cos_mulbias_factors(w.N)
+        bias = oracle.lowrank_bias(phi, phi)
+        bias_fn = lambda b, h: bias
+        attn = oracle.attention_mulbias
+    elif w.bias == "sandwich":
         bias = oracle.sandwich_bias(w.N, w.C)
         bias_fn = lambda b, h: bias
     else:
@@ -74,8 +86,8 @@ def cpu_oracle_baseline(w, budget_s: float):
     for b in range(w.B):
         for h in range(w.H):
             s = time.time()
-            oracle.attention(inp["q"][b:b + 1, h:h + 1], inp["k"][b:b + 1, h:h + 1], inp["v"][b:b + 1, h:h + 1],
-                             bias=lambda _b, _h: bias_fn(b, h), causal=w.causal)
+            attn(inp["q"][b:b + 1, h:h + 1], inp["k"][b:b + 1, h:h + 1], inp["v"][b:b + 1, h:h + 1],
+                 bias=lambda _b, _h: bias_fn(b, h), causal=w.causal)
             t_attn += time.time() - s
             done += 1
             if t_attn >= budget_s:
@@ -93,7 +105,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="sandwich", choices=["sandwich", "gpt2_alibi_causal"])
+    ap.add_argument("--workload", default="sandwich", choices=["sandwich", "gpt2_alibi_causal", "mulbias_cos"])
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of CPU oracle work (0 = skip)")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-bias baseline")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -120,7 +132,16 @@ def main():
     out = torch.empty_like(q)
     phi_dt = torch.float16 if w.dtype != "f32" else torch.float32
     split = 2 if (w.bias == "alibi" and w.dtype != "f32") else 1
-    if w.bias == "sandwich":
+    mul = w.bias == "mulbias_cos"
+    if mul:
+        # b_ij = cos(i - j) = cos i cos j + sin i sin j: fp32 factors [cos i, sin i], an input
+        import numpy as np
+        ii = np.arange(w.N, dtype=np.float64)
+        phi_dt = torch.float32
+        phi = torch.from_numpy(np.stack([np.cos(ii), np.sin(ii)], axis=1)).to(phi_dt).to(dev)
+        ws = torch.empty(fb.fb_mulbias_workspace_bytes(q, w.R) + 256, dtype=torch.uint8, device=dev)
+        fH, fC, R_used = 1, 0, w.R
+    elif w.bias == "sandwich":
         fH, fC, R_used = 1, w.C, w.C * split * (split + 1) // 2
     else:
         fH, fC, R_used = w.H, 0, 2 * split * (split + 1) // 2
@@ -128,13 +149,27 @@ def main():
     # phi_k rows with 16-byte loads (the zero columns add nothing to phi_q phi_k^T)
     ce = 16 // (2 if phi_dt == torch.float16 else 4)
     R_cols = (R_used + ce - 1) // ce * ce
-    pq = torch.empty((fH, w.N, R_cols), dtype=phi_dt, device=dev)
-    pk = torch.empty_like(pq)
+    if not mul:
+        pq = torch.empty((fH, w.N, R_cols), dtype=phi_dt, device=dev)
+        pk = torch.empty_like(pq)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
+    def stage1():
+        """factor generation (additive) or operand expansion (multiplicative)"""
+        if mul:
+            return fb.fb_mulbias_expand(q, k, phi, phi, workspace=ws)
         fb.fb_make_factors(w.bias, fH, w.N, C=fC, dtype=phi_dt, split=split, phi_q=pq, phi_k=pk)
-        fb.fb_attn_fwd_lowrank(q, k, v, pq, pk, causal=w.causal, out=out)
+        return None
+
+    def stage2(e):
+        """the fused attention kernel"""
+        if mul:
+            fb.fb_attn_fwd_lowrank(e["q1"], e["k1"], v, e["phi_q"], e["phi_k"], causal=w.causal, scale=1.0, out=out)
+        else:
+            fb.fb_attn_fwd_lowrank(q, k, v, pq, pk, causal=w.causal, out=out)
+
+    def step():
+        stage2(stage1())
 
     for _ in range(args.warmup):
         step()
@@ -146,9 +181,9 @@ def main():
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(K):
-        fb.fb_make_factors(w.bias, fH, w.N, C=fC, dtype=phi_dt, split=split, phi_q=pq, phi_k=pk)
+        e = stage1()
         ev[i][0].record(stream)
-        fb.fb_attn_fwd_lowrank(q, k, v, pq, pk, causal=w.causal, out=out)
+        stage2(e)
         ev[i][1].record(stream)
     t_stop.record(stream)
     torch.cuda.synchronize()
@@ -162,7 +197,7 @@ def main():
 
     # dense-bias baseline on the same inputs (shared [N,N] bias for Sandwich, per-head for ALiBi)
     dense = None
-    if not args.no_dense:
+    if not args.no_dense and not mul:
         if w.bias == "sandwich":
             bias = fb.fb_make_dense_bias("sandwich", 1, w.N, C=w.C, dtype=dt)
         else:
@@ -220,7 +255,8 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D, "R": w.R, "causal": w.causal,
                    "factor_dtype": "f16" if phi_dt == torch.float16 else "f32", "factor_split": split,
                    "factor_columns": R_used, "factor_columns_padded": R_cols,
-                   "flops_per_step": F},
+                   "flops_per_step": F,
+                   **({"bias_op": "multiplicative", "expanded_width": w.D * w.R} if mul else {})},
         "pct_mfma_peak": round(100.0 * value / peak, 2),
         "kernel_ms": round(kern_ms, 4),
         "kernel_tflops": round(kern_tflops, 2),
@@ -228,7 +264,9 @@ def main():
         "speedup_vs_densebias": round(dense["ms"] / step_ms, 3) if dense else None,
         "roofline": {"bound": "mfma", "achieved": round(kern_tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(kern_tflops / peak, 4), "traffic": traffic,
-                     "algorithmic_bytes": algorithmic_bytes(w, es, 2 if phi_dt == torch.float16 else 4,
+                     "algorithmic_bytes": (4.0 * w.B * w.H * w.N * w.D * es
+                                           + 2.0 * w.B * w.H * w.N * (w.R - 1) * w.D * es) if mul else
+                                          algorithmic_bytes(w, es, 2 if phi_dt == torch.float16 else 4,
                                                             w.bias == "sandwich"),
                      "kernel": "attn_fwd_kernel (fb_attn_fwd_lowrank)"},
         "cpu_baseline": cpu,

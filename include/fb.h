@@ -38,6 +38,7 @@
 #ifndef FLASHBIAS_FB_H
 #define FLASHBIAS_FB_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -231,6 +232,55 @@ fb_status fb_attn_fwd_lowrank(const fb_attn_args* a, const void* phi_q, const vo
  */
 fb_status fb_attn_fwd_densebias(const fb_attn_args* a, const void* bias, fb_dtype bias_dt,
                                 const int64_t sbias[3], hipStream_t stream);
+
+/*
+ * fb_attn_fwd_mulbias -- attention with a multiplicative low-rank bias,
+ *   O = softmax((s Q K^T) .* (phi_q phi_k^T)) V
+ * (FlashBias rebuttal, answer to Reviewer BRmd, Q1 (2): Eq. (1) defines the
+ * multiplicative bias, Eq. (3) rewrites it as plain attention over the expanded
+ * operands q' = [q phi_q,1, ..., q phi_q,R], k' = [k phi_k,1, ..., k phi_k,R] of
+ * width D R).  One expansion kernel writes q' (scaled by s) and k' into the
+ * caller's workspace, then the low-rank kernel runs with their first D columns as
+ * Q / K and the remaining (R - 1) D as factor columns; the N x N bias is never formed.
+ *
+ *   a            shared arguments; a->dt must be FB_BF16 or FB_F16
+ *   phi_q, phi_k device [B][H][N][R] in phi_dt (FB_F32, FB_BF16 or FB_F16), strides
+ *                sphi_q / sphi_k (0 broadcasts over batch and/or heads)
+ *   R            1 <= R and (R - 1) * D <= 128
+ *   workspace    device, at least fb_mulbias_workspace_bytes(a, R) bytes, 256-byte
+ *                aligned; owned by the caller and only used on `stream` during the
+ *                call's work (it may be reused once that work has finished)
+ * Numerics: every element of q' and k' is formed in fp32 and rounded once to dt;
+ * then as fb_attn_fwd_lowrank (the scale is folded into q').
+ * Errors: as fb_attn_fwd_lowrank; FB_EUNSUPPORTED for fp32 or (R - 1) D > 128;
+ * FB_EINVAL for R < 1, null factors or workspace, a workspace that is too small
+ * or misaligned.
+ */
+fb_status fb_attn_fwd_mulbias(const fb_attn_args* a, const void* phi_q, const void* phi_k, fb_dtype phi_dt, int R,
+                              const int64_t sphi_q[3], const int64_t sphi_k[3], void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace fb_attn_fwd_mulbias needs for these arguments and rank:
+ * q' and k' in a->dt, B H N D R elements each, plus alignment.  0 for empty inputs. */
+size_t fb_mulbias_workspace_bytes(const fb_attn_args* a, int R);
+
+/*
+ * fb_mulbias_expand -- the first stage of fb_attn_fwd_mulbias alone: writes the
+ * expanded operands into the workspace and returns; fb_attn_fwd_mulbias is this
+ * followed by fb_attn_fwd_lowrank on them.  Arguments and errors as
+ * fb_attn_fwd_mulbias (v and o are not touched).  Workspace layout, every part
+ * contiguous row-major in a->dt and starting on a 256-byte boundary, with
+ * E = B H N and up(x) = x rounded up to a multiple of 256:
+ *   offset 0                       q1 = s q phi_q,1              [B][H][N][D]
+ *   offset A = up(E D es)          k1 = k phi_k,1                [B][H][N][D]
+ *   offset 2A                      s [q phi_q,2 .. q phi_q,R]    [B][H][N][(R-1) D]
+ *   offset 2A + up(E (R-1) D es)   [k phi_k,2 .. k phi_k,R]      [B][H][N][(R-1) D]
+ * (es = element size of a->dt); run fb_attn_fwd_lowrank with q1, k1, scale 1 and the
+ * last two parts as phi_q / phi_k (R - 1) D columns wide.
+ */
+fb_status fb_mulbias_expand(const fb_attn_args* a, const void* phi_q, const void* phi_k, fb_dtype phi_dt, int R,
+                            const int64_t sphi_q[3], const int64_t sphi_k[3], void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -41,7 +41,7 @@ import numpy as np
 __all__ = [
     "alibi_slopes", "alibi_bias", "alibi_factors",
     "sandwich_frequencies", "sandwich_bias", "sandwich_factors",
-    "lowrank_bias", "attention", "truncated_svd", "bias_energy", "rank_for_energy",
+    "lowrank_bias", "cos_mulbias_factors", "attention", "attention_mulbias", "truncated_svd", "bias_energy", "rank_for_energy",
 ]
 
 BiasLike = Union[None, np.ndarray, Callable[[int, int], np.ndarray]]
@@ -115,6 +115,14 @@ def sandwich_factors(N: int, C: int) -> np.ndarray:
 
 
 # --------------------------------------------------------------- low rank ----
+def cos_mulbias_factors(N: int) -> np.ndarray:
+    """Rank-2 factors of the multiplicative bias b_ij = cos(i - j) from the rebuttal's
+    example (answer to Reviewer BRmd, Q1 (2)): phi(i) = [cos i, sin i] for queries and keys
+    alike, since cos(i - j) = cos i cos j + sin i sin j.  ``[N, 2]`` fp64."""
+    i = np.arange(N, dtype=np.float64)
+    return np.stack([np.cos(i), np.sin(i)], axis=1)
+
+
 def lowrank_bias(phi_q: np.ndarray, phi_k: np.ndarray) -> np.ndarray:
     """``b = phi_q phi_k^T`` over the last two axes (``[..., N, R] x [..., N, R] -> [..., N, N]``)."""
     return np.matmul(phi_q, np.swapaxes(phi_k, -1, -2))
@@ -164,6 +172,39 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, bias: BiasLike = None
             bb = _bias_slice(bias, b, h, B, H)
             if bb is not None:
                 L = L + np.asarray(bb, dtype=np.float64)[rows]
+            if causal:
+                L = np.where(np.arange(Nk)[None, :] > rows[:, None], -np.inf, L)
+            m = L.max(axis=1, keepdims=True)
+            p = np.exp(L - m)
+            l = p.sum(axis=1, keepdims=True)
+            out[b, h] = (p @ v[b, h]) / l
+            lse[b, h] = (m + np.log(l))[:, 0]
+    return out, lse
+
+
+def attention_mulbias(q: np.ndarray, k: np.ndarray, v: np.ndarray, bias: BiasLike,
+                      scale: Optional[float] = None, causal: bool = False,
+                      rows: Optional[np.ndarray] = None):
+    """Naive softmax attention with a multiplicative bias, fp64 (rebuttal, answer to
+    Reviewer BRmd, Q1, Eq. (1)): the scaled scores are multiplied element-wise by the bias.
+
+    Arguments as :func:`attention`, ``bias`` required.  Per (b,h): L = (s*QK^T) * b;
+    L_ij = -inf where masked; m = max_j L_ij; p = exp(L - m); l = sum_j p; O = p V / l;
+    LSE = m + ln l.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, N, D = q.shape
+    Nk = k.shape[2]
+    s = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    out = np.empty((B, H, len(rows), v.shape[3]))
+    lse = np.empty((B, H, len(rows)))
+    for b in range(B):
+        for h in range(H):
+            bb = np.asarray(_bias_slice(bias, b, h, B, H), dtype=np.float64)
+            L = (s * (q[b, h, rows] @ k[b, h].T)) * bb[rows]
             if causal:
                 L = np.where(np.arange(Nk)[None, :] > rows[:, None], -np.inf, L)
             m = L.max(axis=1, keepdims=True)

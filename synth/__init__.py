@@ -13,10 +13,12 @@ Workloads (shapes ``[B, H, N, D]``, factor rank ``R``):
 * ``sandwich``         B4 H8 N4096 D64 R64 (C=64), bf16, Q,K,V ~ N(0,1)*0.5
 * ``vision_svd``       B2 H8 N4096 (64x64 token grid) D16 R8, bf16
 * ``pairformer_svd``   B512 H4 N512 D32 R16, bf16, pair rep 512x512x128
+* ``mulbias_cos``      B4 H8 N4096 D64 R2, bf16, multiplicative bias cos(i - j)
 
 The language-model workloads stand in for GPT-2 with ALiBi / Sandwich bias,
 the vision one for Swin-style relative-position bias (128 channels over 8
-heads, R=8), the last one for an AlphaFold 3 Pairformer pair bias; none of
+heads, R=8), the pairformer one for an AlphaFold 3 Pairformer pair bias, and
+``mulbias_cos`` uses the Sandwich shapes for the multiplicative-bias example; none of
 their datasets or weights are used.  Draw order per workload: Q, K, V, then
 the bias-source parameters, from ``numpy.random.Generator(PCG64(seed))``.
 """
@@ -44,7 +46,7 @@ class Workload:
     R: int
     causal: bool
     dtype: str            # "f32" | "bf16"
-    bias: str             # "alibi" | "sandwich" | "vision" | "pairformer"
+    bias: str             # "alibi" | "sandwich" | "vision" | "pairformer" | "mulbias_cos"
     qkv_std: float
     seed: int
     C: int = 0            # Sandwich channel count
@@ -64,6 +66,8 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("vision_svd", 2, 8, 4096, 16, 8, False, "bf16", "vision", 0.5, 20260004, grid=64),
         Workload("pairformer_svd", 512, 4, 512, 32, 16, False, "bf16", "pairformer", 0.5, 20260005,
                  c_z=128, cp_rank=16),
+        # multiplicative rank-2 bias of the rebuttal's example (closed form, each side builds it)
+        Workload("mulbias_cos", 4, 8, 4096, 64, 2, False, "bf16", "mulbias_cos", 0.5, 20260006),
     ]
 }
 

@@ -133,6 +133,44 @@ def test_densebias_validation(bdt, kw, code):
     assert _dense(_args(), bdt=bdt, **kw) == code
 
 
+def _mul(a, R=2, phi_dt=fb.FB_BF16, pq=FAKE, pk=FAKE, s=(0, 0, 64), ws=0x100000, wsb=None):
+    sp = fb._I64x3(*s)
+    if wsb is None:
+        wsb = fb.load().fb_mulbias_workspace_bytes(ctypes.byref(a), R)
+    return fb.load().fb_attn_fwd_mulbias(ctypes.byref(a), pq, pk, phi_dt, R, ctypes.byref(sp), ctypes.byref(sp),
+                                         ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,mkw,code", [
+    ({}, dict(R=0), fb.FB_EINVAL),
+    ({}, dict(R=4), fb.FB_EUNSUPPORTED),                    # (R - 1) D = 192 > 128
+    (dict(D=32, strides=(2048, 1024, 32)), dict(R=6), fb.FB_EUNSUPPORTED),
+    (dict(dt=fb.FB_F32), {}, fb.FB_EUNSUPPORTED),
+    ({}, dict(pq=None), fb.FB_EINVAL),
+    ({}, dict(phi_dt=9), fb.FB_EUNSUPPORTED),
+    ({}, dict(s=(0, 0, 1)), fb.FB_EINVAL),                  # factor row stride < R
+    ({}, dict(ws=None), fb.FB_EINVAL),
+    ({}, dict(ws=0x100000 + 16), fb.FB_EINVAL),             # workspace not 256-byte aligned
+    ({}, dict(wsb=1024), fb.FB_EINVAL),                     # workspace too small
+    (dict(q=None), {}, fb.FB_EINVAL),
+])
+def test_mulbias_validation(kw, mkw, code):
+    assert _mul(_args(**kw), **mkw) == code
+    assert fb.fb_last_error() != ""
+
+
+def test_mulbias_workspace_size():
+    a = _args(B=2, H=3, N=100, D=32, strides=(9600, 3200, 32))
+    rows, es = 2 * 3 * 100, 2
+    up = lambda x: (x + 255) // 256 * 256
+    for R in (1, 2, 5):
+        want = 2 * up(rows * 32 * es) + 2 * up(rows * (R - 1) * 32 * es)
+        assert fb.load().fb_mulbias_workspace_bytes(ctypes.byref(a), R) == want
+    assert fb.load().fb_mulbias_workspace_bytes(ctypes.byref(a), 0) == 0
+    assert fb.load().fb_mulbias_workspace_bytes(ctypes.byref(_args(N=0)), 2) == 0
+    assert _mul(_args(N=0, q=None, k=None, v=None, o=None), ws=None) == fb.FB_OK
+
+
 def test_make_factors_validation():
     lib = fb.load()
     r = ctypes.c_int(0)

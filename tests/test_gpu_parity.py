@@ -376,3 +376,95 @@ def test_deterministic(fb):
     o2 = c.run_lowrank()
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
+
+
+# ---------------------------------------------------- multiplicative bias ---
+MUL = [
+    # (shape, R, dtype, factor dtype, causal, factors)
+    (dict(B=2, H=3, N=300, D=64), 2, "bf16", "f32", False, "cos"),
+    (dict(B=1, H=2, N=200, D=32), 3, "bf16", "bf16", True, "rand"),
+    (dict(B=1, H=2, N=129, D=32), 5, "f16", "f16", False, "rand"),
+    (dict(B=1, H=2, N=257, D=16), 9, "bf16", "f16", True, "rand"),
+    (dict(B=2, H=2, N=100, D=128), 2, "bf16", "bf16", False, "rand"),
+    (dict(B=1, H=2, N=150, D=64), 1, "bf16", "f32", False, "rand"),
+]
+
+
+@pytest.mark.parametrize("shape,R,dt,pdt,causal,kind", MUL, ids=[f"mul-{i}" for i in range(len(MUL))])
+def test_mulbias_parity(fb, shape, R, dt, pdt, causal, kind):
+    """Multiplicative low-rank bias through operand expansion: every output element and the
+    LSE against the oracle's element-wise definition with the same (rounded) factors."""
+    import torch
+    B, H, N, D = shape["B"], shape["H"], shape["N"], shape["D"]
+    r = np.random.default_rng(500 + N + R)
+    q, k, v = (synth.round_to(r.standard_normal((B, H, N, D)) * 0.5, dt) for _ in range(3))
+    if kind == "cos":
+        pq = pk = synth.round_to(oracle.cos_mulbias_factors(N), pdt)
+    else:
+        pq = synth.round_to(r.standard_normal((H, N, R)) * 0.7, pdt)
+        pk = synth.round_to(r.standard_normal((H, N, R)) * 0.7, pdt)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda:0")
+    o = fb.fb_attn_fwd_mulbias(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), to_dev(pq, pdt), to_dev(pk, pdt),
+                               causal=causal, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_mulbias(q, k, v, oracle.lowrank_bias(pq, pk), causal=causal)
+    assert_close(to_np(o), ro, dt, f"mulbias R={R} D={D} {kind}")
+    np.testing.assert_allclose(lse.cpu().double().numpy(), rl, rtol=0, atol=2e-2)
+
+
+def test_mulbias_strided_inputs_and_reused_workspace(fb):
+    """Q/K as permuted views, per-(b, h) factors, and one workspace reused by two calls."""
+    import torch
+    r = np.random.default_rng(510)
+    B, H, N, D, R = 2, 2, 170, 32, 3
+    big = to_dev(synth.round_to(r.standard_normal((B, N, H, 2 * D)) * 0.5, "bf16"), "bf16")
+    qd = big[..., :D].permute(0, 2, 1, 3)
+    kd = big[..., D:].permute(0, 2, 1, 3)
+    v = synth.round_to(r.standard_normal((B, H, N, D)) * 0.5, "bf16")
+    ws = torch.empty(fb.fb_mulbias_workspace_bytes(qd, R) + 256, dtype=torch.uint8, device="cuda:0")
+    outs = []
+    for t in range(2):
+        pq = synth.round_to(r.standard_normal((B, H, N, R)) * 0.6, "f16")
+        pk = synth.round_to(r.standard_normal((B, H, N, R)) * 0.6, "f16")
+        o = fb.fb_attn_fwd_mulbias(qd, kd, to_dev(v, "bf16"), to_dev(pq, "f16"), to_dev(pk, "f16"), workspace=ws)
+        torch.cuda.synchronize()
+        ro, _ = oracle.attention_mulbias(to_np(qd), to_np(kd), v, oracle.lowrank_bias(pq, pk))
+        assert_close(to_np(o), ro, "bf16", f"mulbias strided call {t}")
+
+
+def test_mulbias_full_size_sampled(fb):
+    """The benchmark's multiplicative workload (b_ij = cos(i - j), B4 H8 N4096 D64 R2) in the
+    bench's launch; sampled rows of sampled (b, h)."""
+    import torch
+    w = synth.workload("mulbias_cos")
+    inp = synth.make_inputs(w)
+    q, k, v, N = inp["q"], inp["k"], inp["v"], w.N
+    phi = synth.round_to(oracle.cos_mulbias_factors(N), "f32")
+    o = fb.fb_attn_fwd_mulbias(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), to_dev(phi, "f32"),
+                               to_dev(phi, "f32"))
+    torch.cuda.synchronize()
+    rows = sample_rows(N, 48, seed=3)
+    bias = oracle.lowrank_bias(phi, phi)
+    for (b, h) in [(0, 0), (1, 5), (3, 7)]:
+        ro, _ = oracle.attention_mulbias(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], bias,
+                                         rows=rows)
+        assert_close(to_np(o[b, h])[rows][None, None], ro, "bf16", f"mulbias full-size b={b} h={h}")
+
+
+def test_mulbias_two_stage_equals_one_call(fb):
+    """Expansion stage + the low-rank kernel on its outputs gives bit-identical results to
+    the one-call entry point (the benchmark times the two stages separately)."""
+    import torch
+    r = np.random.default_rng(520)
+    B, H, N, D, R = 2, 2, 300, 64, 3
+    q, k, v = (to_dev(synth.round_to(r.standard_normal((B, H, N, D)) * 0.5, "bf16"), "bf16") for _ in range(3))
+    pq = to_dev(synth.round_to(r.standard_normal((N, R)), "f32"), "f32")
+    pk = to_dev(synth.round_to(r.standard_normal((N, R)), "f32"), "f32")
+    o1 = fb.fb_attn_fwd_mulbias(q, k, v, pq, pk)
+    e = fb.fb_mulbias_expand(q, k, pq, pk)
+    o2 = fb.fb_attn_fwd_lowrank(e["q1"], e["k1"], v, e["phi_q"], e["phi_k"], scale=1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    s = 1.0 / np.sqrt(D)
+    q1 = (q.double() * pq.double()[:, 0][None, None, :, None] * s)
+    np.testing.assert_allclose(to_np(e["q1"]), to_np(q1), rtol=2 ** -8, atol=0)

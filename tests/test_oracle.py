@@ -336,3 +336,69 @@ def test_rank_for_energy_exact_biases():
     full = oracle.rank_for_energy(sw, 1 - 1e-12, R_max=16)
     assert full["reached"] and full["R"] <= 16
     assert oracle.rank_for_energy(np.zeros((5, 5)), 0.95)["R"] == 1
+
+
+# ------------------------------------------------------- multiplicative bias ---
+def test_mulbias_all_ones_is_plain_attention():
+    r = np.random.default_rng(41)
+    q, k, v = (r.standard_normal((2, 2, 20, 8)) for _ in range(3))
+    o1, l1 = oracle.attention_mulbias(q, k, v, np.ones((20, 20)))
+    o2, l2 = oracle.attention(q, k, v)
+    np.testing.assert_allclose(o1, o2, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_mulbias_brute_force_cos_example(causal):
+    """The pages' example b_ij = cos(i - j) with factors [cos i, sin i] (rank 2), against
+    element-by-element loops that evaluate cos(i - j) directly."""
+    r = np.random.default_rng(42)
+    B, H, N, D = 1, 2, 6, 4
+    q, k, v = (r.standard_normal((B, H, N, D)) for _ in range(3))
+    idx = np.arange(N, dtype=np.float64)
+    phi = np.stack([np.cos(idx), np.sin(idx)], axis=1)
+    got, lse = oracle.attention_mulbias(q, k, v, oracle.lowrank_bias(phi, phi), scale=0.7, causal=causal)
+    for b in range(B):
+        for h in range(H):
+            for i in range(N):
+                L = []
+                for j in range(N):
+                    if causal and j > i:
+                        continue
+                    dot = sum(q[b, h, i, c] * k[b, h, j, c] for c in range(D))
+                    L.append((j, 0.7 * dot * math.cos(i - j)))
+                m = max(x for _, x in L)
+                w = [(j, math.exp(x - m)) for j, x in L]
+                tot = sum(x for _, x in w)
+                for c in range(D):
+                    ref = sum(x * v[b, h, j, c] for j, x in w) / tot
+                    assert abs(got[b, h, i, c] - ref) < 1e-12
+                assert abs(lse[b, h, i] - (m + math.log(tot))) < 1e-12
+
+
+def test_mulbias_expansion_identity():
+    """Eq. (3) of the same answer: with q' = s [q phi_q,1 .. q phi_q,R] and
+    k' = [k phi_k,1 .. k phi_k,R], q' k'^T equals (s q k^T) * (phi_q phi_k^T)."""
+    r = np.random.default_rng(43)
+    N, D, R, s = 9, 5, 3, 0.3
+    q, k = r.standard_normal((N, D)), r.standard_normal((N, D))
+    pq, pk = r.standard_normal((N, R)), r.standard_normal((N, R))
+    qe = s * np.concatenate([q * pq[:, [c]] for c in range(R)], axis=1)
+    ke = np.concatenate([k * pk[:, [c]] for c in range(R)], axis=1)
+    np.testing.assert_allclose(qe @ ke.T, (s * q @ k.T) * oracle.lowrank_bias(pq, pk), rtol=1e-12, atol=1e-12)
+
+
+def test_mulbias_scale_moves_between_scores_and_bias():
+    r = np.random.default_rng(44)
+    q, k, v = (r.standard_normal((1, 1, 15, 8)) for _ in range(3))
+    b = r.standard_normal((15, 15))
+    o1, _ = oracle.attention_mulbias(q, k, v, b, scale=0.5)
+    o2, _ = oracle.attention_mulbias(q, k, v, 2.5 * b, scale=0.2)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-12)
+
+
+def test_cos_mulbias_factors_closed_form():
+    phi = oracle.cos_mulbias_factors(50)
+    i = np.arange(50)
+    np.testing.assert_allclose(oracle.lowrank_bias(phi, phi), np.cos(i[:, None] - i[None, :]), rtol=0, atol=1e-13)
+    assert phi[0].tolist() == [1.0, 0.0]
