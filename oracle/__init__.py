@@ -41,7 +41,8 @@ import numpy as np
 __all__ = [
     "alibi_slopes", "alibi_bias", "alibi_factors",
     "sandwich_frequencies", "sandwich_bias", "sandwich_factors",
-    "lowrank_bias", "cos_mulbias_factors", "attention", "attention_mulbias", "truncated_svd", "bias_energy", "rank_for_energy",
+    "lowrank_bias", "cos_mulbias_factors", "attention", "attention_mulbias", "attention_backward",
+    "lowrank_factor_grads", "truncated_svd", "bias_energy", "rank_for_energy",
 ]
 
 BiasLike = Union[None, np.ndarray, Callable[[int, int], np.ndarray]]
@@ -213,6 +214,54 @@ def attention_mulbias(q: np.ndarray, k: np.ndarray, v: np.ndarray, bias: BiasLik
             out[b, h] = (p @ v[b, h]) / l
             lse[b, h] = (m + np.log(l))[:, 0]
     return out, lse
+
+
+def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, bias: BiasLike = None,
+                       scale: Optional[float] = None, causal: bool = False):
+    """Gradients of ``O = softmax(s Q K^T + b) V`` for an upstream gradient ``dO``, fp64.
+
+    The textbook chain rule, per (b,h), with nothing fused or reordered:
+    L = s Q K^T + b (masked entries -inf); P = softmax_rows(L); O = P V;
+    dV = P^T dO; dP = dO V^T; dL_ij = P_ij (dP_ij - sum_k P_ik dP_ik) (the softmax
+    Jacobian); dQ = s dL K; dK = s dL^T Q; db = dL (the gradient with respect to the
+    bias matrix; masked entries get 0).  The training use of the bias factors is the
+    rebuttal's (answer to Reviewer UJUf, Q1: Sandwich bias in GPT-2 training).
+    Returns ``(dq, dk, dv, db)`` with ``db`` ``[B,H,N,N]``.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, H, N, D = q.shape
+    s = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    db = np.zeros((B, H, N, k.shape[2]))
+    for b in range(B):
+        for h in range(H):
+            L = s * (q[b, h] @ k[b, h].T)
+            bb = _bias_slice(bias, b, h, B, H)
+            if bb is not None:
+                L = L + np.asarray(bb, dtype=np.float64)
+            if causal:
+                L = np.where(np.arange(k.shape[2])[None, :] > np.arange(N)[:, None], -np.inf, L)
+            P = np.exp(L - L.max(axis=1, keepdims=True))
+            P = P / P.sum(axis=1, keepdims=True)
+            dv[b, h] = P.T @ do[b, h]
+            dP = do[b, h] @ v[b, h].T
+            dL = P * (dP - np.sum(P * dP, axis=1, keepdims=True))
+            dq[b, h] = s * (dL @ k[b, h])
+            dk[b, h] = s * (dL.T @ q[b, h])
+            db[b, h] = dL
+    return dq, dk, dv, db
+
+
+def lowrank_factor_grads(db: np.ndarray, phi_q: np.ndarray, phi_k: np.ndarray):
+    """Gradients of a loss with respect to the factors of ``b = phi_q phi_k^T`` from the
+    gradient ``db`` with respect to b: ``dphi_q = db phi_k``, ``dphi_k = db^T phi_q``
+    (over the last two axes; factors broadcast like ``db`` allows)."""
+    db = np.asarray(db, dtype=np.float64)
+    return (np.matmul(db, np.asarray(phi_k, dtype=np.float64)),
+            np.matmul(np.swapaxes(db, -1, -2), np.asarray(phi_q, dtype=np.float64)))
 
 
 # --------------------------------------------------------------------- SVD ---

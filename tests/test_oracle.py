@@ -402,3 +402,65 @@ def test_cos_mulbias_factors_closed_form():
     i = np.arange(50)
     np.testing.assert_allclose(oracle.lowrank_bias(phi, phi), np.cos(i[:, None] - i[None, :]), rtol=0, atol=1e-13)
     assert phi[0].tolist() == [1.0, 0.0]
+
+
+# ------------------------------------------------------------------ backward ---
+def _loss(q, k, v, do, bias, causal, scale):
+    o, _ = oracle.attention(q, k, v, bias=bias, causal=causal, scale=scale)
+    return float(np.sum(o * do))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_finite_differences(causal):
+    """Central differences of <dO, O> in fp64 against the analytic gradients, for every
+    entry of Q, K, V and the bias on a tiny problem."""
+    r = np.random.default_rng(61)
+    B, H, N, D, s = 1, 2, 5, 3, 0.6
+    q, k, v, do = (r.standard_normal((B, H, N, D)) for _ in range(4))
+    bias = r.standard_normal((B, H, N, N))
+    dq, dk, dv, db = oracle.attention_backward(q, k, v, do, bias=bias, causal=causal, scale=s)
+    eps = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv), (bias, db)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            old = x[idx]
+            x[idx] = old + eps
+            lp = _loss(q, k, v, do, bias, causal, s)
+            x[idx] = old - eps
+            lm = _loss(q, k, v, do, bias, causal, s)
+            x[idx] = old
+            num[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8)
+
+
+def test_lowrank_factor_grads_match_finite_differences():
+    r = np.random.default_rng(62)
+    B, H, N, D, R = 1, 1, 6, 4, 3
+    q, k, v, do = (r.standard_normal((B, H, N, D)) for _ in range(4))
+    pq, pk = r.standard_normal((H, N, R)), r.standard_normal((H, N, R))
+    _, _, _, db = oracle.attention_backward(q, k, v, do, bias=oracle.lowrank_bias(pq, pk))
+    gq, gk = oracle.lowrank_factor_grads(db[0], pq, pk)
+    eps = 1e-6
+    for x, g in ((pq, gq), (pk, gk)):
+        for idx in np.ndindex(x.shape):
+            old = x[idx]
+            x[idx] = old + eps
+            lp = _loss(q, k, v, do, oracle.lowrank_bias(pq, pk), False, None)
+            x[idx] = old - eps
+            lm = _loss(q, k, v, do, oracle.lowrank_bias(pq, pk), False, None)
+            x[idx] = old
+            assert abs(g[idx] - (lp - lm) / (2 * eps)) < 1e-7
+
+
+def test_backward_invariants():
+    """dO = 0 gives zero gradients; the bias gradient rows sum to 0 (softmax is shift
+    invariant along a row); with dO = V-independent constant rows, dV columns sum to
+    N times that constant."""
+    r = np.random.default_rng(63)
+    q, k, v = (r.standard_normal((1, 2, 7, 4)) for _ in range(3))
+    z = oracle.attention_backward(q, k, v, np.zeros_like(q))
+    assert all(np.all(x == 0) for x in z)
+    do = r.standard_normal(q.shape)
+    _, _, dv, db = oracle.attention_backward(q, k, v, do, bias=r.standard_normal((7, 7)), causal=True)
+    np.testing.assert_allclose(db.sum(axis=-1), 0.0, atol=1e-13)
+    np.testing.assert_allclose(dv.sum(axis=2), do.sum(axis=2), atol=1e-12)
