@@ -56,6 +56,16 @@ _I64x3 = ctypes.c_int64 * 3
 _DP = ctypes.POINTER(ctypes.c_double)
 
 
+class _BwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("dout", ctypes.c_void_p), ("sdo", _I64x3),
+        ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+        ("sdq", _I64x3), ("sdk", _I64x3), ("sdv", _I64x3),
+        ("dphi_q", ctypes.c_void_p), ("dphi_k", ctypes.c_void_p), ("sdphi_q", _I64x3), ("sdphi_k", _I64x3),
+        ("delta", ctypes.c_void_p),
+    ]
+
+
 def load():
     """Load libflashbias.so (once).  Raises RuntimeError if it is not built."""
     global _lib
@@ -89,6 +99,10 @@ def load():
         lib.fb_attn_fwd_lowrank.argtypes = [ctypes.POINTER(_AttnArgs), ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_int, ctypes.c_int, ctypes.POINTER(_I64x3),
                                             ctypes.POINTER(_I64x3), ctypes.c_void_p]
+        lib.fb_attn_bwd_lowrank.restype = ctypes.c_int
+        lib.fb_attn_bwd_lowrank.argtypes = [ctypes.POINTER(_AttnArgs), ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_int, ctypes.c_int, ctypes.POINTER(_I64x3),
+                                            ctypes.POINTER(_I64x3), ctypes.POINTER(_BwdArgs), ctypes.c_void_p]
         lib.fb_attn_fwd_mulbias.restype = ctypes.c_int
         lib.fb_attn_fwd_mulbias.argtypes = [ctypes.POINTER(_AttnArgs), ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_int, ctypes.c_int, ctypes.POINTER(_I64x3),
@@ -394,3 +408,48 @@ def fb_mulbias_expand(q, k, phi_q, phi_k, *, scale: Optional[float] = None, work
         return workspace[off + byte_off: off + byte_off + n * es].view(q.dtype).view(B, H, N, cols)
     return {"q1": view(0, D), "k1": view(A, D), "phi_q": view(2 * A, W), "phi_k": view(2 * A + up(E * W * es), W),
             "workspace": workspace}
+
+
+def fb_attn_bwd_lowrank(q, k, v, out, lse, dout, phi_q=None, phi_k=None, *, causal: bool = False,
+                        scale: Optional[float] = None, dq=None, dk=None, dv=None, stream=None):
+    """Gradients of fb_attn_fwd_lowrank's output for the upstream gradient ``dout``.
+
+    ``out`` and ``lse`` are the forward's output and LSE (float32 ``[B, H, N]``).  Returns
+    ``(dq, dk, dv, dphi_q, dphi_k)``; the factor gradients are float32 with the factors'
+    own shapes (summed over the axes a factor is broadcast on), None for R = 0."""
+    torch = _torch()
+    B, H, N, D = q.shape
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    a = _attn_args(q, k, v, out, lse, causal, scale)
+    if lse is None:
+        raise ValueError("the forward LSE is required")
+    g = _BwdArgs()
+    for name, t in (("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must match q in shape, dtype and device")
+        setattr(g, name, t.data_ptr())
+        setattr(g, "s" + ("do" if name == "dout" else name), _I64x3(*t.stride()[:3]))
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    g.delta = delta.data_ptr()
+    dpq = dpk = None
+    R = 0 if (phi_q is None or phi_k is None) else phi_q.shape[-1]
+    if R > 0:
+        if phi_q.shape[-1] != phi_k.shape[-1] or phi_q.dtype != phi_k.dtype:
+            raise ValueError("phi_q / phi_k rank or dtype mismatch")
+        eq, sq = _bhn_strides(phi_q, B, H, N, "phi_q")
+        ek, sk = _bhn_strides(phi_k, B, H, N, "phi_k")
+        dpq = torch.empty(phi_q.shape, dtype=torch.float32, device=q.device)
+        dpk = torch.empty(phi_k.shape, dtype=torch.float32, device=q.device)
+        _, gsq = _bhn_strides(dpq, B, H, N, "dphi_q")
+        _, gsk = _bhn_strides(dpk, B, H, N, "dphi_k")
+        g.dphi_q, g.dphi_k, g.sdphi_q, g.sdphi_k = dpq.data_ptr(), dpk.data_ptr(), gsq, gsk
+        st = load().fb_attn_bwd_lowrank(ctypes.byref(a), eq.data_ptr(), ek.data_ptr(), _dt_code(phi_q.dtype), R,
+                                        ctypes.byref(sq), ctypes.byref(sk), ctypes.byref(g),
+                                        _stream_ptr(q.device, stream))
+    else:
+        st = load().fb_attn_bwd_lowrank(ctypes.byref(a), None, None, a.dt, 0, None, None, ctypes.byref(g),
+                                        _stream_ptr(q.device, stream))
+    _check(st)
+    return dq, dk, dv, dpq, dpk

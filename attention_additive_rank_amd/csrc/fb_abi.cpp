@@ -375,6 +375,100 @@ fb_status fb_attn_fwd_mulbias(const fb_attn_args* a, const void* phi_q, const vo
   return st;
 }
 
+fb_status fb_attn_bwd_lowrank(const fb_attn_args* a, const void* phi_q, const void* phi_k, fb_dtype phi_dt, int R,
+                              const int64_t sphi_q[3], const int64_t sphi_k[3], const fb_attn_bwd_args* g,
+                              hipStream_t stream) {
+  const char* fn = "fb_attn_bwd_lowrank";
+  fb_status st = check_common(a, fn);
+  if (st != FB_OK) return st;
+  if (!g) FB_FAIL(FB_EINVAL, "%s: null gradient arguments", fn);
+  if (a->dt != FB_BF16 && a->dt != FB_F16) FB_FAIL(FB_EUNSUPPORTED, "%s: q/k/v must be bf16 or f16", fn);
+  if (a->D != 32 && a->D != 64) FB_FAIL(FB_EUNSUPPORTED, "%s: head dim %d not in {32, 64}", fn, a->D);
+  if (R < 0) FB_FAIL(FB_EINVAL, "%s: negative R", fn);
+  if (R > 64 || R % 8 != 0) FB_FAIL(FB_EUNSUPPORTED, "%s: R = %d (need a multiple of 8, at most 64)", fn, R);
+  if (R > 0) {
+    if (!known_dtype(phi_dt) || phi_dt == FB_F32 || (a->dt == FB_F16 && phi_dt != FB_F16))
+      FB_FAIL(FB_EUNSUPPORTED, "%s: factor dtype does not match the q/k/v dtype", fn);
+  }
+  if ((int64_t)a->B * a->H * a->N == 0) return FB_OK;
+  if (!a->lse) FB_FAIL(FB_EINVAL, "%s: the forward LSE is required", fn);
+  if (!g->dout || !g->dq || !g->dk || !g->dv || !g->delta) FB_FAIL(FB_EINVAL, "%s: null dO, output or workspace", fn);
+  const int es = esize(a->dt);
+  const int64_t* st6[4] = {g->sdo, g->sdq, g->sdk, g->sdv};
+  const void* pt[4] = {g->dout, g->dq, g->dk, g->dv};
+  for (int i = 0; i < 4; ++i) {
+    if (!aligned16(pt[i])) FB_FAIL(FB_EINVAL, "%s: dO/dq/dk/dv must be 16-byte aligned", fn);
+    if (st6[i][0] < 0 || st6[i][1] < 0 || st6[i][2] < 0 || !rows_aligned(st6[i], es))
+      FB_FAIL(FB_EINVAL, "%s: dO/dq/dk/dv strides must be non-negative multiples of %d elements", fn, 16 / es);
+    if (a->N > 1 && st6[i][2] < a->D) FB_FAIL(FB_EINVAL, "%s: gradient row stride < D", fn);
+    if (!strides_fit32(st6[i], a->N)) FB_FAIL(FB_EUNSUPPORTED, "%s: gradient strides exceed 32 bits", fn);
+  }
+  if ((uintptr_t)g->delta & 3u) FB_FAIL(FB_EINVAL, "%s: misaligned delta workspace", fn);
+  BwdParams p{};
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.dout = g->dout;
+  p.lse = a->lse;
+  p.delta = g->delta;
+  p.dq = g->dq;
+  p.dk = g->dk;
+  p.dv = g->dv;
+  for (int i = 0; i < 3; ++i) {
+    p.sq[i] = (int)a->sq[i];
+    p.sk[i] = (int)a->sk[i];
+    p.sv[i] = (int)a->sv[i];
+    p.sdo[i] = (int)g->sdo[i];
+    p.sdq[i] = (int)g->sdq[i];
+    p.sdk[i] = (int)g->sdk[i];
+    p.sdv[i] = (int)g->sdv[i];
+  }
+  p.R = R;
+  p.flags = a->causal ? FLAG_CAUSAL : 0;
+  p.B = a->B;
+  p.H = a->H;
+  p.N = a->N;
+  p.scale = a->scale;
+  p.nblk = (a->N + kBwdRows - 1) / kBwdRows;
+  if (p.nblk * (int64_t)a->H * a->B > 0x7fffffffLL) FB_FAIL(FB_EUNSUPPORTED, "%s: grid too large", fn);
+  int RP = 0;
+  if (R > 0) {
+    if (!phi_q || !phi_k || !sphi_q || !sphi_k || !g->dphi_q || !g->dphi_k)
+      FB_FAIL(FB_EINVAL, "%s: null factor pointer, strides or factor gradient", fn);
+    for (int i = 0; i < 3; ++i)
+      if (sphi_q[i] < 0 || sphi_k[i] < 0 || g->sdphi_q[i] < 0 || g->sdphi_k[i] < 0)
+        FB_FAIL(FB_EINVAL, "%s: negative factor stride", fn);
+    if (!aligned16(phi_q) || !aligned16(phi_k) || !rows_aligned(sphi_q, esize(phi_dt)) ||
+        !rows_aligned(sphi_k, esize(phi_dt)))
+      FB_FAIL(FB_EUNSUPPORTED, "%s: factor rows must be 16-byte aligned", fn);
+    if (a->N > 1 && (sphi_q[2] < R || sphi_k[2] < R || g->sdphi_q[2] < R || g->sdphi_k[2] < R))
+      FB_FAIL(FB_EINVAL, "%s: factor row stride < R", fn);
+    if (((uintptr_t)g->dphi_q & 3u) || ((uintptr_t)g->dphi_k & 3u)) FB_FAIL(FB_EINVAL, "%s: misaligned dphi", fn);
+    if (!strides_fit32(sphi_q, a->N) || !strides_fit32(sphi_k, a->N) || !strides_fit32(g->sdphi_q, a->N) ||
+        !strides_fit32(g->sdphi_k, a->N))
+      FB_FAIL(FB_EUNSUPPORTED, "%s: factor strides exceed 32 bits", fn);
+    p.phq = phi_q;
+    p.phk = phi_k;
+    p.dphq = g->dphi_q;
+    p.dphk = g->dphi_k;
+    for (int i = 0; i < 3; ++i) {
+      p.spq[i] = (int)sphi_q[i];
+      p.spk[i] = (int)sphi_k[i];
+      p.sdpq[i] = (int)g->sdphi_q[i];
+      p.sdpk[i] = (int)g->sdphi_k[i];
+    }
+    p.flags |= FLAG_PHQ_VEC | FLAG_PHK_VEC;
+    RP = R <= 16 ? 16 : R <= 32 ? 32 : 64;
+  }
+  st = launch_attention_bwd_aux(a->dt, a->o, a->so, g->dout, g->sdo, a->B, a->H, a->N, a->D, g->delta,
+                                g->dphi_q, g->sdphi_q, g->dphi_k, g->sdphi_k, R, stream);
+  if (st != FB_OK) return st;
+  st = a->D == 32 ? launch_attention_bwd_d32(a->dt, R > 0 ? phi_dt : a->dt, RP, p, stream)
+                  : launch_attention_bwd_d64(a->dt, R > 0 ? phi_dt : a->dt, RP, p, stream);
+  if (st == FB_EUNSUPPORTED) set_error("%s: no kernel for this dtype / rank combination", fn);
+  return st;
+}
+
 fb_status fb_attn_fwd_densebias(const fb_attn_args* a, const void* bias, fb_dtype bias_dt, const int64_t sbias[3],
                                 hipStream_t stream) {
   const char* fn = "fb_attn_fwd_densebias";

@@ -70,6 +70,40 @@ fb_status launch_mulbias_expand(fb_dtype dt, fb_dtype phi_dt, const void* x, con
                                 const int64_t sphi[3], int B, int H, int N, int D, int R, float scale, void* first,
                                 void* rest, hipStream_t stream);
 
+// Everything one backward launch pair needs (kernel argument, by value).
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* lse;
+  const float* delta;
+  const void* phq;
+  const void* phk;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dphq;
+  float* dphk;
+  int sq[3], sk[3], sv[3], sdo[3], sdq[3], sdk[3], sdv[3];
+  int spq[3], spk[3], sdpq[3], sdpk[3];
+  int R;
+  int flags;        // FLAG_CAUSAL, FLAG_PHQ_VEC, FLAG_PHK_VEC
+  int B, H, N;
+  float scale;
+  int nblk;         // 128-row blocks per (b, h)
+};
+constexpr int kBwdRows = 128;     // rows (keys or queries) per backward workgroup
+
+// Backward kernels (fb_attn_bwd.h): one function per head dim (32 / 64); phi_dt as the
+// forward; RP in {0, 16, 32, 64}.  FB_EUNSUPPORTED when no instance matches.
+fb_status launch_attention_bwd_d32(fb_dtype dt, fb_dtype phi_dt, int RP, const BwdParams& p, hipStream_t s);
+fb_status launch_attention_bwd_d64(fb_dtype dt, fb_dtype phi_dt, int RP, const BwdParams& p, hipStream_t s);
+// Delta = rowsum(dO * O) into delta ([B][H][N] fp32) and, for R > 0, zeroed factor gradients.
+fb_status launch_attention_bwd_aux(fb_dtype dt, const void* o, const int64_t so[3], const void* dout,
+                                   const int64_t sdo[3], int B, int H, int N, int D, float* delta, float* dphq,
+                                   const int64_t sdpq[3], float* dphk, const int64_t sdpk[3], int R, hipStream_t s);
+
 void set_error(const char* fmt, ...);
 
 }  // namespace fb

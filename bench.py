@@ -108,6 +108,8 @@ def main():
     ap.add_argument("--workload", default="sandwich", choices=["sandwich", "gpt2_alibi_causal", "mulbias_cos"])
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of CPU oracle work (0 = skip)")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-bias baseline")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (fb_attn_bwd_lowrank) of the workload instead")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -170,6 +172,11 @@ def main():
 
     def step():
         stage2(stage1())
+
+    if args.backward:
+        if mul:
+            raise SystemExit("--backward covers the additive workloads")
+        return bench_backward(args, w, fb, torch, q, k, v, pq, pk, stage1, out, dev, stream)
 
     for _ in range(args.warmup):
         step()
@@ -272,6 +279,47 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+def bench_backward(args, w, fb, torch, q, k, v, pq_t, pk_t, stage1, out, dev, stream):
+    """Backward step: Delta = rowsum(dO * O), zeroed factor gradients, the key-major dK/dV
+    kernel and the query-major dQ kernel (fb_attn_bwd_lowrank), after one forward that
+    provides O and LSE.  Flops: the five products of the standard backward with the
+    augmented width, 2 B H pairs (3 (D + R) + 2 D); the kernels recompute S and dP once
+    more (the dQ kernel), which is not counted."""
+    import numpy as np
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stage1()                        # the factors, as the forward step makes them
+    fb.fb_attn_fwd_lowrank(q, k, v, pq_t, pk_t, causal=w.causal, out=out, lse=lse)
+    g = np.random.default_rng(w.seed + 7).standard_normal(q.shape) * 0.5
+    dout = torch.from_numpy(g).to(q.dtype).to(dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    for _ in range(args.warmup):
+        fb.fb_attn_bwd_lowrank(q, k, v, out, lse, dout, pq_t, pk_t, causal=w.causal, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    K = args.steps
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(K):
+        fb.fb_attn_bwd_lowrank(q, k, v, out, lse, dout, pq_t, pk_t, causal=w.causal, dq=dq, dk=dk, dv=dv)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / K
+    pairs = w.N * (w.N + 1) / 2 if w.causal else float(w.N) ** 2
+    Rp = pq_t.shape[-1]
+    F = 2.0 * w.B * w.H * pairs * (3 * (w.D + Rp) + 2 * w.D)
+    tf = F / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    print(json.dumps({"metric": "biased-attention bwd TFLOP/s + % MFMA peak", "value": round(tf, 2),
+                      "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+                      "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+                      "data": "synthetic",
+                      "config": {"workload": w.name + "_backward", "B": w.B, "H": w.H, "N": w.N, "D": w.D,
+                                 "R_columns": Rp, "causal": w.causal, "flops_per_step": F},
+                      "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": peak, "unit": "TFLOP/s",
+                                   "frac": round(tf / peak, 4), "traffic": None,
+                                   "kernel": "attn_bwd_dkv_kernel + attn_bwd_dq_kernel (+ delta, zero)"},
+                      "cpu_baseline": None}), flush=True)
 
 
 if __name__ == "__main__":

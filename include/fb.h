@@ -282,6 +282,48 @@ fb_status fb_mulbias_expand(const fb_attn_args* a, const void* phi_q, const void
                             const int64_t sphi_q[3], const int64_t sphi_k[3], void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
 
+/* Outputs and workspace of the attention backward. */
+typedef struct {
+  const void* dout;    /* device [B][H][N][D], strides sdo: the upstream gradient dO (a->dt) */
+  int64_t sdo[3];
+  void* dq;            /* device outputs [B][H][N][D] in a->dt, strides sdq / sdk / sdv */
+  void* dk;
+  void* dv;
+  int64_t sdq[3], sdk[3], sdv[3];
+  float* dphi_q;       /* device fp32 outputs [.][.][N][R] with strides sdphi_q / sdphi_k;
+                          a 0 stride sums the gradient over that axis (a factor shared by
+                          all batches or heads); NULL when R == 0 */
+  float* dphi_k;
+  int64_t sdphi_q[3], sdphi_k[3];
+  float* delta;        /* device workspace [B][H][N] fp32 (rowsum of dO * O) */
+} fb_attn_bwd_args;
+
+/*
+ * fb_attn_bwd_lowrank -- gradients of O = softmax(s Q K^T + phi_q phi_k^T) V with
+ * respect to Q, K, V and both factors, for an upstream gradient dO, without any N x N
+ * tensor: the factor gradients are the last R columns of the gradients of the
+ * augmented operands Q' = [Q*s, phi_q], K' = [K, phi_k] (the pages train with these
+ * biases: FlashBias rebuttal, answer to Reviewer UJUf, Q1, GPT-2 with Sandwich bias):
+ *   dV = P^T dO, dS = P .* (dO V^T - rowsum(dO .* O)), dQ = s dS K, dK = s dS^T Q,
+ *   dphi_q = dS phi_k, dphi_k = dS^T phi_q,    P = exp(s Q K^T + phi_q phi_k^T - LSE).
+ *
+ *   a            the forward's arguments: q, k, v, o (the forward output) and lse (the
+ *                forward's LSE output, required)
+ *   phi_*, R ... the forward's factors (R == 0: plain attention)
+ *   g            dO, the outputs and the Delta workspace (see fb_attn_bwd_args)
+ * Supported: a->dt FB_BF16 or FB_F16, D in {32, 64}, R <= 64 with R % 8 == 0 and 16-byte
+ * aligned factor rows (pad factors with zero columns).  The fused kernels recompute the
+ * scores tile by tile; Q*s is rounded to dt as in the forward (for the key-major kernel
+ * the scale is applied to K, identical when s is a power of two); P and dS are rounded to
+ * dt for their MFMA products; accumulation is fp32.  dphi_* are accumulated with fp32
+ * atomics (summation order not fixed).
+ * Errors: as the forward; FB_EINVAL for null outputs / workspace / lse, negative or
+ * misaligned strides; FB_EUNSUPPORTED outside the supported set.
+ */
+fb_status fb_attn_bwd_lowrank(const fb_attn_args* a, const void* phi_q, const void* phi_k, fb_dtype phi_dt, int R,
+                              const int64_t sphi_q[3], const int64_t sphi_k[3], const fb_attn_bwd_args* g,
+                              hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

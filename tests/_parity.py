@@ -50,6 +50,24 @@ def errors(got: np.ndarray, ref: np.ndarray):
     return float(np.abs(d).max()), float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-300))
 
 
+# Gradient tolerance (16-bit operands): relative L2 error and max-abs error relative to the
+# largest reference magnitude (gradients have no fixed scale).  Budget: the gradients are
+# stored in bf16 (rms relative rounding ~2^-9/sqrt(3) ~ 1.1e-3), P and dS are rounded to
+# bf16 before their products (~1.1e-3 each after averaging over the contraction) and
+# Delta uses the bf16 forward output: about 2e-3 rms, bounded here with a 2.5x margin;
+# the largest element may carry a few half-ulp errors (1e-2 of the largest magnitude).
+GRAD_TOL = (5e-3, 1e-2)
+
+
+def assert_grad_close(got: np.ndarray, ref: np.ndarray, what: str = ""):
+    assert np.all(np.isfinite(got)), f"{what}: non-finite gradient"
+    ma, rl = errors(got, ref)
+    scale = max(float(np.abs(ref).max()), 1e-30)
+    say(f"  {what}: rel-L2 {rl:.3e} (<= {GRAD_TOL[0]}), max-abs/max|ref| {ma / scale:.3e} (<= {GRAD_TOL[1]})")
+    assert rl <= GRAD_TOL[0] and ma / scale <= GRAD_TOL[1], f"{what}: rel-L2 {rl:.3e}, max-abs {ma:.3e}"
+    return ma, rl
+
+
 def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     ma, rl = errors(got, ref)

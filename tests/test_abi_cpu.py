@@ -171,6 +171,45 @@ def test_mulbias_workspace_size():
     assert _mul(_args(N=0, q=None, k=None, v=None, o=None), ws=None) == fb.FB_OK
 
 
+def _bwd(a, R=0, phi_dt=fb.FB_BF16, pq=FAKE, pk=FAKE, s=(0, 0, 64), **gk):
+    g = fb._BwdArgs()
+    st = (a.H * a.N * a.D, a.N * a.D, a.D)
+    g.dout, g.dq, g.dk, g.dv = gk.get("dout", FAKE), gk.get("dq", FAKE), gk.get("dk", FAKE), gk.get("dv", FAKE)
+    for n in ("sdo", "sdq", "sdk", "sdv"):
+        setattr(g, n, fb._I64x3(*gk.get(n, st)))
+    g.dphi_q, g.dphi_k = gk.get("dphi_q", FAKE), gk.get("dphi_k", FAKE)
+    g.sdphi_q = g.sdphi_k = fb._I64x3(0, 0, 64)
+    g.delta = gk.get("delta", FAKE)
+    sp = fb._I64x3(*s)
+    return fb.load().fb_attn_bwd_lowrank(ctypes.byref(a), pq, pk, phi_dt, R, ctypes.byref(sp), ctypes.byref(sp),
+                                         ctypes.byref(g), None)
+
+
+@pytest.mark.parametrize("kw,bkw,code", [
+    (dict(D=16, strides=(1024, 1024, 16), lse=FAKE), {}, fb.FB_EUNSUPPORTED),
+    (dict(D=128, strides=(8192, 8192, 128), lse=FAKE), {}, fb.FB_EUNSUPPORTED),
+    (dict(dt=fb.FB_F32, lse=FAKE), {}, fb.FB_EUNSUPPORTED),
+    (dict(lse=FAKE), dict(R=12), fb.FB_EUNSUPPORTED),           # R not a multiple of 8
+    (dict(lse=FAKE), dict(R=72), fb.FB_EUNSUPPORTED),
+    (dict(lse=FAKE), dict(R=8, phi_dt=fb.FB_F32), fb.FB_EUNSUPPORTED),
+    (dict(lse=FAKE), dict(R=8, pq=FAKE + 8), fb.FB_EUNSUPPORTED),   # factor rows not 16-byte aligned
+    (dict(lse=FAKE), dict(R=8, dphi_q=None), fb.FB_EINVAL),
+    (dict(lse=FAKE), dict(R=-1), fb.FB_EINVAL),
+    ({}, {}, fb.FB_EINVAL),                                     # no forward LSE
+    (dict(lse=FAKE), dict(dq=None), fb.FB_EINVAL),
+    (dict(lse=FAKE), dict(delta=None), fb.FB_EINVAL),
+    (dict(lse=FAKE), dict(dv=FAKE + 8), fb.FB_EINVAL),
+    (dict(lse=FAKE), dict(sdk=(4096, 64, 60)), fb.FB_EINVAL),
+])
+def test_backward_validation(kw, bkw, code):
+    assert _bwd(_args(**kw), **bkw) == code
+    assert fb.fb_last_error() != ""
+
+
+def test_backward_empty_is_noop():
+    assert _bwd(_args(N=0, q=None, k=None, v=None, o=None), dq=None, delta=None) == fb.FB_OK
+
+
 def test_make_factors_validation():
     lib = fb.load()
     r = ctypes.c_int(0)

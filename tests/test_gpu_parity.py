@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import synth
-from _parity import Case, TOL, assert_close, errors, round_exact, sample_rows, say, tdtype, to_dev, to_np
+from _parity import Case, TOL, assert_close, assert_grad_close, errors, round_exact, sample_rows, say, tdtype, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -468,3 +468,77 @@ def test_mulbias_two_stage_equals_one_call(fb):
     s = 1.0 / np.sqrt(D)
     q1 = (q.double() * pq.double()[:, 0][None, None, :, None] * s)
     np.testing.assert_allclose(to_np(e["q1"]), to_np(q1), rtol=2 ** -8, atol=0)
+
+
+# ------------------------------------------------------------------- backward ---
+def _sum_to(x: np.ndarray, shape) -> np.ndarray:
+    """Sum a [B, H, N, R] gradient over the axes a factor of ``shape`` is broadcast on."""
+    shape = tuple(shape)
+    full = (1,) * (4 - len(shape)) + shape
+    for ax in range(4):
+        if full[ax] == 1 and x.shape[ax] != 1:
+            x = x.sum(axis=ax, keepdims=True)
+    return x.reshape(shape)
+
+
+BWD = [
+    # (B, H, N, D, R, factor shape, dtype, factor dtype, causal)
+    (2, 2, 300, 64, 0, None, "bf16", "bf16", False),
+    (1, 2, 257, 64, 0, None, "bf16", "bf16", True),
+    (2, 2, 200, 64, 64, "shared", "bf16", "f16", False),
+    (1, 3, 190, 32, 16, "head", "bf16", "bf16", True),
+    (2, 2, 160, 32, 24, "full", "f16", "f16", False),
+    (1, 2, 130, 64, 8, "head", "bf16", "f16", True),
+]
+
+
+@pytest.mark.parametrize("B,H,N,D,R,fs,dt,pdt,causal", BWD, ids=[f"bwd-{i}" for i in range(len(BWD))])
+def test_backward_parity(fb, B, H, N, D, R, fs, dt, pdt, causal):
+    """dQ, dK, dV and the factor gradients against the oracle's chain rule (fp64) on the
+    same rounded inputs; the forward output and LSE come from the fused forward."""
+    import torch
+    r = np.random.default_rng(700 + N + R)
+    q, k, v, do = (synth.round_to(r.standard_normal((B, H, N, D)) * 0.5, dt) for _ in range(4))
+    shape = {"shared": (N, R), "head": (H, N, R), "full": (B, H, N, R)}.get(fs)
+    pq = pk = None
+    if R:
+        pq = synth.round_to(r.standard_normal(shape) * 0.4, pdt)
+        pk = synth.round_to(r.standard_normal(shape) * 0.4, pdt)
+    qd, kd, vd, dod = (to_dev(x, dt) for x in (q, k, v, do))
+    pqd = to_dev(pq, pdt) if R else None
+    pkd = to_dev(pk, pdt) if R else None
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda:0")
+    o = fb.fb_attn_fwd_lowrank(qd, kd, vd, pqd, pkd, causal=causal, lse=lse)
+    dq, dk, dv, gpq, gpk = fb.fb_attn_bwd_lowrank(qd, kd, vd, o, lse, dod, pqd, pkd, causal=causal)
+    torch.cuda.synchronize()
+    bias = oracle.lowrank_bias(pq, pk) if R else None
+    rq, rk, rv, db = oracle.attention_backward(q, k, v, do, bias=bias, causal=causal)
+    for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        assert_grad_close(to_np(got), ref, f"{name} R={R} D={D} {dt}")
+    if R:
+        full_q = np.broadcast_to(pq, (B, H, N, R)) if pq.ndim < 4 else pq
+        full_k = np.broadcast_to(pk, (B, H, N, R)) if pk.ndim < 4 else pk
+        rgq, rgk = oracle.lowrank_factor_grads(db, full_q, full_k)
+        assert_grad_close(gpq.cpu().double().numpy(), _sum_to(rgq, shape), f"dphi_q R={R}")
+        assert_grad_close(gpk.cpu().double().numpy(), _sum_to(rgk, shape), f"dphi_k R={R}")
+
+
+def test_backward_full_size_sampled(fb):
+    """The Sandwich workload at full size (B4 H8 N4096 D64, R = 64 f16 factors shared by all
+    (b, h)) in the benchmark's launch; every gradient element of two (b, h) pairs."""
+    import torch
+    w = synth.workload("sandwich")
+    c = Case(w)
+    r = np.random.default_rng(20260013)
+    do = synth.round_to(r.standard_normal(c.q.shape) * 0.5, "bf16")
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda:0")
+    o = c.run_lowrank(lse=lse)
+    dq, dk, dv, gpq, gpk = fb.fb_attn_bwd_lowrank(c.qd, c.kd, c.vd, o, lse, to_dev(do, "bf16"), c.phq, c.phk)
+    torch.cuda.synchronize()
+    for (b, h) in [(0, 0), (3, 7)]:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        rq, rk, rv, db = oracle.attention_backward(c.q[sl], c.k[sl], c.v[sl], do[sl],
+                                                   bias=lambda _b, _h: c.bias_ref(b, h))
+        for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+            assert_grad_close(to_np(got[b:b + 1, h:h + 1]), ref, f"full-size {name} b={b} h={h}")
+    say(f"  factor gradients (summed over all (b, h)): finite {bool(torch.isfinite(gpq).all() and torch.isfinite(gpk).all())}")
