@@ -103,6 +103,8 @@ def load():
         lib.fb_attn_bwd_lowrank.argtypes = [ctypes.POINTER(_AttnArgs), ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_int, ctypes.c_int, ctypes.POINTER(_I64x3),
                                             ctypes.POINTER(_I64x3), ctypes.POINTER(_BwdArgs), ctypes.c_void_p]
+        lib.fb_attn_fwd_alibi.restype = ctypes.c_int
+        lib.fb_attn_fwd_alibi.argtypes = [ctypes.POINTER(_AttnArgs), _DP, ctypes.c_void_p]
         lib.fb_attn_fwd_mulbias.restype = ctypes.c_int
         lib.fb_attn_fwd_mulbias.argtypes = [ctypes.POINTER(_AttnArgs), ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_int, ctypes.c_int, ctypes.POINTER(_I64x3),
@@ -453,3 +455,20 @@ def fb_attn_bwd_lowrank(q, k, v, out, lse, dout, phi_q=None, phi_k=None, *, caus
                                         _stream_ptr(q.device, stream))
     _check(st)
     return dq, dk, dv, dpq, dpk
+
+
+def fb_attn_fwd_alibi(q, k, v, slopes=None, *, causal: bool = False, scale: Optional[float] = None, out=None,
+                      lse=None, stream=None):
+    """O = softmax(scale * Q K^T + m_h (j - i)) V with the ALiBi factors formed inside the
+    kernel (no factor tensors).  ``slopes``: H host values or None for 2^(-8(h+1)/H)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    a = _attn_args(q, k, v, out, lse, causal, scale)
+    if slopes is not None and len(np.asarray(slopes).reshape(-1)) != q.shape[1]:
+        raise ValueError("one slope per head")
+    keep, sp = _slopes_ptr(slopes)
+    st = load().fb_attn_fwd_alibi(ctypes.byref(a), sp, _stream_ptr(q.device, stream))
+    del keep
+    _check(st)
+    return out

@@ -469,6 +469,29 @@ fb_status fb_attn_bwd_lowrank(const fb_attn_args* a, const void* phi_q, const vo
   return st;
 }
 
+fb_status fb_attn_fwd_alibi(const fb_attn_args* a, const double* slopes_host, hipStream_t stream) {
+  const char* fn = "fb_attn_fwd_alibi";
+  fb_status st = check_common(a, fn);
+  if (st != FB_OK) return st;
+  if (a->dt != FB_BF16 && a->dt != FB_F16) FB_FAIL(FB_EUNSUPPORTED, "%s: q/k/v must be bf16 or f16", fn);
+  if (a->H > kMaxJitHeads) FB_FAIL(FB_EUNSUPPORTED, "%s: at most %d heads", fn, kMaxJitHeads);
+  if (a->N > 65536) FB_FAIL(FB_EUNSUPPORTED, "%s: N above 65536", fn);
+  if ((int64_t)a->B * a->H * a->N == 0) return FB_OK;
+  AttnParams p = base_params(a);
+  for (int h = 0; h < a->H; ++h) {
+    const double m = slopes_host ? slopes_host[h] : std::exp2(-8.0 * (h + 1) / a->H);
+    if (!std::isfinite(m)) FB_FAIL(FB_EINVAL, "%s: non-finite slope", fn);
+    // m = m_hi + m_lo, each rounded to nearest f16
+    const _Float16 hi = (_Float16)m;
+    const _Float16 lo = (_Float16)(m - (double)hi);
+    p.alibi_m[h] = (uint32_t)__builtin_bit_cast(uint16_t, hi) | ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16);
+  }
+  p.R = 8;
+  st = dispatch_attention(2, a->dt, FB_F16, a->D, 16, p, stream);
+  if (st == FB_EUNSUPPORTED) set_error("%s: no kernel for this configuration", fn);
+  return st;
+}
+
 fb_status fb_attn_fwd_densebias(const fb_attn_args* a, const void* bias, fb_dtype bias_dt, const int64_t sbias[3],
                                 hipStream_t stream) {
   const char* fn = "fb_attn_fwd_densebias";

@@ -74,7 +74,8 @@ static fb_status lowrank_rp(int RP, const AttnParams& p, hipStream_t s) {
 #define FB_QT_NAME _f32
 #endif
 
-// mode 0: low rank (RP = padded factor width, 0 = plain attention); mode 1: dense bias.
+// mode 0: low rank (RP = padded factor width, 0 = plain attention); mode 1: dense bias;
+// mode 2: ALiBi with in-kernel factors (16-bit Q/K/V).
 fb_status FB_CAT3(launch_attention_d, FB_ATTN_D, FB_QT_NAME)(int mode, fb_dtype aux_dt, int RP,
                                                               const AttnParams& p, hipStream_t s) {
   using namespace attn;
@@ -97,6 +98,13 @@ fb_status FB_CAT3(launch_attention_d, FB_ATTN_D, FB_QT_NAME)(int mode, fb_dtype 
   if (mode == 1) {
     if (aux_dt == qdt) return launch_one<QT, QT, D, 0, 1, QT>(p, s);
     return FB_EUNSUPPORTED;
+  }
+  if (mode == 2) {
+#if FB_ATTN_QT != 2
+    return launch_kernel<QT, f16_t, D, 16, 2, QT, true>(p, s);
+#else
+    return FB_EUNSUPPORTED;
+#endif
   }
   if (RP == 0) return launch_one<QT, QT, D, 0, 0, QT>(p, s);
 #if FB_ATTN_QT == 0

@@ -61,6 +61,7 @@ typedef __bf16 bf16_t;
 typedef _Float16 f16_t;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -250,7 +251,12 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   typedef typename Elem<PT>::Frag PFrag;
   constexpr int ES = (int)sizeof(QT);
   static_assert(sizeof(PT) == sizeof(QT), "factor and query element sizes must match");
-  static_assert(MODE == 0 || RP == 0, "dense-bias mode has no factor columns");
+  static_assert(MODE != 1 || RP == 0, "dense-bias mode has no factor columns");
+  // MODE 2: ALiBi with its factor columns formed in registers from the slope and the
+  // query / key indices (the pages' in-kernel factor tiles, rebuttal answer to Reviewer
+  // BRmd, Q2), one 16-wide f16 factor k-step, nothing read from memory for them
+  constexpr bool JIT = MODE == 2;
+  static_assert(!JIT || (RP == 16 && sizeof(QT) == 2 && __is_same(PT, f16_t)), "in-kernel factors: 16-bit, RP 16");
   constexpr int KW = Elem<QT>::KW;        // k elements per lane per MFMA
   constexpr int KS = 2 * KW;              // k per MFMA
   constexpr int CE = 16 / ES;             // elements per 16-byte chunk
@@ -259,7 +265,7 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   constexpr int QSTEPS = D / KS;
   constexpr int PSTEPS = RP / KS;
   constexpr int KCH = D / CE;             // chunks per K row (and data chunks per V row)
-  constexpr int PCH = RP / CE;            // chunks per (padded) phi_k row
+  constexpr int PCH = JIT ? 0 : RP / CE;  // chunks per (padded) phi_k row in LDS
   constexpr int VCH = DP / CE;            // chunks per V row in LDS
   // A K' tile is two swizzled row-major regions, K (64 x KCH chunks) then phi_k
   // (64 x PCH chunks), a V tile one region of 64 x VCH chunks; row = key, and chunk c of
@@ -316,7 +322,7 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   QT* Op = (QT*)p.o + ((int64_t)bb * p.so[0] + (int64_t)hh * p.so[1]);
   const PT* PQp = nullptr;
   const PT* PKp = nullptr;
-  if constexpr (RP > 0) {
+  if constexpr (RP > 0 && !JIT) {
     PQp = (const PT*)p.phq + ((int64_t)bb * p.spq[0] + (int64_t)hh * p.spq[1]);
     PKp = (const PT*)p.phk + ((int64_t)bb * p.spk[0] + (int64_t)hh * p.spk[1]);
   }
@@ -502,7 +508,34 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
     if constexpr (KW == 1) qf[t] = scale_frag<QT>(Qp[qclamp * p.sq[2] + col32(t)], p.scale);
     else qf[t] = scale_frag<QT>(ld16(Qp + qclamp * p.sq[2] + KS * t + KW * hf), p.scale);
   }
-  if constexpr (RP > 0) {
+  // In-kernel ALiBi factors: with the slope m = m_hi + m_lo (two f16) and an index
+  // x = x_hi + x_lo (x_hi a multiple of 2048, both exact in f16),
+  //   phi_q(i) = [m_hi, m_hi, m_lo, m_lo, -i_hi, -i_lo, -i_hi, -i_lo, 0 ...],
+  //   phi_k(j) = [j_hi, j_lo, j_hi, j_lo,  m_hi,  m_hi,  m_lo,  m_lo, 0 ...]:
+  // every product is exact in fp32 and their sum is m (j - i) to the 22 bits of m.
+  // Lane half 1 holds k = 8..15: zeros.
+  f16_t jm_hi = (f16_t)0.f, jm_lo = (f16_t)0.f;
+  if constexpr (JIT) {
+    const uint32_t mb = p.alibi_m[hh];
+    jm_hi = __builtin_bit_cast(f16_t, (uint16_t)(mb & 0xffffu));
+    jm_lo = __builtin_bit_cast(f16_t, (uint16_t)(mb >> 16));
+  }
+  auto jit_pair = [&](int x) __attribute__((always_inline)) {
+    f16x2 r = {(f16_t)(float)(x & ~2047), (f16_t)(float)(x & 2047)};
+    return r;
+  };
+  auto jit_phk = [&](int j) __attribute__((always_inline)) {
+    const f16x2 jx = jit_pair(j);
+    const f16x8 v = {jx[0], jx[1], jx[0], jx[1], jm_hi, jm_hi, jm_lo, jm_lo};
+    const u32x4 r = __builtin_bit_cast(u32x4, v);
+    return hf ? u32x4{0u, 0u, 0u, 0u} : r;
+  };
+  if constexpr (JIT) {
+    const f16x2 ix = jit_pair(qclamp);
+    const f16x8 v = {jm_hi, jm_hi, jm_lo, jm_lo, (f16_t)(-(float)ix[0]), (f16_t)(-(float)ix[1]),
+                     (f16_t)(-(float)ix[0]), (f16_t)(-(float)ix[1])};
+    pf[0] = hf ? u32x4{0u, 0u, 0u, 0u} : __builtin_bit_cast(u32x4, v);
+  } else if constexpr (RP > 0) {
     const PT* prow = PQp + qclamp * p.spq[2];
 #pragma unroll
     for (int t = 0; t < PSTEPS; ++t) {
@@ -578,7 +611,7 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   // zero: row 0 of lacc (register 0 of the lanes of half 0) is then sum_k P[k][query], and
   // the rescaling of O scales it too.  This takes 32 adds per tile off the vector unit.
   // (Dense-bias mode keeps the adds: its bias registers leave no room for lacc.)
-  constexpr bool MROW = KW > 1 && MODE == 0;
+  constexpr bool MROW = KW > 1 && MODE != 1;
   f32x16 lacc = f32x16{};
   const uint32_t one2 = __is_same(QT, bf16_t) ? 0x3F803F80u : 0x3C003C00u;   // two 1.0 values of QT
   const u32x4 ones = ln == 0 ? u32x4{one2, one2, one2, one2} : u32x4{0u, 0u, 0u, 0u};
@@ -660,8 +693,14 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
     vf[j] = r * VCH * 16 + 16 * ((ln >> 2) ^ swz_quad(VCH, r)) + 4 * (ln & 3);
   }
 
-  // S^T = K'(t) Q'^T from the K' tile at sKt
-  auto qk = [&](const unsigned char* sKt) __attribute__((always_inline)) {
+  // factor-chain A operand of k-step t, key block kb2, of the tile whose first key is kbt
+  auto phik = [&](const unsigned char* sKt, int kbt, int t, int kb2) __attribute__((always_inline)) {
+    if constexpr (JIT) return jit_phk(kbt + 32 * kb2 + inv_perm_row(ln));
+    else return kread(sKt, true, t, kb2);
+  };
+
+  // S^T = K'(t) Q'^T from the K' tile at sKt (first key kbt)
+  auto qk = [&](const unsigned char* sKt, int kbt) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb2 = 0; kb2 < NKB; ++kb2) sacc[kb2] = f32x16{};
     if constexpr (KW == 1) {
@@ -689,7 +728,7 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
 #pragma unroll
       for (int t = 0; t < PSTEPS; ++t)
 #pragma unroll
-        for (int kb2 = 0; kb2 < NKB; ++kb2) sacc[kb2] = Mma<PT>::run(kread(sKt, true, t, kb2), pf[t], sacc[kb2]);
+        for (int kb2 = 0; kb2 < NKB; ++kb2) sacc[kb2] = Mma<PT>::run(phik(sKt, kbt, t, kb2), pf[t], sacc[kb2]);
     }
   };
 
@@ -724,7 +763,7 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   // S(t+1) = K'(t+1) Q'^T.  Operands are read two MFMA groups ahead of their use
   // (group = the MFMAs of one k-step), so the LDS latency hides behind the matrix
   // core instead of stalling it; the scheduling-group pins below keep that order.
-  auto mma_phase = [&](const unsigned char* sKn, const unsigned char* sVt) __attribute__((always_inline)) {
+  auto mma_phase = [&](const unsigned char* sKn, int kbn, const unsigned char* sVt) __attribute__((always_inline)) {
     if constexpr (KW > 1) {
       constexpr int NPV = NKB * 2;              // P V groups (kb2, u): 2 DB reads, DB (+1) MFMAs
       constexpr int NQK = QSTEPS + PSTEPS;      // score groups: NKB reads + NKB MFMAs
@@ -738,7 +777,7 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
           const int t = g - NPV;
 #pragma unroll
           for (int kb2 = 0; kb2 < NKB; ++kb2)
-            opnd[g][kb2] = t < QSTEPS ? kread(sKn, false, t, kb2) : kread(sKn, true, t - QSTEPS, kb2);
+            opnd[g][kb2] = t < QSTEPS ? kread(sKn, false, t, kb2) : phik(sKn, kbn, t - QSTEPS, kb2);
         }
       };
 #pragma unroll
@@ -854,7 +893,7 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   }
   load_bias(0);
   __syncthreads();
-  qk(sK0);
+  qk(sK0, 0);
   softmax(0);
   __syncthreads();
 
@@ -879,9 +918,9 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
     const int kb = t * BN;
     if constexpr (!CAUSAL && KW > 1) {
       // past the last tile the scores of a stale buffer are computed and never used
-      mma_phase(kn, vt);
+      mma_phase(kn, kb + BN, vt);
     } else {
-      if (t + 1 < nkt && active(t + 1)) qk(kn);
+      if (t + 1 < nkt && active(t + 1)) qk(kn, kb + BN);
       if (active(t)) pv(vt);
     }
     __builtin_amdgcn_s_barrier();

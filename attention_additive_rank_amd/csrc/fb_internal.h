@@ -28,7 +28,11 @@ struct AttnParams {
   int B, H, N;
   float scale;
   int nqb;                // number of query blocks per (b, h)
+  // in-kernel ALiBi factors (mode 2): slope of head h as two f16 values, bits
+  // m_hi | m_lo << 16 with m_hi + m_lo = m_h to 22 bits
+  uint32_t alibi_m[128];
 };
+constexpr int kMaxJitHeads = 128;
 constexpr int kAttnBlockM = 256;   // query rows per attention workgroup
 constexpr int kAttnKeyTile = 64;   // keys per LDS tile of the attention kernels
 constexpr int FLAG_CAUSAL = 1;
@@ -38,7 +42,8 @@ constexpr int FLAG_BIAS_VEC = 8;  // bias rows 16-byte aligned -> vector loads
 
 // Launch one fused attention forward; one function per head dim (16/32/64/128) and Q/K/V
 // element type.  mode 0: low-rank factors padded to RP columns (0 = plain attention);
-// mode 1: dense bias (RP = 0).  aux_dt is the factor or bias dtype.  FB_EUNSUPPORTED when
+// mode 1: dense bias (RP = 0); mode 2: ALiBi factors formed in the kernel (16-bit only).
+// aux_dt is the factor or bias dtype.  FB_EUNSUPPORTED when
 // no kernel instance matches.
 fb_status launch_attention_d16_bf16(int mode, fb_dtype aux_dt, int RP, const AttnParams& p, hipStream_t s);
 fb_status launch_attention_d16_f16(int mode, fb_dtype aux_dt, int RP, const AttnParams& p, hipStream_t s);

@@ -108,6 +108,8 @@ def main():
     ap.add_argument("--workload", default="sandwich", choices=["sandwich", "gpt2_alibi_causal", "mulbias_cos"])
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of CPU oracle work (0 = skip)")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-bias baseline")
+    ap.add_argument("--alibi-jit", action="store_true",
+                    help="ALiBi workloads: factors formed inside the kernel (fb_attn_fwd_alibi), no factor step")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (fb_attn_bwd_lowrank) of the workload instead")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -156,8 +158,14 @@ def main():
         pk = torch.empty_like(pq)
     stream = torch.cuda.current_stream(dev)
 
+    jit = args.alibi_jit
+    if jit and w.bias != "alibi":
+        raise SystemExit("--alibi-jit needs an ALiBi workload")
+
     def stage1():
         """factor generation (additive) or operand expansion (multiplicative)"""
+        if jit:
+            return None
         if mul:
             return fb.fb_mulbias_expand(q, k, phi, phi, workspace=ws)
         fb.fb_make_factors(w.bias, fH, w.N, C=fC, dtype=phi_dt, split=split, phi_q=pq, phi_k=pk)
@@ -165,7 +173,9 @@ def main():
 
     def stage2(e):
         """the fused attention kernel"""
-        if mul:
+        if jit:
+            fb.fb_attn_fwd_alibi(q, k, v, causal=w.causal, out=out)
+        elif mul:
             fb.fb_attn_fwd_lowrank(e["q1"], e["k1"], v, e["phi_q"], e["phi_k"], causal=w.causal, scale=1.0, out=out)
         else:
             fb.fb_attn_fwd_lowrank(q, k, v, pq, pk, causal=w.causal, out=out)
@@ -263,7 +273,8 @@ def main():
                    "factor_dtype": "f16" if phi_dt == torch.float16 else "f32", "factor_split": split,
                    "factor_columns": R_used, "factor_columns_padded": R_cols,
                    "flops_per_step": F,
-                   **({"bias_op": "multiplicative", "expanded_width": w.D * w.R} if mul else {})},
+                   **({"bias_op": "multiplicative", "expanded_width": w.D * w.R} if mul else {}),
+                   **({"factors": "in-kernel (fb_attn_fwd_alibi)"} if jit else {})},
         "pct_mfma_peak": round(100.0 * value / peak, 2),
         "kernel_ms": round(kern_ms, 4),
         "kernel_tflops": round(kern_tflops, 2),

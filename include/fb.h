@@ -282,6 +282,24 @@ fb_status fb_mulbias_expand(const fb_attn_args* a, const void* phi_q, const void
                             const int64_t sphi_q[3], const int64_t sphi_k[3], void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * fb_attn_fwd_alibi -- O = softmax(s Q K^T + b) V for the ALiBi bias
+ * b[h,i,j] = m_h (j - i) with its rank-2 factors formed inside the kernel from the
+ * slopes and the query / key indices, as the pages deploy ALiBi (FlashBias rebuttal,
+ * answer to Reviewer BRmd, Q2: only the #heads slopes are loaded, the Block_q x 2 and
+ * Block_k x 2 factor tiles are generated in the kernel).  No factor tensor exists: per
+ * tile the kernel builds f16 factor columns whose products sum exactly (in fp32) to
+ * m_h (j - i), with m_h held as two f16 values (22 bits) and i, j split at 2048.
+ *
+ *   a            shared arguments; a->dt FB_BF16 or FB_F16
+ *   slopes_host  host [H] fp64 slopes, or NULL for m_h = 2^(-8(h+1)/H)
+ * Limits: H <= 128 (the slopes travel in the kernel arguments), N <= 65536.
+ * Numerics: as fb_attn_fwd_lowrank with an f16 factor chain.
+ * Errors: as fb_attn_fwd_lowrank; FB_EUNSUPPORTED for fp32, H > 128 or N > 65536;
+ * FB_EINVAL for a non-finite slope.
+ */
+fb_status fb_attn_fwd_alibi(const fb_attn_args* a, const double* slopes_host, hipStream_t stream);
+
 /* Outputs and workspace of the attention backward. */
 typedef struct {
   const void* dout;    /* device [B][H][N][D], strides sdo: the upstream gradient dO (a->dt) */

@@ -210,6 +210,20 @@ def test_backward_empty_is_noop():
     assert _bwd(_args(N=0, q=None, k=None, v=None, o=None), dq=None, delta=None) == fb.FB_OK
 
 
+def test_alibi_in_kernel_validation():
+    lib = fb.load()
+    sl = (ctypes.c_double * 200)(*([0.5] * 200))
+    assert lib.fb_attn_fwd_alibi(ctypes.byref(_args(dt=fb.FB_F32)), sl, None) == fb.FB_EUNSUPPORTED
+    assert lib.fb_attn_fwd_alibi(ctypes.byref(_args(H=129, strides=(129 * 64 * 64, 4096, 64))), sl,
+                                 None) == fb.FB_EUNSUPPORTED
+    assert lib.fb_attn_fwd_alibi(ctypes.byref(_args(N=70000, strides=(70000 * 64, 70000 * 64, 64))), sl,
+                                 None) == fb.FB_EUNSUPPORTED
+    bad = (ctypes.c_double * 1)(float("nan"))
+    assert lib.fb_attn_fwd_alibi(ctypes.byref(_args()), bad, None) == fb.FB_EINVAL
+    assert lib.fb_attn_fwd_alibi(ctypes.byref(_args(D=48)), None, None) == fb.FB_EUNSUPPORTED
+    assert lib.fb_attn_fwd_alibi(ctypes.byref(_args(N=0, q=None, k=None, v=None, o=None)), None, None) == fb.FB_OK
+
+
 def test_make_factors_validation():
     lib = fb.load()
     r = ctypes.c_int(0)

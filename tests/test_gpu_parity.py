@@ -542,3 +542,50 @@ def test_backward_full_size_sampled(fb):
         for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
             assert_grad_close(to_np(got[b:b + 1, h:h + 1]), ref, f"full-size {name} b={b} h={h}")
     say(f"  factor gradients (summed over all (b, h)): finite {bool(torch.isfinite(gpq).all() and torch.isfinite(gpk).all())}")
+
+
+# ------------------------------------------------------- in-kernel ALiBi factors ---
+JIT = [
+    (dict(B=2, H=4, N=300, D=64), "bf16", False, None),
+    (dict(B=1, H=3, N=257, D=32), "bf16", True, None),
+    (dict(B=1, H=2, N=4500, D=64), "bf16", True, None),       # indices past 2048: split hi / lo
+    (dict(B=1, H=2, N=200, D=16), "f16", False, None),
+    (dict(B=1, H=2, N=190, D=128), "bf16", True, None),
+    (dict(B=1, H=3, N=150, D=64), "bf16", False, [0.5, 0.1234567, 1.7]),   # slopes that f16 cannot hold
+]
+
+
+@pytest.mark.parametrize("shape,dt,causal,slopes", JIT, ids=[f"jit-{i}" for i in range(len(JIT))])
+def test_alibi_in_kernel_factors(fb, shape, dt, causal, slopes):
+    """ALiBi with the factors formed in the kernel against the oracle's closed-form bias."""
+    import torch
+    B, H, N, D = shape["B"], shape["H"], shape["N"], shape["D"]
+    r = np.random.default_rng(800 + N + D)
+    q, k, v = (synth.round_to(r.standard_normal((B, H, N, D)) * 0.5, dt) for _ in range(3))
+    m = oracle.alibi_slopes(H) if slopes is None else np.asarray(slopes, dtype=np.float64)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda:0")
+    o = fb.fb_attn_fwd_alibi(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), slopes=slopes, causal=causal, lse=lse)
+    torch.cuda.synchronize()
+    rows = None if N <= 600 else sample_rows(N, 64, seed=4)
+    ro, rl = oracle.attention(q, k, v, bias=oracle.alibi_bias(m, N), causal=causal, rows=rows)
+    got = to_np(o) if rows is None else to_np(o)[:, :, rows]
+    assert_close(got, ro, dt, f"in-kernel ALiBi N={N} D={D}")
+    gl = lse.cpu().double().numpy()
+    np.testing.assert_allclose(gl if rows is None else gl[:, :, rows], rl, rtol=0, atol=2e-2)
+
+
+def test_alibi_in_kernel_full_size_sampled(fb):
+    """The GPT-2 ALiBi causal workload (B8 H12 N2048 D64) with in-kernel factors, in the
+    bench's launch; sampled rows of sampled (b, h)."""
+    import torch
+    w = synth.workload("gpt2_alibi_causal")
+    inp = synth.make_inputs(w)
+    o = fb.fb_attn_fwd_alibi(to_dev(inp["q"], "bf16"), to_dev(inp["k"], "bf16"), to_dev(inp["v"], "bf16"),
+                             causal=True)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.N, 48, seed=5)
+    m = oracle.alibi_slopes(w.H)
+    for (b, h) in [(0, 0), (3, 6), (7, 11)]:
+        ro, _ = oracle.attention(inp["q"][b:b + 1, h:h + 1], inp["k"][b:b + 1, h:h + 1], inp["v"][b:b + 1, h:h + 1],
+                                 bias=oracle.alibi_bias(m[h:h + 1], w.N), causal=True, rows=rows)
+        assert_close(to_np(o[b, h])[rows][None, None], ro, "bf16", f"in-kernel ALiBi b={b} h={h}")
