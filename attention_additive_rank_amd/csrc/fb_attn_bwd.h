@@ -40,7 +40,7 @@ static_assert(32 * BW == kBwdRows, "backward block size");
 // (FCH chunks, the factor columns, at least four chunks so that a 32-column transposed
 // read stays inside the row; columns at or beyond R hold finite stand-ins), region Y (KCH
 // chunks: dO or V), and for the key-major kernel 512 bytes of L and Delta of the tile's
-// queries.  Rows are stored in order; chunk c of row r sits at c ^ swz_key(cpr, r).
+// queries.  Rows are stored in order; chunk c of row r sits at c ^ swzb(cpr, r).
 template <int D, int RP, bool LD>
 struct Tile {
   static constexpr int KCH = D / 8;
@@ -54,29 +54,51 @@ struct Tile {
   static constexpr int NLOAD = NX + NF + NY;
 };
 
+// Chunk swizzle of the backward tiles, read both as rows (the score / dP A operands: the
+// 16 lanes of a 128-bit pass read rows inv_perm_row(0..15) at one chunk) and transposed
+// (64-bit transpose reads: a 32-lane pass reads four consecutive rows at four adjacent
+// chunks).  It uses only row bits 1, 2 and 4, which makes both patterns conflict-free
+// (distinct (row * cpr + position) mod 16 bank groups per pass) and keeps every read
+// address a per-lane base plus an immediate: 8u and 32 rb change bits 3 and 5 only.
+__host__ __device__ constexpr int swzb(int cpr, int r) {
+  return cpr == 8 ? (4 * ((r >> 1) & 1) | 2 * ((r >> 2) & 1) | ((r >> 4) & 1))
+       : cpr == 4 ? (2 * ((r >> 4) & 1) | ((r >> 2) & 1)) : 0;
+}
+
 // Byte offset of 16-bit element group (row, chunk c) in a region of cpr chunks per row.
-__device__ __forceinline__ int toff(int cpr, int row, int c) { return row * cpr * 16 + 16 * (c ^ swz_key(cpr, row)); }
+__device__ __forceinline__ int toff(int cpr, int row, int c) { return row * cpr * 16 + 16 * (c ^ swzb(cpr, row)); }
 
-// A operand from rows of a region (32-row block rb, k-step t): lane (ln, hf) reads row
-// 32 rb + inv_perm_row(ln), chunk 2 t + hf.
-__device__ __forceinline__ u32x4 rowA(const unsigned char* reg, int cpr, int rb, int t, int ln, int hf) {
-  return ld16(reg + toff(cpr, 32 * rb + inv_perm_row(ln), 2 * t + hf));
-}
-
-// Transposed A operand of a region (rows are the contraction index): m-block mb (32
-// columns), 32-row block rb, k-step u.  Lane 4 jj + a of 16-lane group g (g = lane / 16)
-// reads 4 columns 32 mb + 16 (g & 1) + 4 a .. + 3 of rows 32 rb + 16 hf + 8 u + 4 q + jj
-// (q = 0, 1); after the transpose, lane (ln, hf) holds column 32 mb + ln of rows
-// 32 rb + 16 hf + 8 u + 0..7.
-__device__ __forceinline__ u32x4 trA(const unsigned char* reg, int cpr, int rb, int u, int mb, int lane) {
-  const int a = lane & 3, jj = (lane >> 2) & 3, gg = (lane >> 4) & 1, hf = lane >> 5;
-  const int c = 4 * mb + 2 * gg + (a >> 1);
-  const int r0 = 32 * rb + 16 * hf + 8 * u + jj;
-  const s16x4 lo = lds_read_tr16(reg + toff(cpr, r0, c) + 8 * (a & 1));
-  const s16x4 hi = lds_read_tr16(reg + toff(cpr, r0 + 4, c) + 8 * (a & 1));
-  const s16x4 v[2] = {lo, hi};
-  return __builtin_bit_cast(u32x4, v);
-}
+// Per-lane read addresses of one region (cpr chunks per row):
+//  row operand of k-step t (t < cpr / 2): row inv_perm_row(ln) (+ 32 rb), chunk 2 t + hf;
+//  transposed operand of m-block mb, half q: lane 4 jj + a of 16-lane group g reads
+//    columns 32 mb + 16 (g & 1) + 4 a .. + 3 of row 16 hf + 4 q + jj (+ 8 u + 32 rb); after
+//    the two reads (q = 0, 1) lane (ln, hf) holds column 32 mb + ln of rows
+//    32 rb + 16 hf + 8 u + 0..7 (k-slot j = row 16 hf + 8 u + j).
+template <int CPR>
+struct RegionAddr {
+  static constexpr int NT = CPR / 2 > 0 ? CPR / 2 : 1, NM = CPR / 4 > 0 ? CPR / 4 : 1;
+  int row[NT];
+  int tr[2][NM];
+  __device__ __forceinline__ void init(int lane) {
+    const int ln = lane & 31, hf = lane >> 5;
+    const int a = lane & 3, jj = (lane >> 2) & 3, gg = (lane >> 4) & 1;
+    const int pr = inv_perm_row(ln);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) row[t] = toff(CPR, pr, 2 * t + hf);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int mb = 0; mb < NM; ++mb) tr[q][mb] = toff(CPR, 16 * hf + 4 * q + jj, 4 * mb + 2 * gg + (a >> 1)) + 8 * (a & 1);
+  }
+  __device__ __forceinline__ u32x4 rowA(const unsigned char* reg, int rb, int t) const {
+    return ld16(reg + row[t] + 32 * rb * CPR * 16);
+  }
+  __device__ __forceinline__ u32x4 trA(const unsigned char* reg, int rb, int u, int mb) const {
+    const unsigned char* b = reg + (32 * rb + 8 * u) * CPR * 16;
+    const s16x4 v[2] = {lds_read_tr16(b + tr[0][mb]), lds_read_tr16(b + tr[1][mb])};
+    return __builtin_bit_cast(u32x4, v);
+  }
+};
 
 // Eight fp32 values rounded (RNE) into one 16-byte B operand of type T.
 template <typename T>
@@ -106,7 +128,7 @@ __device__ __forceinline__ void load_tile(unsigned char* dst, int r0, int N, int
         else if (n < T::NX + T::NF) { region = 1; nr = n - T::NX; cpr = T::FCH; }
         else { region = 2; nr = n - T::NX - T::NF; cpr = T::KCH; }
         const int row = nr * (64 / cpr) + lane / cpr;
-        int c = (lane % cpr) ^ swz_key(cpr, row);
+        int c = (lane % cpr) ^ swzb(cpr, row);
         const int srow = min(r0 + row, N - 1) - r0;
         if (region == 1 && c >= npch) c = 0;
         const char* base = region == 0 ? xb : region == 1 ? fb : yb;
@@ -135,6 +157,11 @@ __global__ __launch_bounds__(BTH, 2) void attn_bwd_dkv_kernel(BwdParams p) {
   const int bh = blockIdx.x / p.nblk;
   const int hh = bh % p.H, bb = bh / p.H, N = p.N;
   const int kw0 = blk * kBwdRows + wave * 32;          // this wavefront's first key
+  RegionAddr<T::KCH> ax, ay;
+  RegionAddr<(T::FCH > 0 ? T::FCH : 4)> af;
+  ax.init(lane);
+  ay.init(lane);
+  af.init(lane);
   const int key = kw0 + ln;
   const int keyc = min(key, N - 1);
 
@@ -198,13 +225,13 @@ __global__ __launch_bounds__(BTH, 2) void attn_bwd_dkv_kernel(BwdParams p) {
       if (qb0 >= N) continue;
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int t = 0; t < QST; ++t) s = Mma<QT>::run(rowA(tl + T::XOFF, T::KCH, qb, t, ln, hf), kf[t], s);
+      for (int t = 0; t < QST; ++t) s = Mma<QT>::run(ax.rowA(tl + T::XOFF, qb, t), kf[t], s);
       if constexpr (RP > 0) {
 #pragma unroll
-        for (int t = 0; t < PST; ++t) s = Mma<PT>::run(rowA(tl + T::FOFF, T::FCH, qb, t, ln, hf), pkf[t], s);
+        for (int t = 0; t < PST; ++t) s = Mma<PT>::run(af.rowA(tl + T::FOFF, qb, t), pkf[t], s);
       }
 #pragma unroll
-      for (int t = 0; t < QST; ++t) dp = Mma<QT>::run(rowA(tl + T::YOFF, T::KCH, qb, t, ln, hf), vf[t], dp);
+      for (int t = 0; t < QST; ++t) dp = Mma<QT>::run(ay.rowA(tl + T::YOFF, qb, t), vf[t], dp);
       // register i holds query qb0 + 16 hf + i
       const f32x4* lq = (const f32x4*)(tl + T::LOFF + 4 * (32 * qb + 16 * hf));
       const f32x4* dq = (const f32x4*)(tl + T::LOFF + 256 + 4 * (32 * qb + 16 * hf));
@@ -227,14 +254,14 @@ __global__ __launch_bounds__(BTH, 2) void attn_bwd_dkv_kernel(BwdParams p) {
         const u32x4 pb = pack8<QT>(pv + 8 * u);
         const u32x4 dsb = pack8<QT>(dsv + 8 * u);
 #pragma unroll
-        for (int mb = 0; mb < MBQ; ++mb) dvT[mb] = Mma<QT>::run(trA(tl + T::YOFF, T::KCH, qb, u, mb, lane), pb, dvT[mb]);
+        for (int mb = 0; mb < MBQ; ++mb) dvT[mb] = Mma<QT>::run(ay.trA(tl + T::YOFF, qb, u, mb), pb, dvT[mb]);
 #pragma unroll
-        for (int mb = 0; mb < MBQ; ++mb) dkT[mb] = Mma<QT>::run(trA(tl + T::XOFF, T::KCH, qb, u, mb, lane), dsb, dkT[mb]);
+        for (int mb = 0; mb < MBQ; ++mb) dkT[mb] = Mma<QT>::run(ax.trA(tl + T::XOFF, qb, u, mb), dsb, dkT[mb]);
         if constexpr (RP > 0) {
           const u32x4 dsp = pack8<PT>(dsv + 8 * u);
 #pragma unroll
           for (int mb = 0; mb < MBP; ++mb)
-            dkT[MBQ + mb] = Mma<PT>::run(trA(tl + T::FOFF, T::FCH, qb, u, mb, lane), dsp, dkT[MBQ + mb]);
+            dkT[MBQ + mb] = Mma<PT>::run(af.trA(tl + T::FOFF, qb, u, mb), dsp, dkT[MBQ + mb]);
         }
       }
     }
@@ -307,6 +334,11 @@ __global__ __launch_bounds__(BTH, 2) void attn_bwd_dq_kernel(BwdParams p) {
   const int hh = bh % p.H, bb = bh / p.H, N = p.N;
   const int qw0 = blk * kBwdRows + wave * 32;
   const int qrow = qw0 + ln;
+  RegionAddr<T::KCH> ax, ay;
+  RegionAddr<(T::FCH > 0 ? T::FCH : 4)> af;
+  ax.init(lane);
+  ay.init(lane);
+  af.init(lane);
   const int qc = min(qrow, N - 1);
 
   const QT* Qp = (const QT*)p.q + ((int64_t)bb * p.sq[0] + (int64_t)hh * p.sq[1]);
@@ -357,13 +389,13 @@ __global__ __launch_bounds__(BTH, 2) void attn_bwd_dq_kernel(BwdParams p) {
       if (kb0 >= N) continue;
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int t = 0; t < QST; ++t) s = Mma<QT>::run(rowA(tl + T::XOFF, T::KCH, kb, t, ln, hf), qf[t], s);
+      for (int t = 0; t < QST; ++t) s = Mma<QT>::run(ax.rowA(tl + T::XOFF, kb, t), qf[t], s);
       if constexpr (RP > 0) {
 #pragma unroll
-        for (int t = 0; t < PST; ++t) s = Mma<PT>::run(rowA(tl + T::FOFF, T::FCH, kb, t, ln, hf), pqf[t], s);
+        for (int t = 0; t < PST; ++t) s = Mma<PT>::run(af.rowA(tl + T::FOFF, kb, t), pqf[t], s);
       }
 #pragma unroll
-      for (int t = 0; t < QST; ++t) dp = Mma<QT>::run(rowA(tl + T::YOFF, T::KCH, kb, t, ln, hf), of[t], dp);
+      for (int t = 0; t < QST; ++t) dp = Mma<QT>::run(ay.rowA(tl + T::YOFF, kb, t), of[t], dp);
       float dsv[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -376,12 +408,12 @@ __global__ __launch_bounds__(BTH, 2) void attn_bwd_dq_kernel(BwdParams p) {
       for (int u = 0; u < 2; ++u) {
         const u32x4 dsb = pack8<QT>(dsv + 8 * u);
 #pragma unroll
-        for (int mb = 0; mb < MBQ; ++mb) dqT[mb] = Mma<QT>::run(trA(tl + T::XOFF, T::KCH, kb, u, mb, lane), dsb, dqT[mb]);
+        for (int mb = 0; mb < MBQ; ++mb) dqT[mb] = Mma<QT>::run(ax.trA(tl + T::XOFF, kb, u, mb), dsb, dqT[mb]);
         if constexpr (RP > 0) {
           const u32x4 dsp = pack8<PT>(dsv + 8 * u);
 #pragma unroll
           for (int mb = 0; mb < MBP; ++mb)
-            dqT[MBQ + mb] = Mma<PT>::run(trA(tl + T::FOFF, T::FCH, kb, u, mb, lane), dsp, dqT[MBQ + mb]);
+            dqT[MBQ + mb] = Mma<PT>::run(af.trA(tl + T::FOFF, kb, u, mb), dsp, dqT[MBQ + mb]);
         }
       }
     }
