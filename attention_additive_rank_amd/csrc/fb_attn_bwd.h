@@ -110,34 +110,112 @@ __device__ __forceinline__ u32x4 pack8(const float* x) {
   return __builtin_bit_cast(u32x4, r);
 }
 
-// Issue the direct loads of one tile (rows r0 .. r0 + 63 of the three sources) into dst.
-// Load n of the tile: regions X, F, Y in turn (1 KB = 64 chunk slots each).  Wavefront w
-// issues loads w, w + 4, ...  A chunk that is not wanted (a row past N, a factor column at
-// or beyond R) copies a finite stand-in: the last row, or the row's first chunk.
+// Software pipelining of the backward blocks: the blocks are written as explicit
+// instruction sequences (operand reads a fixed distance ahead of their MFMA, direct loads
+// of a later tile one per MFMA), and a full scheduling fence after every step keeps the
+// compiler from regrouping them.
+constexpr int PD_ROW = 3;   // 128-bit operand reads in flight ahead of the score / dP MFMAs
+constexpr int PD_TR = 2;    // gradient MFMAs whose transposed reads are in flight ahead
+__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Workgroup order: dispatch is round-robin over the 8 XCDs, so hardware id x runs on XCD
+// x % 8; the logical id gives each XCD a contiguous range, which puts the blocks of one
+// (b, h) on one XCD, where they share the streamed tiles in its L2.
+__device__ __forceinline__ int xcd_order(int x, int G) {
+  const int xcd = x & 7, idx = x >> 3, per = G >> 3, rem = G & 7;
+  return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+}
+
+// v[i] = w of lane i of the caller's 16-lane row (DPP row broadcast), i = 0..15
+template <int I = 0>
+__device__ __forceinline__ void row_bcast16(f32x16& v, float w) {
+  if constexpr (I < 16) {
+    v[I] = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, w), 0x150 + I, 0xF, 0xF,
+                                                                 false));
+    row_bcast16<I + 1>(v, w);
+  }
+}
+
+// Direct global -> LDS loads of the backward tiles, written as inline asm: the compiler's
+// own wait bookkeeping, which cannot tell the three tile buffers apart, would otherwise
+// wait for every outstanding copy (vmcnt 0) and for every LDS read (lgkmcnt 0) before the
+// next LDS read, serialising the prefetch.  Their completion is waited for explicitly
+// (vmcnt) before the barrier that publishes a tile; the "memory" clobber keeps LDS
+// accesses on their side of the asm.  lds: LDS byte address of lane 0's destination
+// (the low half of a generic LDS pointer); lane l writes lds + 16 l (or 4 l).  The 16-byte
+// form takes a scalar base and a 32-bit per-lane offset.  M0 carries
+// the LDS address and is used by no compiler-generated instruction in these kernels.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+__device__ __forceinline__ void dma16_async(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(off), "s"(base), "s"(lds)
+               : "memory");
+}
+__device__ __forceinline__ void dma4_async(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" :: "v"(src), "s"(lds) : "memory");
+}
+
+// This wavefront's share of the direct loads of a tile: slot i copies load n = wave + BW i
+// (regions X, F, Y in turn, 1 KB = 64 chunk slots each; every region is a multiple of BW
+// loads, so slot i's region is a compile-time constant).  off[i] is the lane's source
+// offset from the tile's first row (row * row stride + swizzled chunk; a factor chunk at
+// or past R copies the row's first chunk).  Per tile, Bases holds each region's first-row
+// address (scalar) and a clamp: rows past N read the last row's last chunk (finite
+// stand-ins, masked by the caller), at the cost of one min per load.
 template <int D, int RP, bool LD>
-__device__ __forceinline__ void load_tile(unsigned char* dst, int r0, int N, int wave, int lane, const char* xb,
-                                          int xs, const char* fb, int fs, int npch, const char* yb, int ys) {
+struct DmaPlan {
   typedef Tile<D, RP, LD> T;
+  static_assert(T::NX % BW == 0 && T::NF % BW == 0 && T::NY % BW == 0, "loads per region");
+  static constexpr int NI = T::NLOAD / BW;
+  static constexpr int region(int i) { return BW * i < T::NX ? 0 : BW * i < T::NX + T::NF ? 1 : 2; }
+  static constexpr int first(int r) { return r == 0 ? 0 : r == 1 ? T::NX : T::NX + T::NF; }
+  static constexpr int cpr(int r) { return r == 1 ? T::FCH : T::KCH; }
+  static constexpr int doff(int r) { return r == 0 ? T::XOFF : r == 1 ? T::FOFF : T::YOFF; }
+  uint32_t off[NI];
+  const char* src[3];
+  int stride2[3];                 // row strides in bytes
+  int cmax[3];                    // last chunk a row may read
+  struct Bases { const char* b[3]; uint32_t lim[3]; };
+  __device__ __forceinline__ void init(int wave, int lane, const char* xb, int xs, const char* fb, int fs, int npch,
+                                       const char* yb, int ys) {
+    src[0] = xb; src[1] = fb; src[2] = yb;
+    stride2[0] = 2 * xs; stride2[1] = 2 * fs; stride2[2] = 2 * ys;
+    cmax[0] = T::KCH - 1; cmax[1] = npch - 1; cmax[2] = T::KCH - 1;
 #pragma unroll
-  for (int i = 0; i < (T::NLOAD + BW - 1) / BW; ++i) {
-    const int n = wave + BW * i;
-    if (n < T::NLOAD) {
-      {
-        int region, nr, cpr;
-        if (n < T::NX) { region = 0; nr = n; cpr = T::KCH; }
-        else if (n < T::NX + T::NF) { region = 1; nr = n - T::NX; cpr = T::FCH; }
-        else { region = 2; nr = n - T::NX - T::NF; cpr = T::KCH; }
-        const int row = nr * (64 / cpr) + lane / cpr;
-        int c = (lane % cpr) ^ swzb(cpr, row);
-        const int srow = min(r0 + row, N - 1) - r0;
-        if (region == 1 && c >= npch) c = 0;
-        const char* base = region == 0 ? xb : region == 1 ? fb : yb;
-        const int stride = region == 0 ? xs : region == 1 ? fs : ys;
-        const int off = region == 0 ? T::XOFF : region == 1 ? T::FOFF : T::YOFF;
-        dma16(base + (int64_t)(r0 + srow) * stride * 2 + c * 16, dst + off + nr * 1024);
-      }
+    for (int i = 0; i < NI; ++i) {
+      const int r = region(i), c0 = cpr(r);
+      const int nr = wave + BW * i - first(r);
+      const int row = nr * (64 / c0) + lane / c0;
+      int c = (lane % c0) ^ swzb(c0, row);
+      if (r == 1 && c >= npch) c = 0;
+      off[i] = (uint32_t)(row * stride2[r] + c * 16);
     }
   }
+  __device__ __forceinline__ Bases bases(int r0, int N) const {
+    Bases t;
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+      t.b[r] = src[r] + (int64_t)r0 * stride2[r];
+      t.lim[r] = (uint32_t)((N - 1 - r0) * stride2[r] + cmax[r] * 16);
+    }
+    return t;
+  }
+  // slot i (a compile-time constant after unrolling) into the tile buffer dst
+  __device__ __forceinline__ void issue(int i, const Bases& t, unsigned char* dst, int wave) const {
+    const int r = region(i);
+    const int nr = wave + BW * i - first(r);
+    dma16_async(t.b[r], min(off[i], t.lim[r]), lds_addr(dst) + doff(r) + nr * 1024);
+  }
+};
+
+// Wait until at most N direct loads of this wavefront are outstanding, then the workgroup
+// barrier (the compiler barrier keeps LDS reads on their side of it).
+template <int N>
+__device__ __forceinline__ void wait_loads_barrier() {
+  static_assert(N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(N | 0x0F70);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // ---------------------------------------------------------------------------------
@@ -148,13 +226,15 @@ __global__ __launch_bounds__(BTH, 2) void attn_bwd_dkv_kernel(BwdParams p) {
   constexpr int QST = D / 16, PST = RP / 16;
   constexpr int MBQ = D / 32, MBP = (RP + 31) / 32;
   static_assert(D % 32 == 0, "head dim multiple of 32");
-  __shared__ __attribute__((aligned(16))) unsigned char sA[T::BYTES];
-  __shared__ __attribute__((aligned(16))) unsigned char sB[T::BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char s0[T::BYTES];   // three tile buffers
+  __shared__ __attribute__((aligned(16))) unsigned char s1[T::BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char s2[T::BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, ln = lane & 31, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int blk = blockIdx.x % p.nblk;
-  const int bh = blockIdx.x / p.nblk;
+  const int L = xcd_order((int)blockIdx.x, (int)gridDim.x);
+  const int blk = L % p.nblk;   // causal: the first key blocks see the most query tiles
+  const int bh = L / p.nblk;
   const int hh = bh % p.H, bb = bh / p.H, N = p.N;
   const int kw0 = blk * kBwdRows + wave * 32;          // this wavefront's first key
   RegionAddr<T::KCH> ax, ay;
@@ -179,20 +259,23 @@ __global__ __launch_bounds__(BTH, 2) void attn_bwd_dkv_kernel(BwdParams p) {
   }
   const int npch = RP > 0 ? p.R / 8 : 0;   // direct-load path needs R % 8 == 0 (host checks)
 
-  // B operands of this wavefront's keys: K*s (scores; the tile holds Q unscaled, so the
-  // scale goes to K here: identical products to the forward's (Q*s) K when s is a power of
-  // two, one rounding apart otherwise), phi_k (factor chain), V (dP)
+  // B operands of this wavefront's keys, negated: -K*s (scores; the tile holds Q unscaled,
+  // so the scale goes to K here: identical products to the forward's (Q*s) K when s is a
+  // power of two, one rounding apart otherwise), -phi_k (factor chain), -V (dP).  With the
+  // chains started at L and Delta they end as L - S and Delta - dP: P = exp(-(L - S)) and
+  // the block computes -dS = P (Delta - dP); the sign goes back at the dK / dphi_k stores.
   u32x4 kf[QST], vf[QST], pkf[PST > 0 ? PST : 1];
+  const u32x4 sgn = {0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
 #pragma unroll
   for (int t = 0; t < QST; ++t) {
-    kf[t] = scale_frag<QT>(ld16(Kp + keyc * p.sk[2] + 16 * t + 8 * hf), p.scale);
-    vf[t] = ld16(Vp + keyc * p.sv[2] + 16 * t + 8 * hf);
+    kf[t] = scale_frag<QT>(ld16(Kp + keyc * p.sk[2] + 16 * t + 8 * hf), -p.scale);
+    vf[t] = ld16(Vp + keyc * p.sv[2] + 16 * t + 8 * hf) ^ sgn;
   }
   if constexpr (RP > 0) {
 #pragma unroll
     for (int t = 0; t < PST; ++t)
       pkf[t] = load_phi_chunk<PT>(PKp + keyc * p.spk[2], 16 * t + 8 * hf, p.R,
-                                  (p.flags & FLAG_PHK_VEC) && 16 * t + 8 * hf + 8 <= p.R);
+                                  (p.flags & FLAG_PHK_VEC) && 16 * t + 8 * hf + 8 <= p.R) ^ sgn;
   }
 
   f32x16 dvT[MBQ], dkT[MBQ + MBP];
@@ -203,86 +286,137 @@ __global__ __launch_bounds__(BTH, 2) void attn_bwd_dkv_kernel(BwdParams p) {
 
   const int nqt = (N + TR - 1) / TR;
   const int qt0 = CAUSAL ? (blk * kBwdRows) / TR : 0;   // earlier query tiles see none of these keys
-  // L and Delta of a query tile: threads 0..63 / 64..127 load one value each when the tile's
-  // copies are issued and store it into the tile before the barrier that publishes it
-  float lval = 0.f;
-  auto issue = [&](unsigned char* dst, int qt) __attribute__((always_inline)) {
-    const int r0 = qt * TR;
-    load_tile<D, RP, true>(dst, r0, N, wave, lane, (const char*)Qp, p.sq[2], (const char*)PQp, p.spq[2], npch,
-                           (const char*)Op, p.sdo[2]);
-    if (tid < 128) lval = (tid < 64 ? Lp : Dp)[min(r0 + (tid & 63), N - 1)];
-  };
-  auto publish = [&](unsigned char* dst) __attribute__((always_inline)) {
-    if (tid < 128) ((float*)(dst + T::LOFF))[tid] = lval;
+  // Three tile buffers: tile qt + 2 streams in while tile qt is computed.  Every wavefront
+  // issues the same number of loads per tile (NV: its chunk slots and one 4-byte copy of
+  // the tile's L (even wavefronts) or Delta (odd) into the tile), so "at most NV
+  // outstanding" means the next tile has landed.
+  DmaPlan<D, RP, true> plan;
+  plan.init(wave, lane, (const char*)Qp, p.sq[2], (const char*)PQp, p.spq[2], npch, (const char*)Op, p.sdo[2]);
+  constexpr int NI = DmaPlan<D, RP, true>::NI, NV = NI + 1, NI0 = (NI + 1) / 2;
+  const float* LDp = (wave & 1) ? Dp : Lp;
+  // direct load j of a tile's NV: chunk slots, then the L / Delta copy
+  // direct load j of a tile's NV: chunk slots, then the L / Delta copy
+  auto issue_one = [&](int j, const typename DmaPlan<D, RP, true>::Bases& tb, unsigned char* dst, int r0)
+      __attribute__((always_inline)) {
+    if (j < NI) plan.issue(j, tb, dst, wave);
+    else dma4_async(LDp + r0 + min(lane, N - 1 - r0), lds_addr(dst + T::LOFF + 256 * (wave & 1)));
   };
 
-  auto compute = [&](const unsigned char* tl, int qt) __attribute__((always_inline)) {
+  constexpr int NS = 2 * QST + PST;     // score / dP MFMAs per block: S (X), dP (Y) alternating, then S (F)
+  constexpr int NCU = 2 * MBQ + MBP;    // gradient MFMAs per k-step u: dV^T, dK^T, dphi_k^T
+  constexpr int NC = 2 * NCU;
+  constexpr int NVB = (NV + 1) / 2;     // direct loads in the first block of a tile
+  static_assert(NVB <= NS && NV - NVB <= NS, "direct loads per block");
+  auto opS = [&](const unsigned char* tl, int qb, int k) __attribute__((always_inline)) {
+    if (k < 2 * QST) return (k & 1) ? ay.rowA(tl + T::YOFF, qb, k >> 1) : ax.rowA(tl + T::XOFF, qb, k >> 1);
+    return af.rowA(tl + T::FOFF, qb, k - 2 * QST);
+  };
+  auto opG = [&](const unsigned char* tl, int qb, int c) __attribute__((always_inline)) {
+    const int u = c / NCU, j = c % NCU;
+    if (j < MBQ) return ay.trA(tl + T::YOFF, qb, u, j);
+    if (j < 2 * MBQ) return ax.trA(tl + T::XOFF, qb, u, j - MBQ);
+    return af.trA(tl + T::FOFF, qb, u, j - 2 * MBQ);
+  };
+
+  // One code path for every block (a second, masked copy of the block costs registers):
+  // blocks with a query past N or (causal) a query before one of the keys take a uniform
+  // branch to the mask; fully masked blocks are computed and contribute zeros.
+  auto compute = [&](const unsigned char* tl, int qt, unsigned char* nb, int qn) __attribute__((always_inline)) {
     const int q0 = qt * TR;
+    const auto tb = plan.bases(qn * TR, N);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int qb0 = q0 + 32 * qb;
-      if (CAUSAL && qb0 + 31 < kw0) continue;        // every query of the block precedes every key
-      if (qb0 >= N) continue;
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int t = 0; t < QST; ++t) s = Mma<QT>::run(ax.rowA(tl + T::XOFF, qb, t), kf[t], s);
-      if constexpr (RP > 0) {
-#pragma unroll
-        for (int t = 0; t < PST; ++t) s = Mma<PT>::run(af.rowA(tl + T::FOFF, qb, t), pkf[t], s);
-      }
-#pragma unroll
-      for (int t = 0; t < QST; ++t) dp = Mma<QT>::run(ay.rowA(tl + T::YOFF, qb, t), vf[t], dp);
-      // register i holds query qb0 + 16 hf + i
+      // register i holds query qb0 + 16 hf + i; the chains start at L and Delta
       const f32x4* lq = (const f32x4*)(tl + T::LOFF + 4 * (32 * qb + 16 * hf));
       const f32x4* dq = (const f32x4*)(tl + T::LOFF + 256 + 4 * (32 * qb + 16 * hf));
-      float pv[16], dsv[16];
+      f32x16 s, dp;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x4 L4 = lq[g], D4 = dq[g];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const int i = 4 * g + c;
-          const int qi = qb0 + 16 * hf + i;
-          const bool ok = qi < N && (!CAUSAL || qi >= key);
-          const float e = __builtin_amdgcn_exp2f((s[i] - L4[c]) * LOG2E);
-          pv[i] = ok ? e : 0.f;
-          dsv[i] = pv[i] * (dp[i] - D4[c]);
+          s[4 * g + c] = L4[c];
+          dp[4 * g + c] = D4[c];
         }
       }
+      u32x4 a[NS];
+#pragma unroll
+      for (int k = 0; k < PD_ROW && k < NS; ++k) a[k] = opS(tl, qb, k);
+      fence();
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        if (k < 2 * QST) {
+          if (k & 1) dp = Mma<QT>::run(a[k], vf[k >> 1], dp);
+          else s = Mma<QT>::run(a[k], kf[k >> 1], s);
+        } else {
+          s = Mma<PT>::run(a[k], pkf[k - 2 * QST], s);
+        }
+        if (k + PD_ROW < NS) a[k + PD_ROW] = opS(tl, qb, k + PD_ROW);
+        if (qb == 0 && k < NVB) issue_one(k, tb, nb, qn * TR);
+        if (qb == 1 && k < NV - NVB) issue_one(NVB + k, tb, nb, qn * TR);
+        fence();
+      }
+      u32x4 g[NC];
+#pragma unroll
+      for (int c = 0; c < PD_TR; ++c) g[c] = opG(tl, qb, c);
+      fence();
+      if (qb0 + 32 > N || (CAUSAL && qb0 < kw0 + 31)) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int qi = qb0 + 16 * hf + i;
+          s[i] = qi < N && (!CAUSAL || qi >= key) ? s[i] : INFINITY;
+        }
+      }
+      float pv[16], dsv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        pv[i] = __builtin_amdgcn_exp2f(s[i] * -LOG2E);
+        dsv[i] = pv[i] * dp[i];
+      }
+      u32x4 pb[2], dsb[2], dsp[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const u32x4 pb = pack8<QT>(pv + 8 * u);
-        const u32x4 dsb = pack8<QT>(dsv + 8 * u);
+        pb[u] = pack8<QT>(pv + 8 * u);
+        dsb[u] = pack8<QT>(dsv + 8 * u);
+        if constexpr (RP > 0) dsp[u] = pack8<PT>(dsv + 8 * u);
+      }
+      fence();
 #pragma unroll
-        for (int mb = 0; mb < MBQ; ++mb) dvT[mb] = Mma<QT>::run(ay.trA(tl + T::YOFF, qb, u, mb), pb, dvT[mb]);
-#pragma unroll
-        for (int mb = 0; mb < MBQ; ++mb) dkT[mb] = Mma<QT>::run(ax.trA(tl + T::XOFF, qb, u, mb), dsb, dkT[mb]);
-        if constexpr (RP > 0) {
-          const u32x4 dsp = pack8<PT>(dsv + 8 * u);
-#pragma unroll
-          for (int mb = 0; mb < MBP; ++mb)
-            dkT[MBQ + mb] = Mma<PT>::run(af.trA(tl + T::FOFF, qb, u, mb), dsp, dkT[MBQ + mb]);
-        }
+      for (int c = 0; c < NC; ++c) {
+        const int u = c / NCU, j = c % NCU;
+        if (j < MBQ) dvT[j] = Mma<QT>::run(g[c], pb[u], dvT[j]);
+        else if (j < 2 * MBQ) dkT[j - MBQ] = Mma<QT>::run(g[c], dsb[u], dkT[j - MBQ]);
+        else dkT[j - MBQ] = Mma<PT>::run(g[c], dsp[u], dkT[j - MBQ]);
+        if (c + PD_TR < NC) g[c + PD_TR] = opG(tl, qb, c + PD_TR);
+        fence();
       }
     }
   };
+  auto run = [&](const unsigned char* tl, int qt, unsigned char* nb) __attribute__((always_inline)) {
+    compute(tl, qt, nb, min(qt + 2, nqt - 1));   // past the end: a copy nothing reads
+  };
 
   if (qt0 < nqt) {
-    issue(sA, qt0);
-    publish(sA);
-    __syncthreads();
-  }
-  for (int qt = qt0; qt < nqt; qt += 2) {
-    if (qt + 1 < nqt) issue(sB, qt + 1);
-    compute(sA, qt);
-    if (qt + 1 < nqt) publish(sB);
-    __syncthreads();
-    if (qt + 1 < nqt) {
-      if (qt + 2 < nqt) issue(sA, qt + 2);
-      compute(sB, qt + 1);
-      if (qt + 2 < nqt) publish(sA);
-      __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NV; ++j) issue_one(j, plan.bases(qt0 * TR, N), s0, qt0 * TR);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) issue_one(j, plan.bases(min(qt0 + 1, nqt - 1) * TR, N), s1, min(qt0 + 1, nqt - 1) * TR);
+    wait_loads_barrier<NV>();
+    // tile qt + 2 goes to the buffer of tile qt - 1
+    for (int qt = qt0; qt < nqt; qt += 3) {
+      run(s0, qt, s2);
+      wait_loads_barrier<NV>();
+      if (qt + 1 < nqt) {
+        run(s1, qt + 1, s0);
+        wait_loads_barrier<NV>();
+      }
+      if (qt + 2 < nqt) {
+        run(s2, qt + 2, s1);
+        wait_loads_barrier<NV>();
+      }
     }
+    __builtin_amdgcn_s_waitcnt(0);   // no copy outlives the workgroup
   }
 
   // register i of block mb: column 32 mb + 8 (i / 4) + 4 hf + i % 4 of this lane's key
@@ -298,7 +432,7 @@ __global__ __launch_bounds__(BTH, 2) void attn_bwd_dkv_kernel(BwdParams p) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           v4[c] = (QT)dvT[mb][4 * a + c];
-          k4[c] = (QT)(dkT[mb][4 * a + c] * p.scale);   // dK = dS^T (Q s)
+          k4[c] = (QT)(dkT[mb][4 * a + c] * -p.scale);   // dK = dS^T (Q s); dkT holds -dS^T Q
         }
         const int col = 32 * mb + 8 * a + 4 * hf;
         *(u32x2*)(dVp + col) = __builtin_bit_cast(u32x2, v4);
@@ -311,7 +445,7 @@ __global__ __launch_bounds__(BTH, 2) void attn_bwd_dkv_kernel(BwdParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int col = 32 * mb + 8 * (i / 4) + 4 * hf + (i % 4);
-          if (col < p.R) atomicAdd(g + col, dkT[MBQ + mb][i]);
+          if (col < p.R) atomicAdd(g + col, -dkT[MBQ + mb][i]);
         }
     }
   }
@@ -324,13 +458,15 @@ __global__ __launch_bounds__(BTH, 2) void attn_bwd_dq_kernel(BwdParams p) {
   typedef Tile<D, RP, false> T;
   constexpr int QST = D / 16, PST = RP / 16;
   constexpr int MBQ = D / 32, MBP = (RP + 31) / 32;
-  __shared__ __attribute__((aligned(16))) unsigned char sA[T::BYTES];
-  __shared__ __attribute__((aligned(16))) unsigned char sB[T::BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char s0[T::BYTES];   // three tile buffers
+  __shared__ __attribute__((aligned(16))) unsigned char s1[T::BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char s2[T::BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, ln = lane & 31, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int blk = blockIdx.x % p.nblk;
-  const int bh = blockIdx.x / p.nblk;
+  const int L = xcd_order((int)blockIdx.x, (int)gridDim.x);
+  const int blk = CAUSAL ? p.nblk - 1 - L % p.nblk : L % p.nblk;   // causal: longest first
+  const int bh = L / p.nblk;
   const int hh = bh % p.H, bb = bh / p.H, N = p.N;
   const int qw0 = blk * kBwdRows + wave * 32;
   const int qrow = qw0 + ln;
@@ -366,7 +502,8 @@ __global__ __launch_bounds__(BTH, 2) void attn_bwd_dq_kernel(BwdParams p) {
       pqf[t] = load_phi_chunk<PT>(PQp + qc * p.spq[2], 16 * t + 8 * hf, p.R,
                                   (p.flags & FLAG_PHQ_VEC) && 16 * t + 8 * hf + 8 <= p.R);
   }
-  const float Lq = p.lse[(int64_t)bh * N + qc];
+  // L (in exp2 units) and Delta of this lane's query
+  const float L2q = p.lse[(int64_t)bh * N + qc] * LOG2E;
   const float Dq = p.delta[(int64_t)bh * N + qc];
 
   f32x16 dqT[MBQ + MBP];
@@ -375,63 +512,108 @@ __global__ __launch_bounds__(BTH, 2) void attn_bwd_dq_kernel(BwdParams p) {
 
   const int kend = CAUSAL ? min(N, blk * kBwdRows + kBwdRows) : N;
   const int nkt = (kend + TR - 1) / TR;
-  auto issue = [&](unsigned char* dst, int kt) __attribute__((always_inline)) {
-    load_tile<D, RP, false>(dst, kt * TR, N, wave, lane, (const char*)Kp, p.sk[2], (const char*)PKp, p.spk[2], npch,
-                            (const char*)Vp, p.sv[2]);
+  // three tile buffers: tile kt + 2 streams in while tile kt is computed (NI loads per
+  // wavefront and tile, so "at most NI outstanding" means the next tile has landed)
+  DmaPlan<D, RP, false> plan;
+  plan.init(wave, lane, (const char*)Kp, p.sk[2], (const char*)PKp, p.spk[2], npch, (const char*)Vp, p.sv[2]);
+  constexpr int NI = DmaPlan<D, RP, false>::NI;
+
+  constexpr int NS = 2 * QST + PST;   // S^T (X) and dP^T (Y) alternating, then S^T (F)
+  constexpr int NCU = MBQ + MBP;      // gradient MFMAs per k-step u: dQ^T, dphi_q^T
+  constexpr int NC = 2 * NCU;
+  constexpr int NVB = (NI + 1) / 2;
+  static_assert(NVB <= NS, "direct loads per block");
+  auto opS = [&](const unsigned char* tl, int kb, int k) __attribute__((always_inline)) {
+    if (k < 2 * QST) return (k & 1) ? ay.rowA(tl + T::YOFF, kb, k >> 1) : ax.rowA(tl + T::XOFF, kb, k >> 1);
+    return af.rowA(tl + T::FOFF, kb, k - 2 * QST);
+  };
+  auto opG = [&](const unsigned char* tl, int kb, int c) __attribute__((always_inline)) {
+    const int u = c / NCU, j = c % NCU;
+    if (j < MBQ) return ax.trA(tl + T::XOFF, kb, u, j);
+    return af.trA(tl + T::FOFF, kb, u, j - MBQ);
   };
 
-  auto compute = [&](const unsigned char* tl, int kt) __attribute__((always_inline)) {
+  // one code path for every block: blocks with a key past N or (causal) a key after one of
+  // the queries take a uniform branch to the mask; fully masked blocks contribute zeros
+  auto compute = [&](const unsigned char* tl, int kt, unsigned char* nb, int kn) __attribute__((always_inline)) {
     const int k0 = kt * TR;
+    const auto tb = plan.bases(kn * TR, N);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int kb0 = k0 + 32 * kb;
-      if (CAUSAL && kb0 > qw0 + 31) continue;        // every key of the block follows every query
-      if (kb0 >= N) continue;
       f32x16 s = f32x16{}, dp = f32x16{};
+      u32x4 a[NS];
 #pragma unroll
-      for (int t = 0; t < QST; ++t) s = Mma<QT>::run(ax.rowA(tl + T::XOFF, kb, t), qf[t], s);
-      if constexpr (RP > 0) {
+      for (int k = 0; k < PD_ROW && k < NS; ++k) a[k] = opS(tl, kb, k);
+      fence();
 #pragma unroll
-        for (int t = 0; t < PST; ++t) s = Mma<PT>::run(af.rowA(tl + T::FOFF, kb, t), pqf[t], s);
+      for (int k = 0; k < NS; ++k) {
+        if (k < 2 * QST) {
+          if (k & 1) dp = Mma<QT>::run(a[k], of[k >> 1], dp);
+          else s = Mma<QT>::run(a[k], qf[k >> 1], s);
+        } else {
+          s = Mma<PT>::run(a[k], pqf[k - 2 * QST], s);
+        }
+        if (k + PD_ROW < NS) a[k + PD_ROW] = opS(tl, kb, k + PD_ROW);
+        if (kb == 0 && k < NVB) plan.issue(k, tb, nb, wave);
+        if (kb == 1 && k < NI - NVB) plan.issue(NVB + k, tb, nb, wave);
+        fence();
       }
+      u32x4 g[NC];
 #pragma unroll
-      for (int t = 0; t < QST; ++t) dp = Mma<QT>::run(ay.rowA(tl + T::YOFF, kb, t), of[t], dp);
+      for (int c = 0; c < PD_TR; ++c) g[c] = opG(tl, kb, c);
+      fence();
+      // register i holds key kb0 + 16 hf + i
+      if (kb0 + 32 > N || (CAUSAL && kb0 + 31 > qw0)) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kj = kb0 + 16 * hf + i;
+          s[i] = kj < N && (!CAUSAL || kj <= qrow) ? s[i] : -INFINITY;
+        }
+      }
       float dsv[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kj = kb0 + 16 * hf + i;
-        const bool ok = kj < N && (!CAUSAL || kj <= qrow);
-        const float e = __builtin_amdgcn_exp2f((s[i] - Lq) * LOG2E);
-        dsv[i] = ok ? e * (dp[i] - Dq) : 0.f;
-      }
+      for (int i = 0; i < 16; ++i) dsv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], LOG2E, -L2q)) * (dp[i] - Dq);
+      u32x4 dsb[2], dsp[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const u32x4 dsb = pack8<QT>(dsv + 8 * u);
+        dsb[u] = pack8<QT>(dsv + 8 * u);
+        if constexpr (RP > 0) dsp[u] = pack8<PT>(dsv + 8 * u);
+      }
+      fence();
 #pragma unroll
-        for (int mb = 0; mb < MBQ; ++mb) dqT[mb] = Mma<QT>::run(ax.trA(tl + T::XOFF, kb, u, mb), dsb, dqT[mb]);
-        if constexpr (RP > 0) {
-          const u32x4 dsp = pack8<PT>(dsv + 8 * u);
-#pragma unroll
-          for (int mb = 0; mb < MBP; ++mb)
-            dqT[MBQ + mb] = Mma<PT>::run(af.trA(tl + T::FOFF, kb, u, mb), dsp, dqT[MBQ + mb]);
-        }
+      for (int c = 0; c < NC; ++c) {
+        const int u = c / NCU, j = c % NCU;
+        if (j < MBQ) dqT[j] = Mma<QT>::run(g[c], dsb[u], dqT[j]);
+        else dqT[j] = Mma<PT>::run(g[c], dsp[u], dqT[j]);
+        if (c + PD_TR < NC) g[c + PD_TR] = opG(tl, kb, c + PD_TR);
+        fence();
       }
     }
   };
+  auto run = [&](const unsigned char* tl, int kt, unsigned char* nb) __attribute__((always_inline)) {
+    compute(tl, kt, nb, min(kt + 2, nkt - 1));   // past the end: a copy nothing reads
+  };
 
   if (nkt > 0) {
-    issue(sA, 0);
-    __syncthreads();
-  }
-  for (int kt = 0; kt < nkt; kt += 2) {
-    if (kt + 1 < nkt) issue(sB, kt + 1);
-    compute(sA, kt);
-    __syncthreads();
-    if (kt + 1 < nkt) {
-      if (kt + 2 < nkt) issue(sA, kt + 2);
-      compute(sB, kt + 1);
-      __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NI; ++j) plan.issue(j, plan.bases(0, N), s0, wave);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) plan.issue(j, plan.bases(min(1, nkt - 1) * TR, N), s1, wave);
+    wait_loads_barrier<NI>();
+    for (int kt = 0; kt < nkt; kt += 3) {
+      run(s0, kt, s2);
+      wait_loads_barrier<NI>();
+      if (kt + 1 < nkt) {
+        run(s1, kt + 1, s0);
+        wait_loads_barrier<NI>();
+      }
+      if (kt + 2 < nkt) {
+        run(s2, kt + 2, s1);
+        wait_loads_barrier<NI>();
+      }
     }
+    __builtin_amdgcn_s_waitcnt(0);   // no copy outlives the workgroup
   }
 
   if (qrow < N) {

@@ -489,6 +489,10 @@ BWD = [
     (1, 3, 190, 32, 16, "head", "bf16", "bf16", True),
     (2, 2, 160, 32, 24, "full", "f16", "f16", False),
     (1, 2, 130, 64, 8, "head", "bf16", "f16", True),
+    # one tile; fewer rows than one MFMA block; many tiles through the three-buffer rotation
+    (1, 1, 64, 64, 16, "shared", "bf16", "f16", True),
+    (1, 2, 17, 32, 8, "shared", "f16", "f16", False),
+    (1, 1, 1000, 64, 64, "shared", "bf16", "f16", True),
 ]
 
 
