@@ -62,7 +62,7 @@ class _BwdArgs(ctypes.Structure):
         ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
         ("sdq", _I64x3), ("sdk", _I64x3), ("sdv", _I64x3),
         ("dphi_q", ctypes.c_void_p), ("dphi_k", ctypes.c_void_p), ("sdphi_q", _I64x3), ("sdphi_k", _I64x3),
-        ("delta", ctypes.c_void_p),
+        ("work", ctypes.c_void_p), ("work_bytes", ctypes.c_size_t),
     ]
 
 
@@ -112,6 +112,9 @@ def load():
                                             ctypes.c_void_p]
         lib.fb_mulbias_expand.restype = ctypes.c_int
         lib.fb_mulbias_expand.argtypes = lib.fb_attn_fwd_mulbias.argtypes
+        lib.fb_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.fb_attn_bwd_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                    ctypes.POINTER(_I64x3), ctypes.POINTER(_I64x3)]
         lib.fb_mulbias_workspace_bytes.restype = ctypes.c_size_t
         lib.fb_mulbias_workspace_bytes.argtypes = [ctypes.POINTER(_AttnArgs), ctypes.c_int]
         lib.fb_attn_fwd_densebias.restype = ctypes.c_int
@@ -433,8 +436,6 @@ def fb_attn_bwd_lowrank(q, k, v, out, lse, dout, phi_q=None, phi_k=None, *, caus
             raise ValueError(f"{name} must match q in shape, dtype and device")
         setattr(g, name, t.data_ptr())
         setattr(g, "s" + ("do" if name == "dout" else name), _I64x3(*t.stride()[:3]))
-    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    g.delta = delta.data_ptr()
     dpq = dpk = None
     R = 0 if (phi_q is None or phi_k is None) else phi_q.shape[-1]
     if R > 0:
@@ -447,6 +448,12 @@ def fb_attn_bwd_lowrank(q, k, v, out, lse, dout, phi_q=None, phi_k=None, *, caus
         _, gsq = _bhn_strides(dpq, B, H, N, "dphi_q")
         _, gsk = _bhn_strides(dpk, B, H, N, "dphi_k")
         g.dphi_q, g.dphi_k, g.sdphi_q, g.sdphi_k = dpq.data_ptr(), dpk.data_ptr(), gsq, gsk
+    # workspace (Delta and per-(b, h) partials of summed factor gradients), 256-byte aligned
+    nbytes = int(load().fb_attn_bwd_workspace_bytes(B, H, N, R, ctypes.byref(g.sdphi_q), ctypes.byref(g.sdphi_k)))
+    work = torch.empty(nbytes + 256, dtype=torch.uint8, device=q.device)
+    g.work = (work.data_ptr() + 255) // 256 * 256
+    g.work_bytes = nbytes
+    if R > 0:
         st = load().fb_attn_bwd_lowrank(ctypes.byref(a), eq.data_ptr(), ek.data_ptr(), _dt_code(phi_q.dtype), R,
                                         ctypes.byref(sq), ctypes.byref(sk), ctypes.byref(g),
                                         _stream_ptr(q.device, stream))
@@ -454,7 +461,16 @@ def fb_attn_bwd_lowrank(q, k, v, out, lse, dout, phi_q=None, phi_k=None, *, caus
         st = load().fb_attn_bwd_lowrank(ctypes.byref(a), None, None, a.dt, 0, None, None, ctypes.byref(g),
                                         _stream_ptr(q.device, stream))
     _check(st)
+    if stream is not None:
+        work.record_stream(stream)   # the workspace outlives this call on a caller's stream
     return dq, dk, dv, dpq, dpk
+
+
+def fb_attn_bwd_workspace_bytes(B: int, H: int, N: int, R: int, sdphi_q=(0, 0, 0), sdphi_k=(0, 0, 0)) -> int:
+    """Device workspace (bytes) that fb_attn_bwd_lowrank needs; strides of the fp32 factor
+    gradients in (batch, head, row) order (a 0 stride sums over that axis)."""
+    return int(load().fb_attn_bwd_workspace_bytes(int(B), int(H), int(N), int(R), ctypes.byref(_I64x3(*sdphi_q)),
+                                                  ctypes.byref(_I64x3(*sdphi_k))))
 
 
 def fb_attn_fwd_alibi(q, k, v, slopes=None, *, causal: bool = False, scale: Optional[float] = None, out=None,

@@ -1,6 +1,7 @@
 // C ABI of libflashbias: argument validation and dispatch.  Every check runs
 // before any launch; nothing here allocates device memory.
 #include <cmath>
+#include <cstdint>
 #include <cstdarg>
 #include <cstdio>
 #include <new>
@@ -119,6 +120,24 @@ void set_error(const char* fmt, ...) {
   va_start(ap, fmt);
   vsnprintf(g_err, sizeof(g_err), fmt, ap);
   va_end(ap);
+}
+
+BwdWork bwd_work_layout(int B, int H, int N, int R, const int64_t sdphi_q[3], const int64_t sdphi_k[3]) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  // a factor gradient needs per-(b, h) partials when an axis of size > 1 has stride 0
+  auto summed = [&](const int64_t* sd) { return R > 0 && ((sd[0] == 0 && B > 1) || (sd[1] == 0 && H > 1)); };
+  const size_t rows = (size_t)B * H * N;
+  BwdWork w{0, SIZE_MAX, SIZE_MAX, up(rows * 4)};
+  if (summed(sdphi_q)) {
+    w.pq_off = w.bytes;
+    w.bytes += up(rows * (size_t)R * 4);
+  }
+  if (summed(sdphi_k)) {
+    w.pk_off = w.bytes;
+    w.bytes += up(rows * (size_t)R * 4);
+  }
+  if (rows == 0) w.bytes = 0;
+  return w;
 }
 
 }  // namespace fb
@@ -282,6 +301,11 @@ size_t fb_mulbias_workspace_bytes(const fb_attn_args* a, int R) {
   return rows == 0 ? 0 : 2 * first + 2 * rest;
 }
 
+size_t fb_attn_bwd_workspace_bytes(int B, int H, int N, int R, const int64_t sdphi_q[3], const int64_t sdphi_k[3]) {
+  if (B < 0 || H < 0 || N < 0 || R < 0 || (R > 0 && (!sdphi_q || !sdphi_k))) return 0;
+  return bwd_work_layout(B, H, N, R, sdphi_q, sdphi_k).bytes;
+}
+
 }  // extern "C"
 
 namespace {
@@ -392,7 +416,7 @@ fb_status fb_attn_bwd_lowrank(const fb_attn_args* a, const void* phi_q, const vo
   }
   if ((int64_t)a->B * a->H * a->N == 0) return FB_OK;
   if (!a->lse) FB_FAIL(FB_EINVAL, "%s: the forward LSE is required", fn);
-  if (!g->dout || !g->dq || !g->dk || !g->dv || !g->delta) FB_FAIL(FB_EINVAL, "%s: null dO, output or workspace", fn);
+  if (!g->dout || !g->dq || !g->dk || !g->dv || !g->work) FB_FAIL(FB_EINVAL, "%s: null dO, output or workspace", fn);
   const int es = esize(a->dt);
   const int64_t* st6[4] = {g->sdo, g->sdq, g->sdk, g->sdv};
   const void* pt[4] = {g->dout, g->dq, g->dk, g->dv};
@@ -403,14 +427,21 @@ fb_status fb_attn_bwd_lowrank(const fb_attn_args* a, const void* phi_q, const vo
     if (a->N > 1 && st6[i][2] < a->D) FB_FAIL(FB_EINVAL, "%s: gradient row stride < D", fn);
     if (!strides_fit32(st6[i], a->N)) FB_FAIL(FB_EUNSUPPORTED, "%s: gradient strides exceed 32 bits", fn);
   }
-  if ((uintptr_t)g->delta & 3u) FB_FAIL(FB_EINVAL, "%s: misaligned delta workspace", fn);
+  if ((uintptr_t)g->work & 255u) FB_FAIL(FB_EINVAL, "%s: workspace not 256-byte aligned", fn);
+  if (R > 0 && (!g->sdphi_q || !g->sdphi_k)) FB_FAIL(FB_EINVAL, "%s: null factor-gradient strides", fn);
+  const BwdWork wl = bwd_work_layout(a->B, a->H, a->N, R, g->sdphi_q, g->sdphi_k);
+  if (g->work_bytes < wl.bytes)
+    FB_FAIL(FB_EINVAL, "%s: workspace of %zu bytes, %zu needed", fn, g->work_bytes, wl.bytes);
+  if ((wl.pq_off != SIZE_MAX || wl.pk_off != SIZE_MAX) && (int64_t)a->H * a->N * R > 0x7fffffffLL)
+    FB_FAIL(FB_EUNSUPPORTED, "%s: per-(b, h) factor gradients exceed 32-bit strides", fn);
   BwdParams p{};
   p.q = a->q;
   p.k = a->k;
   p.v = a->v;
   p.dout = g->dout;
   p.lse = a->lse;
-  p.delta = g->delta;
+  float* const delta = (float*)g->work;
+  p.delta = delta;
   p.dq = g->dq;
   p.dk = g->dk;
   p.dv = g->dv;
@@ -443,7 +474,9 @@ fb_status fb_attn_bwd_lowrank(const fb_attn_args* a, const void* phi_q, const vo
       FB_FAIL(FB_EUNSUPPORTED, "%s: factor rows must be 16-byte aligned", fn);
     if (a->N > 1 && (sphi_q[2] < R || sphi_k[2] < R || g->sdphi_q[2] < R || g->sdphi_k[2] < R))
       FB_FAIL(FB_EINVAL, "%s: factor row stride < R", fn);
-    if (((uintptr_t)g->dphi_q & 3u) || ((uintptr_t)g->dphi_k & 3u)) FB_FAIL(FB_EINVAL, "%s: misaligned dphi", fn);
+    if (((uintptr_t)g->dphi_q & 15u) || ((uintptr_t)g->dphi_k & 15u) || g->sdphi_q[2] % 4 || g->sdphi_k[2] % 4 ||
+        g->sdphi_q[1] % 4 || g->sdphi_k[1] % 4 || g->sdphi_q[0] % 4 || g->sdphi_k[0] % 4)
+      FB_FAIL(FB_EINVAL, "%s: dphi and its strides must be 16-byte aligned", fn);
     if (!strides_fit32(sphi_q, a->N) || !strides_fit32(sphi_k, a->N) || !strides_fit32(g->sdphi_q, a->N) ||
         !strides_fit32(g->sdphi_k, a->N))
       FB_FAIL(FB_EUNSUPPORTED, "%s: factor strides exceed 32 bits", fn);
@@ -457,15 +490,32 @@ fb_status fb_attn_bwd_lowrank(const fb_attn_args* a, const void* phi_q, const vo
       p.sdpq[i] = (int)g->sdphi_q[i];
       p.sdpk[i] = (int)g->sdphi_k[i];
     }
+    // a gradient summed over batches or heads goes to per-(b, h) partials first
+    if (wl.pq_off != SIZE_MAX) {
+      p.dphq = (float*)((char*)g->work + wl.pq_off);
+      p.sdpq[0] = a->H * a->N * R;
+      p.sdpq[1] = a->N * R;
+      p.sdpq[2] = R;
+    }
+    if (wl.pk_off != SIZE_MAX) {
+      p.dphk = (float*)((char*)g->work + wl.pk_off);
+      p.sdpk[0] = a->H * a->N * R;
+      p.sdpk[1] = a->N * R;
+      p.sdpk[2] = R;
+    }
     p.flags |= FLAG_PHQ_VEC | FLAG_PHK_VEC;
     RP = R <= 16 ? 16 : R <= 32 ? 32 : 64;
   }
-  st = launch_attention_bwd_aux(a->dt, a->o, a->so, g->dout, g->sdo, a->B, a->H, a->N, a->D, g->delta,
-                                g->dphi_q, g->sdphi_q, g->dphi_k, g->sdphi_k, R, stream);
+  st = launch_attention_bwd_delta(a->dt, a->o, a->so, g->dout, g->sdo, a->B, a->H, a->N, a->D, delta, stream);
   if (st != FB_OK) return st;
   st = a->D == 32 ? launch_attention_bwd_d32(a->dt, R > 0 ? phi_dt : a->dt, RP, p, stream)
                   : launch_attention_bwd_d64(a->dt, R > 0 ? phi_dt : a->dt, RP, p, stream);
   if (st == FB_EUNSUPPORTED) set_error("%s: no kernel for this dtype / rank combination", fn);
+  if (st != FB_OK) return st;
+  if (wl.pq_off != SIZE_MAX)
+    st = launch_attention_bwd_reduce(p.dphq, a->B, a->H, a->N, R, g->dphi_q, g->sdphi_q, stream);
+  if (st == FB_OK && wl.pk_off != SIZE_MAX)
+    st = launch_attention_bwd_reduce(p.dphk, a->B, a->H, a->N, R, g->dphi_k, g->sdphi_k, stream);
   return st;
 }
 

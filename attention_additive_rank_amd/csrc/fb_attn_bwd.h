@@ -438,14 +438,16 @@ __global__ __launch_bounds__(BTH, 2) void attn_bwd_dkv_kernel(BwdParams p) {
         *(u32x2*)(dVp + col) = __builtin_bit_cast(u32x2, v4);
         *(u32x2*)(dKp + col) = __builtin_bit_cast(u32x2, k4);
       }
-    if constexpr (RP > 0) {
+    if constexpr (RP > 0) {   // this (b, h)'s dphi_k row (its partial when summed): 4 columns a store
       float* g = p.dphk + ((int64_t)bb * p.sdpk[0] + (int64_t)hh * p.sdpk[1] + (int64_t)key * p.sdpk[2]);
 #pragma unroll
       for (int mb = 0; mb < MBP; ++mb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int col = 32 * mb + 8 * (i / 4) + 4 * hf + (i % 4);
-          if (col < p.R) atomicAdd(g + col, -dkT[MBQ + mb][i]);
+        for (int a = 0; a < 4; ++a) {
+          const int col = 32 * mb + 8 * a + 4 * hf;
+          const f32x4 v = {-dkT[MBQ + mb][4 * a], -dkT[MBQ + mb][4 * a + 1], -dkT[MBQ + mb][4 * a + 2],
+                           -dkT[MBQ + mb][4 * a + 3]};
+          if (col < p.R) *(f32x4*)(g + col) = v;
         }
     }
   }
@@ -628,14 +630,16 @@ __global__ __launch_bounds__(BTH, 2) void attn_bwd_dq_kernel(BwdParams p) {
         for (int c = 0; c < 4; ++c) q4[c] = (QT)(dqT[mb][4 * a + c] * p.scale);
         *(u32x2*)(dQp + 32 * mb + 8 * a + 4 * hf) = __builtin_bit_cast(u32x2, q4);
       }
-    if constexpr (RP > 0) {
+    if constexpr (RP > 0) {   // this (b, h)'s dphi_q row (its partial when summed): 4 columns a store
       float* g = p.dphq + ((int64_t)bb * p.sdpq[0] + (int64_t)hh * p.sdpq[1] + (int64_t)qrow * p.sdpq[2]);
 #pragma unroll
       for (int mb = 0; mb < MBP; ++mb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int col = 32 * mb + 8 * (i / 4) + 4 * hf + (i % 4);
-          if (col < p.R) atomicAdd(g + col, dqT[MBQ + mb][i]);
+        for (int a = 0; a < 4; ++a) {
+          const int col = 32 * mb + 8 * a + 4 * hf;
+          const f32x4 v = {dqT[MBQ + mb][4 * a], dqT[MBQ + mb][4 * a + 1], dqT[MBQ + mb][4 * a + 2],
+                           dqT[MBQ + mb][4 * a + 3]};
+          if (col < p.R) *(f32x4*)(g + col) = v;
         }
     }
   }

@@ -1,6 +1,6 @@
-// Small kernels around the attention backward: Delta_i = sum_d dO_id O_id (fp32), and
-// clearing the fp32 factor-gradient outputs before the backward kernels accumulate into
-// them (atomically, so that factors broadcast over batch or heads get summed gradients).
+// Small kernels around the attention backward: Delta_i = sum_d dO_id O_id (fp32) before the
+// fused kernels, and the sum of per-(b, h) factor gradients for a factor shared by several
+// batches or heads after them (fixed order, no atomics).
 #include <algorithm>
 
 #include "fb_attn_bwd.h"
@@ -33,16 +33,22 @@ __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ o, int
   }
 }
 
-__global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ x, int64_t s0, int64_t s1, int64_t s2, int B,
-                                                   int H, int N, int R) {
-  const int64_t total = (int64_t)B * H * N * R;
+// One thread per output element: the partials of the (b, h) pairs it gathers, b outer.
+__global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ part, int B, int H, int N, int R,
+                                                     int Bo, int Ho, float* __restrict__ out, int64_t s0, int64_t s1,
+                                                     int64_t s2) {
+  const int64_t total = (int64_t)Bo * Ho * N * R;
+  const int64_t hstride = (int64_t)N * R, bstride = (int64_t)H * hstride;
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
-    const int r = (int)(t % R);
-    const int64_t row = t / R;
-    const int n = (int)(row % N);
-    const int64_t bh = row / N;
-    const int h = (int)(bh % H), b = (int)(bh / H);
-    x[b * s0 + h * s1 + n * s2 + r] = 0.f;
+    const int64_t nr = t % hstride;
+    const int64_t bh = t / hstride;
+    const int ho = (int)(bh % Ho), bo = (int)(bh / Ho);
+    const int b0 = Bo == 1 ? 0 : bo, b1 = Bo == 1 ? B : bo + 1;
+    const int h0 = Ho == 1 ? 0 : ho, h1 = Ho == 1 ? H : ho + 1;
+    float acc = 0.f;
+    for (int b = b0; b < b1; ++b)
+      for (int h = h0; h < h1; ++h) acc += part[b * bstride + h * hstride + nr];
+    out[bo * s0 + ho * s1 + (nr / R) * s2 + nr % R] = acc;
   }
 }
 
@@ -50,9 +56,8 @@ int grid_for(int64_t work) { return (int)std::min<int64_t>((work + 255) / 256, 8
 
 }  // namespace
 
-fb_status launch_attention_bwd_aux(fb_dtype dt, const void* o, const int64_t so[3], const void* dout,
-                                   const int64_t sdo[3], int B, int H, int N, int D, float* delta, float* dphq,
-                                   const int64_t sdpq[3], float* dphk, const int64_t sdpk[3], int R, hipStream_t s) {
+fb_status launch_attention_bwd_delta(fb_dtype dt, const void* o, const int64_t so[3], const void* dout,
+                                     const int64_t sdo[3], int B, int H, int N, int D, float* delta, hipStream_t s) {
   const int64_t rows = (int64_t)B * H * N;
   if (dt == FB_BF16)
     hipLaunchKernelGGL((delta_kernel<__bf16>), dim3(grid_for(rows)), dim3(256), 0, s, (const __bf16*)o, so[0], so[1],
@@ -60,17 +65,23 @@ fb_status launch_attention_bwd_aux(fb_dtype dt, const void* o, const int64_t so[
   else
     hipLaunchKernelGGL((delta_kernel<_Float16>), dim3(grid_for(rows)), dim3(256), 0, s, (const _Float16*)o, so[0],
                        so[1], so[2], (const _Float16*)dout, sdo[0], sdo[1], sdo[2], B, H, N, D, delta);
-  if (R > 0) {
-    // clear each distinct element once: an axis with stride 0 has one position
-    const int Bq = sdpq[0] ? B : 1, Hq = sdpq[1] ? H : 1, Bk = sdpk[0] ? B : 1, Hk = sdpk[1] ? H : 1;
-    hipLaunchKernelGGL(zero_kernel, dim3(grid_for((int64_t)Bq * Hq * N * R)), dim3(256), 0, s, dphq, sdpq[0], sdpq[1],
-                       sdpq[2], Bq, Hq, N, R);
-    hipLaunchKernelGGL(zero_kernel, dim3(grid_for((int64_t)Bk * Hk * N * R)), dim3(256), 0, s, dphk, sdpk[0], sdpk[1],
-                       sdpk[2], Bk, Hk, N, R);
-  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_error("attention backward preparation failed: %s", hipGetErrorString(e));
+    return FB_EHIP;
+  }
+  return FB_OK;
+}
+
+fb_status launch_attention_bwd_reduce(const float* part, int B, int H, int N, int R, float* out,
+                                      const int64_t sout[3], hipStream_t s) {
+  // an axis of the output with stride 0 has one position and gathers all of that axis
+  const int Bo = sout[0] ? B : 1, Ho = sout[1] ? H : 1;
+  hipLaunchKernelGGL(reduce_kernel, dim3(grid_for((int64_t)Bo * Ho * N * R)), dim3(256), 0, s, part, B, H, N, R, Bo,
+                     Ho, out, sout[0], sout[1], sout[2]);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("factor-gradient reduction failed: %s", hipGetErrorString(e));
     return FB_EHIP;
   }
   return FB_OK;

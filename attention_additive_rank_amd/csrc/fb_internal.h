@@ -104,10 +104,18 @@ constexpr int kBwdRows = 128;     // rows (keys or queries) per backward workgro
 // forward; RP in {0, 16, 32, 64}.  FB_EUNSUPPORTED when no instance matches.
 fb_status launch_attention_bwd_d32(fb_dtype dt, fb_dtype phi_dt, int RP, const BwdParams& p, hipStream_t s);
 fb_status launch_attention_bwd_d64(fb_dtype dt, fb_dtype phi_dt, int RP, const BwdParams& p, hipStream_t s);
-// Delta = rowsum(dO * O) into delta ([B][H][N] fp32) and, for R > 0, zeroed factor gradients.
-fb_status launch_attention_bwd_aux(fb_dtype dt, const void* o, const int64_t so[3], const void* dout,
-                                   const int64_t sdo[3], int B, int H, int N, int D, float* delta, float* dphq,
-                                   const int64_t sdpq[3], float* dphk, const int64_t sdpk[3], int R, hipStream_t s);
+// Delta = rowsum(dO * O) into delta ([B][H][N] fp32).
+fb_status launch_attention_bwd_delta(fb_dtype dt, const void* o, const int64_t so[3], const void* dout,
+                                     const int64_t sdo[3], int B, int H, int N, int D, float* delta, hipStream_t s);
+// out[b'][h'][n][r] = sum of part[b][h][n][r] ([B][H][N][R] dense fp32) over the batches /
+// heads that an axis of out with stride 0 gathers, in (b, h) order.
+fb_status launch_attention_bwd_reduce(const float* part, int B, int H, int N, int R, float* out,
+                                      const int64_t sout[3], hipStream_t s);
+// Workspace layout of the backward: Delta, then the partial factor gradients that need a sum.
+struct BwdWork {
+  size_t delta_off, pq_off, pk_off, bytes;   // pq_off / pk_off = SIZE_MAX: no partial buffer
+};
+BwdWork bwd_work_layout(int B, int H, int N, int R, const int64_t sdphi_q[3], const int64_t sdphi_k[3]);
 
 void set_error(const char* fmt, ...);
 

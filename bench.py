@@ -329,7 +329,7 @@ def bench_backward(args, w, fb, torch, q, k, v, pq_t, pk_t, stage1, out, dev, st
                                  "R_columns": Rp, "causal": w.causal, "flops_per_step": F},
                       "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": peak, "unit": "TFLOP/s",
                                    "frac": round(tf / peak, 4), "traffic": None,
-                                   "kernel": "attn_bwd_dkv_kernel + attn_bwd_dq_kernel (+ delta, zero)"},
+                                   "kernel": "attn_bwd_dkv_kernel + attn_bwd_dq_kernel (+ delta, factor-gradient sum)"},
                       "cpu_baseline": None}), flush=True)
 
 

@@ -313,8 +313,21 @@ typedef struct {
                           all batches or heads); NULL when R == 0 */
   float* dphi_k;
   int64_t sdphi_q[3], sdphi_k[3];
-  float* delta;        /* device workspace [B][H][N] fp32 (rowsum of dO * O) */
+  void* work;          /* device workspace, 256-byte aligned, at least
+                          fb_attn_bwd_workspace_bytes(...) bytes; caller-owned, contents
+                          undefined on return */
+  size_t work_bytes;
 } fb_attn_bwd_args;
+
+/*
+ * fb_attn_bwd_workspace_bytes -- size of the workspace fb_attn_bwd_lowrank needs: the
+ * fp32 row sums Delta = rowsum(dO * O) ([B][H][N]) and, for each factor gradient that is
+ * summed over batches or heads (a 0 stride on an axis of size > 1), one fp32 partial
+ * gradient per (b, h) ([B][H][N][R]), which a final pass adds up in a fixed order (no
+ * atomics: the sums are deterministic).  Each part starts on a 256-byte boundary.
+ * Returns 0 for negative sizes.
+ */
+size_t fb_attn_bwd_workspace_bytes(int B, int H, int N, int R, const int64_t sdphi_q[3], const int64_t sdphi_k[3]);
 
 /*
  * fb_attn_bwd_lowrank -- gradients of O = softmax(s Q K^T + phi_q phi_k^T) V with
@@ -328,15 +341,17 @@ typedef struct {
  *   a            the forward's arguments: q, k, v, o (the forward output) and lse (the
  *                forward's LSE output, required)
  *   phi_*, R ... the forward's factors (R == 0: plain attention)
- *   g            dO, the outputs and the Delta workspace (see fb_attn_bwd_args)
+ *   g            dO, the outputs and the workspace (see fb_attn_bwd_args)
  * Supported: a->dt FB_BF16 or FB_F16, D in {32, 64}, R <= 64 with R % 8 == 0 and 16-byte
  * aligned factor rows (pad factors with zero columns).  The fused kernels recompute the
  * scores tile by tile; Q*s is rounded to dt as in the forward (for the key-major kernel
  * the scale is applied to K, identical when s is a power of two); P and dS are rounded to
- * dt for their MFMA products; accumulation is fp32.  dphi_* are accumulated with fp32
- * atomics (summation order not fixed).
- * Errors: as the forward; FB_EINVAL for null outputs / workspace / lse, negative or
- * misaligned strides; FB_EUNSUPPORTED outside the supported set.
+ * dt for their MFMA products; accumulation is fp32.  dphi_* of one (b, h) are written by
+ * the kernels; a factor shared over batches or heads gets the sum of the per-(b, h)
+ * gradients, added in (b, h) order from the workspace (deterministic).
+ * Errors: as the forward; FB_EINVAL for null outputs / lse, a null, misaligned or too
+ * small workspace, negative or misaligned strides; FB_EUNSUPPORTED outside the
+ * supported set.
  */
 fb_status fb_attn_bwd_lowrank(const fb_attn_args* a, const void* phi_q, const void* phi_k, fb_dtype phi_dt, int R,
                               const int64_t sphi_q[3], const int64_t sphi_k[3], const fb_attn_bwd_args* g,

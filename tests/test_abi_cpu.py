@@ -178,8 +178,9 @@ def _bwd(a, R=0, phi_dt=fb.FB_BF16, pq=FAKE, pk=FAKE, s=(0, 0, 64), **gk):
     for n in ("sdo", "sdq", "sdk", "sdv"):
         setattr(g, n, fb._I64x3(*gk.get(n, st)))
     g.dphi_q, g.dphi_k = gk.get("dphi_q", FAKE), gk.get("dphi_k", FAKE)
-    g.sdphi_q = g.sdphi_k = fb._I64x3(0, 0, 64)
-    g.delta = gk.get("delta", FAKE)
+    g.sdphi_q = g.sdphi_k = fb._I64x3(*gk.get("sdphi", (0, 0, 64)))
+    g.work = gk.get("work", FAKE)
+    g.work_bytes = gk.get("work_bytes", 1 << 40)
     sp = fb._I64x3(*s)
     return fb.load().fb_attn_bwd_lowrank(ctypes.byref(a), pq, pk, phi_dt, R, ctypes.byref(sp), ctypes.byref(sp),
                                          ctypes.byref(g), None)
@@ -197,7 +198,11 @@ def _bwd(a, R=0, phi_dt=fb.FB_BF16, pq=FAKE, pk=FAKE, s=(0, 0, 64), **gk):
     (dict(lse=FAKE), dict(R=-1), fb.FB_EINVAL),
     ({}, {}, fb.FB_EINVAL),                                     # no forward LSE
     (dict(lse=FAKE), dict(dq=None), fb.FB_EINVAL),
-    (dict(lse=FAKE), dict(delta=None), fb.FB_EINVAL),
+    (dict(lse=FAKE), dict(work=None), fb.FB_EINVAL),
+    (dict(lse=FAKE), dict(work=FAKE + 16), fb.FB_EINVAL),              # workspace not 256-byte aligned
+    (dict(lse=FAKE), dict(work_bytes=128), fb.FB_EINVAL),              # workspace too small (256 needed)
+    (dict(lse=FAKE), dict(R=8, dphi_k=FAKE + 8), fb.FB_EINVAL),        # dphi not 16-byte aligned
+    (dict(lse=FAKE), dict(R=8, sdphi=(0, 0, 10)), fb.FB_EINVAL),       # dphi row stride not 4 floats
     (dict(lse=FAKE), dict(dv=FAKE + 8), fb.FB_EINVAL),
     (dict(lse=FAKE), dict(sdk=(4096, 64, 60)), fb.FB_EINVAL),
 ])
@@ -207,7 +212,21 @@ def test_backward_validation(kw, bkw, code):
 
 
 def test_backward_empty_is_noop():
-    assert _bwd(_args(N=0, q=None, k=None, v=None, o=None), dq=None, delta=None) == fb.FB_OK
+    assert _bwd(_args(N=0, q=None, k=None, v=None, o=None), dq=None, work=None) == fb.FB_OK
+
+
+def test_backward_workspace_bytes():
+    """Delta ([B][H][N] fp32), then one [B][H][N][R] fp32 partial per factor gradient that is
+    summed over an axis of size > 1 (0 stride); every part rounded up to 256 bytes."""
+    ws = fb.fb_attn_bwd_workspace_bytes
+    up = lambda x: -(-x // 256) * 256
+    full = (3 * 100 * 8, 100 * 8, 8)
+    assert ws(2, 3, 100, 0) == up(2 * 3 * 100 * 4)
+    assert ws(2, 3, 100, 8, (0, 0, 8), full) == up(2400) + up(2 * 3 * 100 * 8 * 4)
+    assert ws(2, 3, 100, 8, (0, 800, 8), (2400, 0, 8)) == up(2400) + 2 * up(19200)
+    assert ws(2, 3, 100, 8, full, full) == up(2400)                   # per-(b, h) factors: written directly
+    assert ws(1, 1, 100, 8, (0, 0, 8), (0, 0, 8)) == up(400)          # one (b, h): nothing to sum
+    assert ws(0, 3, 100, 8) == 0 and ws(-1, 3, 100, 8) == 0
 
 
 def test_alibi_in_kernel_validation():
