@@ -8,47 +8,57 @@
 namespace fb {
 namespace {
 
-// One thread per (b, h, n) row: D / 8 chunks of dO and O, fp32 products summed in order.
-template <typename T>
+// D / 8 threads per (b, h, n) row, one 16-byte chunk of dO and O each: fp32 products of the
+// chunk, then a butterfly over the row's threads (fixed order); whole waves read whole rows.
+template <typename T, int TPR>
 __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ o, int64_t so0, int64_t so1, int64_t so2,
                                                     const T* __restrict__ d, int64_t sd0, int64_t sd1, int64_t sd2,
-                                                    int B, int H, int N, int D, float* __restrict__ delta) {
+                                                    int B, int H, int N, float* __restrict__ delta) {
   typedef T T8 __attribute__((ext_vector_type(8)));
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   const int64_t rows = (int64_t)B * H * N;
-  for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < rows; r += (int64_t)gridDim.x * blockDim.x) {
+  const int sub = threadIdx.x % TPR;
+  const int64_t step = (int64_t)gridDim.x * (blockDim.x / TPR);
+  // the row loop is uniform over a row's TPR threads, so each butterfly sees its whole row
+  for (int64_t r = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / TPR; r < rows; r += step) {
     const int n = (int)(r % N);
     const int64_t bh = r / N;
     const int h = (int)(bh % H), b = (int)(bh / H);
-    const T* orow = o + b * so0 + h * so1 + n * so2;
-    const T* drow = d + b * sd0 + h * sd1 + n * sd2;
+    const T8 a = __builtin_bit_cast(T8, *(const u32x4*)(o + b * so0 + h * so1 + n * so2 + 8 * sub));
+    const T8 g = __builtin_bit_cast(T8, *(const u32x4*)(d + b * sd0 + h * sd1 + n * sd2 + 8 * sub));
     float acc = 0.f;
-    for (int c = 0; c < D; c += 8) {
-      const T8 a = __builtin_bit_cast(T8, *(const u32x4*)(orow + c));
-      const T8 g = __builtin_bit_cast(T8, *(const u32x4*)(drow + c));
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc += (float)a[j] * (float)g[j];
-    }
-    delta[r] = acc;
+    for (int j = 0; j < 8; ++j) acc += (float)a[j] * (float)g[j];
+#pragma unroll
+    for (int m = TPR / 2; m >= 1; m /= 2) acc += __shfl_xor(acc, m, TPR);
+    if (sub == 0) delta[r] = acc;
   }
 }
 
-// One thread per output element: the partials of the (b, h) pairs it gathers, b outer.
+// One thread per four consecutive output columns: the partials of the (b, h) pairs it
+// gathers, b outer, h inner (16-byte loads and stores; R and the output strides are
+// multiples of 4).
 __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ part, int B, int H, int N, int R,
                                                      int Bo, int Ho, float* __restrict__ out, int64_t s0, int64_t s1,
                                                      int64_t s2) {
-  const int64_t total = (int64_t)Bo * Ho * N * R;
-  const int64_t hstride = (int64_t)N * R, bstride = (int64_t)H * hstride;
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const int R4 = R / 4;
+  const int64_t plane = (int64_t)N * R4;            // float4s per (b, h)
+  const int64_t total = (int64_t)Bo * Ho * plane;
+  const f32x4* p4 = (const f32x4*)part;
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t nr = t % hstride;
-    const int64_t bh = t / hstride;
+    const int64_t nr = t % plane;
+    const int64_t bh = t / plane;
     const int ho = (int)(bh % Ho), bo = (int)(bh / Ho);
     const int b0 = Bo == 1 ? 0 : bo, b1 = Bo == 1 ? B : bo + 1;
     const int h0 = Ho == 1 ? 0 : ho, h1 = Ho == 1 ? H : ho + 1;
-    float acc = 0.f;
-    for (int b = b0; b < b1; ++b)
-      for (int h = h0; h < h1; ++h) acc += part[b * bstride + h * hstride + nr];
-    out[bo * s0 + ho * s1 + (nr / R) * s2 + nr % R] = acc;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int b = b0; b < b1; ++b) {
+#pragma unroll 4
+      for (int h = h0; h < h1; ++h) acc += p4[((int64_t)b * H + h) * plane + nr];
+    }
+    const int n = (int)(nr / R4), c = (int)(nr % R4) * 4;
+    *(f32x4*)(out + bo * s0 + ho * s1 + n * s2 + c) = acc;
   }
 }
 
@@ -59,12 +69,20 @@ int grid_for(int64_t work) { return (int)std::min<int64_t>((work + 255) / 256, 8
 fb_status launch_attention_bwd_delta(fb_dtype dt, const void* o, const int64_t so[3], const void* dout,
                                      const int64_t sdo[3], int B, int H, int N, int D, float* delta, hipStream_t s) {
   const int64_t rows = (int64_t)B * H * N;
-  if (dt == FB_BF16)
-    hipLaunchKernelGGL((delta_kernel<__bf16>), dim3(grid_for(rows)), dim3(256), 0, s, (const __bf16*)o, so[0], so[1],
-                       so[2], (const __bf16*)dout, sdo[0], sdo[1], sdo[2], B, H, N, D, delta);
+  const int tpr = D / 8;   // D in {32, 64} (checked by the caller)
+  const dim3 grid(grid_for(rows * tpr));
+  if (dt == FB_BF16 && tpr == 8)
+    hipLaunchKernelGGL((delta_kernel<__bf16, 8>), grid, dim3(256), 0, s, (const __bf16*)o, so[0], so[1], so[2],
+                       (const __bf16*)dout, sdo[0], sdo[1], sdo[2], B, H, N, delta);
+  else if (dt == FB_BF16)
+    hipLaunchKernelGGL((delta_kernel<__bf16, 4>), grid, dim3(256), 0, s, (const __bf16*)o, so[0], so[1], so[2],
+                       (const __bf16*)dout, sdo[0], sdo[1], sdo[2], B, H, N, delta);
+  else if (tpr == 8)
+    hipLaunchKernelGGL((delta_kernel<_Float16, 8>), grid, dim3(256), 0, s, (const _Float16*)o, so[0], so[1], so[2],
+                       (const _Float16*)dout, sdo[0], sdo[1], sdo[2], B, H, N, delta);
   else
-    hipLaunchKernelGGL((delta_kernel<_Float16>), dim3(grid_for(rows)), dim3(256), 0, s, (const _Float16*)o, so[0],
-                       so[1], so[2], (const _Float16*)dout, sdo[0], sdo[1], sdo[2], B, H, N, D, delta);
+    hipLaunchKernelGGL((delta_kernel<_Float16, 4>), grid, dim3(256), 0, s, (const _Float16*)o, so[0], so[1], so[2],
+                       (const _Float16*)dout, sdo[0], sdo[1], sdo[2], B, H, N, delta);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_error("attention backward preparation failed: %s", hipGetErrorString(e));
@@ -77,8 +95,8 @@ fb_status launch_attention_bwd_reduce(const float* part, int B, int H, int N, in
                                       const int64_t sout[3], hipStream_t s) {
   // an axis of the output with stride 0 has one position and gathers all of that axis
   const int Bo = sout[0] ? B : 1, Ho = sout[1] ? H : 1;
-  hipLaunchKernelGGL(reduce_kernel, dim3(grid_for((int64_t)Bo * Ho * N * R)), dim3(256), 0, s, part, B, H, N, R, Bo,
-                     Ho, out, sout[0], sout[1], sout[2]);
+  hipLaunchKernelGGL(reduce_kernel, dim3(grid_for((int64_t)Bo * Ho * N * (R / 4))), dim3(256), 0, s, part, B, H, N,
+                     R, Bo, Ho, out, sout[0], sout[1], sout[2]);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_error("factor-gradient reduction failed: %s", hipGetErrorString(e));
