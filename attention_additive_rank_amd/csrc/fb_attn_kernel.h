@@ -49,7 +49,7 @@
 //   * Workgroup ids are remapped so that the query blocks of one (b, h) run on
 //     one XCD (dispatch is round-robin over the 8 XCDs): their K'/V tiles are
 //     then shared in that XCD's L2.  Causal launches take the longest query
-//     blocks first.
+//     blocks first, over the whole grid.
 #pragma once
 
 #include "fb_internal.h"
@@ -310,8 +310,15 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   const int per = G >> 3, rem = G & 7;
   const int L = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
   int qb = L % p.nqb;
-  const int bh = L / p.nqb;
-  if (CAUSAL) qb = p.nqb - 1 - qb;
+  int bh = L / p.nqb;
+  if (CAUSAL) {
+    // longest first over the whole grid (dispatch order): all last query blocks, then the
+    // ones before; (b, h) fastest, so with B H a multiple of 8 each (b, h) stays on one
+    // XCD (hardware id mod 8) at every level
+    const int BH = p.B * p.H;
+    qb = p.nqb - 1 - wg / BH;
+    bh = wg % BH;
+  }
   const int hh = bh % p.H;
   const int bb = bh / p.H;
   const int N = p.N;
@@ -825,15 +832,22 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
     if (need_mask) {
 #pragma unroll
       for (int kb2 = 0; kb2 < NKB; ++kb2) {
-        const int j0 = kb + 32 * kb2 + 16 * hf;
-        int lim = N - j0;
-        if constexpr (CAUSAL) lim = min(lim, qrow + 1 - j0);
-        // One compare-select at a time: the scheduling fence keeps the compiler from
-        // hoisting all compares into simultaneously live scalar lane masks.
+        const int jb = kb + 32 * kb2;   // first key of the block (uniform)
+        if (CAUSAL && (jb >= N || jb > q0w + 31)) {
+          // every key of the block is past N or after every query of the wavefront
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          sacc[kb2][r] = r < lim ? sacc[kb2][r] : -INFINITY;
-          __builtin_amdgcn_sched_barrier(0);
+          for (int r = 0; r < 16; ++r) sacc[kb2][r] = -INFINITY;
+        } else if (!CAUSAL || jb + 32 > N || jb + 31 > q0w) {
+          const int j0 = jb + 16 * hf;
+          int lim = N - j0;
+          if constexpr (CAUSAL) lim = min(lim, qrow + 1 - j0);
+          // One compare-select at a time: the scheduling fence keeps the compiler from
+          // hoisting all compares into simultaneously live scalar lane masks.
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            sacc[kb2][r] = r < lim ? sacc[kb2][r] : -INFINITY;
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
     }
@@ -916,8 +930,12 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   auto step = [&](int t, unsigned char* kt, unsigned char* kn, unsigned char* vt,
                   unsigned char* vn) __attribute__((always_inline)) {
     const int kb = t * BN;
-    if constexpr (!CAUSAL && KW > 1) {
-      // past the last tile the scores of a stale buffer are computed and never used
+    if constexpr (KW > 1) {
+      // past the last tile the scores of a stale buffer are computed and never used.
+      // Causal: also the tiles past a wavefront's queries (near the diagonal) go through
+      // the same fused phase, with all-masked scores and P = 0: one code path (a second
+      // one costs registers) and no time lost, as the ping-pong keeps the wavefronts of
+      // a workgroup in step anyway.
       mma_phase(kn, kb + BN, vt);
     } else {
       if (t + 1 < nkt && active(t + 1)) qk(kn, kb + BN);
@@ -929,7 +947,7 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
       dma_tile(kbk, kbv, grp ? kn : kt, grp ? vt : vn, kbk < nkt * BN, kbv < nkt * BN);
     }
     if (!phk_fast && grp == 1 && t + 3 < nkt) phi_load(kb + 3 * BN);
-    if (t + 1 < nkt && active(t + 1)) softmax(t + 1);
+    if (t + 1 < nkt && (KW > 1 || active(t + 1))) softmax(t + 1);
     if (!phk_fast && grp == 1 && t + 3 < nkt) phi_store(kn);
     __syncthreads();
   };
