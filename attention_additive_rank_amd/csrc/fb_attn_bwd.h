@@ -120,7 +120,9 @@ __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // Workgroup order: dispatch is round-robin over the 8 XCDs, so hardware id x runs on XCD
 // x % 8; the logical id gives each XCD a contiguous range, which puts the blocks of one
-// (b, h) on one XCD, where they share the streamed tiles in its L2.
+// (b, h) on one XCD, where they share the streamed tiles in its L2.  Causal launches instead
+// go longest-first over the whole grid, (b, h) fastest (each (b, h) stays on one XCD when
+// B H is a multiple of 8).
 __device__ __forceinline__ int xcd_order(int x, int G) {
   const int xcd = x & 7, idx = x >> 3, per = G >> 3, rem = G & 7;
   return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
@@ -233,8 +235,12 @@ __global__ __launch_bounds__(BTH, 2) void attn_bwd_dkv_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, ln = lane & 31, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int L = xcd_order((int)blockIdx.x, (int)gridDim.x);
-  const int blk = L % p.nblk;   // causal: the first key blocks see the most query tiles
-  const int bh = L / p.nblk;
+  int blk = L % p.nblk, bh = L / p.nblk;
+  if (CAUSAL) {   // longest first over the grid: the first key blocks see the most query tiles
+    const int BH = p.B * p.H;
+    blk = (int)blockIdx.x / BH;
+    bh = (int)blockIdx.x % BH;
+  }
   const int hh = bh % p.H, bb = bh / p.H, N = p.N;
   const int kw0 = blk * kBwdRows + wave * 32;          // this wavefront's first key
   RegionAddr<T::KCH> ax, ay;
@@ -467,8 +473,12 @@ __global__ __launch_bounds__(BTH, 2) void attn_bwd_dq_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, ln = lane & 31, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int L = xcd_order((int)blockIdx.x, (int)gridDim.x);
-  const int blk = CAUSAL ? p.nblk - 1 - L % p.nblk : L % p.nblk;   // causal: longest first
-  const int bh = L / p.nblk;
+  int blk = L % p.nblk, bh = L / p.nblk;
+  if (CAUSAL) {   // longest first over the grid: the last query blocks see the most key tiles
+    const int BH = p.B * p.H;
+    blk = p.nblk - 1 - (int)blockIdx.x / BH;
+    bh = (int)blockIdx.x % BH;
+  }
   const int hh = bh % p.H, bb = bh / p.H, N = p.N;
   const int qw0 = blk * kBwdRows + wave * 32;
   const int qrow = qw0 + ln;
