@@ -20,7 +20,7 @@
 // so that output register r of lane half h is row 16h + r; transposed A operands come
 // from ds_read_b64_tr_b16 with k-slot j of half h in k-step u = row 16h + 8u + j, which
 // matches the register order of P / dS used as B operands.  Tiles arrive by direct
-// global->LDS loads (1 KB of consecutive rows per load) one tile ahead, double-buffered.
+// global->LDS loads (1 KB of consecutive rows per load) two tiles ahead, in three buffers.
 #pragma once
 
 #include "fb_attn_kernel.h"

@@ -493,6 +493,8 @@ BWD = [
     (1, 1, 64, 64, 16, "shared", "bf16", "f16", True),
     (1, 2, 17, 32, 8, "shared", "f16", "f16", False),
     (1, 1, 1000, 64, 64, "shared", "bf16", "f16", True),
+    # a per-head factor shared over three batches: gradient summed over the batch axis only
+    (3, 2, 150, 64, 16, "head", "bf16", "f16", False),
 ]
 
 
