@@ -108,6 +108,8 @@ def main():
     ap.add_argument("--workload", default="sandwich", choices=["sandwich", "gpt2_alibi_causal", "mulbias_cos"])
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of CPU oracle work (0 = skip)")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-bias baseline")
+    ap.add_argument("--cold-launches", type=int, default=21,
+                    help="launches timed one by one after a cache flush (median reported; 0 = skip)")
     ap.add_argument("--alibi-jit", action="store_true",
                     help="ALiBi workloads: factors formed inside the kernel (fb_attn_fwd_alibi), no factor step")
     ap.add_argument("--backward", action="store_true",
@@ -207,6 +209,26 @@ def main():
     step_ms = t_start.elapsed_time(t_stop) / K
     kern_ms = sum(a.elapsed_time(b) for a, b in ev) / K
 
+    # cold caches: a 512 MiB scratch write before each launch evicts L2 and the Infinity
+    # Cache, so the kernel reads its inputs from HBM; median over the launches
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def cold_median(fn, n=args.cold_launches):
+        ts = []
+        for _ in range(n):
+            scratch.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return sorted(ts)[len(ts) // 2] if ts else None
+
+    cold_step_ms = cold_median(step)
+    e0 = stage1()
+    cold_kern_ms = cold_median(lambda: stage2(e0))
+
     F = flops(w)
     value = F / (step_ms * 1e-3) / 1e12
     kern_tflops = F / (kern_ms * 1e-3) / 1e12
@@ -229,9 +251,12 @@ def main():
         b.record(stream)
         torch.cuda.synchronize()
         dense_ms = a.elapsed_time(b) / K
+        dense_cold = cold_median(lambda: fb.fb_attn_fwd_densebias(q, k, v, bias, causal=w.causal, out=out))
         dense = {"ms": round(dense_ms, 4), "tflops": round(F / (dense_ms * 1e-3) / 1e12, 2),
+                 "cold_ms_median": round(dense_cold, 4) if dense_cold else None,
                  "bias_shape": list(bias.shape), "bias_bytes_unique": bias.numel() * bias.element_size()}
         del bias
+    del scratch
 
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib * (1 << 20) // 4
@@ -278,6 +303,10 @@ def main():
         "pct_mfma_peak": round(100.0 * value / peak, 2),
         "kernel_ms": round(kern_ms, 4),
         "kernel_tflops": round(kern_tflops, 2),
+        "cold": {"step_ms_median": round(cold_step_ms, 4) if cold_step_ms else None,
+                 "kernel_ms_median": round(cold_kern_ms, 4) if cold_kern_ms else None,
+                 "launches": args.cold_launches,
+                 "flush": "512 MiB scratch written before each launch (L2 and Infinity Cache evicted)"},
         "densebias": dense,
         "speedup_vs_densebias": round(dense["ms"] / step_ms, 3) if dense else None,
         "roofline": {"bound": "mfma", "achieved": round(kern_tflops, 2), "peak": peak, "unit": "TFLOP/s",
