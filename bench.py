@@ -57,8 +57,9 @@ def algorithmic_bytes(w, es: int, phi_es: int, phi_shared_over_heads: bool) -> f
     return qkvo + 2.0 * phi_rows * w.R * phi_es
 
 
-def cpu_oracle_baseline(w, budget_s: float):
-    """Time the fp64 oracle (numpy) on (b, h) pairs of the same workload until the budget is used."""
+def cpu_oracle_baseline(w, budget_s: float, factors=None):
+    """Time the fp64 oracle (numpy) on (b, h) pairs of the same workload until the budget is used.
+    ``factors``: per-head (phi_q, phi_k) [H, N, R] of a low-rank (SVD) workload."""
     import numpy as np
     import oracle
     import synth
@@ -78,6 +79,8 @@ def cpu_oracle_baseline(w, budget_s: float):
     elif w.bias == "sandwich":
         bias = oracle.sandwich_bias(w.N, w.C)
         bias_fn = lambda b, h: bias
+    elif factors is not None:
+        bias_fn = lambda b, h: oracle.lowrank_bias(factors[0][h], factors[1][h])
     else:
         slopes = oracle.alibi_slopes(w.H)
         bias_fn = lambda b, h: oracle.alibi_bias(slopes[h:h + 1], w.N)[0]
@@ -105,7 +108,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="sandwich", choices=["sandwich", "gpt2_alibi_causal", "mulbias_cos"])
+    ap.add_argument("--workload", default="sandwich",
+                    choices=["sandwich", "gpt2_alibi_causal", "mulbias_cos", "vision_svd", "pairformer_svd"])
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of CPU oracle work (0 = skip)")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-bias baseline")
     ap.add_argument("--cold-launches", type=int, default=21,
@@ -131,9 +135,20 @@ def main():
     fb.load()
     dev = torch.device("cuda:0")
     w = synth.workload(args.workload)
-    inp = synth.make_inputs(w, with_bias_source=False)
+    svd = w.bias in ("vision", "pairformer")
+    inp = synth.make_inputs(w, with_bias_source=svd)
     dt = {"bf16": torch.bfloat16, "f32": torch.float32}[w.dtype]
     q, k, v = (torch.from_numpy(inp[n]).to(dt).to(dev) for n in "qkv")
+    svd_info = None
+    if svd:
+        # static per-head biases: rank-R factors from the library's host SVD (offline, not
+        # timed); the dense-bias baseline streams the full [H, N, N] bias
+        import numpy as np
+        t0 = time.time()
+        fs = [fb.fb_svd_factors(inp["bias_src"][h], w.R, seed=h) for h in range(w.H)]
+        svd_info = {"seconds": round(time.time() - t0, 2), "energy_min": round(min(f["energy"] for f in fs), 6)}
+        svd_phi = [np.stack([f[n] for f in fs]) for n in ("phi_q", "phi_k")]
+        svd_bias = torch.from_numpy(inp["bias_src"]).to(dt).to(dev)
     del inp
     out = torch.empty_like(q)
     phi_dt = torch.float16 if w.dtype != "f32" else torch.float32
@@ -149,6 +164,8 @@ def main():
         fH, fC, R_used = 1, 0, w.R
     elif w.bias == "sandwich":
         fH, fC, R_used = 1, w.C, w.C * split * (split + 1) // 2
+    elif svd:
+        fH, fC, R_used = w.H, 0, w.R
     else:
         fH, fC, R_used = w.H, 0, 2 * split * (split + 1) // 2
     # factor rows padded with zero columns to a whole 16-byte chunk: the kernel then copies
@@ -156,8 +173,11 @@ def main():
     ce = 16 // (2 if phi_dt == torch.float16 else 4)
     R_cols = (R_used + ce - 1) // ce * ce
     if not mul:
-        pq = torch.empty((fH, w.N, R_cols), dtype=phi_dt, device=dev)
-        pk = torch.empty_like(pq)
+        pq = torch.zeros((fH, w.N, R_cols), dtype=phi_dt, device=dev)
+        pk = torch.zeros_like(pq)
+    if svd:
+        pq[..., :w.R] = torch.from_numpy(svd_phi[0]).to(phi_dt).to(dev)
+        pk[..., :w.R] = torch.from_numpy(svd_phi[1]).to(phi_dt).to(dev)
     stream = torch.cuda.current_stream(dev)
 
     jit = args.alibi_jit
@@ -166,7 +186,7 @@ def main():
 
     def stage1():
         """factor generation (additive) or operand expansion (multiplicative)"""
-        if jit:
+        if jit or svd:
             return None
         if mul:
             return fb.fb_mulbias_expand(q, k, phi, phi, workspace=ws)
@@ -239,6 +259,8 @@ def main():
     if not args.no_dense and not mul:
         if w.bias == "sandwich":
             bias = fb.fb_make_dense_bias("sandwich", 1, w.N, C=w.C, dtype=dt)
+        elif svd:
+            bias = svd_bias
         else:
             bias = fb.fb_make_dense_bias("alibi", w.H, w.N, dtype=dt)
         for _ in range(args.warmup):
@@ -256,6 +278,8 @@ def main():
                  "cold_ms_median": round(dense_cold, 4) if dense_cold else None,
                  "bias_shape": list(bias.shape), "bias_bytes_unique": bias.numel() * bias.element_size()}
         del bias
+    if svd:
+        del svd_bias
     del scratch
 
     if args.calib_copy_mib > 0:
@@ -278,7 +302,7 @@ def main():
 
     cpu = None
     if args.cpu_budget > 0:
-        cpu = cpu_oracle_baseline(w, args.cpu_budget)
+        cpu = cpu_oracle_baseline(w, args.cpu_budget, factors=svd_phi if svd else None)
 
     es = 2 if w.dtype != "f32" else 4
     rec = {
@@ -299,7 +323,8 @@ def main():
                    "factor_columns": R_used, "factor_columns_padded": R_cols,
                    "flops_per_step": F,
                    **({"bias_op": "multiplicative", "expanded_width": w.D * w.R} if mul else {}),
-                   **({"factors": "in-kernel (fb_attn_fwd_alibi)"} if jit else {})},
+                   **({"factors": "in-kernel (fb_attn_fwd_alibi)"} if jit else {}),
+                   **({"factors": "host SVD per head (fb_svd_factors, not timed)", "svd": svd_info} if svd else {})},
         "pct_mfma_peak": round(100.0 * value / peak, 2),
         "kernel_ms": round(kern_ms, 4),
         "kernel_tflops": round(kern_tflops, 2),
