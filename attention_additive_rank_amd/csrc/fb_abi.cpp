@@ -427,6 +427,9 @@ fb_status fb_attn_bwd_lowrank(const fb_attn_args* a, const void* phi_q, const vo
     if (a->N > 1 && st6[i][2] < a->D) FB_FAIL(FB_EINVAL, "%s: gradient row stride < D", fn);
     if (!strides_fit32(st6[i], a->N)) FB_FAIL(FB_EUNSUPPORTED, "%s: gradient strides exceed 32 bits", fn);
   }
+  // the streamed tiles (Q and dO; K and V) address 64 rows with 32-bit offsets
+  if (!tile_fits32(a->sq[2], es) || !tile_fits32(g->sdo[2], es))
+    FB_FAIL(FB_EUNSUPPORTED, "%s: a 64-row tile of Q or dO spans 2^31 bytes or more", fn);
   if ((uintptr_t)g->work & 255u) FB_FAIL(FB_EINVAL, "%s: workspace not 256-byte aligned", fn);
   if (R > 0 && (!g->sdphi_q || !g->sdphi_k)) FB_FAIL(FB_EINVAL, "%s: null factor-gradient strides", fn);
   const BwdWork wl = bwd_work_layout(a->B, a->H, a->N, R, g->sdphi_q, g->sdphi_k);
@@ -478,7 +481,8 @@ fb_status fb_attn_bwd_lowrank(const fb_attn_args* a, const void* phi_q, const vo
         g->sdphi_q[1] % 4 || g->sdphi_k[1] % 4 || g->sdphi_q[0] % 4 || g->sdphi_k[0] % 4)
       FB_FAIL(FB_EINVAL, "%s: dphi and its strides must be 16-byte aligned", fn);
     if (!strides_fit32(sphi_q, a->N) || !strides_fit32(sphi_k, a->N) || !strides_fit32(g->sdphi_q, a->N) ||
-        !strides_fit32(g->sdphi_k, a->N))
+        !strides_fit32(g->sdphi_k, a->N) || !tile_fits32(sphi_q[2], esize(phi_dt)) ||
+        !tile_fits32(sphi_k[2], esize(phi_dt)))
       FB_FAIL(FB_EUNSUPPORTED, "%s: factor strides exceed 32 bits", fn);
     p.phq = phi_q;
     p.phk = phi_k;

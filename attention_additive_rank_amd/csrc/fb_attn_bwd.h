@@ -192,12 +192,15 @@ struct DmaPlan {
       off[i] = (uint32_t)(row * stride2[r] + c * 16);
     }
   }
+  // clamp row: the last row if it lies in the tile, else one past the tile's rows (no row
+  // reaches it), so the 32-bit offsets stay within a tile
   __device__ __forceinline__ Bases bases(int r0, int N) const {
     Bases t;
+    const int last = min(N - 1 - r0, TR - 1);
 #pragma unroll
     for (int r = 0; r < 3; ++r) {
       t.b[r] = src[r] + (int64_t)r0 * stride2[r];
-      t.lim[r] = (uint32_t)((N - 1 - r0) * stride2[r] + cmax[r] * 16);
+      t.lim[r] = (uint32_t)(last * stride2[r] + cmax[r] * 16);
     }
     return t;
   }

@@ -205,6 +205,7 @@ def _bwd(a, R=0, phi_dt=fb.FB_BF16, pq=FAKE, pk=FAKE, s=(0, 0, 64), **gk):
     (dict(lse=FAKE), dict(R=8, sdphi=(0, 0, 10)), fb.FB_EINVAL),       # dphi row stride not 4 floats
     (dict(lse=FAKE), dict(dv=FAKE + 8), fb.FB_EINVAL),
     (dict(lse=FAKE), dict(sdk=(4096, 64, 60)), fb.FB_EINVAL),
+    (dict(lse=FAKE), dict(sdo=(1 << 30, 1 << 30, 1 << 24)), fb.FB_EUNSUPPORTED),   # a dO tile spans 2^31 bytes
 ])
 def test_backward_validation(kw, bkw, code):
     assert _bwd(_args(**kw), **bkw) == code
