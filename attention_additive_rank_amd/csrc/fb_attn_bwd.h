@@ -128,16 +128,6 @@ __device__ __forceinline__ int xcd_order(int x, int G) {
   return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
 }
 
-// v[i] = w of lane i of the caller's 16-lane row (DPP row broadcast), i = 0..15
-template <int I = 0>
-__device__ __forceinline__ void row_bcast16(f32x16& v, float w) {
-  if constexpr (I < 16) {
-    v[I] = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, w), 0x150 + I, 0xF, 0xF,
-                                                                 false));
-    row_bcast16<I + 1>(v, w);
-  }
-}
-
 // Direct global -> LDS loads of the backward tiles, written as inline asm: the compiler's
 // own wait bookkeeping, which cannot tell the three tile buffers apart, would otherwise
 // wait for every outstanding copy (vmcnt 0) and for every LDS read (lgkmcnt 0) before the
