@@ -595,3 +595,55 @@ def test_alibi_in_kernel_full_size_sampled(fb):
         ro, _ = oracle.attention(inp["q"][b:b + 1, h:h + 1], inp["k"][b:b + 1, h:h + 1], inp["v"][b:b + 1, h:h + 1],
                                  bias=oracle.alibi_bias(m[h:h + 1], w.N), causal=True, rows=rows)
         assert_close(to_np(o[b, h])[rows][None, None], ro, "bf16", f"in-kernel ALiBi b={b} h={h}")
+
+
+# ------------------------------------------------------- seeded random sweep ----
+def _sweep_configs(n=16, seed=20260200):
+    """Small random configurations across the supported space (shapes, ranks, factor
+    shapes, dtypes, causal), drawn once from a fixed seed."""
+    r = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        D = int(r.choice([32, 64]))
+        R = int(r.choice([0, 8, 16, 24, 40, 64]))
+        N = int(r.integers(1, 330))
+        B, H = int(r.integers(1, 4)), int(r.integers(1, 4))
+        fs = str(r.choice(["shared", "head", "full"]))
+        dt = str(r.choice(["bf16", "f16"]))
+        pdt = "f16" if dt == "f16" else str(r.choice(["bf16", "f16"]))
+        out.append((B, H, N, D, R, fs, dt, pdt, bool(r.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("B,H,N,D,R,fs,dt,pdt,causal", _sweep_configs(), ids=[f"sweep-{i}" for i in range(16)])
+def test_random_sweep_forward_and_backward(fb, B, H, N, D, R, fs, dt, pdt, causal):
+    """Forward output and LSE, then all gradients, against the oracle on the same rounded
+    inputs, for a seeded random configuration."""
+    import torch
+    r = np.random.default_rng(900 + B * 1000 + H * 100 + N + R)
+    q, k, v, do = (synth.round_to(r.standard_normal((B, H, N, D)) * 0.5, dt) for _ in range(4))
+    shape = {"shared": (N, R), "head": (H, N, R), "full": (B, H, N, R)}[fs]
+    pq = pk = None
+    if R:
+        pq = synth.round_to(r.standard_normal(shape) * 0.4, pdt)
+        pk = synth.round_to(r.standard_normal(shape) * 0.4, pdt)
+    qd, kd, vd, dod = (to_dev(x, dt) for x in (q, k, v, do))
+    pqd = to_dev(pq, pdt) if R else None
+    pkd = to_dev(pk, pdt) if R else None
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda:0")
+    o = fb.fb_attn_fwd_lowrank(qd, kd, vd, pqd, pkd, causal=causal, lse=lse)
+    dq, dk, dv, gpq, gpk = fb.fb_attn_bwd_lowrank(qd, kd, vd, o, lse, dod, pqd, pkd, causal=causal)
+    torch.cuda.synchronize()
+    bias = oracle.lowrank_bias(pq, pk) if R else None
+    ro, rl = oracle.attention(q, k, v, bias=bias, causal=causal)
+    assert_close(to_np(o), ro, dt, f"O {B}x{H}x{N} D={D} R={R} {fs} {dt}/{pdt} causal={causal}")
+    np.testing.assert_allclose(lse.cpu().double().numpy(), rl, rtol=0, atol=2e-2)
+    rq, rk, rv, db = oracle.attention_backward(q, k, v, do, bias=bias, causal=causal)
+    for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        assert_grad_close(to_np(got), ref, name)
+    if R:
+        full_q = np.broadcast_to(pq, (B, H, N, R)) if pq.ndim < 4 else pq
+        full_k = np.broadcast_to(pk, (B, H, N, R)) if pk.ndim < 4 else pk
+        rgq, rgk = oracle.lowrank_factor_grads(db, full_q, full_k)
+        assert_grad_close(gpq.cpu().double().numpy(), _sum_to(rgq, shape), "dphi_q")
+        assert_grad_close(gpk.cpu().double().numpy(), _sum_to(rgk, shape), "dphi_k")
