@@ -217,7 +217,7 @@ def attention_mulbias(q: np.ndarray, k: np.ndarray, v: np.ndarray, bias: BiasLik
 
 
 def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, bias: BiasLike = None,
-                       scale: Optional[float] = None, causal: bool = False):
+                       scale: Optional[float] = None, causal: bool = False, o_stored: Optional[np.ndarray] = None):
     """Gradients of ``O = softmax(s Q K^T + b) V`` for an upstream gradient ``dO``, fp64.
 
     The textbook chain rule, per (b,h), with nothing fused or reordered:
@@ -226,6 +226,10 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarr
     Jacobian); dQ = s dL K; dK = s dL^T Q; db = dL (the gradient with respect to the
     bias matrix; masked entries get 0).  The training use of the bias factors is the
     rebuttal's (answer to Reviewer UJUf, Q1: Sandwich bias in GPT-2 training).
+    ``o_stored``: when given, the row term sum_k P_ik dP_ik is taken as rowsum(dO * O) with
+    this O (the two are equal for the exact O, since sum_k P_ik dP_ik = sum_d dO_id O_id);
+    a backward that receives the forward's stored output, rounded to the input dtype, uses
+    that form.
     Returns ``(dq, dk, dv, db)`` with ``db`` ``[B,H,N,N]``.
     """
     q = np.asarray(q, dtype=np.float64)
@@ -248,7 +252,11 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarr
             P = P / P.sum(axis=1, keepdims=True)
             dv[b, h] = P.T @ do[b, h]
             dP = do[b, h] @ v[b, h].T
-            dL = P * (dP - np.sum(P * dP, axis=1, keepdims=True))
+            if o_stored is None:
+                row = np.sum(P * dP, axis=1, keepdims=True)
+            else:
+                row = np.sum(do[b, h] * np.asarray(o_stored[b, h], dtype=np.float64), axis=1, keepdims=True)
+            dL = P * (dP - row)
             dq[b, h] = s * (dL @ k[b, h])
             dk[b, h] = s * (dL.T @ q[b, h])
             db[b, h] = dL

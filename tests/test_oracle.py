@@ -464,3 +464,25 @@ def test_backward_invariants():
     _, _, dv, db = oracle.attention_backward(q, k, v, do, bias=r.standard_normal((7, 7)), causal=True)
     np.testing.assert_allclose(db.sum(axis=-1), 0.0, atol=1e-13)
     np.testing.assert_allclose(dv.sum(axis=2), do.sum(axis=2), atol=1e-12)
+
+
+def test_backward_stored_output_form():
+    """The row term as rowsum(dO * O) with the exact O (computed here by the forward
+    oracle) gives the same gradients as sum_k P_ik dP_ik (the identity
+    sum_k P_ik (dO V^T)_ik = sum_d dO_id (P V)_id); with a perturbed O the gradients move
+    by exactly P (dO . dO_err) terms, so the option is really used."""
+    r = np.random.default_rng(64)
+    q, k, v, do = (r.standard_normal((2, 2, 9, 4)) for _ in range(4))
+    bias = r.standard_normal((9, 9))
+    o, _ = oracle.attention(q, k, v, bias=bias, causal=True)
+    a = oracle.attention_backward(q, k, v, do, bias=bias, causal=True)
+    b = oracle.attention_backward(q, k, v, do, bias=bias, causal=True, o_stored=o)
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(y, x, rtol=0, atol=1e-12)
+    e = 1e-3 * r.standard_normal(o.shape)
+    _, _, dv2, db2 = oracle.attention_backward(q, k, v, do, bias=bias, causal=True, o_stored=o + e)
+    np.testing.assert_allclose(dv2, a[2], atol=1e-15)              # dV does not involve the row term
+    P = db2 - a[3]                                                 # = -P * rowsum(dO * e)
+    shift = np.sum(do * e, axis=-1, keepdims=True)
+    P0 = np.where(np.abs(shift) > 0, -P / shift, 0.0)              # recovers P, rows sum to 1
+    np.testing.assert_allclose(P0.sum(axis=-1), 1.0, atol=1e-9)
