@@ -20,8 +20,8 @@ import numpy as np
 
 __all__ = [
     "FbError", "load", "library_path", "fb_status_str", "fb_last_error",
-    "fb_make_factors", "fb_make_dense_bias", "fb_svd_factors",
-    "fb_attn_fwd_lowrank", "fb_attn_fwd_densebias",
+    "fb_make_factors", "fb_make_factors_log2", "fb_make_dense_bias", "fb_svd_factors",
+    "fb_attn_fwd_lowrank", "fb_attn_fwd_lowrank_log2", "fb_attn_fwd_densebias",
     "FB_ALIBI", "FB_SANDWICH", "factor_columns",
 ]
 
@@ -82,10 +82,11 @@ def load():
         lib.fb_status_str.argtypes = [ctypes.c_int]
         lib.fb_last_error.restype = ctypes.c_char_p
         lib.fb_last_error.argtypes = []
-        lib.fb_make_factors.restype = ctypes.c_int
-        lib.fb_make_factors.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _DP, ctypes.c_int,
-                                        ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
-                                        ctypes.POINTER(ctypes.c_int), ctypes.c_void_p]
+        for fn in (lib.fb_make_factors, lib.fb_make_factors_log2):
+            fn.restype = ctypes.c_int
+            fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _DP, ctypes.c_int,
+                           ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                           ctypes.POINTER(ctypes.c_int), ctypes.c_void_p]
         lib.fb_make_dense_bias.restype = ctypes.c_int
         lib.fb_make_dense_bias.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _DP,
                                            ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
@@ -95,10 +96,10 @@ def load():
         lib.fb_svd_rank_for_energy.restype = ctypes.c_int
         lib.fb_svd_rank_for_energy.argtypes = [_DP, ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_uint64,
                                                ctypes.POINTER(ctypes.c_int), _DP, ctypes.POINTER(ctypes.c_int)]
-        lib.fb_attn_fwd_lowrank.restype = ctypes.c_int
-        lib.fb_attn_fwd_lowrank.argtypes = [ctypes.POINTER(_AttnArgs), ctypes.c_void_p, ctypes.c_void_p,
-                                            ctypes.c_int, ctypes.c_int, ctypes.POINTER(_I64x3),
-                                            ctypes.POINTER(_I64x3), ctypes.c_void_p]
+        for fn in (lib.fb_attn_fwd_lowrank, lib.fb_attn_fwd_lowrank_log2):
+            fn.restype = ctypes.c_int
+            fn.argtypes = [ctypes.POINTER(_AttnArgs), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                           ctypes.POINTER(_I64x3), ctypes.POINTER(_I64x3), ctypes.c_void_p]
         lib.fb_attn_bwd_lowrank.restype = ctypes.c_int
         lib.fb_attn_bwd_lowrank.argtypes = [ctypes.POINTER(_AttnArgs), ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_int, ctypes.c_int, ctypes.POINTER(_I64x3),
@@ -180,6 +181,18 @@ def fb_make_factors(kind, H: int, N: int, C: int = 0, slopes=None, dtype=None, s
                     R_pad: Optional[int] = None, phi_q=None, phi_k=None, device="cuda", stream=None):
     """Exact ALiBi / Sandwich factors on the GPU.  Returns ``(phi_q, phi_k, R_used)`` with
     ``phi_*`` of shape ``[H, N, R_pad]`` (allocated here if not given)."""
+    return _make_factors("fb_make_factors", kind, H, N, C, slopes, dtype, split, R_pad, phi_q, phi_k, device, stream)
+
+
+def fb_make_factors_log2(kind, H: int, N: int, C: int = 0, slopes=None, dtype=None, split: int = 1,
+                         R_pad: Optional[int] = None, phi_q=None, phi_k=None, device="cuda", stream=None):
+    """As :func:`fb_make_factors` with ``phi_q`` in exp2 units (times log2(e) before rounding),
+    the factors :func:`fb_attn_fwd_lowrank_log2` takes."""
+    return _make_factors("fb_make_factors_log2", kind, H, N, C, slopes, dtype, split, R_pad, phi_q, phi_k, device,
+                         stream)
+
+
+def _make_factors(entry, kind, H, N, C, slopes, dtype, split, R_pad, phi_q, phi_k, device, stream):
     torch = _torch()
     dtype = dtype or torch.bfloat16
     used = factor_columns(kind, C, split)
@@ -193,7 +206,7 @@ def fb_make_factors(kind, H: int, N: int, C: int = 0, slopes=None, dtype=None, s
             raise ValueError("phi_q / phi_k must be contiguous [H, N, R_pad]")
     keep, sp = _slopes_ptr(slopes)
     r_used = ctypes.c_int(0)
-    st = load().fb_make_factors(_kind_code(kind), H, N, C, sp, _dt_code(phi_q.dtype), split, phi_q.data_ptr(),
+    st = getattr(load(), entry)(_kind_code(kind), H, N, C, sp, _dt_code(phi_q.dtype), split, phi_q.data_ptr(),
                                 phi_k.data_ptr(), R_pad, ctypes.byref(r_used), _stream_ptr(phi_q.device, stream))
     _check(st)
     return phi_q, phi_k, r_used.value
@@ -297,13 +310,25 @@ def fb_attn_fwd_lowrank(q, k, v, phi_q=None, phi_k=None, *, causal: bool = False
     ``q, k, v``: ``[B, H, N, D]`` device tensors (fp32 / bf16 / fp16, contiguous last axis).
     ``phi_q, phi_k``: ``[..., N, R]`` broadcastable to ``[B, H, N, R]`` (or None for R = 0).
     ``scale`` defaults to 1/sqrt(D).  ``lse``: optional float32 ``[B, H, N]`` output."""
+    return _lowrank("fb_attn_fwd_lowrank", q, k, v, phi_q, phi_k, causal, scale, out, lse, stream)
+
+
+def fb_attn_fwd_lowrank_log2(q, k, v, phi_q=None, phi_k=None, *, causal: bool = False,
+                             scale: Optional[float] = None, out=None, lse=None, stream=None):
+    """O = softmax(scale * Q K^T + ln(2) phi_q phi_k^T) V: ``phi_q`` in exp2 units (as
+    :func:`fb_make_factors_log2` writes it); bf16 / fp16 only.  Otherwise as
+    :func:`fb_attn_fwd_lowrank`."""
+    return _lowrank("fb_attn_fwd_lowrank_log2", q, k, v, phi_q, phi_k, causal, scale, out, lse, stream)
+
+
+def _lowrank(entry, q, k, v, phi_q, phi_k, causal, scale, out, lse, stream):
     torch = _torch()
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     a = _attn_args(q, k, v, out, lse, causal, scale)
     B, H, N, _ = q.shape
     if phi_q is None or phi_k is None or phi_q.shape[-1] == 0:
-        st = load().fb_attn_fwd_lowrank(ctypes.byref(a), None, None, a.dt, 0, None, None, _stream_ptr(q.device, stream))
+        st = getattr(load(), entry)(ctypes.byref(a), None, None, a.dt, 0, None, None, _stream_ptr(q.device, stream))
     else:
         if phi_q.shape[-1] != phi_k.shape[-1]:
             raise ValueError("phi_q and phi_k need the same rank")
@@ -311,9 +336,8 @@ def fb_attn_fwd_lowrank(q, k, v, phi_q=None, phi_k=None, *, causal: bool = False
             raise ValueError("phi_q / phi_k dtype or device mismatch")
         eq, sq = _bhn_strides(phi_q, B, H, N, "phi_q")
         ek, sk = _bhn_strides(phi_k, B, H, N, "phi_k")
-        st = load().fb_attn_fwd_lowrank(ctypes.byref(a), eq.data_ptr(), ek.data_ptr(), _dt_code(phi_q.dtype),
-                                        phi_q.shape[-1], ctypes.byref(sq), ctypes.byref(sk),
-                                        _stream_ptr(q.device, stream))
+        st = getattr(load(), entry)(ctypes.byref(a), eq.data_ptr(), ek.data_ptr(), _dt_code(phi_q.dtype),
+                                    phi_q.shape[-1], ctypes.byref(sq), ctypes.byref(sk), _stream_ptr(q.device, stream))
     _check(st)
     return out
 

@@ -159,9 +159,13 @@ const char* fb_status_str(fb_status st) {
 
 const char* fb_last_error(void) { return g_err; }
 
-fb_status fb_make_factors(fb_bias_kind kind, int H, int N, int C, const double* slopes_host, fb_dtype out_dt,
-                          int split, void* phi_q, void* phi_k, int R_pad, int* R_used, hipStream_t stream) {
-  const char* fn = "fb_make_factors";
+}  // extern "C"
+
+namespace {
+
+fb_status make_factors(const char* fn, double qscale, fb_bias_kind kind, int H, int N, int C,
+                       const double* slopes_host, fb_dtype out_dt, int split, void* phi_q, void* phi_k, int R_pad,
+                       int* R_used, hipStream_t stream) {
   if (kind != FB_ALIBI && kind != FB_SANDWICH) FB_FAIL(FB_EINVAL, "%s: unknown bias kind", fn);
   if (!known_dtype(out_dt)) FB_FAIL(FB_EINVAL, "%s: unknown dtype", fn);
   if (H < 1 || N < 1) FB_FAIL(FB_EINVAL, "%s: H and N must be >= 1", fn);
@@ -177,7 +181,24 @@ fb_status fb_make_factors(fb_bias_kind kind, int H, int N, int C, const double* 
   if (!aligned16(phi_q) || !aligned16(phi_k)) FB_FAIL(FB_EINVAL, "%s: factor pointers must be 16-byte aligned", fn);
   if ((int64_t)H * N * R_pad > (int64_t)1 << 40) FB_FAIL(FB_EUNSUPPORTED, "%s: too large", fn);
   return launch_make_factors(kind, H, N, C, kind == FB_ALIBI ? slopes_host : nullptr, out_dt, split, phi_q,
-                             phi_k, R_pad, r_nat, stream);
+                             phi_k, R_pad, r_nat, qscale, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+fb_status fb_make_factors(fb_bias_kind kind, int H, int N, int C, const double* slopes_host, fb_dtype out_dt,
+                          int split, void* phi_q, void* phi_k, int R_pad, int* R_used, hipStream_t stream) {
+  return make_factors("fb_make_factors", 1.0, kind, H, N, C, slopes_host, out_dt, split, phi_q, phi_k, R_pad,
+                      R_used, stream);
+}
+
+fb_status fb_make_factors_log2(fb_bias_kind kind, int H, int N, int C, const double* slopes_host, fb_dtype out_dt,
+                               int split, void* phi_q, void* phi_k, int R_pad, int* R_used, hipStream_t stream) {
+  // log2(e) = 1 / ln 2 in double
+  return make_factors("fb_make_factors_log2", 1.4426950408889634074, kind, H, N, C, slopes_host, out_dt, split,
+                      phi_q, phi_k, R_pad, R_used, stream);
 }
 
 fb_status fb_make_dense_bias(fb_bias_kind kind, int H, int N, int C, const double* slopes_host, fb_dtype out_dt,
@@ -247,11 +268,17 @@ fb_status fb_svd_rank_for_energy(const double* bias, int N, int R_max, double ta
   }
 }
 
-fb_status fb_attn_fwd_lowrank(const fb_attn_args* a, const void* phi_q, const void* phi_k, fb_dtype phi_dt,
-                              int R, const int64_t sphi_q[3], const int64_t sphi_k[3], hipStream_t stream) {
-  const char* fn = "fb_attn_fwd_lowrank";
+}  // extern "C"
+
+namespace {
+
+// Both low-rank forward entry points; log2 != 0: phi_q comes in exp2 units (mode 3).
+fb_status lowrank_forward(const char* fn, int log2, const fb_attn_args* a, const void* phi_q, const void* phi_k,
+                          fb_dtype phi_dt, int R, const int64_t sphi_q[3], const int64_t sphi_k[3],
+                          hipStream_t stream) {
   fb_status st = check_common(a, fn);
   if (st != FB_OK) return st;
+  if (log2 && a->dt == FB_F32) FB_FAIL(FB_EUNSUPPORTED, "%s: q/k/v must be bf16 or f16", fn);
   if (R < 0) FB_FAIL(FB_EINVAL, "%s: negative R", fn);
   const int maxR = a->dt == FB_F32 ? 32 : 128;
   if (R > maxR) FB_FAIL(FB_EUNSUPPORTED, "%s: R = %d above the limit %d", fn, R, maxR);
@@ -287,9 +314,23 @@ fb_status fb_attn_fwd_lowrank(const fb_attn_args* a, const void* phi_q, const vo
     else { if (RP == 48) RP = 64; else if (RP > 64) RP = 128; }
   }
   const fb_dtype aux = R > 0 ? phi_dt : a->dt;
-  st = dispatch_attention(0, a->dt, aux, a->D, RP, p, stream);
+  st = dispatch_attention(log2 ? 3 : 0, a->dt, aux, a->D, RP, p, stream);
   if (st == FB_EUNSUPPORTED) set_error("%s: no kernel for this dtype / rank combination", fn);
   return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+fb_status fb_attn_fwd_lowrank(const fb_attn_args* a, const void* phi_q, const void* phi_k, fb_dtype phi_dt,
+                              int R, const int64_t sphi_q[3], const int64_t sphi_k[3], hipStream_t stream) {
+  return lowrank_forward("fb_attn_fwd_lowrank", 0, a, phi_q, phi_k, phi_dt, R, sphi_q, sphi_k, stream);
+}
+
+fb_status fb_attn_fwd_lowrank_log2(const fb_attn_args* a, const void* phi_q, const void* phi_k, fb_dtype phi_dt,
+                                   int R, const int64_t sphi_q[3], const int64_t sphi_k[3], hipStream_t stream) {
+  return lowrank_forward("fb_attn_fwd_lowrank_log2", 1, a, phi_q, phi_k, phi_dt, R, sphi_q, sphi_k, stream);
 }
 
 size_t fb_mulbias_workspace_bytes(const fb_attn_args* a, int R) {

@@ -15,7 +15,7 @@ template <typename QT, typename PT, int D, int RP, int MODE, typename BT, bool P
 static fb_status launch_kernel(const AttnParams& p, hipStream_t stream) {
   const int64_t grid = (int64_t)p.nqb * p.H * p.B;
   // loader wavefronts where their register budget (three wavefronts on one SIMD) holds
-  constexpr bool LOADER = PHI_DMA && sizeof(QT) == 2 && D <= 64 && RP <= 64 && (MODE == 0 || sizeof(BT) == 2);
+  constexpr bool LOADER = PHI_DMA && sizeof(QT) == 2 && D <= 64 && RP <= 64 && (MODE != 1 || sizeof(BT) == 2);
   const dim3 block(LOADER ? NT + NLW * 64 : NT);
   if (p.flags & FLAG_CAUSAL)
     hipLaunchKernelGGL((attn_fwd_kernel<QT, PT, D, RP, MODE, BT, true, PHI_DMA, LOADER>), dim3((unsigned)grid), block, 0,
@@ -43,16 +43,16 @@ static fb_status launch_one(const AttnParams& p, hipStream_t stream) {
   return launch_kernel<QT, PT, D, RP, MODE, BT, true>(p, stream);
 }
 
-template <typename QT, typename PT, int D>
+template <typename QT, typename PT, int D, int MODE = 0>
 static fb_status lowrank_rp(int RP, const AttnParams& p, hipStream_t s) {
   if constexpr (sizeof(QT) == 2) {
     switch (RP) {
-      case 16: return launch_one<QT, PT, D, 16, 0, QT>(p, s);
-      case 32: return launch_one<QT, PT, D, 32, 0, QT>(p, s);
-      case 64: return launch_one<QT, PT, D, 64, 0, QT>(p, s);
-      case 128: return launch_one<QT, PT, D, 128, 0, QT>(p, s);
+      case 16: return launch_one<QT, PT, D, 16, MODE, QT>(p, s);
+      case 32: return launch_one<QT, PT, D, 32, MODE, QT>(p, s);
+      case 64: return launch_one<QT, PT, D, 64, MODE, QT>(p, s);
+      case 128: return launch_one<QT, PT, D, 128, MODE, QT>(p, s);
     }
-  } else {
+  } else if constexpr (MODE == 0) {
     switch (RP) {
       case 8: return launch_one<QT, PT, D, 8, 0, QT>(p, s);
       case 16: return launch_one<QT, PT, D, 16, 0, QT>(p, s);
@@ -75,7 +75,8 @@ static fb_status lowrank_rp(int RP, const AttnParams& p, hipStream_t s) {
 #endif
 
 // mode 0: low rank (RP = padded factor width, 0 = plain attention); mode 1: dense bias;
-// mode 2: ALiBi with in-kernel factors (16-bit Q/K/V).
+// mode 2: ALiBi with in-kernel factors (16-bit Q/K/V); mode 3: low rank with phi_q in
+// exp2 units (16-bit Q/K/V).
 fb_status FB_CAT3(launch_attention_d, FB_ATTN_D, FB_QT_NAME)(int mode, fb_dtype aux_dt, int RP,
                                                               const AttnParams& p, hipStream_t s) {
   using namespace attn;
@@ -106,7 +107,19 @@ fb_status FB_CAT3(launch_attention_d, FB_ATTN_D, FB_QT_NAME)(int mode, fb_dtype 
     return FB_EUNSUPPORTED;
 #endif
   }
+#if FB_ATTN_QT != 2
+  if (mode == 3 && RP == 0) return launch_one<QT, QT, D, 0, 3, QT>(p, s);
+#endif
   if (RP == 0) return launch_one<QT, QT, D, 0, 0, QT>(p, s);
+#if FB_ATTN_QT != 2
+  if (mode == 3) {
+#if FB_ATTN_QT == 0
+    if (aux_dt == FB_BF16) return lowrank_rp<QT, bf16_t, D, 3>(RP, p, s);
+#endif
+    if (aux_dt == FB_F16) return lowrank_rp<QT, f16_t, D, 3>(RP, p, s);
+    return FB_EUNSUPPORTED;
+  }
+#endif
 #if FB_ATTN_QT == 0
   if (aux_dt == FB_BF16) return lowrank_rp<QT, bf16_t, D>(RP, p, s);
   if (aux_dt == FB_F16) return lowrank_rp<QT, f16_t, D>(RP, p, s);

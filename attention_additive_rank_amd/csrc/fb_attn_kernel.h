@@ -77,6 +77,7 @@ static_assert(BM == kAttnBlockM, "host and kernel block sizes differ");
 constexpr int BN = 64;         // keys per LDS tile
 constexpr int NKB = BN / 32;   // 32-key blocks per tile
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
 constexpr float RESCALE_GAP = 8.0f / LOG2E;   // 2^8 in exp2 units, as a natural-log gap
 
 template <typename T> struct Elem;
@@ -256,6 +257,14 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   // query / key indices (the pages' in-kernel factor tiles, rebuttal answer to Reviewer
   // BRmd, Q2), one 16-wide f16 factor k-step, nothing read from memory for them
   constexpr bool JIT = MODE == 2;
+  // MODE 3: low rank with phi_q given in exp2 units (phi_q log2(e), rounded once where the
+  // factors are made; RP 0 is plain attention).  MODE 3 computes the scores in exp2 units
+  // with the running max already subtracted: Q s is rounded as Q s log2(e), and every score
+  // chain starts from an accumulator holding -M (M the running max in exp2 units), so the
+  // softmax applies exp2 to the MFMA result directly, one vector operation per score fewer.
+  // (Scaling general phi_q by log2(e) in the kernel would round it a second time and break
+  // factors that are exact by construction, such as split pieces.)
+  constexpr bool FOLD = Elem<QT>::KW > 1 && MODE == 3;
   static_assert(!JIT || (RP == 16 && sizeof(QT) == 2 && __is_same(PT, f16_t)), "in-kernel factors: 16-bit, RP 16");
   constexpr int KW = Elem<QT>::KW;        // k elements per lane per MFMA
   constexpr int KS = 2 * KW;              // k per MFMA
@@ -513,7 +522,7 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
 #pragma unroll
   for (int t = 0; t < QSTEPS; ++t) {
     if constexpr (KW == 1) qf[t] = scale_frag<QT>(Qp[qclamp * p.sq[2] + col32(t)], p.scale);
-    else qf[t] = scale_frag<QT>(ld16(Qp + qclamp * p.sq[2] + KS * t + KW * hf), p.scale);
+    else qf[t] = scale_frag<QT>(ld16(Qp + qclamp * p.sq[2] + KS * t + KW * hf), FOLD ? p.scale * LOG2E : p.scale);
   }
   // In-kernel ALiBi factors: with the slope m = m_hi + m_lo (two f16) and an index
   // x = x_hi + x_lo (x_hi a multiple of 2048, both exact in f16),
@@ -613,12 +622,15 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   float m_run = -INFINITY;
   float l_run = 0.f;      // row sum (vector-unit path)
+  float M2 = 0.f;                 // FOLD: running max in exp2 units
+  f32x16 minit = f32x16{};        // FOLD: -M2 in every register, the score chains' start
+  auto chain_init = [&]() __attribute__((always_inline)) { return FOLD ? minit : f32x16{}; };
   // Low-rank mode, 16-bit: the row sum of P rides on the matrix core as one more MFMA per
   // k-step, with an A operand whose row 0 is all ones (lane 0 of each half) and rows 1..31
   // zero: row 0 of lacc (register 0 of the lanes of half 0) is then sum_k P[k][query], and
   // the rescaling of O scales it too.  This takes 32 adds per tile off the vector unit.
   // (Dense-bias mode keeps the adds: its bias registers leave no room for lacc.)
-  constexpr bool MROW = KW > 1 && MODE != 1;
+  constexpr bool MROW = KW > 1 && MODE != 1 && !FOLD;
   f32x16 lacc = f32x16{};
   const uint32_t one2 = __is_same(QT, bf16_t) ? 0x3F803F80u : 0x3C003C00u;   // two 1.0 values of QT
   const u32x4 ones = ln == 0 ? u32x4{one2, one2, one2, one2} : u32x4{0u, 0u, 0u, 0u};
@@ -709,7 +721,7 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   // S^T = K'(t) Q'^T from the K' tile at sKt (first key kbt)
   auto qk = [&](const unsigned char* sKt, int kbt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb2 = 0; kb2 < NKB; ++kb2) sacc[kb2] = f32x16{};
+    for (int kb2 = 0; kb2 < NKB; ++kb2) sacc[kb2] = chain_init();
     if constexpr (KW == 1) {
 #pragma unroll
       for (int t4 = 0; t4 < QSTEPS / 4; ++t4)
@@ -788,7 +800,7 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
         }
       };
 #pragma unroll
-      for (int kb2 = 0; kb2 < NKB; ++kb2) sacc[kb2] = f32x16{};
+      for (int kb2 = 0; kb2 < NKB; ++kb2) sacc[kb2] = chain_init();
       issue(0);
       issue(1);
 #pragma unroll
@@ -857,6 +869,43 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb2][r]);
     mx = halves_max(mx);
+    if constexpr (FOLD) {
+      // scores are S log2(e) - M2; the first tile sets M2 to its max (key 0 is always
+      // visible, so that max is finite), later tiles move it when they exceed it by 8
+      const bool first = t == 0;
+      const bool grow = first || mx > 8.f;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float d = grow ? mx : 0.f;
+        if (!first) {
+          const float alpha = __builtin_amdgcn_exp2f(-d);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+          l_run *= alpha;
+        }
+        M2 += d;
+#pragma unroll
+        for (int kb2 = 0; kb2 < NKB; ++kb2) sacc[kb2] -= d;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) minit[r] = -M2;
+      }
+      typedef QT T8 __attribute__((ext_vector_type(8)));
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          T8 pb;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float e = __builtin_amdgcn_exp2f(sacc[kb2][8 * u + j]);
+            pb[j] = from_f32<QT>(e);
+            ls[j & 3] += e;
+          }
+          pfrag[kb2 * 2 + u] = __builtin_bit_cast(u32x4, pb);
+        }
+      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      return;
+    }
     const bool grow = mx > m_run + RESCALE_GAP;
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
       const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - mx) * LOG2E) : 1.f;  // 0 on the first tile
@@ -995,7 +1044,8 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
           *(T4*)(orow + d0) = v;
         }
       }
-    if (p.lse && hf == 0) p.lse[((int64_t)bb * p.H + hh) * N + qrow] = m_run + logf(l_tot);
+    if (p.lse && hf == 0)
+      p.lse[((int64_t)bb * p.H + hh) * N + qrow] = FOLD ? (M2 + __log2f(l_tot)) * LN2 : m_run + logf(l_tot);
   }
 }
 

@@ -70,7 +70,7 @@ __device__ __forceinline__ void pair_of(int idx, int& a, int& b) {
 
 template <typename T>
 __global__ void make_factors_kernel(fb_bias_kind kind, int H, int N, int C, Slopes slopes, int use_host,
-                                    int split, T* phq, T* phk, int R_pad, int R_nat) {
+                                    int split, T* phq, T* phk, int R_pad, int R_nat, double qscale) {
   const int64_t total = (int64_t)H * N * R_pad;
   const int npairs = split * (split + 1) / 2;
   const int R_used = R_nat * npairs;
@@ -95,7 +95,7 @@ __global__ void make_factors_kernel(fb_bias_kind kind, int H, int N, int C, Slop
         const double ang = (double)n * sandwich_freq(k, C);
         fq = fk = (c & 1) ? sin(ang) : cos(ang);
       }
-      vq = piece<T>(fq, a);
+      vq = piece<T>(fq * qscale, a);
       vk = piece<T>(fk, b);
     }
     phq[t] = exact_to<T>(vq);
@@ -141,22 +141,22 @@ int grid_for(int64_t total) {
 
 fb_status launch_make_factors(fb_bias_kind kind, int H, int N, int C, const double* slopes_host,
                               fb_dtype out_dt, int split, void* phq, void* phk, int R_pad, int R_nat,
-                              hipStream_t stream) {
+                              double qscale, hipStream_t stream) {
   const Slopes s = pack_slopes(slopes_host, H);
   const int use_host = slopes_host != nullptr;
   const int grid = grid_for((int64_t)H * N * R_pad);
   switch (out_dt) {
     case FB_F32:
       hipLaunchKernelGGL(make_factors_kernel<float>, dim3(grid), dim3(256), 0, stream, kind, H, N, C, s,
-                         use_host, split, (float*)phq, (float*)phk, R_pad, R_nat);
+                         use_host, split, (float*)phq, (float*)phk, R_pad, R_nat, qscale);
       break;
     case FB_BF16:
       hipLaunchKernelGGL(make_factors_kernel<__bf16>, dim3(grid), dim3(256), 0, stream, kind, H, N, C, s,
-                         use_host, split, (__bf16*)phq, (__bf16*)phk, R_pad, R_nat);
+                         use_host, split, (__bf16*)phq, (__bf16*)phk, R_pad, R_nat, qscale);
       break;
     case FB_F16:
       hipLaunchKernelGGL(make_factors_kernel<_Float16>, dim3(grid), dim3(256), 0, stream, kind, H, N, C, s,
-                         use_host, split, (_Float16*)phq, (_Float16*)phk, R_pad, R_nat);
+                         use_host, split, (_Float16*)phq, (_Float16*)phk, R_pad, R_nat, qscale);
       break;
     default:
       return FB_EUNSUPPORTED;

@@ -62,7 +62,7 @@ fb_status launch_attention_d128_f32(int mode, fb_dtype aux_dt, int RP, const Att
 constexpr int kMaxSlopes = 256;
 fb_status launch_make_factors(fb_bias_kind kind, int H, int N, int C, const double* slopes_host,
                               fb_dtype out_dt, int split, void* phq, void* phk, int R_pad, int R_nat,
-                              hipStream_t stream);
+                              double qscale, hipStream_t stream);
 
 fb_status launch_make_dense_bias(fb_bias_kind kind, int H, int N, int C, const double* slopes_host,
                                  fb_dtype out_dt, void* bias, int64_t head_stride, int64_t row_stride,

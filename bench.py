@@ -2,8 +2,9 @@
 
 One step = the whole hot path over one batch of synthetic input, inputs already
 resident in HBM:
-  1. exact factor generation on the GPU (fb_make_factors), and
-  2. the fused low-rank-biased attention forward (fb_attn_fwd_lowrank).
+  1. exact factor generation on the GPU (fb_make_factors_log2: phi_q in exp2 units), and
+  2. the fused low-rank-biased attention forward (fb_attn_fwd_lowrank_log2)
+(fp32 workloads: fb_make_factors and fb_attn_fwd_lowrank, natural units).
 (--workload mulbias_cos, the multiplicative bias b_ij = cos(i - j) of rank 2: 1. the
 operand expansion fb_mulbias_expand, 2. the same fused kernel on the expanded operands.)
 Default workload: Sandwich-bias attention, B=4, H=8, N=4096, D=64, C=R=64, bf16
@@ -184,13 +185,17 @@ def main():
     if jit and w.bias != "alibi":
         raise SystemExit("--alibi-jit needs an ALiBi workload")
 
-    def stage1():
+    # exact biases in 16 bits: phi_q in exp2 units, so the kernel skips one operation per score
+    use_log2 = not (jit or mul or svd) and w.dtype != "f32"
+
+    def stage1(log2=use_log2):
         """factor generation (additive) or operand expansion (multiplicative)"""
         if jit or svd:
             return None
         if mul:
             return fb.fb_mulbias_expand(q, k, phi, phi, workspace=ws)
-        fb.fb_make_factors(w.bias, fH, w.N, C=fC, dtype=phi_dt, split=split, phi_q=pq, phi_k=pk)
+        make = fb.fb_make_factors_log2 if log2 else fb.fb_make_factors
+        make(w.bias, fH, w.N, C=fC, dtype=phi_dt, split=split, phi_q=pq, phi_k=pk)
         return None
 
     def stage2(e):
@@ -199,6 +204,8 @@ def main():
             fb.fb_attn_fwd_alibi(q, k, v, causal=w.causal, out=out)
         elif mul:
             fb.fb_attn_fwd_lowrank(e["q1"], e["k1"], v, e["phi_q"], e["phi_k"], causal=w.causal, scale=1.0, out=out)
+        elif use_log2:
+            fb.fb_attn_fwd_lowrank_log2(q, k, v, pq, pk, causal=w.causal, out=out)
         else:
             fb.fb_attn_fwd_lowrank(q, k, v, pq, pk, causal=w.causal, out=out)
 
@@ -340,7 +347,8 @@ def main():
                                            + 2.0 * w.B * w.H * w.N * (w.R - 1) * w.D * es) if mul else
                                           algorithmic_bytes(w, es, 2 if phi_dt == torch.float16 else 4,
                                                             w.bias == "sandwich"),
-                     "kernel": "attn_fwd_kernel (fb_attn_fwd_lowrank)"},
+                     "kernel": "attn_fwd_kernel (fb_attn_fwd_lowrank_log2)" if use_log2 else
+                               "attn_fwd_kernel (fb_attn_fwd_lowrank)"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
@@ -354,7 +362,7 @@ def bench_backward(args, w, fb, torch, q, k, v, pq_t, pk_t, stage1, out, dev, st
     more (the dQ kernel), which is not counted."""
     import numpy as np
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
-    stage1()                        # the factors, as the forward step makes them
+    stage1(False)                   # the factors, as the forward step makes them, in natural units
     fb.fb_attn_fwd_lowrank(q, k, v, pq_t, pk_t, causal=w.causal, out=out, lse=lse)
     g = np.random.default_rng(w.seed + 7).standard_normal(q.shape) * 0.5
     dout = torch.from_numpy(g).to(q.dtype).to(dev)

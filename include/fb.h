@@ -107,6 +107,17 @@ fb_status fb_make_factors(fb_bias_kind kind, int H, int N, int C, const double* 
                           int* R_used, hipStream_t stream);
 
 /*
+ * fb_make_factors_log2 -- as fb_make_factors, with phi_q in exp2 units: every
+ * phi_q value is multiplied by log2(e) in fp64 before it is split and rounded,
+ * so phi_q phi_k^T = b log2(e) (split pieces stay exact products).  These are the
+ * factors fb_attn_fwd_lowrank_log2 takes.  Arguments and errors as
+ * fb_make_factors.
+ */
+fb_status fb_make_factors_log2(fb_bias_kind kind, int H, int N, int C, const double* slopes_host,
+                               fb_dtype out_dt, int split, void* phi_q, void* phi_k, int R_pad,
+                               int* R_used, hipStream_t stream);
+
+/*
  * fb_make_dense_bias -- the same closed-form biases, materialised as a dense
  * [H][N][N] tensor (the input of the dense-bias baseline, fb_attn_fwd_densebias).
  * Computed in fp64 from the defining formula (ALiBi m_h (j - i); Sandwich the
@@ -216,6 +227,25 @@ typedef struct {
 fb_status fb_attn_fwd_lowrank(const fb_attn_args* a, const void* phi_q, const void* phi_k,
                               fb_dtype phi_dt, int R, const int64_t sphi_q[3],
                               const int64_t sphi_k[3], hipStream_t stream);
+
+/*
+ * fb_attn_fwd_lowrank_log2 -- the same attention with phi_q given in exp2 units:
+ *   O = softmax(s Q K^T + ln(2) phi_q phi_k^T) V,
+ * i.e. phi_q = log2(e) phi_q' for the factors phi_q' of fb_attn_fwd_lowrank
+ * (fb_make_factors_log2 writes them).  The kernel then works in exp2 units
+ * throughout (Q s is rounded as Q s log2(e); every score chain starts from the
+ * running max), which saves one vector operation per score in the softmax.
+ * The pages' formulation is unchanged (FlashBias rebuttal, answer to Reviewer UJUf,
+ * Q2: the factor columns are concatenated with queries and keys); only the unit of
+ * phi_q differs.
+ * Arguments, alignment and errors as fb_attn_fwd_lowrank, for bf16 / f16 Q/K/V
+ * only (FB_EUNSUPPORTED for fp32).  Numerics differ in two roundings: Q s log2(e)
+ * is rounded to dt, and the row sum of P is taken in fp32 before P is rounded.
+ * R == 0 is plain attention in the same exp2 form.
+ */
+fb_status fb_attn_fwd_lowrank_log2(const fb_attn_args* a, const void* phi_q, const void* phi_k,
+                                   fb_dtype phi_dt, int R, const int64_t sphi_q[3],
+                                   const int64_t sphi_k[3], hipStream_t stream);
 
 /*
  * fb_attn_fwd_densebias -- O = softmax(s Q K^T + b) V with b read as a dense

@@ -109,15 +109,16 @@ def exact_bias_oracle(w: synth.Workload):
     raise ValueError(w.bias)
 
 
-def device_exact_factors(w: synth.Workload, device="cuda:0"):
-    """fb_make_factors on the GPU for an exact-bias workload; returns (phi_q, phi_k) views
-    broadcastable to [B, H, N, R]."""
+def device_exact_factors(w: synth.Workload, device="cuda:0", log2: bool = False):
+    """fb_make_factors (log2: fb_make_factors_log2) on the GPU for an exact-bias workload;
+    returns (phi_q, phi_k) views broadcastable to [B, H, N, R]."""
     import attention_additive_rank_amd as fb
     dt, split = factor_plan(w)
+    make = fb.fb_make_factors_log2 if log2 else fb.fb_make_factors
     if w.bias == "alibi":
-        pq, pk, r = fb.fb_make_factors("alibi", w.H, w.N, dtype=tdtype(dt), split=split, device=device)
+        pq, pk, r = make("alibi", w.H, w.N, dtype=tdtype(dt), split=split, device=device)
         return pq, pk
-    pq, pk, r = fb.fb_make_factors("sandwich", 1, w.N, C=w.C, dtype=tdtype(dt), split=split, device=device)
+    pq, pk, r = make("sandwich", 1, w.N, C=w.C, dtype=tdtype(dt), split=split, device=device)
     return pq, pk
 
 
@@ -139,27 +140,37 @@ def oracle_svd_factors(w: synth.Workload, bias_src: np.ndarray, phi_dtype: str =
 class Case:
     """One workload prepared for both sides."""
 
-    def __init__(self, w: synth.Workload, device="cuda:0", rows: Optional[np.ndarray] = None):
+    def __init__(self, w: synth.Workload, device="cuda:0", rows: Optional[np.ndarray] = None, log2: bool = False):
+        """log2: the kernel gets phi_q in exp2 units (fb_attn_fwd_lowrank_log2); the oracle's
+        bias is unchanged for exact biases, and ln(2) phi_q phi_k^T of the very same rounded
+        factors for SVD workloads."""
         self.w = w
         self.device = device
         self.rows = rows
+        self.log2 = log2
         inp = synth.make_inputs(w)
         self.q, self.k, self.v = inp["q"], inp["k"], inp["v"]
         self.qd, self.kd, self.vd = (to_dev(x, w.dtype, device) for x in (self.q, self.k, self.v))
         if w.bias in ("alibi", "sandwich"):
             self.bias_ref = exact_bias_oracle(w)
-            self.phq, self.phk = device_exact_factors(w, device)
+            self.phq, self.phk = device_exact_factors(w, device, log2)
             self.energy = None
         else:
             pq, pk, self.energy = oracle_svd_factors(w, inp["bias_src"], "f16")
             self.bias_full = inp["bias_src"]
             self.pq_np, self.pk_np = pq, pk
-            self.bias_ref = lambda b, h: oracle.lowrank_bias(pq[h], pk[h])
-            self.phq, self.phk = to_dev(pq, "f16", device), to_dev(pk, "f16", device)
+            if log2:
+                pq2 = round_exact(pq * (1.0 / math.log(2.0)), "f16")
+                self.bias_ref = lambda b, h: math.log(2.0) * oracle.lowrank_bias(pq2[h], pk[h])
+                self.phq, self.phk = to_dev(pq2, "f16", device), to_dev(pk, "f16", device)
+            else:
+                self.bias_ref = lambda b, h: oracle.lowrank_bias(pq[h], pk[h])
+                self.phq, self.phk = to_dev(pq, "f16", device), to_dev(pk, "f16", device)
 
     def run_lowrank(self, **kw):
         import attention_additive_rank_amd as fb
-        return fb.fb_attn_fwd_lowrank(self.qd, self.kd, self.vd, self.phq, self.phk, causal=self.w.causal, **kw)
+        run = fb.fb_attn_fwd_lowrank_log2 if self.log2 else fb.fb_attn_fwd_lowrank
+        return run(self.qd, self.kd, self.vd, self.phq, self.phk, causal=self.w.causal, **kw)
 
     def reference(self, rows=None, bh=None):
         """Oracle output for all (b, h) or the listed pairs, restricted to `rows`."""

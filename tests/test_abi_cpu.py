@@ -68,9 +68,9 @@ def _args(**kw):
     return a
 
 
-def _lowrank(a, R=0, phi_dt=fb.FB_BF16, pq=FAKE, pk=FAKE, s=(0, 0, 64)):
+def _lowrank(a, R=0, phi_dt=fb.FB_BF16, pq=FAKE, pk=FAKE, s=(0, 0, 64), entry="fb_attn_fwd_lowrank"):
     sp = fb._I64x3(*s)
-    return fb.load().fb_attn_fwd_lowrank(ctypes.byref(a), pq, pk, phi_dt, R, ctypes.byref(sp), ctypes.byref(sp), None)
+    return getattr(fb.load(), entry)(ctypes.byref(a), pq, pk, phi_dt, R, ctypes.byref(sp), ctypes.byref(sp), None)
 
 
 def _dense(a, bias=FAKE, bdt=fb.FB_BF16, s=(0, 0, 64)):
@@ -94,6 +94,7 @@ def _dense(a, bias=FAKE, bdt=fb.FB_BF16, s=(0, 0, 64)):
 ])
 def test_attention_validation(kw, code):
     assert _lowrank(_args(**kw)) == code
+    assert _lowrank(_args(**kw), entry="fb_attn_fwd_lowrank_log2") == code
     assert fb.fb_last_error() != ""
     if kw.get("dt") is None:
         assert _dense(_args(**kw)) == code
@@ -115,6 +116,13 @@ def test_empty_inputs_are_noops():
 ])
 def test_lowrank_factor_validation(R, phi_dt, kw, code):
     assert _lowrank(_args(), R=R, phi_dt=phi_dt, **kw) == code
+    assert _lowrank(_args(), R=R, phi_dt=phi_dt, entry="fb_attn_fwd_lowrank_log2", **kw) == code
+
+
+def test_lowrank_log2_needs_16bit():
+    a = _args(dt=fb.FB_F32, D=32, strides=(2048, 1024, 32))
+    assert _lowrank(a, R=8, phi_dt=fb.FB_F32, entry="fb_attn_fwd_lowrank_log2") == fb.FB_EUNSUPPORTED
+    assert "bf16 or f16" in fb.fb_last_error()
 
 
 def test_lowrank_fp32_limits():
@@ -247,8 +255,10 @@ def test_alibi_in_kernel_validation():
 def test_make_factors_validation():
     lib = fb.load()
     r = ctypes.c_int(0)
-    call = lambda kind=0, H=2, N=16, C=0, dt=fb.FB_F16, split=1, pq=FAKE, pk=FAKE, R_pad=16: \
-        lib.fb_make_factors(kind, H, N, C, None, dt, split, pq, pk, R_pad, ctypes.byref(r), None)
+    call = lambda kind=0, H=2, N=16, C=0, dt=fb.FB_F16, split=1, pq=FAKE, pk=FAKE, R_pad=16, fn=lib.fb_make_factors: \
+        fn(kind, H, N, C, None, dt, split, pq, pk, R_pad, ctypes.byref(r), None)
+    assert call(fn=lib.fb_make_factors_log2, kind=5) == fb.FB_EINVAL
+    assert call(fn=lib.fb_make_factors_log2, split=2, R_pad=4) == fb.FB_EINVAL and r.value == 6
     assert call(kind=5) == fb.FB_EINVAL
     assert call(H=0) == fb.FB_EINVAL
     assert call(kind=1, C=3) == fb.FB_EINVAL

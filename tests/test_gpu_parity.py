@@ -134,6 +134,64 @@ def test_attention_parity_full_size_sampled(fb, name):
     assert_close(got, ro, w.dtype, f"{name} sampled O")
 
 
+LOG2 = [x for x in REDUCED if synth.workload(x[0], **x[1]).dtype != "f32"]
+
+
+@pytest.mark.parametrize("name,over", LOG2, ids=[f"{n}-{i}" for i, (n, _) in enumerate(LOG2)])
+def test_log2_factors_parity_reduced(fb, name, over):
+    """fb_attn_fwd_lowrank_log2 with phi_q in exp2 units (fb_make_factors_log2 for the exact
+    biases): every output element and LSE against the oracle, to the same bars."""
+    w = synth.workload(name, **over)
+    say(f"log2 parity {w}")
+    c = Case(w, log2=True)
+    import torch
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda:0")
+    o = c.run_lowrank(lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = c.reference()
+    assert_close(to_np(o), ro, w.dtype, f"{name} log2 O")
+    np.testing.assert_allclose(lse.cpu().double().numpy(), rl, rtol=0, atol=2e-2)
+
+
+@pytest.mark.parametrize("name", ["gpt2_alibi_causal", "sandwich"])
+def test_log2_factors_full_size_sampled(fb, name):
+    """The log2 entry point at full size, in the benchmark's launch; sampled rows of sampled
+    (b, h)."""
+    w = synth.workload(name)
+    rows = sample_rows(w.N, 48, seed=3)
+    c = Case(w, rows=rows, log2=True)
+    import torch
+    say(f"full-size log2 parity {name}: launch")
+    o = c.run_lowrank()
+    torch.cuda.synchronize()
+    bh = [(0, 0), (w.B - 1, w.H - 1), (w.B // 2, w.H // 2)]
+    ro, _ = c.reference(bh=bh)
+    got = np.stack([to_np(o[b, h])[rows] for (b, h) in bh])
+    assert_close(got, ro, w.dtype, f"{name} log2 sampled O")
+
+
+@pytest.mark.parametrize("kind,dt,split", [("sandwich", "f16", 1), ("alibi", "f16", 2), ("alibi", "bf16", 3)])
+def test_log2_factor_kernel(fb, kind, dt, split):
+    """fb_make_factors_log2: phi_q is the exact factor times log2(e), split and rounded like
+    fb_make_factors; phi_k is fb_make_factors' phi_k."""
+    H, N = (3, 700) if kind == "alibi" else (1, 1000)
+    say(f"log2 factors {kind} {dt} split={split}")
+    args = dict(C=64) if kind == "sandwich" else {}
+    q2, k2, r = fb.fb_make_factors_log2(kind, H, N, dtype=tdtype(dt), split=split, **args)
+    q1, k1, _ = fb.fb_make_factors(kind, H, N, dtype=tdtype(dt), split=split, **args)
+    np.testing.assert_array_equal(to_np(k2), to_np(k1))
+    if kind == "sandwich":
+        ref = oracle.sandwich_factors(N, 64)[None] / np.log(2.0)
+        assert np.all(np.abs(to_np(q2) - round_exact(ref, dt)) <= _ulp(ref, dt))
+    # the pieces' products reproduce log2(e) b
+    b = oracle.alibi_bias(oracle.alibi_slopes(H), N) if kind == "alibi" else oracle.sandwich_bias(N, 64)[None]
+    rec = oracle.lowrank_bias(to_np(q2)[:, :, :r], to_np(k2)[:, :, :r]) * np.log(2.0)
+    rec1 = oracle.lowrank_bias(to_np(q1)[:, :, :r], to_np(k1)[:, :, :r])
+    e2, e1 = np.abs(rec - b).max(), np.abs(rec1 - b).max()
+    say(f"  max |ln2 phi_q phi_k^T - b| = {e2:.3e} (fb_make_factors: {e1:.3e})")
+    assert e2 <= 2 * e1 + 1e-6
+
+
 def test_svd_approximation_error_reported(fb):
     """For SVD workloads the rank-R factors are an approximation: report it (not a bar)."""
     w = synth.workload("pairformer_svd", B=2, H=2, N=256)
@@ -207,6 +265,10 @@ def test_rank0_equals_densebias_zero(fb):
     assert np.all(np.abs(a - b) <= _ulp(np.maximum(np.abs(a), np.abs(b)), "bf16"))
     ro, _ = oracle.attention(c.q, c.k, c.v)
     assert_close(to_np(o1), ro, "bf16", "R=0")
+    # plain attention in the exp2 form (the log2 entry point without factors)
+    o3 = fb.fb_attn_fwd_lowrank_log2(c.qd, c.kd, c.vd)
+    torch.cuda.synchronize()
+    assert_close(to_np(o3), ro, "bf16", "R=0, exp2 form")
 
 
 # -------------------------------------------------------------- edge cases ---
