@@ -34,6 +34,9 @@ KERNEL_SOURCES = ["attention_additive_rank_amd/csrc/fb_attn_kernel.h",
                   "attention_additive_rank_amd/csrc/fb_attn_inst.hip"]
 
 
+LOG2E = 1.4426950408889634   # log2(e)
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
@@ -176,17 +179,17 @@ def main():
     if not mul:
         pq = torch.zeros((fH, w.N, R_cols), dtype=phi_dt, device=dev)
         pk = torch.zeros_like(pq)
-    if svd:
-        pq[..., :w.R] = torch.from_numpy(svd_phi[0]).to(phi_dt).to(dev)
-        pk[..., :w.R] = torch.from_numpy(svd_phi[1]).to(phi_dt).to(dev)
-    stream = torch.cuda.current_stream(dev)
-
     jit = args.alibi_jit
     if jit and w.bias != "alibi":
         raise SystemExit("--alibi-jit needs an ALiBi workload")
+    # 16-bit workloads take phi_q in exp2 units (phi_q log2(e), rounded once): the kernel then
+    # skips one operation per score.  SVD factors are scaled on the host, in fp64.
+    use_log2 = not (jit or mul or args.backward) and w.dtype != "f32"
+    if svd:
+        pq[..., :w.R] = torch.from_numpy(svd_phi[0] * (LOG2E if use_log2 else 1.0)).to(phi_dt).to(dev)
+        pk[..., :w.R] = torch.from_numpy(svd_phi[1]).to(phi_dt).to(dev)
+    stream = torch.cuda.current_stream(dev)
 
-    # exact biases in 16 bits: phi_q in exp2 units, so the kernel skips one operation per score
-    use_log2 = not (jit or mul or svd) and w.dtype != "f32"
 
     def stage1(log2=use_log2):
         """factor generation (additive) or operand expansion (multiplicative)"""
