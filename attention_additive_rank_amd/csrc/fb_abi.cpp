@@ -179,7 +179,7 @@ fb_status make_factors(const char* fn, double qscale, fb_bias_kind kind, int H, 
   if (R_pad < used) FB_FAIL(FB_EINVAL, "%s: R_pad %d < %d columns needed", fn, R_pad, used);
   if (!phi_q || !phi_k) FB_FAIL(FB_EINVAL, "%s: null factor pointer", fn);
   if (!aligned16(phi_q) || !aligned16(phi_k)) FB_FAIL(FB_EINVAL, "%s: factor pointers must be 16-byte aligned", fn);
-  if ((int64_t)H * N * R_pad > (int64_t)1 << 40) FB_FAIL(FB_EUNSUPPORTED, "%s: too large", fn);
+  if ((int64_t)H * N * R_pad > 0x7fffffffLL) FB_FAIL(FB_EUNSUPPORTED, "%s: H N R_pad must stay below 2^31", fn);
   return launch_make_factors(kind, H, N, C, kind == FB_ALIBI ? slopes_host : nullptr, out_dt, split, phi_q,
                              phi_k, R_pad, r_nat, qscale, stream);
 }

@@ -68,38 +68,57 @@ __device__ __forceinline__ void pair_of(int idx, int& a, int& b) {
   b = s - idx;
 }
 
+// One thread per (head, row, pair of natural columns): columns 2g and 2g+1 (Sandwich's cos and
+// sin of one angle, from one sincos; ALiBi's two columns for g = 0) with all their split
+// pieces, i.e. output columns [2g npairs, (2g+2) npairs); columns at or beyond R_used are
+// written as zero.  Index arithmetic is 32-bit (the host caps H N R_pad below 2^31).
 template <typename T>
 __global__ void make_factors_kernel(fb_bias_kind kind, int H, int N, int C, Slopes slopes, int use_host,
                                     int split, T* phq, T* phk, int R_pad, int R_nat, double qscale) {
-  const int64_t total = (int64_t)H * N * R_pad;
   const int npairs = split * (split + 1) / 2;
   const int R_used = R_nat * npairs;
-  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
-       t += (int64_t)gridDim.x * blockDim.x) {
-    const int col = (int)(t % R_pad);
-    const int64_t hn = t / R_pad;
-    const int n = (int)(hn % N);
-    const int h = (int)(hn / N);
-    double vq = 0.0, vk = 0.0;
-    if (col < R_used) {
-      const int c = col / npairs;
-      int a, b;
-      pair_of(col % npairs, a, b);
-      double fq, fk;
+  const int G = (R_pad + 2 * npairs - 1) / (2 * npairs);
+  const int total = H * N * G;
+  for (int64_t t64 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t64 < total;
+       t64 += (int64_t)gridDim.x * blockDim.x) {
+    const int t = (int)t64;
+    const int g = t % G;
+    const int hn = t / G;
+    const int n = hn % N;
+    const int h = hn / N;
+    double fq[2] = {0.0, 0.0}, fk[2] = {0.0, 0.0};
+    if (2 * g < R_nat) {
       if (kind == FB_ALIBI) {
         const double m = alibi_slope(slopes, use_host, h, H);
-        fq = (c == 0) ? 1.0 : (double)n;
-        fk = (c == 0) ? m * (double)n : -m;
+        fq[0] = 1.0;
+        fq[1] = (double)n;
+        fk[0] = m * (double)n;
+        fk[1] = -m;
       } else {
-        const int k = c / 2 + 1;
-        const double ang = (double)n * sandwich_freq(k, C);
-        fq = fk = (c & 1) ? sin(ang) : cos(ang);
+        double sn, cs;
+        sincos((double)n * sandwich_freq(g + 1, C), &sn, &cs);
+        fq[0] = fk[0] = cs;
+        fq[1] = fk[1] = sn;
       }
-      vq = piece<T>(fq * qscale, a);
-      vk = piece<T>(fk, b);
     }
-    phq[t] = exact_to<T>(vq);
-    phk[t] = exact_to<T>(vk);
+    T* rq = phq + (int64_t)hn * R_pad;
+    T* rk = phk + (int64_t)hn * R_pad;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      for (int pi = 0; pi < npairs; ++pi) {
+        const int col = (2 * g + u) * npairs + pi;
+        if (col >= R_pad) break;
+        double vq = 0.0, vk = 0.0;
+        if (col < R_used) {
+          int a, b;
+          pair_of(pi, a, b);
+          vq = piece<T>(fq[u] * qscale, a);
+          vk = piece<T>(fk[u], b);
+        }
+        rq[col] = exact_to<T>(vq);
+        rk[col] = exact_to<T>(vk);
+      }
+    }
   }
 }
 
@@ -144,7 +163,8 @@ fb_status launch_make_factors(fb_bias_kind kind, int H, int N, int C, const doub
                               double qscale, hipStream_t stream) {
   const Slopes s = pack_slopes(slopes_host, H);
   const int use_host = slopes_host != nullptr;
-  const int grid = grid_for((int64_t)H * N * R_pad);
+  const int split_pairs = split * (split + 1) / 2;
+  const int grid = grid_for((int64_t)H * N * ((R_pad + 2 * split_pairs - 1) / (2 * split_pairs)));
   switch (out_dt) {
     case FB_F32:
       hipLaunchKernelGGL(make_factors_kernel<float>, dim3(grid), dim3(256), 0, stream, kind, H, N, C, s,

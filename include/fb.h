@@ -100,6 +100,7 @@ const char* fb_last_error(void);
  * The values are computed in fp64 on the device and rounded to nearest even.
  * Errors: FB_EINVAL (null pointers, H or N < 1, odd or < 2 C for Sandwich,
  * split outside 1..3, R_pad < R_used, 16-byte-misaligned phi pointers);
+ * FB_EUNSUPPORTED (H * N * R_pad of 2^31 or more; more than 256 explicit slopes);
  * FB_EHIP.
  */
 fb_status fb_make_factors(fb_bias_kind kind, int H, int N, int C, const double* slopes_host,
