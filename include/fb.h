@@ -242,7 +242,9 @@ fb_status fb_attn_fwd_lowrank(const fb_attn_args* a, const void* phi_q, const vo
  * Arguments, alignment and errors as fb_attn_fwd_lowrank, for bf16 / f16 Q/K/V
  * only (FB_EUNSUPPORTED for fp32).  Numerics differ in two roundings: Q s log2(e)
  * is rounded to dt, and the row sum of P is taken in fp32 before P is rounded.
- * R == 0 is plain attention in the same exp2 form.
+ * R == 0 is plain attention in the same exp2 form.  LSE (when requested) is the
+ * natural-log value as for fb_attn_fwd_lowrank; fb_attn_bwd_lowrank takes natural-unit
+ * factors (phi_q ln(2) for the factors given here).
  */
 fb_status fb_attn_fwd_lowrank_log2(const fb_attn_args* a, const void* phi_q, const void* phi_k,
                                    fb_dtype phi_dt, int R, const int64_t sphi_q[3],
