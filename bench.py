@@ -331,6 +331,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D, "R": w.R, "causal": w.causal,
                    "factor_dtype": "f16" if phi_dt == torch.float16 else "f32", "factor_split": split,
                    "factor_columns": R_used, "factor_columns_padded": R_cols,
+                   "factor_units": "exp2 (phi_q log2(e))" if use_log2 else "natural",
                    "flops_per_step": F,
                    **({"bias_op": "multiplicative", "expanded_width": w.D * w.R} if mul else {}),
                    **({"factors": "in-kernel (fb_attn_fwd_alibi)"} if jit else {}),
