@@ -287,6 +287,13 @@ def test_edge_shapes(fb, N, D, causal):
     torch.cuda.synchronize()
     ro, _ = oracle.attention(q, k, v, bias=oracle.lowrank_bias(pq, pk), causal=causal)
     assert_close(to_np(o), ro, "bf16", f"N={N} D={D} causal={causal}")
+    # the exp2-unit kernel on the same shapes, phi_q times log2(e) rounded once to f16
+    pq2 = round_exact(pq / np.log(2.0), "f16")
+    o2 = fb.fb_attn_fwd_lowrank_log2(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"),
+                                     to_dev(pq2, "f16"), to_dev(pk, "f16"), causal=causal)
+    torch.cuda.synchronize()
+    ro2, _ = oracle.attention(q, k, v, bias=np.log(2.0) * oracle.lowrank_bias(pq2, pk), causal=causal)
+    assert_close(to_np(o2), ro2, "bf16", f"exp2 units N={N} D={D} causal={causal}")
 
 
 @pytest.mark.parametrize("R,phi", [(0, "f16"), (3, "bf16"), (16, "f16"), (20, "f16"), (48, "bf16"), (64, "f16"),
@@ -303,6 +310,12 @@ def test_ranks(fb, R, phi):
     torch.cuda.synchronize()
     ro, _ = oracle.attention(q, k, v, bias=oracle.lowrank_bias(pq, pk))
     assert_close(to_np(o), ro, "bf16", f"R={R} {phi}")
+    pq2 = round_exact(pq / np.log(2.0), phi)
+    o2 = fb.fb_attn_fwd_lowrank_log2(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"),
+                                     to_dev(pq2, phi), to_dev(pk, phi))
+    torch.cuda.synchronize()
+    ro2, _ = oracle.attention(q, k, v, bias=np.log(2.0) * oracle.lowrank_bias(pq2, pk))
+    assert_close(to_np(o2), ro2, "bf16", f"exp2 units R={R} {phi}")
 
 
 @pytest.mark.parametrize("R", [1, 2, 4, 7, 32])
