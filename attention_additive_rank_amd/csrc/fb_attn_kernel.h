@@ -53,6 +53,7 @@
 #pragma once
 
 #include "fb_internal.h"
+#include "fb_tile_map.h"
 
 namespace fb {
 namespace attn {
@@ -116,17 +117,6 @@ template <typename T> __device__ __forceinline__ T from_f32(float x) { return (T
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
-
-// Position inside a 32-row MFMA block that holds logical index k (key or head dim):
-// MFMA row m = 8a + 4h + c carries index 16h + 4a + c, so that output register r
-// of lane half h corresponds to index 16h + r.
-__host__ __device__ constexpr int perm_row(int k) {
-  return (k & ~31) | (((k & 15) >> 2) << 3) | (((k >> 4) & 1) << 2) | (k & 3);
-}
-// The inverse: the logical index held by MFMA row r.
-__host__ __device__ constexpr int inv_perm_row(int r) {
-  return (r & ~31) | (((r >> 2) & 1) << 4) | (((r & 31) >> 3) << 2) | (r & 3);
-}
 
 // Scale the KW query elements of one fragment by s and round them back to T.
 template <typename T>
@@ -218,26 +208,6 @@ __device__ __forceinline__ void mma_pins() {
     mma_pins<G + 1, NG, NPV, DB, NKB, MPV>();
   }
 }
-
-// Swizzled row-major tiles.  A region of 64 rows x cpr 16-byte chunks (cpr a power of
-// two) stores chunk c of row r at chunk position c ^ swz(r), which keeps every row's
-// chunks inside the row while spreading the rows over the LDS banks.  The LDS serves a
-// 128-bit read in passes of 16 lanes over 64 four-byte banks (256 bytes), so the lanes of
-// a pass must touch 16 different 16-byte bank groups, i.e. distinct (row * cpr + position)
-// mod 16:
-//   swz_rows: 16 consecutive rows read at one chunk (the score MFMA operands);
-//   swz_quad: four consecutive rows read at four adjacent chunks (the 64-bit transpose
-//             reads of V, 32 lanes of 8 bytes per pass).
-__host__ __device__ constexpr int swz_rows(int cpr, int r) {
-  return cpr >= 16 ? (r & 15) : cpr == 8 ? ((r >> 1) & 7) : cpr == 4 ? ((r >> 2) & 3) : cpr == 2 ? ((r >> 2) & 1) : 0;
-}
-__host__ __device__ constexpr int swz_quad(int cpr, int r) {
-  return cpr >= 8 ? 2 * (r & 3) : cpr == 4 ? 2 * ((r >> 1) & 1) : 0;
-}
-// K and phi_k rows are stored in key order but read by the score MFMA in the order
-// of perm_row (lane ln of a 32-key block reads key inv_perm_row(ln)), so their swizzle
-// follows the reading lane: eight lanes that read together still hit eight groups.
-__host__ __device__ constexpr int swz_key(int cpr, int key) { return swz_rows(cpr, perm_row(key)); }
 
 // 64-bit transpose read of 16-bit elements (ds_read_b64_tr_b16): within each group of
 // 16 lanes, value j of output lane 4a + c is element c of the 64-bit row read by lane 4j + a.
@@ -355,30 +325,19 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   // n' (64 / cpr) + l / cpr, chunk position l % cpr, i.e. logical chunk (l % cpr) ^ swz(row).
   // One load thus reads 1 KB of consecutive rows from global memory (the concurrent
   // workgroups of a head read the same tiles: scattered rows there cost L2 throughput).
-  // Chunks that are never loaded (phi_k at or beyond R, V past D) hold zeros.
+  // Without loader wavefronts, chunks that are never loaded (phi_k at or beyond R, V past
+  // D) hold zeros; the loader wavefronts copy in-row stand-ins there (loader_src_byte).
   // With PHI_DMA false (phi_k rows not 16-byte loadable: unaligned, or R not a multiple of
   // a chunk) the phi_k region is staged through registers instead (phi_load / phi_store).
   constexpr bool phk_fast = PHI_DMA;
   const int npch = phk_fast ? p.R / CE : 0;     // phi_k chunks that the direct path loads
-  struct Slot { int region, cpr, row, c; };
-  auto slot_of = [&](int n) __attribute__((always_inline)) {
-    Slot d;
-    int nr = n;
-    if (n < KCH) { d.region = 0; d.cpr = KCH; }
-    else if (n < KCH + PCH) { d.region = 1; d.cpr = PCH; nr = n - KCH; }
-    else { d.region = 2; d.cpr = VCH; nr = n - KCH - PCH; }
-    d.row = nr * (64 / d.cpr) + lane / d.cpr;
-    d.c = (lane % d.cpr) ^ (d.region == 2 ? swz_quad(d.cpr, d.row) : swz_key(d.cpr, d.row));
-    return d;
-  };
+  auto slot_of = [&](int n) __attribute__((always_inline)) { return tile_slot(n, lane, KCH, PCH, VCH); };
   // source byte offset of this lane's chunk of load n relative to the tile's first row, ~0
   // for a chunk that is not loaded
   auto src_offset = [&](int n) __attribute__((always_inline)) {
-    const Slot d = slot_of(n);
-    const int key = d.row;
+    const TileSlot d = slot_of(n);
     const int stride = d.region == 0 ? p.sk[2] : d.region == 1 ? p.spk[2] : p.sv[2];
-    const bool ok = d.region == 0 || (d.region == 1 ? d.c < npch : d.c < KCH);
-    return ok ? (uint32_t)(key * (stride * ES) + d.c * 16) : ~0u;
+    return slot_has_data(d, KCH, npch) ? (uint32_t)(d.row * (stride * ES) + d.c * 16) : ~0u;
   };
   // issue load n of K'(kbk) (into dK) or V(kbv) (into dV), given its offset; rows past N
   // are not loaded (their scores are masked; V rows keep finite data)
@@ -391,7 +350,7 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
     unsigned char* dst = region == 2 ? dV + (n - KCH - PCH) * 1024 : dK + n * 1024;
     bool ok = off != ~0u;
     if (kb + BN > N) {
-      const Slot d = slot_of(n);
+      const TileSlot d = slot_of(n);
       ok = ok && d.row < N - kb;
     }
     if (ok) dma16(base + off, dst);
@@ -433,9 +392,10 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   // before tile t (K'(t+2), V(t+1), needed from tile t+1 on), so copies stay in flight
   // across barriers instead of draining every tile.  That wait counts this wavefront's
   // outstanding loads, so every load is issued with all lanes active: a lane whose chunk
-  // is not wanted (a row past N, a phi_k chunk at or beyond R) copies a finite stand-in
-  // (the last row's chunk, the row's first chunk) that the scores mask or that meets zero
-  // phi_q columns.
+  // is not wanted copies a finite stand-in from inside the tensor: for a row past N the
+  // last row's chunk (the scores mask it), for a phi_k chunk at or beyond R or a V chunk
+  // past D (VCH > KCH when D < 32) the row's first chunk (it meets zero phi_q columns, or
+  // feeds only head dims >= D, which are never stored).
   if constexpr (LOADER) {
     static_assert(PHI_DMA, "the loaders copy phi_k directly");
     if (wave >= NW) {
@@ -451,9 +411,9 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
         rowi[i] = cbyte[i] = 0;
         off[i] = 0;
         if (n < NDMA) {
-          const Slot d = slot_of(n);
+          const TileSlot d = slot_of(n);
           rowi[i] = d.row;
-          cbyte[i] = d.region == 1 && d.c >= npch ? 0 : d.c * 16;
+          cbyte[i] = loader_src_byte(d, KCH, npch);
           const int stride = d.region == 0 ? p.sk[2] : d.region == 1 ? p.spk[2] : p.sv[2];
           off[i] = (uint32_t)(d.row * stride * ES + cbyte[i]);
         }
