@@ -486,3 +486,44 @@ def test_backward_stored_output_form():
     shift = np.sum(do * e, axis=-1, keepdims=True)
     P0 = np.where(np.abs(shift) > 0, -P / shift, 0.0)              # recovers P, rows sum to 1
     np.testing.assert_allclose(P0.sum(axis=-1), 1.0, atol=1e-9)
+
+
+# ------------------------------------------------ approximation error report ---
+def test_bias_energy_eckart_young_closed_form():
+    """A bias with chosen singular values 4, 2, 1, 1/2 (random orthogonal U, V, built here,
+    not by the oracle's SVD) truncated to rank R with the known singular vectors: the
+    relative Frobenius error is sqrt(sum_{r>=R} s_r^2 / sum_r s_r^2) exactly, e.g.
+    sqrt(5.25 / 21.25) at R = 1 and sqrt(0.25 / 21.25) at R = 3, and rank 4 leaves nothing."""
+    N = 12
+    r = np.random.default_rng(5)
+    U, _ = np.linalg.qr(r.standard_normal((N, N)))
+    V, _ = np.linalg.qr(r.standard_normal((N, N)))
+    sig = np.array([4.0, 2.0, 1.0, 0.5])
+    b = (U[:, :4] * sig) @ V[:, :4].T
+    for R, expect in ((1, math.sqrt(5.25 / 21.25)), (2, math.sqrt(1.25 / 21.25)), (3, math.sqrt(0.25 / 21.25)),
+                      (4, 0.0)):
+        pq = U[:, :R] * np.sqrt(sig[:R])
+        pk = V[:, :R] * np.sqrt(sig[:R])
+        e = oracle.bias_energy(b, pq, pk)
+        assert e["rel_fro"] == pytest.approx(expect, abs=1e-13), R
+    # the residual after rank 3 is the rank-1 term 0.5 u_4 v_4^T: its largest entry
+    pq, pk = U[:, :3] * np.sqrt(sig[:3]), V[:, :3] * np.sqrt(sig[:3])
+    res = 0.5 * np.abs(np.outer(U[:, 3], V[:, 3])).max()
+    assert oracle.bias_energy(b, pq, pk)["max_abs"] == pytest.approx(res, rel=1e-12)
+
+
+def test_bias_energy_single_entry_residual_and_orientation():
+    """b = phi_q phi_k^T plus one entry c at (i, j), with asymmetric factors: the residual is
+    that one entry, so max-abs is |c| and the relative Frobenius error |c| / ||b||_F.  Using
+    phi_k phi_q^T (a transposed product) instead would leave a far larger residual."""
+    r = np.random.default_rng(6)
+    N, R = 9, 2
+    pq, pk = r.standard_normal((N, R)), 3.0 * r.standard_normal((N, R))
+    b = pq @ pk.T
+    c = -0.625
+    b[2, 7] += c
+    e = oracle.bias_energy(b, pq, pk)
+    assert e["max_abs"] == pytest.approx(abs(c), abs=1e-14)
+    assert e["rel_fro"] == pytest.approx(abs(c) / math.sqrt(float(np.sum(b * b))), rel=1e-12)
+    wrong = oracle.bias_energy(b, pk, pq)
+    assert wrong["max_abs"] > 10 * abs(c)
