@@ -91,8 +91,9 @@ def load():
         lib.fb_make_dense_bias.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _DP,
                                            ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                            ctypes.c_void_p]
-        lib.fb_svd_factors.restype = ctypes.c_int
-        lib.fb_svd_factors.argtypes = [_DP, ctypes.c_int, ctypes.c_int, ctypes.c_uint64, _DP, _DP, _DP, _DP]
+        for fn in (lib.fb_svd_factors, lib.fb_svd_factors_log2):
+            fn.restype = ctypes.c_int
+            fn.argtypes = [_DP, ctypes.c_int, ctypes.c_int, ctypes.c_uint64, _DP, _DP, _DP, _DP]
         lib.fb_svd_rank_for_energy.restype = ctypes.c_int
         lib.fb_svd_rank_for_energy.argtypes = [_DP, ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_uint64,
                                                ctypes.POINTER(ctypes.c_int), _DP, ctypes.POINTER(ctypes.c_int)]
@@ -227,9 +228,10 @@ def fb_make_dense_bias(kind, H: int, N: int, C: int = 0, slopes=None, dtype=None
     return out
 
 
-def fb_svd_factors(bias: np.ndarray, R: int, seed: int = 0):
+def fb_svd_factors(bias: np.ndarray, R: int, seed: int = 0, log2: bool = False):
     """Host truncated SVD of one ``[N, N]`` bias.  Returns a dict with ``phi_q``, ``phi_k``
-    (``[N, R]`` fp64), ``sigma`` (``[R]``) and ``energy`` (retained energy)."""
+    (``[N, R]`` fp64), ``sigma`` (``[R]``) and ``energy`` (retained energy).  ``log2``:
+    ``phi_q`` in exp2 units (fb_svd_factors_log2), the factors fb_attn_fwd_lowrank_log2 takes."""
     a = np.ascontiguousarray(np.asarray(bias, dtype=np.float64))
     if a.ndim != 2 or a.shape[0] != a.shape[1]:
         raise ValueError("bias must be a square [N, N] matrix")
@@ -238,8 +240,9 @@ def fb_svd_factors(bias: np.ndarray, R: int, seed: int = 0):
     pk = np.empty((N, R))
     sig = np.empty(R)
     en = ctypes.c_double(0.0)
-    st = load().fb_svd_factors(a.ctypes.data_as(_DP), N, R, seed, pq.ctypes.data_as(_DP), pk.ctypes.data_as(_DP),
-                               sig.ctypes.data_as(_DP), ctypes.byref(en))
+    fn = load().fb_svd_factors_log2 if log2 else load().fb_svd_factors
+    st = fn(a.ctypes.data_as(_DP), N, R, seed, pq.ctypes.data_as(_DP), pk.ctypes.data_as(_DP),
+            sig.ctypes.data_as(_DP), ctypes.byref(en))
     _check(st)
     return {"phi_q": pq, "phi_k": pk, "sigma": sig, "energy": en.value}
 

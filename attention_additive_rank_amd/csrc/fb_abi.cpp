@@ -232,6 +232,16 @@ fb_status fb_svd_factors(const double* bias, int N, int R, uint64_t seed, double
   }
 }
 
+fb_status fb_svd_factors_log2(const double* bias, int N, int R, uint64_t seed, double* phi_q, double* phi_k,
+                              double* sigma, double* energy) {
+  const fb_status st = fb_svd_factors(bias, N, R, seed, phi_q, phi_k, sigma, energy);
+  if (st != FB_OK) return st;
+  // phi_q in exp2 units, scaled in fp64 before the caller rounds it
+  const double log2e = 1.4426950408889634074;
+  for (int64_t t = 0; t < (int64_t)N * R; ++t) phi_q[t] *= log2e;
+  return FB_OK;
+}
+
 fb_status fb_svd_rank_for_energy(const double* bias, int N, int R_max, double target, uint64_t seed,
                                  int* R_out, double* energy_out, int* reached) {
   const char* fn = "fb_svd_rank_for_energy";

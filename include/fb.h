@@ -158,6 +158,16 @@ fb_status fb_svd_factors(const double* bias, int N, int R, uint64_t seed, double
                          double* phi_k, double* sigma, double* energy);
 
 /*
+ * fb_svd_factors_log2 -- as fb_svd_factors, with phi_q in exp2 units: every phi_q value is
+ * multiplied by log2(e) in fp64 before it is returned, so phi_q phi_k^T = log2(e) times the
+ * rank-R approximation.  These are the factors fb_attn_fwd_lowrank_log2 takes (after the
+ * caller rounds them to the factor dtype).  sigma and energy are those of fb_svd_factors.
+ * Arguments and errors as fb_svd_factors.
+ */
+fb_status fb_svd_factors_log2(const double* bias, int N, int R, uint64_t seed, double* phi_q,
+                              double* phi_k, double* sigma, double* energy);
+
+/*
  * fb_svd_rank_for_energy -- the smallest rank whose truncated SVD keeps a target share
  * of a bias's energy.  The pages apply the low-rank path only where a rank-R factorisation
  * keeps 95% of a head's bias energy (rebuttal, answer to Reviewer Bp2x, Q2, with the

@@ -311,6 +311,27 @@ def test_host_svd_exact_rank():
     assert got["energy"] == pytest.approx(1.0, abs=1e-12)
 
 
+def test_host_svd_log2_units():
+    """fb_svd_factors_log2: phi_q in exp2 units, so ln(2) phi_q phi_k^T is the same best rank-R
+    approximation (Eckart-Young against the oracle's singular values); phi_k and sigma are
+    fb_svd_factors' own."""
+    r = np.random.default_rng(5)
+    N, R = 120, 6
+    b = r.standard_normal((N, N)) @ np.diag(0.8 ** np.arange(N)) @ r.standard_normal((N, N))
+    got = fb.fb_svd_factors(b, R, seed=3, log2=True)
+    nat = fb.fb_svd_factors(b, R, seed=3)
+    ref = oracle.truncated_svd(b, R)
+    np.testing.assert_array_equal(got["phi_k"], nat["phi_k"])
+    np.testing.assert_array_equal(got["sigma"], nat["sigma"])
+    np.testing.assert_allclose(got["phi_q"] * np.log(2.0), nat["phi_q"], rtol=1e-15, atol=0)
+    err2 = np.linalg.norm(b - np.log(2.0) * oracle.lowrank_bias(got["phi_q"], got["phi_k"])) ** 2
+    assert err2 == pytest.approx(np.sum(ref["sigma"][R:] ** 2), rel=1e-7)
+    lib = fb.load()
+    a = np.zeros((4, 4))
+    p = a.ctypes.data_as(fb._DP)
+    assert lib.fb_svd_factors_log2(None, 4, 2, 0, p, p, None, None) == fb.FB_EINVAL
+
+
 @pytest.mark.parametrize("kind", ["vision", "pairformer"])
 def test_host_svd_on_workload_biases(kind):
     """Small versions of the vision (spatial) and pair-rep biases: the host SVD
