@@ -101,10 +101,10 @@ def load():
             fn.restype = ctypes.c_int
             fn.argtypes = [ctypes.POINTER(_AttnArgs), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                            ctypes.POINTER(_I64x3), ctypes.POINTER(_I64x3), ctypes.c_void_p]
-        lib.fb_attn_bwd_lowrank.restype = ctypes.c_int
-        lib.fb_attn_bwd_lowrank.argtypes = [ctypes.POINTER(_AttnArgs), ctypes.c_void_p, ctypes.c_void_p,
-                                            ctypes.c_int, ctypes.c_int, ctypes.POINTER(_I64x3),
-                                            ctypes.POINTER(_I64x3), ctypes.POINTER(_BwdArgs), ctypes.c_void_p]
+        for fn in (lib.fb_attn_bwd_lowrank, lib.fb_attn_bwd_lowrank_noalloc):
+            fn.restype = ctypes.c_int
+            fn.argtypes = [ctypes.POINTER(_AttnArgs), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                           ctypes.POINTER(_I64x3), ctypes.POINTER(_I64x3), ctypes.POINTER(_BwdArgs), ctypes.c_void_p]
         lib.fb_attn_fwd_alibi.restype = ctypes.c_int
         lib.fb_attn_fwd_alibi.argtypes = [ctypes.POINTER(_AttnArgs), _DP, ctypes.c_void_p]
         lib.fb_attn_fwd_mulbias.restype = ctypes.c_int
@@ -443,12 +443,15 @@ def fb_mulbias_expand(q, k, phi_q, phi_k, *, scale: Optional[float] = None, work
 
 
 def fb_attn_bwd_lowrank(q, k, v, out, lse, dout, phi_q=None, phi_k=None, *, causal: bool = False,
-                        scale: Optional[float] = None, dq=None, dk=None, dv=None, stream=None):
+                        scale: Optional[float] = None, dq=None, dk=None, dv=None, dphi_q=None, dphi_k=None,
+                        stream=None, noalloc: bool = False):
     """Gradients of fb_attn_fwd_lowrank's output for the upstream gradient ``dout``.
 
     ``out`` and ``lse`` are the forward's output and LSE (float32 ``[B, H, N]``).  Returns
     ``(dq, dk, dv, dphi_q, dphi_k)``; the factor gradients are float32 with the factors'
-    own shapes (summed over the axes a factor is broadcast on), None for R = 0."""
+    own shapes (summed over the axes a factor is broadcast on), None for R = 0.
+    ``noalloc``: call fb_attn_bwd_lowrank_noalloc, whose workspace is the library's device
+    scratch (with every output passed in, this wrapper then allocates nothing either)."""
     torch = _torch()
     B, H, N, D = q.shape
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
@@ -470,25 +473,32 @@ def fb_attn_bwd_lowrank(q, k, v, out, lse, dout, phi_q=None, phi_k=None, *, caus
             raise ValueError("phi_q / phi_k rank or dtype mismatch")
         eq, sq = _bhn_strides(phi_q, B, H, N, "phi_q")
         ek, sk = _bhn_strides(phi_k, B, H, N, "phi_k")
-        dpq = torch.empty(phi_q.shape, dtype=torch.float32, device=q.device)
-        dpk = torch.empty(phi_k.shape, dtype=torch.float32, device=q.device)
+        dpq = torch.empty(phi_q.shape, dtype=torch.float32, device=q.device) if dphi_q is None else dphi_q
+        dpk = torch.empty(phi_k.shape, dtype=torch.float32, device=q.device) if dphi_k is None else dphi_k
+        for name, t, f in (("dphi_q", dpq, phi_q), ("dphi_k", dpk, phi_k)):
+            if tuple(t.shape) != tuple(f.shape) or t.dtype != torch.float32 or t.device != q.device:
+                raise ValueError(f"{name} must be float32 with the factor's shape, on q's device")
         _, gsq = _bhn_strides(dpq, B, H, N, "dphi_q")
         _, gsk = _bhn_strides(dpk, B, H, N, "dphi_k")
         g.dphi_q, g.dphi_k, g.sdphi_q, g.sdphi_k = dpq.data_ptr(), dpk.data_ptr(), gsq, gsk
-    # workspace (Delta and per-(b, h) partials of summed factor gradients), 256-byte aligned
-    nbytes = int(load().fb_attn_bwd_workspace_bytes(B, H, N, R, ctypes.byref(g.sdphi_q), ctypes.byref(g.sdphi_k)))
-    work = torch.empty(nbytes + 256, dtype=torch.uint8, device=q.device)
-    g.work = (work.data_ptr() + 255) // 256 * 256
-    g.work_bytes = nbytes
-    if R > 0:
-        st = load().fb_attn_bwd_lowrank(ctypes.byref(a), eq.data_ptr(), ek.data_ptr(), _dt_code(phi_q.dtype), R,
-                                        ctypes.byref(sq), ctypes.byref(sk), ctypes.byref(g),
-                                        _stream_ptr(q.device, stream))
+    work = None
+    if noalloc:
+        entry = load().fb_attn_bwd_lowrank_noalloc
+        g.work, g.work_bytes = None, 0
     else:
-        st = load().fb_attn_bwd_lowrank(ctypes.byref(a), None, None, a.dt, 0, None, None, ctypes.byref(g),
-                                        _stream_ptr(q.device, stream))
+        # workspace (Delta and per-(b, h) partials of summed factor gradients), 256-byte aligned
+        entry = load().fb_attn_bwd_lowrank
+        nbytes = int(load().fb_attn_bwd_workspace_bytes(B, H, N, R, ctypes.byref(g.sdphi_q), ctypes.byref(g.sdphi_k)))
+        work = torch.empty(nbytes + 256, dtype=torch.uint8, device=q.device)
+        g.work = (work.data_ptr() + 255) // 256 * 256
+        g.work_bytes = nbytes
+    if R > 0:
+        st = entry(ctypes.byref(a), eq.data_ptr(), ek.data_ptr(), _dt_code(phi_q.dtype), R, ctypes.byref(sq),
+                   ctypes.byref(sk), ctypes.byref(g), _stream_ptr(q.device, stream))
+    else:
+        st = entry(ctypes.byref(a), None, None, a.dt, 0, None, None, ctypes.byref(g), _stream_ptr(q.device, stream))
     _check(st)
-    if stream is not None:
+    if stream is not None and work is not None:
         work.record_stream(stream)   # the workspace outlives this call on a caller's stream
     return dq, dk, dv, dpq, dpk
 

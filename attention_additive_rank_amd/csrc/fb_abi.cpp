@@ -453,7 +453,14 @@ fb_status fb_attn_fwd_mulbias(const fb_attn_args* a, const void* phi_q, const vo
 fb_status fb_attn_bwd_lowrank(const fb_attn_args* a, const void* phi_q, const void* phi_k, fb_dtype phi_dt, int R,
                               const int64_t sphi_q[3], const int64_t sphi_k[3], const fb_attn_bwd_args* g,
                               hipStream_t stream) {
-  const char* fn = "fb_attn_bwd_lowrank";
+  return fb::attn_bwd_lowrank_impl(a, phi_q, phi_k, phi_dt, R, sphi_q, sphi_k, g, stream, "fb_attn_bwd_lowrank");
+}
+}  // extern "C"
+
+namespace fb {
+fb_status attn_bwd_lowrank_impl(const fb_attn_args* a, const void* phi_q, const void* phi_k, fb_dtype phi_dt, int R,
+                                const int64_t sphi_q[3], const int64_t sphi_k[3], const fb_attn_bwd_args* g,
+                                hipStream_t stream, const char* fn) {
   fb_status st = check_common(a, fn);
   if (st != FB_OK) return st;
   if (!g) FB_FAIL(FB_EINVAL, "%s: null gradient arguments", fn);
@@ -482,7 +489,6 @@ fb_status fb_attn_bwd_lowrank(const fb_attn_args* a, const void* phi_q, const vo
   if (!tile_fits32(a->sq[2], es) || !tile_fits32(g->sdo[2], es))
     FB_FAIL(FB_EUNSUPPORTED, "%s: a 64-row tile of Q or dO spans 2^31 bytes or more", fn);
   if ((uintptr_t)g->work & 255u) FB_FAIL(FB_EINVAL, "%s: workspace not 256-byte aligned", fn);
-  if (R > 0 && (!g->sdphi_q || !g->sdphi_k)) FB_FAIL(FB_EINVAL, "%s: null factor-gradient strides", fn);
   const BwdWork wl = bwd_work_layout(a->B, a->H, a->N, R, g->sdphi_q, g->sdphi_k);
   if (g->work_bytes < wl.bytes)
     FB_FAIL(FB_EINVAL, "%s: workspace of %zu bytes, %zu needed", fn, g->work_bytes, wl.bytes);
@@ -573,6 +579,9 @@ fb_status fb_attn_bwd_lowrank(const fb_attn_args* a, const void* phi_q, const vo
     st = launch_attention_bwd_reduce(p.dphk, a->B, a->H, a->N, R, g->dphi_k, g->sdphi_k, stream);
   return st;
 }
+}  // namespace fb
+
+extern "C" {
 
 fb_status fb_attn_fwd_alibi(const fb_attn_args* a, const double* slopes_host, hipStream_t stream) {
   const char* fn = "fb_attn_fwd_alibi";

@@ -119,4 +119,11 @@ BwdWork bwd_work_layout(int B, int H, int N, int R, const int64_t sdphi_q[3], co
 
 void set_error(const char* fmt, ...);
 
+// The backward pass behind fb_attn_bwd_lowrank (validation, then the launches); `fn` names
+// the public entry point in error messages.  g->work must hold at least
+// bwd_work_layout(...).bytes bytes.
+fb_status attn_bwd_lowrank_impl(const fb_attn_args* a, const void* phi_q, const void* phi_k, fb_dtype phi_dt, int R,
+                                const int64_t sphi_q[3], const int64_t sphi_k[3], const fb_attn_bwd_args* g,
+                                hipStream_t stream, const char* fn);
+
 }  // namespace fb

@@ -19,8 +19,10 @@
  * Conventions shared by every entry point
  *   - Every call returns fb_status; no C++ exception crosses the ABI.
  *   - Device pointers are caller-allocated (e.g. by PyTorch) and stay owned by
- *     the caller.  The library never allocates or frees device memory and
- *     keeps no workspace.  Host buffers are read/written only during the call.
+ *     the caller.  The library never allocates or frees device memory; its only
+ *     device memory of its own is the fixed scratch array behind
+ *     fb_attn_bwd_lowrank_noalloc.  Host buffers are read/written only during
+ *     the call.
  *   - Argument validation is synchronous and happens before any launch; on a
  *     validation error nothing is launched and no output is touched.
  *   - Kernels are launched asynchronously on the caller's `stream`
@@ -399,6 +401,33 @@ size_t fb_attn_bwd_workspace_bytes(int B, int H, int N, int R, const int64_t sdp
 fb_status fb_attn_bwd_lowrank(const fb_attn_args* a, const void* phi_q, const void* phi_k, fb_dtype phi_dt, int R,
                               const int64_t sphi_q[3], const int64_t sphi_k[3], const fb_attn_bwd_args* g,
                               hipStream_t stream);
+
+/* Size of the device scratch array behind fb_attn_bwd_lowrank_noalloc (64 MiB per GPU). */
+#define FB_BWD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * fb_attn_bwd_lowrank_noalloc -- fb_attn_bwd_lowrank for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight training loops, harnesses that forbid
+ * hipMalloc.  It neither allocates nor frees anything; its workspace is a file-scope
+ * device array of FB_BWD_NOALLOC_SCRATCH_BYTES bytes in the library, one copy per GPU,
+ * which each GPU the library runs this on holds until the process ends.
+ *
+ *   Arguments as fb_attn_bwd_lowrank, except that g->work must be NULL and g->work_bytes 0.
+ *   The stream (NULL = the null stream) must belong to the calling thread's current device.
+ *   Results are those of fb_attn_bwd_lowrank on the same inputs (the same kernels).
+ * Every call on one GPU shares that GPU's array and leaves the last call's contents in it
+ * (nothing in it needs to start at zero: every byte the kernels read is written earlier in
+ * the same call); calls that overlap on one GPU (other streams, other threads) race.
+ * Errors: as fb_attn_bwd_lowrank; FB_EINVAL for a non-NULL g->work or nonzero
+ * g->work_bytes, or a stream of another device; FB_EUNSUPPORTED when the sizes need more
+ * workspace than the scratch holds (fb_attn_bwd_workspace_bytes above
+ * FB_BWD_NOALLOC_SCRATCH_BYTES), checked before any HIP call; FB_EHIP when the scratch
+ * address cannot be looked up.
+ */
+fb_status fb_attn_bwd_lowrank_noalloc(const fb_attn_args* a, const void* phi_q, const void* phi_k,
+                                      fb_dtype phi_dt, int R, const int64_t sphi_q[3],
+                                      const int64_t sphi_k[3], const fb_attn_bwd_args* g,
+                                      hipStream_t stream);
 
 #ifdef __cplusplus
 }

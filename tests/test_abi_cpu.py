@@ -220,6 +220,32 @@ def test_backward_validation(kw, bkw, code):
     assert fb.fb_last_error() != ""
 
 
+def _bwd_noalloc(a, R=0, **gk):
+    g = fb._BwdArgs()
+    st = (a.H * a.N * a.D, a.N * a.D, a.D)
+    g.dout = g.dq = g.dk = g.dv = g.dphi_q = g.dphi_k = FAKE
+    for n in ("sdo", "sdq", "sdk", "sdv"):
+        setattr(g, n, fb._I64x3(*st))
+    g.sdphi_q = g.sdphi_k = fb._I64x3(*gk.get("sdphi", (0, 0, 64)))
+    g.work = gk.get("work", None)
+    g.work_bytes = gk.get("work_bytes", 0)
+    sp = fb._I64x3(0, 0, 64)
+    return fb.load().fb_attn_bwd_lowrank_noalloc(ctypes.byref(a), FAKE, FAKE, fb.FB_F16, R, ctypes.byref(sp),
+                                                 ctypes.byref(sp), ctypes.byref(g), None)
+
+
+def test_backward_noalloc_validation():
+    """The no-alloc backward rejects a caller workspace, and sizes whose workspace exceeds its
+    scratch, before any HIP call; empty inputs are a no-op."""
+    assert _bwd_noalloc(_args(lse=FAKE), work=FAKE, work_bytes=1 << 20) == fb.FB_EINVAL
+    assert _bwd_noalloc(_args(lse=FAKE), work_bytes=256) == fb.FB_EINVAL
+    # shared R = 64 factors over B8 H8 N8192: Delta plus two [B][H][N][64] fp32 partials, 268 MB
+    big = _args(B=8, H=8, N=8192, lse=FAKE, strides=(8 * 8192 * 64, 8192 * 64, 64))
+    assert _bwd_noalloc(big, R=64) == fb.FB_EUNSUPPORTED
+    assert "scratch" in fb.fb_last_error()
+    assert _bwd_noalloc(_args(N=0, q=None, k=None, v=None, o=None)) == fb.FB_OK
+
+
 def test_backward_empty_is_noop():
     assert _bwd(_args(N=0, q=None, k=None, v=None, o=None), dq=None, work=None) == fb.FB_OK
 
