@@ -194,3 +194,40 @@ def sample_rows(N: int, n: int, seed: int = 0) -> np.ndarray:
     fixed = [0, 1, 31, 32, 63, 64, 127, 128, N // 2, N - 2, N - 1]
     extra = r.choice(N, size=min(N, n), replace=False)
     return np.unique(np.clip(np.concatenate([fixed, extra]), 0, N - 1))
+
+
+def compare_whole(o_dev, ref_fn, B: int, H: int, dtype: str, what: str, lse_dev=None):
+    """Every (b, h) and every row of a full-size output against the oracle, streamed one
+    (b, h) at a time: ``ref_fn(b, h) -> (O [N, D], LSE [N])`` in fp64.  The relative L2 error
+    is taken over the whole tensor (the contract's bar), max-abs over every element; the
+    LSE (when given) to 2e-2 (16-bit) / 1e-4 (fp32) absolute."""
+    got = to_np(o_dev)
+    gl = lse_dev.detach().cpu().double().numpy() if lse_dev is not None else None
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    num = den = 0.0
+    mx = lmx = 0.0
+    for b in range(B):
+        for h in range(H):
+            ro, rl = ref_fn(b, h)
+            d = got[b, h] - ro
+            num += float(np.sum(d * d))
+            den += float(np.sum(ro * ro))
+            mx = max(mx, float(np.abs(d).max()))
+            if gl is not None:
+                lmx = max(lmx, float(np.abs(gl[b, h] - rl).max()))
+    rl2 = math.sqrt(num / max(den, 1e-300))
+    amax, rmax = TOL[dtype]
+    ltol = 1e-4 if dtype == "f32" else 2e-2
+    say(f"  {what}: {B * H} (b, h) x all rows: max-abs {mx:.3e} (<= {amax}), rel-L2 {rl2:.3e} (<= {rmax})"
+        + (f", LSE max-abs {lmx:.3e} (<= {ltol})" if gl is not None else ""))
+    assert mx <= amax and rl2 <= rmax, f"{what}: max-abs {mx:.3e}, rel-L2 {rl2:.3e}"
+    if gl is not None:
+        assert lmx <= ltol, f"{what}: LSE max-abs {lmx:.3e}"
+    return mx, rl2
+
+
+def pair_reference(c, b: int, h: int):
+    """Oracle O and LSE of one (b, h) of a Case, all rows."""
+    sl = (slice(b, b + 1), slice(h, h + 1))
+    o, l = oracle.attention(c.q[sl], c.k[sl], c.v[sl], bias=lambda _b, _h: c.bias_ref(b, h), causal=c.w.causal)
+    return o[0, 0], l[0, 0]

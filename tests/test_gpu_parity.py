@@ -111,29 +111,6 @@ def test_attention_parity_reduced(fb, name, over):
     np.testing.assert_allclose(lse.cpu().double().numpy(), rl, rtol=0, atol=2e-2 if w.dtype != "f32" else 1e-4)
 
 
-FULL = ["tiny_alibi_f32", "gpt2_alibi_causal", "sandwich", "vision_svd", "pairformer_svd"]
-
-
-@pytest.mark.parametrize("name", FULL)
-def test_attention_parity_full_size_sampled(fb, name):
-    """Full workload size, same launch as the bench; sampled rows of sampled (b, h)."""
-    w = synth.workload(name)
-    say(f"full-size parity {name}: preparing inputs")
-    rows = sample_rows(w.N, 48, seed=1)
-    c = Case(w, rows=rows)
-    if c.energy is not None:
-        say(f"  retained SVD energy per head: {np.round(c.energy, 4).tolist()}")
-    import torch
-    say(f"full-size parity {name}: launch")
-    o = c.run_lowrank()
-    torch.cuda.synchronize()
-    r = np.random.default_rng(2)
-    bh = sorted({(0, 0), (w.B - 1, w.H - 1)} | {(int(r.integers(w.B)), int(r.integers(w.H))) for _ in range(4)})
-    ro, _ = c.reference(bh=bh)
-    got = np.stack([to_np(o[b, h])[rows] for (b, h) in bh])
-    assert_close(got, ro, w.dtype, f"{name} sampled O")
-
-
 LOG2 = [x for x in REDUCED if synth.workload(x[0], **x[1]).dtype != "f32"]
 
 
@@ -151,23 +128,6 @@ def test_log2_factors_parity_reduced(fb, name, over):
     ro, rl = c.reference()
     assert_close(to_np(o), ro, w.dtype, f"{name} log2 O")
     np.testing.assert_allclose(lse.cpu().double().numpy(), rl, rtol=0, atol=2e-2)
-
-
-@pytest.mark.parametrize("name", ["gpt2_alibi_causal", "sandwich"])
-def test_log2_factors_full_size_sampled(fb, name):
-    """The log2 entry point at full size, in the benchmark's launch; sampled rows of sampled
-    (b, h)."""
-    w = synth.workload(name)
-    rows = sample_rows(w.N, 48, seed=3)
-    c = Case(w, rows=rows, log2=True)
-    import torch
-    say(f"full-size log2 parity {name}: launch")
-    o = c.run_lowrank()
-    torch.cuda.synchronize()
-    bh = [(0, 0), (w.B - 1, w.H - 1), (w.B // 2, w.H // 2)]
-    ro, _ = c.reference(bh=bh)
-    got = np.stack([to_np(o[b, h])[rows] for (b, h) in bh])
-    assert_close(got, ro, w.dtype, f"{name} log2 sampled O")
 
 
 @pytest.mark.parametrize("kind,dt,split", [("sandwich", "f16", 1), ("alibi", "f16", 2), ("alibi", "bf16", 3)])
@@ -211,19 +171,18 @@ def test_svd_approximation_error_reported(fb):
                                        ("gpt2_alibi_causal", dict(B=1, H=4, N=257)),
                                        ("tiny_alibi_f32", dict(N=200))])
 def test_densebias_kernel_parity(fb, name, over):
-    """The dense-bias baseline against the oracle fed the same rounded dense bias."""
+    """The dense-bias baseline against the oracle fed the same rounded dense bias (the
+    oracle's closed form, rounded once to the input dtype on the host, is both sides' input)."""
     import torch
     w = synth.workload(name, **over)
     say(f"densebias parity {w}")
     c = Case(w)
-    dt = tdtype(w.dtype)
     if w.bias == "alibi":
-        bias = fb.fb_make_dense_bias("alibi", w.H, w.N, dtype=dt)
+        bnp = round_exact(oracle.alibi_bias(oracle.alibi_slopes(w.H), w.N), w.dtype)
     else:
-        bias = fb.fb_make_dense_bias("sandwich", 1, w.N, C=w.C, dtype=dt)
-    o = fb.fb_attn_fwd_densebias(c.qd, c.kd, c.vd, bias, causal=w.causal)
+        bnp = round_exact(oracle.sandwich_bias(w.N, w.C), w.dtype)
+    o = fb.fb_attn_fwd_densebias(c.qd, c.kd, c.vd, to_dev(bnp, w.dtype), causal=w.causal)
     torch.cuda.synchronize()
-    bnp = to_np(bias)
     ro, _ = oracle.attention(c.q, c.k, c.v, bias=bnp, causal=w.causal)
     assert_close(to_np(o), ro, w.dtype, f"densebias {name}")
 
@@ -236,11 +195,11 @@ def test_lowrank_and_densebias_on_same_factors(fb):
     w = synth.workload("vision_svd", B=1, H=2, grid=16)
     c = Case(w)
     o1 = c.run_lowrank()
-    dense = torch.matmul(c.phq.double(), c.phk.double().transpose(-1, -2)).to(torch.bfloat16).contiguous()
-    o2 = fb.fb_attn_fwd_densebias(c.qd, c.kd, c.vd, dense)
+    dense_np = round_exact(oracle.lowrank_bias(c.pq_np, c.pk_np), "bf16")   # [H, N, N], rounded once
+    o2 = fb.fb_attn_fwd_densebias(c.qd, c.kd, c.vd, to_dev(dense_np, "bf16"))
     torch.cuda.synchronize()
     ro1, _ = c.reference()
-    ro2, _ = oracle.attention(c.q, c.k, c.v, bias=to_np(dense))
+    ro2, _ = oracle.attention(c.q, c.k, c.v, bias=dense_np)
     assert_close(to_np(o1), ro1, "bf16", "lowrank vs oracle(phi_q phi_k^T)")
     assert_close(to_np(o2), ro2, "bf16", "densebias vs oracle(bf16(phi_q phi_k^T))")
     ma, rl = errors(to_np(o1), to_np(o2))
@@ -507,25 +466,6 @@ def test_mulbias_strided_inputs_and_reused_workspace(fb):
         assert_close(to_np(o), ro, "bf16", f"mulbias strided call {t}")
 
 
-def test_mulbias_full_size_sampled(fb):
-    """The benchmark's multiplicative workload (b_ij = cos(i - j), B4 H8 N4096 D64 R2) in the
-    bench's launch; sampled rows of sampled (b, h)."""
-    import torch
-    w = synth.workload("mulbias_cos")
-    inp = synth.make_inputs(w)
-    q, k, v, N = inp["q"], inp["k"], inp["v"], w.N
-    phi = synth.round_to(oracle.cos_mulbias_factors(N), "f32")
-    o = fb.fb_attn_fwd_mulbias(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), to_dev(phi, "f32"),
-                               to_dev(phi, "f32"))
-    torch.cuda.synchronize()
-    rows = sample_rows(N, 48, seed=3)
-    bias = oracle.lowrank_bias(phi, phi)
-    for (b, h) in [(0, 0), (1, 5), (3, 7)]:
-        ro, _ = oracle.attention_mulbias(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], bias,
-                                         rows=rows)
-        assert_close(to_np(o[b, h])[rows][None, None], ro, "bf16", f"mulbias full-size b={b} h={h}")
-
-
 def test_mulbias_two_stage_equals_one_call(fb):
     """Expansion stage + the low-rank kernel on its outputs gives bit-identical results to
     the one-call entry point (the benchmark times the two stages separately)."""
@@ -606,46 +546,49 @@ def test_backward_parity(fb, B, H, N, D, R, fs, dt, pdt, causal):
 
 def test_backward_full_size_sampled(fb):
     """The Sandwich workload at full size (B4 H8 N4096 D64, R = 64 f16 factors shared by all
-    (b, h)) in the benchmark's launch; every gradient element of two (b, h) pairs, the factor
-    gradients through a per-(b, h) view of the same factors."""
+    (b, h)) in the benchmark's launch, the backward alone: every gradient element of two
+    (b, h) pairs, given the oracle's forward output, and the factor gradients through a
+    per-(b, h) view of the same factors.  (The backward on its own forward's output is
+    covered over every (b, h) in the full-size tests.)"""
     import torch
     w = synth.workload("sandwich")
-    c = Case(w)
+    inp = synth.make_inputs(w)
+    q, k, v = inp["q"], inp["k"], inp["v"]
     r = np.random.default_rng(20260013)
-    do = synth.round_to(r.standard_normal(c.q.shape) * 0.5, "bf16")
+    do = synth.round_to(r.standard_normal(q.shape) * 0.5, "bf16")
+    # the oracle's Sandwich factors rounded once to f16: both sides' input
+    pq = pk = round_exact(oracle.sandwich_factors(w.N, w.C), "f16")
+    qd, kd, vd = (to_dev(x, "bf16") for x in (q, k, v))
+    phd = to_dev(pq, "f16")
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda:0")
-    o = c.run_lowrank(lse=lse)
+    o = fb.fb_attn_fwd_lowrank(qd, kd, vd, phd, phd, lse=lse)
     torch.cuda.synchronize()
     # The row term Delta = rowsum(dO * O) reads the stored forward output.  For the sampled
     # pairs both sides take the oracle's O rounded to bf16 and its LSE, so the check measures
     # the backward alone: dphi = dS phi cancels for the smooth low-frequency Sandwich columns
     # (sum_j dS_ij = 0), and an error e in Delta_i moves dphi_i by about e |phi| while the
     # result itself is of size |phi| |dP - Delta| sqrt(sum_j P_ij^2), some sqrt(N) smaller, so
-    # the forward's own rounding of O would swamp the comparison.  The backward's inputs are the
-    # f16 factors, so the oracle's bias is their product (as in the reduced backward cases), not
-    # the exact Sandwich formula.
-    pq = c.phq.double().cpu().numpy().reshape(w.N, -1)
-    pk = c.phk.double().cpu().numpy().reshape(w.N, -1)
+    # the forward's own rounding of O would swamp the comparison.
     bias = oracle.lowrank_bias(pq, pk)
     pairs = [(0, 0), (3, 7)]
     refs = {}
     for (b, h) in pairs:
         sl = (slice(b, b + 1), slice(h, h + 1))
-        o_ref, l_ref = oracle.attention(c.q[sl], c.k[sl], c.v[sl], bias=bias)
+        o_ref, l_ref = oracle.attention(q[sl], k[sl], v[sl], bias=bias)
         o_16 = round_exact(o_ref, "bf16")
         o[b, h] = torch.from_numpy(o_16[0, 0]).to(o.dtype).to(o.device)
         lse[b, h] = torch.from_numpy(l_ref[0, 0]).float().to(lse.device)
         refs[(b, h)] = o_16
-    dq, dk, dv, gpq, gpk = fb.fb_attn_bwd_lowrank(c.qd, c.kd, c.vd, o, lse, to_dev(do, "bf16"), c.phq, c.phk)
+    dq, dk, dv, gpq, gpk = fb.fb_attn_bwd_lowrank(qd, kd, vd, o, lse, to_dev(do, "bf16"), phd, phd)
     # the same factors as a [B, H, N, R] view (0 strides): the factor gradients then come per
     # (b, h), written directly, so single pairs can be compared with the oracle
-    shape4 = (w.B, w.H, w.N, c.phq.shape[-1])
-    _, _, _, gpq4, gpk4 = fb.fb_attn_bwd_lowrank(c.qd, c.kd, c.vd, o, lse, to_dev(do, "bf16"),
-                                                 c.phq.expand(shape4), c.phk.expand(shape4))
+    shape4 = (w.B, w.H, w.N, phd.shape[-1])
+    _, _, _, gpq4, gpk4 = fb.fb_attn_bwd_lowrank(qd, kd, vd, o, lse, to_dev(do, "bf16"),
+                                                 phd.expand(shape4), phd.expand(shape4))
     torch.cuda.synchronize()
     for (b, h) in pairs:
         sl = (slice(b, b + 1), slice(h, h + 1))
-        rq, rk, rv, db = oracle.attention_backward(c.q[sl], c.k[sl], c.v[sl], do[sl], bias=bias,
+        rq, rk, rv, db = oracle.attention_backward(q[sl], k[sl], v[sl], do[sl], bias=bias,
                                                    o_stored=refs[(b, h)])
         for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
             assert_grad_close(to_np(got[b:b + 1, h:h + 1]), ref, f"full-size {name} b={b} h={h}")
@@ -661,7 +604,15 @@ def test_backward_full_size_sampled(fb):
             ratio = np.linalg.norm(g - ref) / np.linalg.norm(M)
             say(f"  full-size {name} b={b} h={h}: |err|_F / |M|_F {ratio:.3e} (<= {2.0 ** -9:.3e})")
             assert ratio <= 2.0 ** -9, name
-    say(f"  factor gradients summed over all (b, h): finite {bool(torch.isfinite(gpq).all() and torch.isfinite(gpk).all())}")
+    # the factor gradients summed over all (b, h) equal the per-(b, h) ones added up (the same
+    # fp32 partials in another order)
+    for name, g, g4 in (("dphi_q", gpq, gpq4), ("dphi_k", gpk, gpk4)):
+        g = g.double().cpu().numpy()
+        assert np.all(np.isfinite(g)), name
+        host = g4.double().cpu().numpy().sum(axis=(0, 1))
+        rl = float(np.linalg.norm(g - host) / np.linalg.norm(host))
+        say(f"  summed {name} vs host sum of per-(b, h) gradients: rel-L2 {rl:.3e}")
+        assert rl <= 1e-5, name
 
 
 # ------------------------------------------------------- in-kernel ALiBi factors ---
@@ -692,23 +643,6 @@ def test_alibi_in_kernel_factors(fb, shape, dt, causal, slopes):
     assert_close(got, ro, dt, f"in-kernel ALiBi N={N} D={D}")
     gl = lse.cpu().double().numpy()
     np.testing.assert_allclose(gl if rows is None else gl[:, :, rows], rl, rtol=0, atol=2e-2)
-
-
-def test_alibi_in_kernel_full_size_sampled(fb):
-    """The GPT-2 ALiBi causal workload (B8 H12 N2048 D64) with in-kernel factors, in the
-    bench's launch; sampled rows of sampled (b, h)."""
-    import torch
-    w = synth.workload("gpt2_alibi_causal")
-    inp = synth.make_inputs(w)
-    o = fb.fb_attn_fwd_alibi(to_dev(inp["q"], "bf16"), to_dev(inp["k"], "bf16"), to_dev(inp["v"], "bf16"),
-                             causal=True)
-    torch.cuda.synchronize()
-    rows = sample_rows(w.N, 48, seed=5)
-    m = oracle.alibi_slopes(w.H)
-    for (b, h) in [(0, 0), (3, 6), (7, 11)]:
-        ro, _ = oracle.attention(inp["q"][b:b + 1, h:h + 1], inp["k"][b:b + 1, h:h + 1], inp["v"][b:b + 1, h:h + 1],
-                                 bias=oracle.alibi_bias(m[h:h + 1], w.N), causal=True, rows=rows)
-        assert_close(to_np(o[b, h])[rows][None, None], ro, "bf16", f"in-kernel ALiBi b={b} h={h}")
 
 
 # ------------------------------------------------------- seeded random sweep ----
