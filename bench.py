@@ -12,16 +12,30 @@ Default workload: Sandwich-bias attention, B=4, H=8, N=4096, D=64, C=R=64, bf16
 
 Prints ONE JSON line (rank 0): metric/value (whole-step TFLOP/s with
 F = 4*B*H*N^2*(D + R/2)), the dominant kernel's roofline (HIP-event timed, against
-the bf16 dense MFMA peak), the in-house dense-bias kernel on the same inputs
-(speedup), and the fp64 CPU oracle timed on a bounded sample of the same work.
+the dense matrix-core peak of its dtype), the in-house dense-bias kernel on the same
+inputs (speedup), and the fp64 CPU oracle timed on a bounded sample of the same work.
+
+Before the warm-up steps the step runs untimed for --settle-ms of wall time: the GPU
+raises its shader clock over tens of milliseconds of sustained load, and a handful of
+warm-up steps alone would time part of that ramp.  The shader clock seen during the
+settle phase (amdsmi, when available) is reported.
+
+``--profile`` is the rocprofv3 harness: before touching the GPU it runs this script
+under rocprofv3 in child processes (a kernel trace, then one counter pass each for
+FETCH_SIZE, WRITE_SIZE and the matrix-core busy counters), parses their CSV output and
+writes ``profiles/harness_<workload>.json`` and ``profiles/<kernel>_<workload>.md``;
+later bench lines read HBM traffic, GB/s and matrix-core busy from that file while the
+kernel sources are unchanged (by hash).
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
-import math
 import os
+import subprocess
 import sys
 import time
 
@@ -30,9 +44,12 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # MI355X dense matrix peaks
 PEAK_HBM_GBS = 8000.0
+N_XCD = 8
 KERNEL_SOURCES = ["attention_additive_rank_amd/csrc/fb_attn_kernel.h",
+                  "attention_additive_rank_amd/csrc/fb_tile_map.h",
                   "attention_additive_rank_amd/csrc/fb_attn_inst.hip"]
-
+WORKLOAD_CHOICES = ["sandwich", "gpt2_alibi_causal", "mulbias_cos", "vision_svd", "pairformer_svd",
+                    "tiny_alibi_f32"]
 
 LOG2E = 1.4426950408889634   # log2(e)
 
@@ -54,11 +71,14 @@ def flops(w) -> float:
     return 4.0 * w.B * w.H * pairs * (w.D + w.R / 2.0)
 
 
-def algorithmic_bytes(w, es: int, phi_es: int, phi_shared_over_heads: bool) -> float:
-    """Q, K, V read and O written once, plus the factors (read once)."""
+def algorithmic_bytes(w, es: int, phi_es: int, phi_rows: int) -> float:
+    """Q, K, V read and O written once, plus the factors (read once; phi_rows rows of each)."""
     qkvo = 4.0 * w.B * w.H * w.N * w.D * es
-    phi_rows = w.N if phi_shared_over_heads else w.H * w.N
     return qkvo + 2.0 * phi_rows * w.R * phi_es
+
+
+def harness_file(w) -> str:
+    return os.path.join(ROOT, "profiles", f"harness_{w.name}.json")
 
 
 def cpu_oracle_baseline(w, budget_s: float, factors=None):
@@ -107,13 +127,38 @@ def cpu_oracle_baseline(w, budget_s: float, factors=None):
                       f"bias materialisation {t_bias:.2f}s not included", "seconds": round(t_attn, 2)}
 
 
+class ClockReader:
+    """Current shader (GFX) clock of the first GPU through amdsmi, or None where unavailable."""
+
+    def __init__(self):
+        self.h = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            hs = amdsmi.amdsmi_get_processor_handles()
+            if len(hs) == 1:
+                self.amdsmi, self.h = amdsmi, hs[0]
+        except Exception:
+            self.h = None
+
+    def mhz(self):
+        if self.h is None:
+            return None
+        try:
+            c = self.amdsmi.amdsmi_get_clock_info(self.h, self.amdsmi.AmdSmiClkType.GFX)
+            return float(c["clk"])
+        except Exception:
+            return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="sandwich",
-                    choices=["sandwich", "gpt2_alibi_causal", "mulbias_cos", "vision_svd", "pairformer_svd"])
+    ap.add_argument("--settle-ms", type=float, default=400.0,
+                    help="untimed steps for this much wall time before the warm-up (shader clock ramp)")
+    ap.add_argument("--workload", default="sandwich", choices=WORKLOAD_CHOICES)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of CPU oracle work (0 = skip)")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-bias baseline")
     ap.add_argument("--cold-launches", type=int, default=21,
@@ -124,6 +169,10 @@ def main():
                     help="time the backward pass (fb_attn_bwd_lowrank) of the workload instead")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one device copy of this many MiB (HBM counter calibration)")
+    ap.add_argument("--profile", action="store_true",
+                    help="rocprofv3 harness: trace + counter passes in child processes, then write profiles/")
+    ap.add_argument("--profile-reparse", action="store_true",
+                    help="with --profile: only re-read the CSV files of an earlier harness run")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -131,6 +180,8 @@ def main():
         print(json.dumps({"error": "this build runs on exactly one GPU; multi-GPU runs are not provided "
                                    "(every (batch, head) pair is independent: see DESIGN.md for how it would shard)"}))
         sys.exit(2)
+    if args.profile:
+        sys.exit(profile_harness(args))
 
     import torch
     import attention_additive_rank_amd as fb
@@ -143,13 +194,21 @@ def main():
     inp = synth.make_inputs(w, with_bias_source=svd)
     dt = {"bf16": torch.bfloat16, "f32": torch.float32}[w.dtype]
     q, k, v = (torch.from_numpy(inp[n]).to(dt).to(dev) for n in "qkv")
+    jit = args.alibi_jit
+    if jit and w.bias != "alibi":
+        raise SystemExit("--alibi-jit needs an ALiBi workload")
+    mul = w.bias == "mulbias_cos"
+    # 16-bit workloads take phi_q in exp2 units (phi_q log2(e), rounded once): the kernel then
+    # skips one operation per score.
+    use_log2 = not (jit or mul or args.backward) and w.dtype != "f32"
     svd_info = None
     if svd:
         # static per-head biases: rank-R factors from the library's host SVD (offline, not
-        # timed); the dense-bias baseline streams the full [H, N, N] bias
+        # timed; phi_q in exp2 units from fb_svd_factors_log2); the dense-bias baseline
+        # streams the full [H, N, N] bias
         import numpy as np
         t0 = time.time()
-        fs = [fb.fb_svd_factors(inp["bias_src"][h], w.R, seed=h) for h in range(w.H)]
+        fs = [fb.fb_svd_factors(inp["bias_src"][h], w.R, seed=h, log2=use_log2) for h in range(w.H)]
         svd_info = {"seconds": round(time.time() - t0, 2), "energy_min": round(min(f["energy"] for f in fs), 6)}
         svd_phi = [np.stack([f[n] for f in fs]) for n in ("phi_q", "phi_k")]
         svd_bias = torch.from_numpy(inp["bias_src"]).to(dt).to(dev)
@@ -157,7 +216,6 @@ def main():
     out = torch.empty_like(q)
     phi_dt = torch.float16 if w.dtype != "f32" else torch.float32
     split = 2 if (w.bias == "alibi" and w.dtype != "f32") else 1
-    mul = w.bias == "mulbias_cos"
     if mul:
         # b_ij = cos(i - j) = cos i cos j + sin i sin j: fp32 factors [cos i, sin i], an input
         import numpy as np
@@ -179,17 +237,10 @@ def main():
     if not mul:
         pq = torch.zeros((fH, w.N, R_cols), dtype=phi_dt, device=dev)
         pk = torch.zeros_like(pq)
-    jit = args.alibi_jit
-    if jit and w.bias != "alibi":
-        raise SystemExit("--alibi-jit needs an ALiBi workload")
-    # 16-bit workloads take phi_q in exp2 units (phi_q log2(e), rounded once): the kernel then
-    # skips one operation per score.  SVD factors are scaled on the host, in fp64.
-    use_log2 = not (jit or mul or args.backward) and w.dtype != "f32"
     if svd:
-        pq[..., :w.R] = torch.from_numpy(svd_phi[0] * (LOG2E if use_log2 else 1.0)).to(phi_dt).to(dev)
+        pq[..., :w.R] = torch.from_numpy(svd_phi[0]).to(phi_dt).to(dev)
         pk[..., :w.R] = torch.from_numpy(svd_phi[1]).to(phi_dt).to(dev)
     stream = torch.cuda.current_stream(dev)
-
 
     def stage1(log2=use_log2):
         """factor generation (additive) or operand expansion (multiplicative)"""
@@ -220,6 +271,8 @@ def main():
             raise SystemExit("--backward covers the additive workloads")
         return bench_backward(args, w, fb, torch, q, k, v, pq, pk, stage1, out, dev, stream)
 
+    clock = ClockReader()
+    settle = settle_phase(torch, step, args.settle_ms, clock)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -237,7 +290,9 @@ def main():
     t_stop.record(stream)
     torch.cuda.synchronize()
     step_ms = t_start.elapsed_time(t_stop) / K
-    kern_ms = sum(a.elapsed_time(b) for a, b in ev) / K
+    launch_ms = sorted(a.elapsed_time(b) for a, b in ev)
+    kern_ms = sum(launch_ms) / K                     # average launch duration (roofline)
+    kern_med = launch_ms[K // 2]
 
     # cold caches: a 512 MiB scratch write before each launch evicts L2 and the Infinity
     # Cache, so the kernel reads its inputs from HBM; median over the launches
@@ -273,17 +328,19 @@ def main():
             bias = svd_bias
         else:
             bias = fb.fb_make_dense_bias("alibi", w.H, w.N, dtype=dt)
+        dstep = lambda: fb.fb_attn_fwd_densebias(q, k, v, bias, causal=w.causal, out=out)
+        settle_phase(torch, dstep, args.settle_ms / 4, None)
         for _ in range(args.warmup):
-            fb.fb_attn_fwd_densebias(q, k, v, bias, causal=w.causal, out=out)
+            dstep()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         for _ in range(K):
-            fb.fb_attn_fwd_densebias(q, k, v, bias, causal=w.causal, out=out)
+            dstep()
         b.record(stream)
         torch.cuda.synchronize()
         dense_ms = a.elapsed_time(b) / K
-        dense_cold = cold_median(lambda: fb.fb_attn_fwd_densebias(q, k, v, bias, causal=w.causal, out=out))
+        dense_cold = cold_median(dstep)
         dense = {"ms": round(dense_ms, 4), "tflops": round(F / (dense_ms * 1e-3) / 1e12, 2),
                  "cold_ms_median": round(dense_cold, 4) if dense_cold else None,
                  "bias_shape": list(bias.shape), "bias_bytes_unique": bias.numel() * bias.element_size()}
@@ -301,20 +358,33 @@ def main():
         torch.cuda.synchronize()
         del x, y
 
-    # HBM traffic from rocprofv3 counters, only while they describe this kernel source
-    traffic = None
-    tfile = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
-    if os.path.exists(tfile):
-        with open(tfile) as f:
-            tr = json.load(f)
-        if tr.get("kernel_source_hash") == kernel_source_hash():
-            traffic = tr.get("bytes_per_launch")
+    # rocprofv3 counters (the --profile harness), only while they describe this kernel source
+    es = 2 if w.dtype != "f32" else 4
+    phi_es = {torch.float16: 2, torch.bfloat16: 2, torch.float32: 4}[phi_dt]
+    if mul:
+        alg_bytes = 4.0 * w.B * w.H * w.N * w.D * es + 2.0 * w.B * w.H * w.N * (w.R - 1) * w.D * es
+    elif jit:
+        alg_bytes = algorithmic_bytes(w, es, phi_es, 0)
+    else:
+        alg_bytes = algorithmic_bytes(w, es, phi_es, fH * w.N)
+    counters = None
+    hf = harness_file(w)
+    if os.path.exists(hf):
+        with open(hf) as f:
+            hr = json.load(f)
+        if hr.get("kernel_source_hash") == kernel_source_hash() and hr.get("entry") == entry_name(use_log2, jit, mul):
+            counters = {k2: hr.get(k2) for k2 in ("bytes_per_launch", "fetch_bytes", "write_bytes", "mfma_busy",
+                                                  "sclk_mhz_counters", "trace_avg_us")}
+            counters["hbm_gbs"] = round(hr["bytes_per_launch"] / (kern_ms * 1e-3) / 1e9, 1) \
+                if hr.get("bytes_per_launch") else None
+            counters["source"] = os.path.relpath(hf, ROOT)
 
     cpu = None
     if args.cpu_budget > 0:
-        cpu = cpu_oracle_baseline(w, args.cpu_budget, factors=svd_phi if svd else None)
+        # the oracle takes the factors in natural units
+        nat = (svd_phi[0] / LOG2E if use_log2 else svd_phi[0], svd_phi[1]) if svd else None
+        cpu = cpu_oracle_baseline(w, args.cpu_budget, factors=nat)
 
-    es = 2 if w.dtype != "f32" else 4
     rec = {
         "metric": "biased-attention fwd TFLOP/s + % MFMA peak; speedup vs dense-bias kernel",
         "value": round(value, 2),
@@ -338,7 +408,9 @@ def main():
                    **({"factors": "host SVD per head (fb_svd_factors, not timed)", "svd": svd_info} if svd else {})},
         "pct_mfma_peak": round(100.0 * value / peak, 2),
         "kernel_ms": round(kern_ms, 4),
+        "kernel_ms_median": round(kern_med, 4),
         "kernel_tflops": round(kern_tflops, 2),
+        "settle": settle,
         "cold": {"step_ms_median": round(cold_step_ms, 4) if cold_step_ms else None,
                  "kernel_ms_median": round(cold_kern_ms, 4) if cold_kern_ms else None,
                  "launches": args.cold_launches,
@@ -346,16 +418,45 @@ def main():
         "densebias": dense,
         "speedup_vs_densebias": round(dense["ms"] / step_ms, 3) if dense else None,
         "roofline": {"bound": "mfma", "achieved": round(kern_tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(kern_tflops / peak, 4), "traffic": traffic,
-                     "algorithmic_bytes": (4.0 * w.B * w.H * w.N * w.D * es
-                                           + 2.0 * w.B * w.H * w.N * (w.R - 1) * w.D * es) if mul else
-                                          algorithmic_bytes(w, es, 2 if phi_dt == torch.float16 else 4,
-                                                            w.bias == "sandwich"),
-                     "kernel": "attn_fwd_kernel (fb_attn_fwd_lowrank_log2)" if use_log2 else
-                               "attn_fwd_kernel (fb_attn_fwd_lowrank)"},
+                     "frac": round(kern_tflops / peak, 4),
+                     "traffic": counters["bytes_per_launch"] if counters else None,
+                     "algorithmic_bytes": alg_bytes,
+                     "timing": "average of the timed launches (HIP events on the launch stream)",
+                     "kernel": f"attn_fwd_kernel ({entry_name(use_log2, jit, mul)})"},
+        "counters": counters,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+def entry_name(use_log2: bool, jit: bool, mul: bool) -> str:
+    if jit:
+        return "fb_attn_fwd_alibi"
+    if use_log2:
+        return "fb_attn_fwd_lowrank_log2"
+    return "fb_attn_fwd_lowrank"
+
+
+def settle_phase(torch, fn, ms: float, clock):
+    """Untimed steps, enqueued 16 at a time, for ``ms`` of wall time; samples the shader
+    clock while the GPU works.  Returns {"steps", "ms", "sclk_mhz"}."""
+    if ms <= 0:
+        return {"steps": 0, "ms": 0.0, "sclk_mhz": None}
+    t0 = time.time()
+    n = 0
+    mhz = []
+    while (time.time() - t0) * 1e3 < ms:
+        for _ in range(16):
+            fn()
+        n += 16
+        if clock is not None:
+            m = clock.mhz()
+            if m:
+                mhz.append(m)
+        torch.cuda.synchronize()
+    mhz = sorted(mhz[len(mhz) // 2:])       # the second half, after the ramp
+    return {"steps": n, "ms": round((time.time() - t0) * 1e3, 1),
+            "sclk_mhz": mhz[len(mhz) // 2] if mhz else None}
 
 
 def bench_backward(args, w, fb, torch, q, k, v, pq_t, pk_t, stage1, out, dev, stream):
@@ -371,14 +472,16 @@ def bench_backward(args, w, fb, torch, q, k, v, pq_t, pk_t, stage1, out, dev, st
     g = np.random.default_rng(w.seed + 7).standard_normal(q.shape) * 0.5
     dout = torch.from_numpy(g).to(q.dtype).to(dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    bstep = lambda: fb.fb_attn_bwd_lowrank(q, k, v, out, lse, dout, pq_t, pk_t, causal=w.causal, dq=dq, dk=dk, dv=dv)
+    settle = settle_phase(torch, bstep, args.settle_ms, ClockReader())
     for _ in range(args.warmup):
-        fb.fb_attn_bwd_lowrank(q, k, v, out, lse, dout, pq_t, pk_t, causal=w.causal, dq=dq, dk=dk, dv=dv)
+        bstep()
     torch.cuda.synchronize()
     K = args.steps
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(stream)
     for _ in range(K):
-        fb.fb_attn_bwd_lowrank(q, k, v, out, lse, dout, pq_t, pk_t, causal=w.causal, dq=dq, dk=dk, dv=dv)
+        bstep()
     b.record(stream)
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / K
@@ -393,10 +496,194 @@ def bench_backward(args, w, fb, torch, q, k, v, pq_t, pk_t, stage1, out, dev, st
                       "data": "synthetic",
                       "config": {"workload": w.name + "_backward", "B": w.B, "H": w.H, "N": w.N, "D": w.D,
                                  "R_columns": Rp, "causal": w.causal, "flops_per_step": F},
+                      "settle": settle,
                       "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": peak, "unit": "TFLOP/s",
                                    "frac": round(tf / peak, 4), "traffic": None,
                                    "kernel": "attn_bwd_dkv_kernel + attn_bwd_dq_kernel (+ delta, factor-gradient sum)"},
                       "cpu_baseline": None}), flush=True)
+
+
+# --------------------------------------------------------------------------------------
+# rocprofv3 harness (--profile).  Runs before anything in this process touches the GPU:
+# every GPU run is a child process under rocprofv3.
+def _csv_rows(pattern):
+    rows = []
+    for path in sorted(glob.glob(pattern, recursive=True)):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _run_child(cmd, log, timeout_s):
+    """One profiled child run; returns its exit status (0 also when rocprofv3 itself faults
+    after the program printed its result line)."""
+    print(f"[harness] {' '.join(cmd)}", flush=True)
+    env = dict(os.environ, TMPDIR="/tmp")
+    with open(log, "w") as f:
+        r = subprocess.run(["timeout", "-s", "KILL", str(timeout_s)] + cmd, stdout=f, stderr=subprocess.STDOUT,
+                           cwd="/tmp", env=env)
+    with open(log) as f:
+        text = f.read()
+    printed = '"metric"' in text
+    print(f"[harness]   exit {r.returncode}{' (result line printed)' if printed else ''}", flush=True)
+    if r.returncode != 0 and not (printed and r.returncode in (139, -11)):
+        print(text[-3000:], flush=True)
+        return r.returncode or 1
+    return 0
+
+
+def profile_harness(args) -> int:
+    import synth
+    w = synth.workload(args.workload)
+    out_root = os.path.join(ROOT, "gpurun_out", "harness", w.name)
+    os.makedirs(out_root, exist_ok=True)
+    py = sys.executable or "python3"
+    bench = os.path.join(ROOT, "bench.py")
+    base = [py, bench, "--workload", w.name, "--cpu-budget", "0", "--cold-launches", "0"]
+    if args.alibi_jit:
+        base.append("--alibi-jit")
+    # 1. kernel trace of the timed command (steps / warm-up as given)
+    trace_cmd = ["rocprofv3", "--kernel-trace", "--stats", "-d", os.path.join(out_root, "trace"), "-o", "trace",
+                 "--output-format", "csv", "--"] + base + ["--steps", str(args.steps), "--warmup", str(args.warmup),
+                                                          "--settle-ms", str(args.settle_ms)]
+    if not args.profile_reparse and _run_child(trace_cmd, os.path.join(out_root, "trace.log"), 300):
+        return 1
+    # 2.-4. counter passes: short runs (every dispatch is serialised under --pmc), with one
+    # 512 MiB device copy as the HBM calibration
+    short = base + ["--steps", "3", "--warmup", "1", "--settle-ms", "0", "--no-dense", "--calib-copy-mib", "512"]
+    passes = {"fetch": ["FETCH_SIZE"], "write": ["WRITE_SIZE"],
+              "busy": ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES",
+                       "GRBM_GUI_ACTIVE", "GRBM_COUNT"]}
+    def shown(cmd):
+        """the command as run from the repository root (the child runs with cwd /tmp)"""
+        return "cd $REPO && TMPDIR=/tmp " + " ".join(("python3" if c == py else c.replace(ROOT + os.sep, ""))
+                                                  for c in cmd)
+    cmds = {"trace": shown(trace_cmd)}
+    for name, ctrs in passes.items():
+        cmd = ["rocprofv3", "--pmc"] + ctrs + ["-d", os.path.join(out_root, name), "-o", name,
+                                               "--output-format", "csv", "--"] + short
+        cmds[name] = shown(cmd)
+        if not args.profile_reparse and _run_child(cmd, os.path.join(out_root, f"{name}.log"), 120):
+            if name != "busy":
+                return 1
+            print("[harness] the busy-counter pass failed; continuing without it", flush=True)
+
+    # ---- parse
+    stats = _csv_rows(os.path.join(out_root, "trace", "**", "*kernel_stats.csv"))
+    entry = entry_name(not (args.alibi_jit or w.bias == "mulbias_cos") and w.dtype != "f32", args.alibi_jit,
+                       w.bias == "mulbias_cos")
+
+    def is_attn(name):
+        return "attn_fwd_kernel" in name
+
+    # the step's attention kernel: the attn_fwd_kernel instance that is not the dense-bias one
+    # (template MODE 1 shows as "Li1E" after the head dim and the factor width)
+    def mode_of(name):
+        try:
+            parts = name.split("attn_fwd_kernel")[1].split("Li")
+            return int(parts[3].split("E")[0])
+        except Exception:
+            return -1
+    trace_rows = []
+    for r in stats:
+        nm = r.get("Name") or r.get("KernelName") or r.get("Kernel_Name") or ""
+        avg = float(r.get("AverageNs") or r.get("Average_Ns") or r.get("AVG_NS") or 0) / 1e3
+        calls = int(float(r.get("Calls") or r.get("Count") or 0))
+        trace_rows.append((nm, calls, avg, float(r.get("MinNs") or 0) / 1e3, float(r.get("MaxNs") or 0) / 1e3,
+                           float(r.get("Percentage") or 0)))
+    main_k = [t for t in trace_rows if is_attn(t[0]) and mode_of(t[0]) != 1]
+    dense_k = [t for t in trace_rows if is_attn(t[0]) and mode_of(t[0]) == 1]
+    if not main_k:
+        print("[harness] no attention kernel in the trace", flush=True)
+        return 1
+    kname, _, kavg, _, _, _ = max(main_k, key=lambda t: t[1])
+
+    durations = {}
+
+    def counter(name, kernel_pred):
+        vals = {}
+        for r in _csv_rows(os.path.join(out_root, name, "**", "*counter_collection.csv")):
+            kn = r.get("Kernel_Name") or r.get("Kernel-Name") or ""
+            if not kernel_pred(kn):
+                continue
+            cid = r.get("Correlation_Id") or r.get("Dispatch_Id")
+            cn = r.get("Counter_Name")
+            vals.setdefault(cn, {}).setdefault(cid, 0.0)
+            vals[cn][cid] += float(r.get("Counter_Value") or 0)
+            try:
+                durations.setdefault(name, {})[cid] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+            except (KeyError, ValueError, TypeError):
+                pass
+        return {c: sum(d.values()) / len(d) for c, d in vals.items() if d}
+
+    step_pred = lambda kn: is_attn(kn) and mode_of(kn) != 1
+    copy_pred = lambda kn: "copyBuffer" in kn
+    f_k, f_c = counter("fetch", step_pred), counter("fetch", copy_pred)
+    w_k, w_c = counter("write", step_pred), counter("write", copy_pred)
+    busy = counter("busy", step_pred)
+    calib = 512 * 1024.0                                     # KiB copied by the calibration run
+    res = {"workload": w.name, "entry": entry, "kernel": kname, "kernel_source_hash": kernel_source_hash(),
+           "trace_avg_us": round(kavg, 2), "commands": cmds}
+    if "FETCH_SIZE" in f_k and "FETCH_SIZE" in f_c and "WRITE_SIZE" in w_k and "WRITE_SIZE" in w_c:
+        fs, ws = calib / f_c["FETCH_SIZE"], calib / w_c["WRITE_SIZE"]
+        res.update({"fetch_kib_raw": f_k["FETCH_SIZE"], "write_kib_raw": w_k["WRITE_SIZE"],
+                    "fetch_scale": fs, "write_scale": ws,
+                    "fetch_bytes": int(f_k["FETCH_SIZE"] * fs * 1024), "write_bytes": int(w_k["WRITE_SIZE"] * ws * 1024)})
+        res["bytes_per_launch"] = res["fetch_bytes"] + res["write_bytes"]
+    if busy:
+        res["busy_counters"] = busy
+        if busy.get("SQ_BUSY_CU_CYCLES"):
+            res["mfma_busy"] = round(busy.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (4.0 * busy["SQ_BUSY_CU_CYCLES"]), 4)
+    res["counter_runs"] = "3 steps after 1 warm-up, no settle phase (dispatches serialised by the profiler)"
+    # shader clock of the counter runs: GRBM_COUNT counts clocks, summed over the XCDs, over
+    # the dispatch's duration (start and end timestamps of the same rows)
+    dur = sorted(durations.get("busy", {}).values())
+    if busy.get("GRBM_COUNT") and dur:
+        res["counter_run_us"] = round(dur[len(dur) // 2], 2)
+        res["sclk_mhz_counters"] = round(busy["GRBM_COUNT"] / N_XCD / dur[len(dur) // 2], 0)
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(harness_file(w), "w") as f:
+        json.dump(res, f, indent=1)
+
+    # ---- markdown summary
+    shape = f"b{w.B}h{w.H}n{w.N}d{w.D}" + (f"r{w.R}" if not args.alibi_jit else "")
+    md = os.path.join(ROOT, "profiles", f"{entry.replace('fb_', '')}_{w.name}_{shape}.md")
+    lines = [f"# `{entry}` on the {w.name} workload (B={w.B} H={w.H} N={w.N} D={w.D} R={w.R}, {w.dtype})", "",
+             "Written by `python bench.py --profile --workload " + w.name +
+             (" --alibi-jit" if args.alibi_jit else "") + f" --steps {args.steps} --warmup {args.warmup}` "
+             "(the rocprofv3 harness in bench.py); raw CSV under gpurun_out/harness/.", "",
+             "Kernel trace (rocprofv3 --kernel-trace --stats):", "", "```", cmds["trace"], "```", "",
+             "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
+    for t in sorted(trace_rows, key=lambda t: -t[5])[:6]:
+        lines.append(f"| `{t[0][:110]}` | {t[1]} | {t[2]:.1f} | {t[3]:.1f} | {t[4]:.1f} | {t[5]:.1f} |")
+    lines += ["", f"Step kernel: `{kname}`, average {kavg:.1f} us per launch in the trace."]
+    if dense_k:
+        lines.append(f"Dense-bias kernel (same inputs): average {dense_k[0][2]:.1f} us.")
+    lines += ["", "Counter passes (one rocprofv3 --pmc run each, 3 steps after 1 warm-up, with a 512 MiB "
+              "device copy for calibration):", "", "```"] + [cmds[n] for n in passes] + ["```", ""]
+    if "bytes_per_launch" in res:
+        lines.append(f"Calibration: the 512 MiB copy reads as FETCH_SIZE {f_c['FETCH_SIZE']:.0f} KiB (scale x"
+                     f"{res['fetch_scale']:.3f}) and WRITE_SIZE {w_c['WRITE_SIZE']:.0f} KiB (scale x{res['write_scale']:.3f}).")
+        lines.append(f"Step kernel per launch: FETCH_SIZE {res['fetch_kib_raw']:.0f} KiB -> {res['fetch_bytes'] / 1e6:.1f} MB "
+                     f"read, WRITE_SIZE {res['write_kib_raw']:.0f} KiB -> {res['write_bytes'] / 1e6:.1f} MB written; "
+                     f"{res['bytes_per_launch'] / 1e6:.1f} MB in all, "
+                     f"{res['bytes_per_launch'] / (kavg * 1e-6) / 1e9:.0f} GB/s at the traced average.")
+    if "mfma_busy" in res:
+        b = res["busy_counters"]
+        lines.append(f"SQ_VALU_MFMA_BUSY_CYCLES {b.get('SQ_VALU_MFMA_BUSY_CYCLES', 0):.4g}, SQ_BUSY_CU_CYCLES "
+                     f"{b.get('SQ_BUSY_CU_CYCLES', 0):.4g}: matrix cores busy {100 * res['mfma_busy']:.1f}% of the "
+                     "busy CU cycles (MFMA busy / (4 SIMDs x CU busy cycles)); SQ_WAVE_CYCLES "
+                     f"{b.get('SQ_WAVE_CYCLES', 0):.4g}, SQ_BUSY_CYCLES {b.get('SQ_BUSY_CYCLES', 0):.4g}, "
+                     f"GRBM_GUI_ACTIVE {b.get('GRBM_GUI_ACTIVE', 0):.4g}, GRBM_COUNT {b.get('GRBM_COUNT', 0):.4g}.")
+    if "sclk_mhz_counters" in res:
+        lines.append(f"Shader clock in the counter runs: GRBM_COUNT / {N_XCD} XCDs / {res['counter_run_us']} us "
+                     f"(the dispatch's own timestamps) = {res['sclk_mhz_counters']:.0f} MHz.")
+    with open(md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps({"harness": os.path.relpath(harness_file(w), ROOT), "summary": os.path.relpath(md, ROOT),
+                      "trace_avg_us": res["trace_avg_us"], "bytes_per_launch": res.get("bytes_per_launch"),
+                      "mfma_busy": res.get("mfma_busy")}), flush=True)
+    return 0
 
 
 if __name__ == "__main__":
