@@ -107,6 +107,8 @@ def load():
                            ctypes.POINTER(_I64x3), ctypes.POINTER(_I64x3), ctypes.POINTER(_BwdArgs), ctypes.c_void_p]
         lib.fb_attn_fwd_alibi.restype = ctypes.c_int
         lib.fb_attn_fwd_alibi.argtypes = [ctypes.POINTER(_AttnArgs), _DP, ctypes.c_void_p]
+        lib.fb_attn_fwd_sandwich.restype = ctypes.c_int
+        lib.fb_attn_fwd_sandwich.argtypes = [ctypes.POINTER(_AttnArgs), ctypes.c_int, ctypes.c_void_p]
         lib.fb_attn_fwd_mulbias.restype = ctypes.c_int
         lib.fb_attn_fwd_mulbias.argtypes = [ctypes.POINTER(_AttnArgs), ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_int, ctypes.c_int, ctypes.POINTER(_I64x3),
@@ -523,5 +525,19 @@ def fb_attn_fwd_alibi(q, k, v, slopes=None, *, causal: bool = False, scale: Opti
     keep, sp = _slopes_ptr(slopes)
     st = load().fb_attn_fwd_alibi(ctypes.byref(a), sp, _stream_ptr(q.device, stream))
     del keep
+    _check(st)
+    return out
+
+
+def fb_attn_fwd_sandwich(q, k, v, C: int = 64, *, causal: bool = False, scale: Optional[float] = None, out=None,
+                         lse=None, stream=None):
+    """O = softmax(scale * Q K^T + b) V for the Sandwich bias b_ij = sum_k cos((i - j) w_k) with
+    its cos / sin factors formed inside the kernel (no factor tensors).  ``C``: even channel
+    count, 2..64; bf16 / fp16, head dim <= 64."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    a = _attn_args(q, k, v, out, lse, causal, scale)
+    st = load().fb_attn_fwd_sandwich(ctypes.byref(a), int(C), _stream_ptr(q.device, stream))
     _check(st)
     return out

@@ -606,6 +606,52 @@ fb_status fb_attn_fwd_alibi(const fb_attn_args* a, const double* slopes_host, hi
   return st;
 }
 
+fb_status fb_attn_fwd_sandwich(const fb_attn_args* a, int C, hipStream_t stream) {
+  const char* fn = "fb_attn_fwd_sandwich";
+  fb_status st = check_common(a, fn);
+  if (st != FB_OK) return st;
+  if (C < 2 || C % 2) FB_FAIL(FB_EINVAL, "%s: C must be even and >= 2", fn);
+  if (a->dt != FB_BF16 && a->dt != FB_F16) FB_FAIL(FB_EUNSUPPORTED, "%s: q/k/v must be bf16 or f16", fn);
+  if (a->D > 64) FB_FAIL(FB_EUNSUPPORTED, "%s: head dims up to 64", fn);
+  if (C > 2 * kMaxSandwichPairs) FB_FAIL(FB_EUNSUPPORTED, "%s: C above %d", fn, 2 * kMaxSandwichPairs);
+  if (a->N > 65536) FB_FAIL(FB_EUNSUPPORTED, "%s: N above 65536", fn);
+  if ((int64_t)a->B * a->H * a->N == 0) return FB_OK;
+  AttnParams p = base_params(a);
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int f = 0; f < kMaxSandwichPairs; ++f) {
+    if (f < C / 2) {
+      // w_f = 10000^(-2(f+1)/C); nu_f = w_f / (2 pi) in revolutions, split so that an index
+      // below 2^16 times either of the first two pieces is exact in fp32
+      const double w = std::pow(10000.0, -2.0 * (f + 1) / C);
+      double rest = w / two_pi;
+      for (int i = 0; i < 2; ++i) {
+        double piece = 0.0;
+        if (rest != 0.0) {
+          int e;
+          std::frexp(rest, &e);
+          const double q = std::ldexp(1.0, e - 8);    // 8 significant bits
+          piece = std::nearbyint(rest / q) * q;
+        }
+        p.sw_nu[i][f] = (float)piece;
+        rest -= piece;
+      }
+      p.sw_nu[2][f] = (float)rest;
+      p.sw_rot[0][f] = std::cos(64.0 * w);
+      p.sw_rot[1][f] = std::sin(64.0 * w);
+    } else {
+      p.sw_nu[0][f] = p.sw_nu[1][f] = p.sw_nu[2][f] = 0.f;
+      p.sw_rot[0][f] = 1.0;
+      p.sw_rot[1][f] = 0.0;
+    }
+  }
+  p.sw_pairs = C / 2;
+  p.R = C;
+  const int RP = C <= 16 ? 16 : C <= 32 ? 32 : 64;   // a power-of-two number of 16-byte chunks per row
+  st = dispatch_attention(4, a->dt, FB_F16, a->D, RP, p, stream);
+  if (st == FB_EUNSUPPORTED) set_error("%s: no kernel for this configuration", fn);
+  return st;
+}
+
 fb_status fb_attn_fwd_densebias(const fb_attn_args* a, const void* bias, fb_dtype bias_dt, const int64_t sbias[3],
                                 hipStream_t stream) {
   const char* fn = "fb_attn_fwd_densebias";

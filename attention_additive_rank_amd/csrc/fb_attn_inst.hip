@@ -76,7 +76,8 @@ static fb_status lowrank_rp(int RP, const AttnParams& p, hipStream_t s) {
 
 // mode 0: low rank (RP = padded factor width, 0 = plain attention); mode 1: dense bias;
 // mode 2: ALiBi with in-kernel factors (16-bit Q/K/V); mode 3: low rank with phi_q in
-// exp2 units (16-bit Q/K/V).
+// exp2 units (16-bit Q/K/V); mode 4: Sandwich with in-kernel factors in exp2 units
+// (16-bit Q/K/V, D <= 64, RP = C rounded up to 16 <= 64).
 fb_status FB_CAT3(launch_attention_d, FB_ATTN_D, FB_QT_NAME)(int mode, fb_dtype aux_dt, int RP,
                                                               const AttnParams& p, hipStream_t s) {
   using namespace attn;
@@ -109,6 +110,17 @@ fb_status FB_CAT3(launch_attention_d, FB_ATTN_D, FB_QT_NAME)(int mode, fb_dtype 
   }
 #if FB_ATTN_QT != 2
   if (mode == 3 && RP == 0) return launch_one<QT, QT, D, 0, 3, QT>(p, s);
+  if (mode == 4) {
+    // in-kernel Sandwich factors: the loader wavefronts write the phi_k tiles (D <= 64)
+    if constexpr (D <= 64) {
+      switch (RP) {
+        case 16: return launch_kernel<QT, f16_t, D, 16, 4, QT, true>(p, s);
+        case 32: return launch_kernel<QT, f16_t, D, 32, 4, QT, true>(p, s);
+        case 64: return launch_kernel<QT, f16_t, D, 64, 4, QT, true>(p, s);
+      }
+    }
+    return FB_EUNSUPPORTED;
+  }
 #endif
   if (RP == 0) return launch_one<QT, QT, D, 0, 0, QT>(p, s);
 #if FB_ATTN_QT != 2

@@ -209,6 +209,19 @@ __device__ __forceinline__ void mma_pins() {
   }
 }
 
+// (cos, sin) of 2 pi x nu for an integer 0 <= x < 2^16, with nu = n0 + n1 + n2 split on the
+// host so that n0 and n1 have at most 8 significant bits: x n0 and x n1 are exact in fp32, so
+// their fractional parts are exact, and x n2 is below 2^-8 of a revolution per 2^8 of x; the
+// reduced angle (in revolutions, the unit of v_sin_f32 / v_cos_f32) is off by about 2^-24.
+__device__ __forceinline__ void sincos_rev(int x, float n0, float n1, float n2, float& c, float& s) {
+  const float xf = (float)x;
+  const float a = __builtin_amdgcn_fractf(xf * n0);
+  const float b = __builtin_amdgcn_fractf(xf * n1);
+  const float r = __builtin_amdgcn_fractf(a + b + xf * n2);
+  c = __builtin_amdgcn_cosf(r);
+  s = __builtin_amdgcn_sinf(r);
+}
+
 // 64-bit transpose read of 16-bit elements (ds_read_b64_tr_b16): within each group of
 // 16 lanes, value j of output lane 4a + c is element c of the 64-bit row read by lane 4j + a.
 __device__ __forceinline__ s16x4 lds_read_tr16(const unsigned char* p) {
@@ -234,8 +247,16 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   // softmax applies exp2 to the MFMA result directly, one vector operation per score fewer.
   // (Scaling general phi_q by log2(e) in the kernel would round it a second time and break
   // factors that are exact by construction, such as split pieces.)
-  constexpr bool FOLD = Elem<QT>::KW > 1 && MODE == 3;
+  // MODE 4: Sandwich with its cos / sin factor columns formed in the kernel (the pages'
+  // in-kernel factor tiles, rebuttal answers to Reviewer BRmd, Q2 and Reviewer UJUf, Q1):
+  // phi_q in exp2 units (as MODE 3) from the query index at the start, and each key tile's
+  // phi_k region written into LDS by the loader wavefronts instead of copied; nothing is read
+  // from memory for the factors.
+  constexpr bool SWJIT = MODE == 4;
+  constexpr bool FOLD = Elem<QT>::KW > 1 && (MODE == 3 || MODE == 4);
   static_assert(!JIT || (RP == 16 && sizeof(QT) == 2 && __is_same(PT, f16_t)), "in-kernel factors: 16-bit, RP 16");
+  static_assert(!SWJIT || (LOADER && sizeof(QT) == 2 && __is_same(PT, f16_t) && RP >= 16 && RP <= 64),
+                "in-kernel Sandwich factors: 16-bit with loader wavefronts, RP 16..64");
   constexpr int KW = Elem<QT>::KW;        // k elements per lane per MFMA
   constexpr int KS = 2 * KW;              // k per MFMA
   constexpr int CE = 16 / ES;             // elements per 16-byte chunk
@@ -399,18 +420,21 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   if constexpr (LOADER) {
     static_assert(PHI_DMA, "the loaders copy phi_k directly");
     if (wave >= NW) {
-      constexpr int PER = (NDMA + NLW - 1) / NLW;   // most loads per loader wavefront and tile
-      constexpr int PMIN = NDMA / NLW;              // fewest
+      // loads m = 0 .. NLD-1 of a tile, tile load n_of(m) (MODE 4 skips the phi_k region)
+      constexpr int NLD = NDMA - (SWJIT ? PCH : 0);
+      constexpr int PER = (NLD + NLW - 1) / NLW;    // most loads per loader wavefront and tile
+      constexpr int PMIN = NLD / NLW;               // fewest
       static_assert(PMIN >= 1 && PMIN <= 15, "loads per wavefront and tile");
+      auto n_of = [&](int m) __attribute__((always_inline)) { return SWJIT && m >= KCH ? m + PCH : m; };
       const int lw = wave - NW;
       int rowi[PER], cbyte[PER];
       uint32_t off[PER];
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
-        const int n = lw + NLW * i;
+        const int n = n_of(lw + NLW * i);
         rowi[i] = cbyte[i] = 0;
         off[i] = 0;
-        if (n < NDMA) {
+        if (lw + NLW * i < NLD) {
           const TileSlot d = slot_of(n);
           rowi[i] = d.row;
           cbyte[i] = loader_src_byte(d, KCH, npch);
@@ -427,9 +451,9 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
         kbv = min(kbv, (nkt - 1) * BN);
 #pragma unroll
         for (int i = i0; i < i1; ++i) {
-          const int n = lw + NLW * i;
+          const int n = n_of(lw + NLW * i);
           const int region = n < KCH ? 0 : n < KCH + PCH ? 1 : 2;
-          if (n < NDMA && (region == 2 ? do_v : do_k)) {
+          if (lw + NLW * i < NLD && (region == 2 ? do_v : do_k)) {
             const int kb = region == 2 ? kbv : kbk;
             const int stride = region == 0 ? p.sk[2] : region == 1 ? p.spk[2] : p.sv[2];
             const char* base = region == 0 ? (const char*)(Kp + (int64_t)kb * p.sk[2])
@@ -442,18 +466,63 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
           }
         }
       };
+      // MODE 4: the phi_k region of each tile, [cos(j w_f), sin(j w_f)] in f16 for the 64 keys j
+      // of the tile and the RP / 2 column pairs f (zero past the C / 2 frequencies).  Loader lane
+      // g = 64 lw + lane owns pair f = g % NPAIR of the rows g / NPAIR + RSTEP m.  With the tile's
+      // first key kb, cos / sin (kb + r) w = rotation of (cos r w, sin r w) by kb w: the offsets r
+      // are evaluated once (fp32, exact revolution reduction), the rotation by kb w advances by 64 w
+      // per tile in fp64 (rotation of 64 w from the host in fp64), so no error builds up.
+      constexpr int NPAIR = SWJIT ? RP / 2 : 4;
+      constexpr int RSTEP = NLW * 64 / NPAIR;
+      constexpr int NROW = 64 / RSTEP;
+      double bc = 1.0, bs = 0.0, rc = 1.0, rs = 0.0;
+      float tc[NROW], ts[NROW];
+      uint32_t woff[NROW];
+      if constexpr (SWJIT) {
+        const int g = lw * 64 + lane;
+        const int f = g % NPAIR;
+        const bool live = f < p.sw_pairs;
+        rc = live ? p.sw_rot[0][f] : 1.0;
+        rs = live ? p.sw_rot[1][f] : 0.0;
+#pragma unroll
+        for (int m = 0; m < NROW; ++m) {
+          const int r = g / NPAIR + RSTEP * m;
+          sincos_rev(r, p.sw_nu[0][f], p.sw_nu[1][f], p.sw_nu[2][f], tc[m], ts[m]);
+          tc[m] *= live ? 1.f : 0.f;
+          ts[m] *= live ? 1.f : 0.f;
+          woff[m] = KREG + r * PCH * 16 + 16 * ((f >> 2) ^ swz_key(PCH, r)) + 4 * (f & 3);
+        }
+      }
+      auto gen_phk = [&](unsigned char* dK) __attribute__((always_inline)) {
+        if constexpr (SWJIT) {
+          const float c = (float)bc, sn = (float)bs;
+#pragma unroll
+          for (int m = 0; m < NROW; ++m) {
+            const f16x2 v = {(f16_t)(c * tc[m] - sn * ts[m]), (f16_t)(sn * tc[m] + c * ts[m])};
+            *(uint32_t*)(dK + woff[m]) = __builtin_bit_cast(uint32_t, v);
+          }
+          const double nc = bc * rc - bs * rs;
+          bs = bs * rc + bc * rs;
+          bc = nc;
+        }
+      };
+      gen_phk(sK0);
+      gen_phk(sK1);
       loads(0, PER, 0, 0, sK0, sV0, true, true);          // K'(0), V(0)
       loads(0, PER, BN, 0, sK1, sV0, true, false);        // K'(1)
       __syncthreads();                                    // (waits for them)
+      gen_phk(sK2);
       loads(0, PER, 2 * BN, BN, sK2, sV1, true, true);    // K'(2), V(1)
       __builtin_amdgcn_s_barrier();
       auto lstep = [&](int t, unsigned char* kd, unsigned char* vd) __attribute__((always_inline)) {
         const int kb = t * BN;
+        gen_phk(kd);
         loads(0, PER / 2, kb + 3 * BN, kb + 2 * BN, kd, vd, true, true);
         __builtin_amdgcn_s_barrier();
         loads(PER / 2, PER, kb + 3 * BN, kb + 2 * BN, kd, vd, true, true);
-        // vmcnt(PMIN): at most PMIN loads outstanding, so all of the previous tile's are done
-        __builtin_amdgcn_s_waitcnt(PMIN | 0x0F70);
+        // vmcnt(PMIN): at most PMIN loads outstanding, so all of the previous tile's are done;
+        // MODE 4 also waits for its LDS writes (lgkmcnt(0))
+        __builtin_amdgcn_s_waitcnt(PMIN | (SWJIT ? 0x0070 : 0x0F70));
         __builtin_amdgcn_s_barrier();
       };
       for (int t = 0; t < nkt; t += 3) {
@@ -506,7 +575,24 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
     const u32x4 r = __builtin_bit_cast(u32x4, v);
     return hf ? u32x4{0u, 0u, 0u, 0u} : r;
   };
-  if constexpr (JIT) {
+  if constexpr (SWJIT) {
+    // phi_q(i) in exp2 units: lane half h of k-step t holds column pairs f = 8t + 4h + e (e < 4)
+    // of the query row, [cos(i w_f), sin(i w_f)] log2(e), zero past the C / 2 frequencies
+#pragma unroll
+    for (int t = 0; t < PSTEPS; ++t) {
+      f16x8 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int f = 8 * t + 4 * hf + e;
+        float c, sn;
+        sincos_rev(qclamp, p.sw_nu[0][f], p.sw_nu[1][f], p.sw_nu[2][f], c, sn);
+        const float w = f < p.sw_pairs ? LOG2E : 0.f;
+        v[2 * e] = (f16_t)(c * w);
+        v[2 * e + 1] = (f16_t)(sn * w);
+      }
+      pf[t] = __builtin_bit_cast(u32x4, v);
+    }
+  } else if constexpr (JIT) {
     const f16x2 ix = jit_pair(qclamp);
     const f16x8 v = {jm_hi, jm_hi, jm_lo, jm_lo, (f16_t)(-(float)ix[0]), (f16_t)(-(float)ix[1]),
                      (f16_t)(-(float)ix[0]), (f16_t)(-(float)ix[1])};

@@ -31,7 +31,14 @@ struct AttnParams {
   // in-kernel ALiBi factors (mode 2): slope of head h as two f16 values, bits
   // m_hi | m_lo << 16 with m_hi + m_lo = m_h to 22 bits
   uint32_t alibi_m[128];
+  // in-kernel Sandwich factors (mode 4): C / 2 frequencies w_f; nu_f = w_f / (2 pi) as three
+  // fp32 pieces (the first two with at most 8 significant bits), and the rotation by 64 w_f
+  // (cos, sin) in fp64; sw_pairs = C / 2
+  float sw_nu[3][32];
+  double sw_rot[2][32];
+  int sw_pairs;
 };
+constexpr int kMaxSandwichPairs = 32;
 constexpr int kMaxJitHeads = 128;
 constexpr int kAttnBlockM = 256;   // query rows per attention workgroup
 constexpr int kAttnKeyTile = 64;   // keys per LDS tile of the attention kernels

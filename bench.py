@@ -77,8 +77,8 @@ def algorithmic_bytes(w, es: int, phi_es: int, phi_rows: int) -> float:
     return qkvo + 2.0 * phi_rows * w.R * phi_es
 
 
-def harness_file(w) -> str:
-    return os.path.join(ROOT, "profiles", f"harness_{w.name}.json")
+def harness_file(w, jit: bool = False) -> str:
+    return os.path.join(ROOT, "profiles", f"harness_{w.name}{'_jit' if jit else ''}.json")
 
 
 def cpu_oracle_baseline(w, budget_s: float, factors=None):
@@ -163,8 +163,9 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-bias baseline")
     ap.add_argument("--cold-launches", type=int, default=21,
                     help="launches timed one by one after a cache flush (median reported; 0 = skip)")
-    ap.add_argument("--alibi-jit", action="store_true",
-                    help="ALiBi workloads: factors formed inside the kernel (fb_attn_fwd_alibi), no factor step")
+    ap.add_argument("--jit", "--alibi-jit", dest="jit", action="store_true",
+                    help="exact biases: factors formed inside the kernel (fb_attn_fwd_alibi / fb_attn_fwd_sandwich), "
+                         "no factor step")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (fb_attn_bwd_lowrank) of the workload instead")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -194,9 +195,9 @@ def main():
     inp = synth.make_inputs(w, with_bias_source=svd)
     dt = {"bf16": torch.bfloat16, "f32": torch.float32}[w.dtype]
     q, k, v = (torch.from_numpy(inp[n]).to(dt).to(dev) for n in "qkv")
-    jit = args.alibi_jit
-    if jit and w.bias != "alibi":
-        raise SystemExit("--alibi-jit needs an ALiBi workload")
+    jit = args.jit
+    if jit and w.bias not in ("alibi", "sandwich"):
+        raise SystemExit("--jit needs an ALiBi or Sandwich workload")
     mul = w.bias == "mulbias_cos"
     # 16-bit workloads take phi_q in exp2 units (phi_q log2(e), rounded once): the kernel then
     # skips one operation per score.
@@ -254,8 +255,10 @@ def main():
 
     def stage2(e):
         """the fused attention kernel"""
-        if jit:
+        if jit and w.bias == "alibi":
             fb.fb_attn_fwd_alibi(q, k, v, causal=w.causal, out=out)
+        elif jit:
+            fb.fb_attn_fwd_sandwich(q, k, v, C=w.C, causal=w.causal, out=out)
         elif mul:
             fb.fb_attn_fwd_lowrank(e["q1"], e["k1"], v, e["phi_q"], e["phi_k"], causal=w.causal, scale=1.0, out=out)
         elif use_log2:
@@ -368,11 +371,11 @@ def main():
     else:
         alg_bytes = algorithmic_bytes(w, es, phi_es, fH * w.N)
     counters = None
-    hf = harness_file(w)
+    hf = harness_file(w, jit)
     if os.path.exists(hf):
         with open(hf) as f:
             hr = json.load(f)
-        if hr.get("kernel_source_hash") == kernel_source_hash() and hr.get("entry") == entry_name(use_log2, jit, mul):
+        if hr.get("kernel_source_hash") == kernel_source_hash() and hr.get("entry") == entry_name(use_log2, jit, mul, w):
             counters = {k2: hr.get(k2) for k2 in ("bytes_per_launch", "fetch_bytes", "write_bytes", "mfma_busy",
                                                   "sclk_mhz_counters", "trace_avg_us")}
             counters["hbm_gbs"] = round(hr["bytes_per_launch"] / (kern_ms * 1e-3) / 1e9, 1) \
@@ -401,10 +404,10 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D, "R": w.R, "causal": w.causal,
                    "factor_dtype": "f16" if phi_dt == torch.float16 else "f32", "factor_split": split,
                    "factor_columns": R_used, "factor_columns_padded": R_cols,
-                   "factor_units": "exp2 (phi_q log2(e))" if use_log2 else "natural",
+                   "factor_units": "exp2 (phi_q log2(e))" if (use_log2 or (jit and w.bias == "sandwich")) else "natural",
                    "flops_per_step": F,
                    **({"bias_op": "multiplicative", "expanded_width": w.D * w.R} if mul else {}),
-                   **({"factors": "in-kernel (fb_attn_fwd_alibi)"} if jit else {}),
+                   **({"factors": f"in-kernel ({entry_name(use_log2, jit, mul, w)})"} if jit else {}),
                    **({"factors": "host SVD per head (fb_svd_factors, not timed)", "svd": svd_info} if svd else {})},
         "pct_mfma_peak": round(100.0 * value / peak, 2),
         "kernel_ms": round(kern_ms, 4),
@@ -422,16 +425,16 @@ def main():
                      "traffic": counters["bytes_per_launch"] if counters else None,
                      "algorithmic_bytes": alg_bytes,
                      "timing": "average of the timed launches (HIP events on the launch stream)",
-                     "kernel": f"attn_fwd_kernel ({entry_name(use_log2, jit, mul)})"},
+                     "kernel": f"attn_fwd_kernel ({entry_name(use_log2, jit, mul, w)})"},
         "counters": counters,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
 
 
-def entry_name(use_log2: bool, jit: bool, mul: bool) -> str:
+def entry_name(use_log2: bool, jit: bool, mul: bool, w=None) -> str:
     if jit:
-        return "fb_attn_fwd_alibi"
+        return "fb_attn_fwd_sandwich" if w is not None and w.bias == "sandwich" else "fb_attn_fwd_alibi"
     if use_log2:
         return "fb_attn_fwd_lowrank_log2"
     return "fb_attn_fwd_lowrank"
@@ -535,13 +538,13 @@ def _run_child(cmd, log, timeout_s):
 def profile_harness(args) -> int:
     import synth
     w = synth.workload(args.workload)
-    out_root = os.path.join(ROOT, "gpurun_out", "harness", w.name)
+    out_root = os.path.join(ROOT, "gpurun_out", "harness", w.name + ("_jit" if args.jit else ""))
     os.makedirs(out_root, exist_ok=True)
     py = sys.executable or "python3"
     bench = os.path.join(ROOT, "bench.py")
     base = [py, bench, "--workload", w.name, "--cpu-budget", "0", "--cold-launches", "0"]
-    if args.alibi_jit:
-        base.append("--alibi-jit")
+    if args.jit:
+        base.append("--jit")
     # 1. kernel trace of the timed command (steps / warm-up as given)
     trace_cmd = ["rocprofv3", "--kernel-trace", "--stats", "-d", os.path.join(out_root, "trace"), "-o", "trace",
                  "--output-format", "csv", "--"] + base + ["--steps", str(args.steps), "--warmup", str(args.warmup),
@@ -570,8 +573,8 @@ def profile_harness(args) -> int:
 
     # ---- parse
     stats = _csv_rows(os.path.join(out_root, "trace", "**", "*kernel_stats.csv"))
-    entry = entry_name(not (args.alibi_jit or w.bias == "mulbias_cos") and w.dtype != "f32", args.alibi_jit,
-                       w.bias == "mulbias_cos")
+    entry = entry_name(not (args.jit or w.bias == "mulbias_cos") and w.dtype != "f32", args.jit,
+                       w.bias == "mulbias_cos", w)
 
     def is_attn(name):
         return "attn_fwd_kernel" in name
@@ -622,7 +625,11 @@ def profile_harness(args) -> int:
     w_k, w_c = counter("write", step_pred), counter("write", copy_pred)
     busy = counter("busy", step_pred)
     calib = 512 * 1024.0                                     # KiB copied by the calibration run
-    res = {"workload": w.name, "entry": entry, "kernel": kname, "kernel_source_hash": kernel_source_hash(),
+    src_hash = kernel_source_hash()
+    if args.profile_reparse and os.path.exists(harness_file(w, args.jit)):
+        with open(harness_file(w, args.jit)) as f:          # the sources the counters were taken with
+            src_hash = json.load(f).get("kernel_source_hash", src_hash)
+    res = {"workload": w.name, "entry": entry, "kernel": kname, "kernel_source_hash": src_hash,
            "trace_avg_us": round(kavg, 2), "commands": cmds}
     if "FETCH_SIZE" in f_k and "FETCH_SIZE" in f_c and "WRITE_SIZE" in w_k and "WRITE_SIZE" in w_c:
         fs, ws = calib / f_c["FETCH_SIZE"], calib / w_c["WRITE_SIZE"]
@@ -642,15 +649,15 @@ def profile_harness(args) -> int:
         res["counter_run_us"] = round(dur[len(dur) // 2], 2)
         res["sclk_mhz_counters"] = round(busy["GRBM_COUNT"] / N_XCD / dur[len(dur) // 2], 0)
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(harness_file(w), "w") as f:
+    with open(harness_file(w, args.jit), "w") as f:
         json.dump(res, f, indent=1)
 
     # ---- markdown summary
-    shape = f"b{w.B}h{w.H}n{w.N}d{w.D}" + (f"r{w.R}" if not args.alibi_jit else "")
+    shape = f"b{w.B}h{w.H}n{w.N}d{w.D}" + (f"r{w.R}" if not (args.jit and w.bias == "alibi") else "")
     md = os.path.join(ROOT, "profiles", f"{entry.replace('fb_', '')}_{w.name}_{shape}.md")
     lines = [f"# `{entry}` on the {w.name} workload (B={w.B} H={w.H} N={w.N} D={w.D} R={w.R}, {w.dtype})", "",
              "Written by `python bench.py --profile --workload " + w.name +
-             (" --alibi-jit" if args.alibi_jit else "") + f" --steps {args.steps} --warmup {args.warmup}` "
+             (" --jit" if args.jit else "") + f" --steps {args.steps} --warmup {args.warmup}` "
              "(the rocprofv3 harness in bench.py); raw CSV under gpurun_out/harness/.", "",
              "Kernel trace (rocprofv3 --kernel-trace --stats):", "", "```", cmds["trace"], "```", "",
              "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
@@ -680,7 +687,7 @@ def profile_harness(args) -> int:
                      f"(the dispatch's own timestamps) = {res['sclk_mhz_counters']:.0f} MHz.")
     with open(md, "w") as f:
         f.write("\n".join(lines) + "\n")
-    print(json.dumps({"harness": os.path.relpath(harness_file(w), ROOT), "summary": os.path.relpath(md, ROOT),
+    print(json.dumps({"harness": os.path.relpath(harness_file(w, args.jit), ROOT), "summary": os.path.relpath(md, ROOT),
                       "trace_avg_us": res["trace_avg_us"], "bytes_per_launch": res.get("bytes_per_launch"),
                       "mfma_busy": res.get("mfma_busy")}), flush=True)
     return 0

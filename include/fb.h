@@ -345,6 +345,27 @@ fb_status fb_mulbias_expand(const fb_attn_args* a, const void* phi_q, const void
  */
 fb_status fb_attn_fwd_alibi(const fb_attn_args* a, const double* slopes_host, hipStream_t stream);
 
+/*
+ * fb_attn_fwd_sandwich -- O = softmax(s Q K^T + b) V for the Sandwich bias
+ * b[i,j] = sum_{k=1}^{C/2} cos((i - j) w_k), w_k = 10000^(-2k/C), with its cos / sin factor
+ * columns formed inside the kernel (FlashBias rebuttal, answer to Reviewer UJUf, Q1 (1)-(2):
+ * the factor functions phi(i) = [cos(i w_1), sin(i w_1), ...] with b = phi phi^T; answer to
+ * Reviewer BRmd, Q2: the factor tiles are generated in the kernel instead of being loaded).
+ * No factor tensor exists: phi_q of each query (in exp2 units, times log2(e)) is formed once
+ * per query row and rounded to f16; each key tile's phi_k (f16) is written into on-chip memory
+ * by the kernel, rotating exact per-offset values by the tile's first key in fp64.
+ *
+ *   a   shared arguments; a->dt FB_BF16 or FB_F16, a->D <= 64
+ *   C   even, 2 <= C <= 64 (the Sandwich channel count; C/2 frequencies)
+ * Limits: N <= 65536.
+ * Numerics: as fb_attn_fwd_lowrank_log2 with f16 factor columns (C of them, zero-padded to
+ * 16, 32 or 64); the factor values are within about 1e-6 of the exact cos / sin before
+ * their f16 rounding.
+ * Errors: as fb_attn_fwd_lowrank; FB_EINVAL for an odd C or C < 2; FB_EUNSUPPORTED for
+ * fp32, D > 64, C > 64 or N > 65536.
+ */
+fb_status fb_attn_fwd_sandwich(const fb_attn_args* a, int C, hipStream_t stream);
+
 /* Outputs and workspace of the attention backward. */
 typedef struct {
   const void* dout;    /* device [B][H][N][D], strides sdo: the upstream gradient dO (a->dt) */

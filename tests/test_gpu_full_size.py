@@ -92,6 +92,25 @@ def test_full_size_alibi_in_kernel(fb):
     compare_whole(o, ref, w.B, w.H, "bf16", "gpt2 ALiBi in-kernel factors", lse)
 
 
+def test_full_size_sandwich_in_kernel(fb):
+    """The Sandwich workload (B4 H8 N4096 D64, C = 64) with the cos / sin factors formed in the
+    kernel (fb_attn_fwd_sandwich) against the oracle's sum of cosines: every row."""
+    import torch
+    w = synth.workload("sandwich")
+    inp = synth.make_inputs(w)
+    lse = _lse(w)
+    o = fb.fb_attn_fwd_sandwich(to_dev(inp["q"], "bf16"), to_dev(inp["k"], "bf16"), to_dev(inp["v"], "bf16"),
+                                C=w.C, lse=lse)
+    torch.cuda.synchronize()
+    bias = oracle.sandwich_bias(w.N, w.C)
+
+    def ref(b, h):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ro, rl = oracle.attention(inp["q"][sl], inp["k"][sl], inp["v"][sl], bias=bias)
+        return ro[0, 0], rl[0, 0]
+    compare_whole(o, ref, w.B, w.H, "bf16", "Sandwich in-kernel factors", lse)
+
+
 def test_full_size_mulbias(fb):
     """The multiplicative workload (b_ij = cos(i - j), B4 H8 N4096 D64 R2, fp32 factors) through
     fb_attn_fwd_mulbias: every row against the oracle's element-wise definition."""

@@ -645,6 +645,38 @@ def test_alibi_in_kernel_factors(fb, shape, dt, causal, slopes):
     np.testing.assert_allclose(gl if rows is None else gl[:, :, rows], rl, rtol=0, atol=2e-2)
 
 
+# ---------------------------------------------------- in-kernel Sandwich factors ---
+SWJIT = [
+    # (B, H, N, D, C, dtype, causal, rows sampled)
+    (1, 2, 520, 64, 64, "bf16", False, False),
+    (2, 1, 300, 32, 32, "bf16", True, False),
+    (1, 3, 200, 16, 16, "f16", False, False),
+    (1, 1, 129, 64, 2, "bf16", True, False),
+    (1, 2, 64, 64, 48, "f16", False, False),
+    (1, 1, 12000, 64, 64, "bf16", True, True),     # key indices far past one tile table
+]
+
+
+@pytest.mark.parametrize("B,H,N,D,C,dt,causal,sampled", SWJIT, ids=[f"swjit-{i}" for i in range(len(SWJIT))])
+def test_sandwich_in_kernel_factors(fb, B, H, N, D, C, dt, causal, sampled):
+    """Sandwich with the cos / sin factors formed in the kernel (fb_attn_fwd_sandwich) against
+    the oracle's bias from its defining sum of cosines: O and LSE."""
+    import torch
+    r = np.random.default_rng(1100 + N + C)
+    q, k, v = (synth.round_to(r.standard_normal((B, H, N, D)) * 0.5, dt) for _ in range(3))
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda:0")
+    say(f"in-kernel Sandwich B={B} H={H} N={N} D={D} C={C} {dt} causal={causal}")
+    o = fb.fb_attn_fwd_sandwich(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), C=C, causal=causal, lse=lse)
+    torch.cuda.synchronize()
+    rows = sample_rows(N, 64, seed=6) if sampled else None
+    ro, rl = oracle.attention(q, k, v, bias=oracle.sandwich_bias(N, C), causal=causal, rows=rows)
+    got, gl = to_np(o), lse.cpu().double().numpy()
+    if sampled:
+        got, gl = got[:, :, rows], gl[:, :, rows]
+    assert_close(got, ro, dt, f"in-kernel Sandwich N={N} C={C}")
+    np.testing.assert_allclose(gl, rl, rtol=0, atol=2e-2)
+
+
 # ------------------------------------------------------- seeded random sweep ----
 def _sweep_configs(n=16, seed=20260200):
     """Small random configurations across the supported space (shapes, ranks, factor
