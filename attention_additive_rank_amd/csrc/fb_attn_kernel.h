@@ -669,14 +669,30 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   float m_run = -INFINITY;
   float l_run = 0.f;      // row sum (vector-unit path)
   float M2 = 0.f;                 // FOLD: running max in exp2 units
-  f32x16 minit = f32x16{};        // FOLD: -M2 in every register, the score chains' start
-  auto chain_init = [&]() __attribute__((always_inline)) { return FOLD ? minit : f32x16{}; };
   // Low-rank mode, 16-bit: the row sum of P rides on the matrix core as one more MFMA per
   // k-step, with an A operand whose row 0 is all ones (lane 0 of each half) and rows 1..31
   // zero: row 0 of lacc (register 0 of the lanes of half 0) is then sum_k P[k][query], and
   // the rescaling of O scales it too.  This takes 32 adds per tile off the vector unit.
-  // (Dense-bias mode keeps the adds: its bias registers leave no room for lacc.)
-  constexpr bool MROW = KW > 1 && MODE != 1 && !FOLD;
+  // (Dense-bias mode keeps the adds: its bias registers leave no room for lacc.  In exp2
+  // units at rank 64, where the score chain is longest, the extra MFMAs measured slower
+  // than the adds, so that case keeps them too.)
+  constexpr bool MROW = KW > 1 && MODE != 1 && (!FOLD || RP < 64);
+  // FOLD: every score chain starts from -M2 in all 16 registers.  Without MROW a copy of
+  // that vector is kept (minit); with MROW its registers hold lacc instead and the vector is
+  // written into the accumulator when the chain starts.
+  f32x16 minit = f32x16{};
+  auto chain_init = [&]() __attribute__((always_inline)) {
+    if constexpr (FOLD && !MROW) {
+      return minit;
+    } else {
+      f32x16 c = f32x16{};
+      if constexpr (FOLD) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) c[r] = -M2;
+      }
+      return c;
+    }
+  };
   f32x16 lacc = f32x16{};
   const uint32_t one2 = __is_same(QT, bf16_t) ? 0x3F803F80u : 0x3C003C00u;   // two 1.0 values of QT
   const u32x4 ones = ln == 0 ? u32x4{one2, one2, one2, one2} : u32x4{0u, 0u, 0u, 0u};
@@ -926,13 +942,18 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
           const float alpha = __builtin_amdgcn_exp2f(-d);
 #pragma unroll
           for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-          l_run *= alpha;
+          if constexpr (MROW)
+            lacc *= alpha;
+          else
+            l_run *= alpha;
         }
         M2 += d;
 #pragma unroll
         for (int kb2 = 0; kb2 < NKB; ++kb2) sacc[kb2] -= d;
+        if constexpr (!MROW) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) minit[r] = -M2;
+          for (int r = 0; r < 16; ++r) minit[r] = -M2;
+        }
       }
       typedef QT T8 __attribute__((ext_vector_type(8)));
       float ls[4] = {0.f, 0.f, 0.f, 0.f};
@@ -945,11 +966,11 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
           for (int j = 0; j < 8; ++j) {
             const float e = __builtin_amdgcn_exp2f(sacc[kb2][8 * u + j]);
             pb[j] = from_f32<QT>(e);
-            ls[j & 3] += e;
+            if constexpr (!MROW) ls[j & 3] += e;
           }
           pfrag[kb2 * 2 + u] = __builtin_bit_cast(u32x4, pb);
         }
-      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      if constexpr (!MROW) l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
       return;
     }
     const bool grow = mx > m_run + RESCALE_GAP;

@@ -252,8 +252,10 @@ fb_status fb_attn_fwd_lowrank(const fb_attn_args* a, const void* phi_q, const vo
  * Q2: the factor columns are concatenated with queries and keys); only the unit of
  * phi_q differs.
  * Arguments, alignment and errors as fb_attn_fwd_lowrank, for bf16 / f16 Q/K/V
- * only (FB_EUNSUPPORTED for fp32).  Numerics differ in two roundings: Q s log2(e)
- * is rounded to dt, and the row sum of P is taken in fp32 before P is rounded.
+ * only (FB_EUNSUPPORTED for fp32).  Numerics differ in one rounding, Q s log2(e) is
+ * rounded to dt, and for R > 32 (factor columns padded to 64) in one more: the row sum of
+ * P is taken in fp32 before P is rounded (for R <= 32 it is taken from the rounded P, as
+ * in fb_attn_fwd_lowrank).
  * R == 0 is plain attention in the same exp2 form.  LSE (when requested) is the
  * natural-log value as for fb_attn_fwd_lowrank; fb_attn_bwd_lowrank takes natural-unit
  * factors (phi_q ln(2) for the factors given here).
@@ -359,7 +361,7 @@ fb_status fb_attn_fwd_alibi(const fb_attn_args* a, const double* slopes_host, hi
  *   C   even, 2 <= C <= 64 (the Sandwich channel count; C/2 frequencies)
  * Limits: N <= 65536.
  * Numerics: as fb_attn_fwd_lowrank_log2 with f16 factor columns (C of them, zero-padded to
- * 16, 32 or 64); the factor values are within about 1e-6 of the exact cos / sin before
+ * 16, 32 or 64, which sets R for the row-sum rule there); the factor values are within about 1e-6 of the exact cos / sin before
  * their f16 rounding.
  * Errors: as fb_attn_fwd_lowrank; FB_EINVAL for an odd C or C < 2; FB_EUNSUPPORTED for
  * fp32, D > 64, C > 64 or N > 65536.
