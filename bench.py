@@ -17,8 +17,8 @@ inputs (speedup), and the fp64 CPU oracle timed on a bounded sample of the same 
 
 Before the warm-up steps the step runs untimed for --settle-ms of wall time: the GPU
 raises its shader clock over tens of milliseconds of sustained load, and a handful of
-warm-up steps alone would time part of that ramp.  The shader clock seen during the
-settle phase (amdsmi, when available) is reported.
+warm-up steps alone would time part of that ramp.  (The shader clock itself is read in
+the --profile harness, from GRBM_COUNT over a dispatch's own timestamps.)
 
 ``--profile`` is the rocprofv3 harness: before touching the GPU it runs this script
 under rocprofv3 in child processes (a kernel trace, then one counter pass each for
@@ -127,30 +127,6 @@ def cpu_oracle_baseline(w, budget_s: float, factors=None):
                       f"bias materialisation {t_bias:.2f}s not included", "seconds": round(t_attn, 2)}
 
 
-class ClockReader:
-    """Current shader (GFX) clock of the first GPU through amdsmi, or None where unavailable."""
-
-    def __init__(self):
-        self.h = None
-        try:
-            import amdsmi
-            amdsmi.amdsmi_init()
-            hs = amdsmi.amdsmi_get_processor_handles()
-            if len(hs) == 1:
-                self.amdsmi, self.h = amdsmi, hs[0]
-        except Exception:
-            self.h = None
-
-    def mhz(self):
-        if self.h is None:
-            return None
-        try:
-            c = self.amdsmi.amdsmi_get_clock_info(self.h, self.amdsmi.AmdSmiClkType.GFX)
-            return float(c["clk"])
-        except Exception:
-            return None
-
-
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -178,8 +154,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; multi-GPU runs are not provided "
-                                   "(every (batch, head) pair is independent: see DESIGN.md for how it would shard)"}))
+        print(json.dumps({"error": "only one GPU is supported; multi-GPU runs are not provided (every (batch, head) "
+                                   "pair is independent, so the work would shard over GPUs by (batch, head) with "
+                                   "the factors replicated)"}))
         sys.exit(2)
     if args.profile:
         sys.exit(profile_harness(args))
@@ -274,8 +251,7 @@ def main():
             raise SystemExit("--backward covers the additive workloads")
         return bench_backward(args, w, fb, torch, q, k, v, pq, pk, stage1, out, dev, stream)
 
-    clock = ClockReader()
-    settle = settle_phase(torch, step, args.settle_ms, clock)
+    settle = settle_phase(torch, step, args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -332,7 +308,7 @@ def main():
         else:
             bias = fb.fb_make_dense_bias("alibi", w.H, w.N, dtype=dt)
         dstep = lambda: fb.fb_attn_fwd_densebias(q, k, v, bias, causal=w.causal, out=out)
-        settle_phase(torch, dstep, args.settle_ms / 4, None)
+        settle_phase(torch, dstep, args.settle_ms / 4)
         for _ in range(args.warmup):
             dstep()
         torch.cuda.synchronize()
@@ -440,26 +416,18 @@ def entry_name(use_log2: bool, jit: bool, mul: bool, w=None) -> str:
     return "fb_attn_fwd_lowrank"
 
 
-def settle_phase(torch, fn, ms: float, clock):
-    """Untimed steps, enqueued 16 at a time, for ``ms`` of wall time; samples the shader
-    clock while the GPU works.  Returns {"steps", "ms", "sclk_mhz"}."""
+def settle_phase(torch, fn, ms: float):
+    """Untimed steps, enqueued 16 at a time, for ``ms`` of wall time.  Returns {"steps", "ms"}."""
     if ms <= 0:
-        return {"steps": 0, "ms": 0.0, "sclk_mhz": None}
+        return {"steps": 0, "ms": 0.0}
     t0 = time.time()
     n = 0
-    mhz = []
     while (time.time() - t0) * 1e3 < ms:
         for _ in range(16):
             fn()
         n += 16
-        if clock is not None:
-            m = clock.mhz()
-            if m:
-                mhz.append(m)
         torch.cuda.synchronize()
-    mhz = sorted(mhz[len(mhz) // 2:])       # the second half, after the ramp
-    return {"steps": n, "ms": round((time.time() - t0) * 1e3, 1),
-            "sclk_mhz": mhz[len(mhz) // 2] if mhz else None}
+    return {"steps": n, "ms": round((time.time() - t0) * 1e3, 1)}
 
 
 def bench_backward(args, w, fb, torch, q, k, v, pq_t, pk_t, stage1, out, dev, stream):
@@ -476,7 +444,7 @@ def bench_backward(args, w, fb, torch, q, k, v, pq_t, pk_t, stage1, out, dev, st
     dout = torch.from_numpy(g).to(q.dtype).to(dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     bstep = lambda: fb.fb_attn_bwd_lowrank(q, k, v, out, lse, dout, pq_t, pk_t, causal=w.causal, dq=dq, dk=dk, dv=dv)
-    settle = settle_phase(torch, bstep, args.settle_ms, ClockReader())
+    settle = settle_phase(torch, bstep, args.settle_ms)
     for _ in range(args.warmup):
         bstep()
     torch.cuda.synchronize()
@@ -549,8 +517,12 @@ def profile_harness(args) -> int:
     trace_cmd = ["rocprofv3", "--kernel-trace", "--stats", "-d", os.path.join(out_root, "trace"), "-o", "trace",
                  "--output-format", "csv", "--"] + base + ["--steps", str(args.steps), "--warmup", str(args.warmup),
                                                           "--settle-ms", str(args.settle_ms)]
-    if not args.profile_reparse and _run_child(trace_cmd, os.path.join(out_root, "trace.log"), 300):
-        return 1
+    hash_file = os.path.join(out_root, "kernel_source_hash")
+    if not args.profile_reparse:
+        with open(hash_file, "w") as f:                      # the sources these runs profile
+            f.write(kernel_source_hash() + "\n")
+        if _run_child(trace_cmd, os.path.join(out_root, "trace.log"), 300):
+            return 1
     # 2.-4. counter passes: short runs (every dispatch is serialised under --pmc), with one
     # 512 MiB device copy as the HBM calibration
     short = base + ["--steps", "3", "--warmup", "1", "--settle-ms", "0", "--no-dense", "--calib-copy-mib", "512"]
@@ -603,7 +575,9 @@ def profile_harness(args) -> int:
 
     durations = {}
 
-    def counter(name, kernel_pred):
+    def counter(name, kernel_pred, largest=False):
+        """Per-dispatch counter values of the matching kernels, averaged (largest: the
+        largest dispatch's, for the calibration copy among the run's other buffer copies)."""
         vals = {}
         for r in _csv_rows(os.path.join(out_root, name, "**", "*counter_collection.csv")):
             kn = r.get("Kernel_Name") or r.get("Kernel-Name") or ""
@@ -617,18 +591,20 @@ def profile_harness(args) -> int:
                 durations.setdefault(name, {})[cid] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
             except (KeyError, ValueError, TypeError):
                 pass
+        if largest:
+            return {c: max(d.values()) for c, d in vals.items() if d}
         return {c: sum(d.values()) / len(d) for c, d in vals.items() if d}
 
     step_pred = lambda kn: is_attn(kn) and mode_of(kn) != 1
     copy_pred = lambda kn: "copyBuffer" in kn
-    f_k, f_c = counter("fetch", step_pred), counter("fetch", copy_pred)
-    w_k, w_c = counter("write", step_pred), counter("write", copy_pred)
+    f_k, f_c = counter("fetch", step_pred), counter("fetch", copy_pred, largest=True)
+    w_k, w_c = counter("write", step_pred), counter("write", copy_pred, largest=True)
     busy = counter("busy", step_pred)
     calib = 512 * 1024.0                                     # KiB copied by the calibration run
     src_hash = kernel_source_hash()
-    if args.profile_reparse and os.path.exists(harness_file(w, args.jit)):
-        with open(harness_file(w, args.jit)) as f:          # the sources the counters were taken with
-            src_hash = json.load(f).get("kernel_source_hash", src_hash)
+    if os.path.exists(hash_file):                            # the sources the runs were taken with
+        with open(hash_file) as f:
+            src_hash = f.read().strip() or src_hash
     res = {"workload": w.name, "entry": entry, "kernel": kname, "kernel_source_hash": src_hash,
            "trace_avg_us": round(kavg, 2), "commands": cmds}
     if "FETCH_SIZE" in f_k and "FETCH_SIZE" in f_c and "WRITE_SIZE" in w_k and "WRITE_SIZE" in w_c:
