@@ -514,12 +514,11 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
       gen_phk(sK2);
       loads(0, PER, 2 * BN, BN, sK2, sV1, true, true);    // K'(2), V(1)
       __builtin_amdgcn_s_barrier();
+      // one barrier per tile (see the key loop of the compute wavefronts)
       auto lstep = [&](int t, unsigned char* kd, unsigned char* vd) __attribute__((always_inline)) {
         const int kb = t * BN;
         gen_phk(kd);
-        loads(0, PER / 2, kb + 3 * BN, kb + 2 * BN, kd, vd, true, true);
-        __builtin_amdgcn_s_barrier();
-        loads(PER / 2, PER, kb + 3 * BN, kb + 2 * BN, kd, vd, true, true);
+        loads(0, PER, kb + 3 * BN, kb + 2 * BN, kd, vd, true, true);
         // vmcnt(PMIN): at most PMIN loads outstanding, so all of the previous tile's are done;
         // MODE 4 also waits for its LDS writes (lgkmcnt(0))
         __builtin_amdgcn_s_waitcnt(PMIN | (SWJIT ? 0x0070 : 0x0F70));
@@ -1046,6 +1045,24 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   auto step = [&](int t, unsigned char* kt, unsigned char* kn, unsigned char* vt,
                   unsigned char* vn) __attribute__((always_inline)) {
     const int kb = t * BN;
+    if constexpr (LOADER) {
+      // One barrier per tile: group 0 runs MFMA(t) then softmax(t+1), group 1 the same
+      // sequence with its barrier between them, i.e. softmax(t) then MFMA(t) within a tile.
+      // Each wavefront goes on to its next phase as soon as its own work allows, so one
+      // wavefront's matrix work overlaps the other's softmax without either waiting at a
+      // barrier for the other's phase to end.  Both groups read K'(t+1) and V(t) in tile t;
+      // the loaders overwrite those buffers only after the barrier that ends it.  Group 1's
+      // softmax, which opens the tile and is followed by its MFMA phase, issues at a raised
+      // wavefront priority: group 0's softmax, which closes the tile, would otherwise take
+      // the vector unit from it where they overlap (the older wavefront wins the issue).
+      mma_phase(kn, kb + BN, vt);
+      if (grp == 1) __syncthreads();
+      if (grp == 1) __builtin_amdgcn_s_setprio(2);
+      if (t + 1 < nkt) softmax(t + 1);
+      __builtin_amdgcn_s_setprio(0);
+      if (grp == 0) __syncthreads();
+      return;
+    }
     if constexpr (KW > 1) {
       // past the last tile the scores of a stale buffer are computed and never used.
       // Causal: also the tiles past a wavefront's queries (near the diagonal) go through
@@ -1067,7 +1084,7 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
     if (!phk_fast && grp == 1 && t + 3 < nkt) phi_store(kn);
     __syncthreads();
   };
-  if (grp == 1) {
+  if (!LOADER && grp == 1) {
     // group 1's first phase: its loads of K'(2) (into K'(0)'s buffer, free now) and V(1),
     // and the phi_k region of tile 2
     dma_tile(2 * BN, BN, sK0, sV1, 2 < nkt, 1 < nkt);
@@ -1089,7 +1106,8 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
       if (t + 1 < nkt) step(t + 1, sK1, sK0, sV1, sV0);
     }
   }
-  if (grp == 0) __builtin_amdgcn_s_barrier();   // matches group 1's extra first phase
+  // matches group 1's extra first phase (with loader wavefronts: their final barrier)
+  if (LOADER || grp == 0) __builtin_amdgcn_s_barrier();
 
   // ---- epilogue: O = O / l, LSE = m + ln l -----------------------------------
   // register r of lane half hf in head-dim block db holds head dim 32 db + 8 (r / 4) + 4 hf + r % 4
