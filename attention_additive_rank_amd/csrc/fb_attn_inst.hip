@@ -13,16 +13,33 @@ namespace attn {
 
 template <typename QT, typename PT, int D, int RP, int MODE, typename BT, bool PHI_DMA>
 static fb_status launch_kernel(const AttnParams& p, hipStream_t stream) {
-  const int64_t grid = (int64_t)p.nqb * p.H * p.B;
   // loader wavefronts where their register budget (three wavefronts on one SIMD) holds
   constexpr bool LOADER = PHI_DMA && sizeof(QT) == 2 && D <= 64 && RP <= 64 && (MODE != 1 || sizeof(BT) == 2);
+  const bool causal = (p.flags & FLAG_CAUSAL) != 0;
+  // work items (b, h, query block); with more items than compute units, kernels that can
+  // take several items per workgroup get one workgroup per compute unit (ceil(items / CUs)
+  // items each: the same number of item-times as one item per workgroup, without a
+  // workgroup start and end per item)
+  AttnParams q = p;
+  const int64_t items = (int64_t)p.nqb * p.H * p.B;
+  q.n_items = (int)items;
+  q.ipw = 1;
+  if (!causal && attn_multi_item(D, RP, MODE, LOADER, false, (int)sizeof(QT))) {
+    const int ncu = device_cu_count();
+    if (ncu > 0 && items > ncu) q.ipw = (int)((items + ncu - 1) / ncu);
+  }
+  const int64_t grid = (items + q.ipw - 1) / q.ipw;
   const dim3 block(LOADER ? NT + NLW * 64 : NT);
-  if (p.flags & FLAG_CAUSAL)
+  if (causal)
     hipLaunchKernelGGL((attn_fwd_kernel<QT, PT, D, RP, MODE, BT, true, PHI_DMA, LOADER>), dim3((unsigned)grid), block, 0,
-                       stream, p);
-  else
+                       stream, q);
+  else if (q.ipw > 1) {
+    if constexpr (attn_multi_item(D, RP, MODE, LOADER, false, (int)sizeof(QT)))
+      hipLaunchKernelGGL((attn_fwd_kernel<QT, PT, D, RP, MODE, BT, false, PHI_DMA, LOADER, true>), dim3((unsigned)grid),
+                         block, 0, stream, q);
+  } else
     hipLaunchKernelGGL((attn_fwd_kernel<QT, PT, D, RP, MODE, BT, false, PHI_DMA, LOADER>), dim3((unsigned)grid), block, 0,
-                       stream, p);
+                       stream, q);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_error("attention launch failed: %s", hipGetErrorString(e));

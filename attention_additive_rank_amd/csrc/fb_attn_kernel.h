@@ -81,6 +81,14 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr float RESCALE_GAP = 8.0f / LOG2E;   // 2^8 in exp2 units, as a natural-log gap
 
+// Kernels whose workgroups take several work items ((b, h, query block) triples) one after
+// another, with one stream of key tiles across them and the next item's query rows loaded
+// while the current item runs: non-causal 16-bit kernels with loader wavefronts (not the
+// dense-bias mode) whose Q' fragments are narrow enough to hold the next item's as well.
+constexpr bool attn_multi_item(int D, int RP, int MODE, bool loader, bool causal, int es) {
+  return loader && !causal && es == 2 && MODE != 1 && D + RP <= 64;
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<bf16_t> { typedef u32x4 Frag; static constexpr int KW = 8; };
 template <> struct Elem<f16_t>  { typedef u32x4 Frag; static constexpr int KW = 8; };
@@ -196,6 +204,14 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_base) {
   __builtin_amdgcn_global_load_lds((global_void*)src, dst, 16, 0, 0);
 }
 
+// Workgroup barrier that orders LDS accesses only: outstanding global loads and stores
+// (prefetches, output stores) stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Scheduling-group pins of the matrix phase (see mma_phase): for group G, its MFMAs
 // (MPV in a P V group, NKB in a score group), then the LDS reads of group G + 2
 // (two transpose reads per head-dim block, or one 128-bit read per key block).
@@ -229,7 +245,10 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const unsigned char* p) {
 }
 
 // LOADER: NLW more wavefronts (one per SIMD) issue every tile copy (see the key loop).
-template <typename QT, typename PT, int D, int RP, int MODE, typename BT, bool CAUSAL, bool PHI_DMA, bool LOADER>
+// ITEMS: the instance that takes several work items per workgroup (attn_multi_item kernels
+// launched with more items than compute units); the one-item instance has none of its code.
+template <typename QT, typename PT, int D, int RP, int MODE, typename BT, bool CAUSAL, bool PHI_DMA, bool LOADER,
+          bool ITEMS = false>
 __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kernel(AttnParams p) {
   typedef typename Elem<QT>::Frag QFrag;
   typedef typename Elem<PT>::Frag PFrag;
@@ -309,8 +328,16 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   const int xcd = wg & 7, idx = wg >> 3;
   const int per = G >> 3, rem = G & 7;
   const int L = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
-  int qb = L % p.nqb;
-  int bh = L / p.nqb;
+  // work items: (b, h, query block), query block fastest; this workgroup takes items
+  // item0 .. item0 + nitems - 1 (one item unless MULTI)
+  constexpr bool MULTI = ITEMS && attn_multi_item(D, RP, MODE, LOADER, CAUSAL, ES);
+  int item0 = L, nitems = 1;
+  if constexpr (MULTI) {
+    item0 = L * p.ipw;
+    nitems = min(p.ipw, p.n_items - item0);
+  }
+  int qb = item0 % p.nqb;
+  int bh = item0 / p.nqb;
   if (CAUSAL) {
     // longest first over the whole grid (dispatch order): all last query blocks, then the
     // ones before; (b, h) fastest, so with B H a multiple of 8 each (b, h) stays on one
@@ -319,8 +346,8 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
     qb = p.nqb - 1 - wg / BH;
     bh = wg % BH;
   }
-  const int hh = bh % p.H;
-  const int bb = bh / p.H;
+  int hh = bh % p.H;
+  int bb = bh / p.H;
   const int N = p.N;
 
   const QT* Qp = (const QT*)p.q + ((int64_t)bb * p.sq[0] + (int64_t)hh * p.sq[1]);
@@ -336,9 +363,11 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   const BT* Bp = nullptr;
   if constexpr (MODE == 1) Bp = (const BT*)p.bias + ((int64_t)bb * p.sb[0] + (int64_t)hh * p.sb[1]);
 
-  const int q0 = qb * BM;
-  const int kend = CAUSAL ? min(N, q0 + BM) : N;
+  int q0 = qb * BM;
+  const int kend = CAUSAL ? min(N, q0 + BM) : N;   // (MULTI: not causal, the same for every item)
   const int nkt = (kend + BN - 1) / BN;
+  // the workgroup's key tiles in order: tile t of item i is step i nkt + t
+  const int nsteps = nitems * nkt;
 
   // ---- tile copies -----------------------------------------------------------------
   // Load n of a tile: n < KCH fills K-region bytes [1024 n, 1024 (n+1)), then the
@@ -442,23 +471,49 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
           off[i] = (uint32_t)(d.row * stride * ES + cbyte[i]);
         }
       }
-      // loads [i0, i1) of this wavefront for K'(kbk) into dK and V(kbv) into dV; tiles past
-      // the last are replaced by the last one (their copies land in buffers that nothing
-      // reads again)
-      auto loads = [&](int i0, int i1, int kbk, int kbv, unsigned char* dK, unsigned char* dV, bool do_k, bool do_v)
+      // Source of step vv of the workgroup's tile stream: the first rows of its K, phi_k and
+      // V tiles and its first key.  Steps past the last are replaced by the last one (their
+      // copies land in buffers that nothing reads again).
+      struct Src {
+        const char* k;
+        const char* pk;
+        const char* v;
+        int kb;
+      };
+      auto src_of = [&](int vv) __attribute__((always_inline)) {
+        vv = min(vv, nsteps - 1);
+        Src r;
+        if constexpr (MULTI) {
+          const int it = vv / nkt;
+          r.kb = (vv - it * nkt) * BN;
+          const int bhi = (item0 + it) / p.nqb;
+          const int64_t b = bhi / p.H, h = bhi % p.H;
+          r.k = (const char*)((const QT*)p.k + (b * p.sk[0] + h * p.sk[1] + (int64_t)r.kb * p.sk[2]));
+          r.v = (const char*)((const QT*)p.v + (b * p.sv[0] + h * p.sv[1] + (int64_t)r.kb * p.sv[2]));
+          r.pk = nullptr;
+          if constexpr (RP > 0 && !JIT)
+            r.pk = (const char*)((const PT*)p.phk + (b * p.spk[0] + h * p.spk[1] + (int64_t)r.kb * p.spk[2]));
+        } else {
+          r.kb = vv * BN;
+          r.k = (const char*)(Kp + (int64_t)r.kb * p.sk[2]);
+          r.pk = (const char*)(PKp + (int64_t)r.kb * p.spk[2]);
+          r.v = (const char*)(Vp + (int64_t)r.kb * p.sv[2]);
+        }
+        return r;
+      };
+      // loads [i0, i1) of this wavefront for K' of stream step vk into dK and V of step vv
+      // into dV
+      auto loads = [&](int i0, int i1, int vk, int vv, unsigned char* dK, unsigned char* dV, bool do_k, bool do_v)
           __attribute__((always_inline)) {
-        kbk = min(kbk, (nkt - 1) * BN);
-        kbv = min(kbv, (nkt - 1) * BN);
+        const Src sk = src_of(vk), sv = src_of(vv);
 #pragma unroll
         for (int i = i0; i < i1; ++i) {
           const int n = n_of(lw + NLW * i);
           const int region = n < KCH ? 0 : n < KCH + PCH ? 1 : 2;
           if (lw + NLW * i < NLD && (region == 2 ? do_v : do_k)) {
-            const int kb = region == 2 ? kbv : kbk;
+            const int kb = region == 2 ? sv.kb : sk.kb;
             const int stride = region == 0 ? p.sk[2] : region == 1 ? p.spk[2] : p.sv[2];
-            const char* base = region == 0 ? (const char*)(Kp + (int64_t)kb * p.sk[2])
-                             : region == 1 ? (const char*)(PKp + (int64_t)kb * p.spk[2])
-                                           : (const char*)(Vp + (int64_t)kb * p.sv[2]);
+            const char* base = region == 0 ? sk.k : region == 1 ? sk.pk : sv.v;
             unsigned char* dst = region == 2 ? dV + (n - KCH - PCH) * 1024 : dK + n * 1024;
             uint32_t o = off[i];
             if (kb + BN > N) o = (uint32_t)(min(rowi[i], N - 1 - kb) * stride * ES + cbyte[i]);
@@ -493,8 +548,13 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
           woff[m] = KREG + r * PCH * 16 + 16 * ((f >> 2) ^ swz_key(PCH, r)) + 4 * (f & 3);
         }
       }
-      auto gen_phk = [&](unsigned char* dK) __attribute__((always_inline)) {
+      // phi_k of stream step vv (generated in stream order; each item's keys start at 0)
+      auto gen_phk = [&](unsigned char* dK, int vv) __attribute__((always_inline)) {
         if constexpr (SWJIT) {
+          if (MULTI && vv < nsteps && vv % nkt == 0) {
+            bc = 1.0;
+            bs = 0.0;
+          }
           const float c = (float)bc, sn = (float)bs;
 #pragma unroll
           for (int m = 0; m < NROW; ++m) {
@@ -506,28 +566,27 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
           bc = nc;
         }
       };
-      gen_phk(sK0);
-      gen_phk(sK1);
+      gen_phk(sK0, 0);
+      gen_phk(sK1, 1);
       loads(0, PER, 0, 0, sK0, sV0, true, true);          // K'(0), V(0)
-      loads(0, PER, BN, 0, sK1, sV0, true, false);        // K'(1)
+      loads(0, PER, 1, 0, sK1, sV0, true, false);         // K'(1)
       __syncthreads();                                    // (waits for them)
-      gen_phk(sK2);
-      loads(0, PER, 2 * BN, BN, sK2, sV1, true, true);    // K'(2), V(1)
+      gen_phk(sK2, 2);
+      loads(0, PER, 2, 1, sK2, sV1, true, true);          // K'(2), V(1)
       __builtin_amdgcn_s_barrier();
       // one barrier per tile (see the key loop of the compute wavefronts)
       auto lstep = [&](int t, unsigned char* kd, unsigned char* vd) __attribute__((always_inline)) {
-        const int kb = t * BN;
-        gen_phk(kd);
-        loads(0, PER, kb + 3 * BN, kb + 2 * BN, kd, vd, true, true);
+        gen_phk(kd, t + 3);
+        loads(0, PER, t + 3, t + 2, kd, vd, true, true);
         // vmcnt(PMIN): at most PMIN loads outstanding, so all of the previous tile's are done;
         // MODE 4 also waits for its LDS writes (lgkmcnt(0))
         __builtin_amdgcn_s_waitcnt(PMIN | (SWJIT ? 0x0070 : 0x0F70));
         __builtin_amdgcn_s_barrier();
       };
-      for (int t = 0; t < nkt; t += 3) {
+      for (int t = 0; t < nsteps; t += 3) {
         lstep(t, sK0, sV2);
-        if (t + 1 < nkt) lstep(t + 1, sK1, sV0);
-        if (t + 2 < nkt) lstep(t + 2, sK2, sV1);
+        if (t + 1 < nsteps) lstep(t + 1, sK1, sV0);
+        if (t + 2 < nsteps) lstep(t + 2, sK2, sV1);
       }
       __builtin_amdgcn_s_waitcnt(0);   // no copy outlives the workgroup
       __builtin_amdgcn_s_barrier();
@@ -535,10 +594,11 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
     }
   }
 
-  const int q0w = q0 + wave * 32;
-  const int qrow = q0w + ln;
-  const bool qvalid = qrow < N;
-  const int qclamp = qvalid ? qrow : N - 1;
+  // this wavefront's query rows of the current item
+  int q0w = q0 + wave * 32;
+  int qrow = q0w + ln;
+  bool qvalid = qrow < N;
+  int qclamp = qvalid ? qrow : N - 1;
 
   // ---- Q' fragments (B operand of S^T = K' Q'^T), resident for the whole loop
   // 16-bit: k-step t of lane half h covers chunk 2t + h.  fp32 (one element per lane and
@@ -559,11 +619,14 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   // every product is exact in fp32 and their sum is m (j - i) to the 22 bits of m.
   // Lane half 1 holds k = 8..15: zeros.
   f16_t jm_hi = (f16_t)0.f, jm_lo = (f16_t)0.f;
-  if constexpr (JIT) {
-    const uint32_t mb = p.alibi_m[hh];
-    jm_hi = __builtin_bit_cast(f16_t, (uint16_t)(mb & 0xffffu));
-    jm_lo = __builtin_bit_cast(f16_t, (uint16_t)(mb >> 16));
-  }
+  auto set_slope = [&](int h) __attribute__((always_inline)) {
+    if constexpr (JIT) {
+      const uint32_t mb = p.alibi_m[h];
+      jm_hi = __builtin_bit_cast(f16_t, (uint16_t)(mb & 0xffffu));
+      jm_lo = __builtin_bit_cast(f16_t, (uint16_t)(mb >> 16));
+    }
+  };
+  set_slope(hh);
   auto jit_pair = [&](int x) __attribute__((always_inline)) {
     f16x2 r = {(f16_t)(float)(x & ~2047), (f16_t)(float)(x & 2047)};
     return r;
@@ -574,29 +637,34 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
     const u32x4 r = __builtin_bit_cast(u32x4, v);
     return hf ? u32x4{0u, 0u, 0u, 0u} : r;
   };
-  if constexpr (SWJIT) {
-    // phi_q(i) in exp2 units: lane half h of k-step t holds column pairs f = 8t + 4h + e (e < 4)
-    // of the query row, [cos(i w_f), sin(i w_f)] log2(e), zero past the C / 2 frequencies
+  // phi_q fragments formed in the kernel (in-kernel factor modes) for query row qc
+  auto make_pf = [&](int qc) __attribute__((always_inline)) {
+    if constexpr (SWJIT) {
+      // phi_q(i) in exp2 units: lane half h of k-step t holds column pairs f = 8t + 4h + e (e < 4)
+      // of the query row, [cos(i w_f), sin(i w_f)] log2(e), zero past the C / 2 frequencies
 #pragma unroll
-    for (int t = 0; t < PSTEPS; ++t) {
-      f16x8 v;
+      for (int t = 0; t < PSTEPS; ++t) {
+        f16x8 v;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int f = 8 * t + 4 * hf + e;
-        float c, sn;
-        sincos_rev(qclamp, p.sw_nu[0][f], p.sw_nu[1][f], p.sw_nu[2][f], c, sn);
-        const float w = f < p.sw_pairs ? LOG2E : 0.f;
-        v[2 * e] = (f16_t)(c * w);
-        v[2 * e + 1] = (f16_t)(sn * w);
+        for (int e = 0; e < 4; ++e) {
+          const int f = 8 * t + 4 * hf + e;
+          float c, sn;
+          sincos_rev(qc, p.sw_nu[0][f], p.sw_nu[1][f], p.sw_nu[2][f], c, sn);
+          const float w = f < p.sw_pairs ? LOG2E : 0.f;
+          v[2 * e] = (f16_t)(c * w);
+          v[2 * e + 1] = (f16_t)(sn * w);
+        }
+        pf[t] = __builtin_bit_cast(u32x4, v);
       }
-      pf[t] = __builtin_bit_cast(u32x4, v);
+    } else if constexpr (JIT) {
+      const f16x2 ix = jit_pair(qc);
+      const f16x8 v = {jm_hi, jm_hi, jm_lo, jm_lo, (f16_t)(-(float)ix[0]), (f16_t)(-(float)ix[1]),
+                       (f16_t)(-(float)ix[0]), (f16_t)(-(float)ix[1])};
+      pf[0] = hf ? u32x4{0u, 0u, 0u, 0u} : __builtin_bit_cast(u32x4, v);
     }
-  } else if constexpr (JIT) {
-    const f16x2 ix = jit_pair(qclamp);
-    const f16x8 v = {jm_hi, jm_hi, jm_lo, jm_lo, (f16_t)(-(float)ix[0]), (f16_t)(-(float)ix[1]),
-                     (f16_t)(-(float)ix[0]), (f16_t)(-(float)ix[1])};
-    pf[0] = hf ? u32x4{0u, 0u, 0u, 0u} : __builtin_bit_cast(u32x4, v);
-  } else if constexpr (RP > 0) {
+  };
+  make_pf(qclamp);
+  if constexpr (RP > 0 && !JIT && !SWJIT) {
     const PT* prow = PQp + qclamp * p.spq[2];
 #pragma unroll
     for (int t = 0; t < PSTEPS; ++t) {
@@ -609,6 +677,44 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
       }
     }
   }
+
+  // ---- MULTI: the next work item ----------------------------------------------------
+  // Its Q' (and phi_q) rows are loaded into qnx / pnx as soon as the current item starts and
+  // become the fragments at the step whose score MFMAs first need them.
+  int cur = item0;     // current item
+  int vbase = 0;       // its first stream step
+  u32x4 qnx[MULTI ? QSTEPS : 1];
+  PFrag pnx[MULTI && RP > 0 && !JIT && !SWJIT ? PSTEPS : 1];
+  struct ItemRows {
+    int b, h, q0, qc;
+  };
+  auto item_rows = [&](int item) __attribute__((always_inline)) {
+    ItemRows r;
+    const int bhi = item / p.nqb;
+    r.q0 = (item - bhi * p.nqb) * BM;
+    r.h = bhi % p.H;
+    r.b = bhi / p.H;
+    r.qc = min(r.q0 + wave * 32 + ln, N - 1);
+    return r;
+  };
+  auto prefetch_q = [&](int item) __attribute__((always_inline)) {
+    if constexpr (MULTI) {
+      const ItemRows r = item_rows(item);
+      const QT* qp = (const QT*)p.q + ((int64_t)r.b * p.sq[0] + (int64_t)r.h * p.sq[1] + (int64_t)r.qc * p.sq[2]);
+#pragma unroll
+      for (int t = 0; t < QSTEPS; ++t) qnx[t] = ld16(qp + KS * t + KW * hf);
+      if constexpr (RP > 0 && !JIT && !SWJIT) {
+        const PT* pr =
+            (const PT*)p.phq + ((int64_t)r.b * p.spq[0] + (int64_t)r.h * p.spq[1] + (int64_t)r.qc * p.spq[2]);
+#pragma unroll
+        for (int t = 0; t < PSTEPS; ++t) {
+          const int c0 = KS * t + KW * hf;
+          pnx[t] = load_phi_chunk<PT>(pr, c0, p.R, (p.flags & FLAG_PHQ_VEC) && c0 + KW <= p.R);
+        }
+      }
+    }
+  };
+  if (MULTI && nitems > 1) prefetch_q(item0 + 1);
 
   // tile copies by the compute wavefronts (no loader): wavefront w issues loads w, w+8, ...
   uint32_t coff[LOADER ? 1 : DPW];
@@ -1026,6 +1132,68 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   softmax(0);
   __syncthreads();
 
+  // ---- one item's epilogue: O = O / l, LSE = m + ln l ------------------------------
+  auto store_item = [&]() __attribute__((always_inline)) {
+    // register r of lane half hf in head-dim block db holds head dim 32 db + 8 (r / 4) + 4 hf + r % 4
+    // (register 0 of lacc is row 0 in half 0 and row 4, all zeros, in half 1)
+    const float l_tot = halves_sum(MROW ? lacc[0] : l_run);
+    if (qvalid) {
+      const float inv = 1.f / l_tot;
+      QT* orow = Op + qrow * p.so[2];
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int d0 = 32 * db + 8 * c + 4 * hf;
+          if (d0 < D) {
+            typedef QT T4 __attribute__((ext_vector_type(4)));
+            T4 v;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = from_f32<QT>(oacc[db][4 * c + j] * inv);
+            *(T4*)(orow + d0) = v;
+          }
+        }
+      if (p.lse && hf == 0)
+        p.lse[((int64_t)bb * p.H + hh) * N + qrow] = FOLD ? (M2 + __log2f(l_tot)) * LN2 : m_run + logf(l_tot);
+    }
+  };
+  // MULTI: the next item's fragments, before the MFMA phase whose score MFMAs use them
+  auto next_frags = [&]() __attribute__((always_inline)) {
+    if constexpr (MULTI) {
+      const ItemRows r = item_rows(cur + 1);
+#pragma unroll
+      for (int t = 0; t < QSTEPS; ++t) qf[t] = scale_frag<QT>(qnx[t], FOLD ? p.scale * LOG2E : p.scale);
+      set_slope(r.h);
+      make_pf(r.qc);
+      if constexpr (RP > 0 && !JIT && !SWJIT) {
+#pragma unroll
+        for (int t = 0; t < PSTEPS; ++t) pf[t] = pnx[t];
+      }
+    }
+  };
+  // MULTI: after the current item's epilogue, the next item becomes the current one
+  auto next_item = [&]() __attribute__((always_inline)) {
+    if constexpr (MULTI) {
+      ++cur;
+      vbase += nkt;
+      const ItemRows r = item_rows(cur);
+      bb = r.b;
+      hh = r.h;
+      q0 = r.q0;
+      q0w = q0 + wave * 32;
+      qrow = q0w + ln;
+      qvalid = qrow < N;
+      qclamp = qvalid ? qrow : N - 1;
+      Op = (QT*)p.o + ((int64_t)bb * p.so[0] + (int64_t)hh * p.so[1]);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+      lacc = f32x16{};
+      l_run = 0.f;
+      m_run = -INFINITY;
+      if (cur + 1 < item0 + nitems) prefetch_q(cur + 1);
+    }
+  };
+
   // ---- ping-pong: per SIMD, one wavefront multiplies while the other does softmax ----
   // Every wavefront runs the same sequence  MFMA(t) | softmax(t+1) | MFMA(t+1) | ...  with
   // MFMA(t) = {S(t+1) = K'(t+1) Q'^T, O += V(t)^T P(t)}, one phase per barrier; group 1
@@ -1055,12 +1223,23 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
       // softmax, which opens the tile and is followed by its MFMA phase, issues at a raised
       // wavefront priority: group 0's softmax, which closes the tile, would otherwise take
       // the vector unit from it where they overlap (the older wavefront wins the issue).
-      mma_phase(kn, kb + BN, vt);
-      if (grp == 1) __syncthreads();
+      // MULTI: at the last step of an item the score MFMAs already work on the first tile
+      // of the next item (its fragments are swapped in first), then the item is stored.
+      const int tt = t - vbase;          // tile of the current item
+      const bool last = tt == nkt - 1;
+      const bool more = MULTI && last && t + 1 < nsteps;
+      const int tn = last ? 0 : tt + 1;  // tile whose scores the MFMA phase computes
+      if (more) next_frags();
+      mma_phase(kn, tn * BN, vt);
+      if (more) {
+        store_item();
+        next_item();
+      }
+      if (grp == 1) lds_barrier();
       if (grp == 1) __builtin_amdgcn_s_setprio(2);
-      if (t + 1 < nkt) softmax(t + 1);
+      if (!last || more) softmax(tn);
       __builtin_amdgcn_s_setprio(0);
-      if (grp == 0) __syncthreads();
+      if (grp == 0) lds_barrier();
       return;
     }
     if constexpr (KW > 1) {
@@ -1095,10 +1274,10 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
     __syncthreads();
   }
   if constexpr (LOADER) {
-    for (int t = 0; t < nkt; t += 3) {
+    for (int t = 0; t < nsteps; t += 3) {
       step(t, sK0, sK1, sV0, sV1);
-      if (t + 1 < nkt) step(t + 1, sK1, sK2, sV1, sV2);
-      if (t + 2 < nkt) step(t + 2, sK2, sK0, sV2, sV0);
+      if (t + 1 < nsteps) step(t + 1, sK1, sK2, sV1, sV2);
+      if (t + 2 < nsteps) step(t + 2, sK2, sK0, sV2, sV0);
     }
   } else {
     for (int t = 0; t < nkt; t += 2) {
@@ -1110,28 +1289,7 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   if (LOADER || grp == 0) __builtin_amdgcn_s_barrier();
 
   // ---- epilogue: O = O / l, LSE = m + ln l -----------------------------------
-  // register r of lane half hf in head-dim block db holds head dim 32 db + 8 (r / 4) + 4 hf + r % 4
-  // (register 0 of lacc is row 0 in half 0 and row 4, all zeros, in half 1)
-  const float l_tot = halves_sum(MROW ? lacc[0] : l_run);
-  if (qvalid) {
-    const float inv = 1.f / l_tot;
-    QT* orow = Op + qrow * p.so[2];
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int d0 = 32 * db + 8 * c + 4 * hf;
-        if (d0 < D) {
-          typedef QT T4 __attribute__((ext_vector_type(4)));
-          T4 v;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) v[j] = from_f32<QT>(oacc[db][4 * c + j] * inv);
-          *(T4*)(orow + d0) = v;
-        }
-      }
-    if (p.lse && hf == 0)
-      p.lse[((int64_t)bb * p.H + hh) * N + qrow] = FOLD ? (M2 + __log2f(l_tot)) * LN2 : m_run + logf(l_tot);
-  }
+  store_item();
 }
 
 }  // namespace attn

@@ -37,8 +37,14 @@ struct AttnParams {
   float sw_nu[3][32];
   double sw_rot[2][32];
   int sw_pairs;
+  // work items (b, h, query block), query block fastest: ipw consecutive items per
+  // workgroup (instances with attn_multi_item only; 1 otherwise), n_items in all
+  int ipw;
+  int n_items;
 };
 constexpr int kMaxSandwichPairs = 32;
+// compute units of the calling thread's current device (cached per device); 0 on error
+int device_cu_count();
 constexpr int kMaxJitHeads = 128;
 constexpr int kAttnBlockM = 256;   // query rows per attention workgroup
 constexpr int kAttnKeyTile = 64;   // keys per LDS tile of the attention kernels

@@ -727,3 +727,53 @@ def test_random_sweep_forward_and_backward(fb, B, H, N, D, R, fs, dt, pdt, causa
         rgq, rgk = oracle.lowrank_factor_grads(db, full_q, full_k)
         assert_grad_close(gpq.cpu().double().numpy(), _sum_to(rgq, shape), "dphi_q")
         assert_grad_close(gpk.cpu().double().numpy(), _sum_to(rgk, shape), "dphi_k")
+
+
+# ------------------------------------------- several work items per workgroup ----
+# Non-causal 16-bit kernels with D + R_pad <= 64 take several (b, h, query block) items per
+# workgroup when there are more items than compute units: one key-tile stream runs across
+# the items and the next item's query rows load while the current one runs.  These shapes
+# have more items than the 256 compute units of an MI355X, ragged sequence lengths (partial
+# key tiles and query blocks) and a last workgroup with fewer items than the others.
+MULTI = [
+    # (entry, B, H, N, D, R, dtype)
+    ("lowrank_log2", 40, 8, 300, 32, 16, "bf16"),
+    ("lowrank", 40, 8, 300, 32, 16, "bf16"),
+    ("lowrank_log2", 70, 4, 200, 16, 8, "f16"),
+    ("lowrank_log2", 30, 10, 130, 32, 20, "bf16"),
+    ("lowrank", 30, 10, 130, 32, 0, "bf16"),
+    ("sandwich", 20, 8, 512, 32, 32, "bf16"),
+    ("alibi", 33, 8, 260, 32, 0, "bf16"),
+]
+
+
+@pytest.mark.parametrize("entry,B,H,N,D,R,dt", MULTI, ids=[f"{m[0]}-{i}" for i, m in enumerate(MULTI)])
+def test_multi_item_workgroups(fb, entry, B, H, N, D, R, dt):
+    """Every output row and LSE of shapes with more work items than compute units, against
+    the oracle (the factors the kernel reads, or the exact bias for in-kernel factors)."""
+    import torch
+    nqb = (N + 255) // 256
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    say(f"multi-item {entry} B={B} H={H} N={N} D={D} R={R} {dt}: {B * H * nqb} items, {ncu} CUs")
+    r = np.random.default_rng(1500 + N + D + R)
+    q, k, v = (synth.round_to(r.standard_normal((B, H, N, D)) * 0.5, dt) for _ in range(3))
+    qd, kd, vd = (to_dev(x, dt) for x in (q, k, v))
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda:0")
+    if entry in ("lowrank", "lowrank_log2"):
+        pq = synth.round_to(r.standard_normal((H, N, R)) * 0.5, "f16") if R else None
+        pk = synth.round_to(r.standard_normal((H, N, R)) * 0.5, "f16") if R else None
+        run = fb.fb_attn_fwd_lowrank_log2 if entry == "lowrank_log2" else fb.fb_attn_fwd_lowrank
+        o = run(qd, kd, vd, to_dev(pq, "f16") if R else None, to_dev(pk, "f16") if R else None, lse=lse)
+        bias = None
+        if R:
+            bias = oracle.lowrank_bias(pq, pk) * (np.log(2.0) if entry == "lowrank_log2" else 1.0)
+    elif entry == "sandwich":
+        o = fb.fb_attn_fwd_sandwich(qd, kd, vd, C=R, lse=lse)
+        bias = oracle.sandwich_bias(N, R)
+    else:
+        o = fb.fb_attn_fwd_alibi(qd, kd, vd, lse=lse)
+        bias = oracle.alibi_bias(oracle.alibi_slopes(H), N)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(q, k, v, bias=bias)
+    assert_close(to_np(o), ro, dt, f"multi-item {entry}")
+    np.testing.assert_allclose(lse.cpu().double().numpy(), rl, rtol=0, atol=2e-2)
