@@ -353,7 +353,10 @@ def main():
             hr = json.load(f)
         if hr.get("kernel_source_hash") == kernel_source_hash() and hr.get("entry") == entry_name(use_log2, jit, mul, w):
             counters = {k2: hr.get(k2) for k2 in ("bytes_per_launch", "fetch_bytes", "write_bytes", "mfma_busy",
-                                                  "sclk_mhz_counters", "trace_avg_us")}
+                                                  "l2_hit_rate", "sclk_mhz_counters", "trace_avg_us")}
+            if hr.get("dense_bias_kernel"):
+                counters["dense_bias_kernel"] = {k2: hr["dense_bias_kernel"].get(k2) for k2 in
+                                                 ("bytes_per_launch", "mfma_busy", "l2_hit_rate", "hbm_gbs")}
             counters["hbm_gbs"] = round(hr["bytes_per_launch"] / (kern_ms * 1e-3) / 1e9, 1) \
                 if hr.get("bytes_per_launch") else None
             counters["source"] = os.path.relpath(hf, ROOT)
@@ -525,10 +528,12 @@ def profile_harness(args) -> int:
             return 1
     # 2.-4. counter passes: short runs (every dispatch is serialised under --pmc), with one
     # 512 MiB device copy as the HBM calibration
-    short = base + ["--steps", "3", "--warmup", "1", "--settle-ms", "0", "--no-dense", "--calib-copy-mib", "512"]
+    # (the dense-bias kernel runs in the same short runs, so its counters come from the same passes)
+    short = base + ["--steps", "3", "--warmup", "1", "--settle-ms", "0", "--calib-copy-mib", "512"]
     passes = {"fetch": ["FETCH_SIZE"], "write": ["WRITE_SIZE"],
               "busy": ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES",
-                       "GRBM_GUI_ACTIVE", "GRBM_COUNT"]}
+                       "GRBM_GUI_ACTIVE", "GRBM_COUNT"],
+              "l2": ["TCC_HIT_sum", "TCC_MISS_sum"]}
     def shown(cmd):
         """the command as run from the repository root (the child runs with cwd /tmp)"""
         return "cd $REPO && TMPDIR=/tmp " + " ".join(("python3" if c == py else c.replace(ROOT + os.sep, ""))
@@ -539,9 +544,9 @@ def profile_harness(args) -> int:
                                                "--output-format", "csv", "--"] + short
         cmds[name] = shown(cmd)
         if not args.profile_reparse and _run_child(cmd, os.path.join(out_root, f"{name}.log"), 120):
-            if name != "busy":
+            if name in ("fetch", "write"):
                 return 1
-            print("[harness] the busy-counter pass failed; continuing without it", flush=True)
+            print(f"[harness] the {name} counter pass failed; continuing without it", flush=True)
 
     # ---- parse
     stats = _csv_rows(os.path.join(out_root, "trace", "**", "*kernel_stats.csv"))
@@ -600,6 +605,8 @@ def profile_harness(args) -> int:
     f_k, f_c = counter("fetch", step_pred), counter("fetch", copy_pred, largest=True)
     w_k, w_c = counter("write", step_pred), counter("write", copy_pred, largest=True)
     busy = counter("busy", step_pred)
+    l2 = counter("l2", step_pred)
+    dense_pred = lambda kn: is_attn(kn) and mode_of(kn) == 1
     calib = 512 * 1024.0                                     # KiB copied by the calibration run
     src_hash = kernel_source_hash()
     if os.path.exists(hash_file):                            # the sources the runs were taken with
@@ -613,10 +620,31 @@ def profile_harness(args) -> int:
                     "fetch_scale": fs, "write_scale": ws,
                     "fetch_bytes": int(f_k["FETCH_SIZE"] * fs * 1024), "write_bytes": int(w_k["WRITE_SIZE"] * ws * 1024)})
         res["bytes_per_launch"] = res["fetch_bytes"] + res["write_bytes"]
+    def hit_rate(c):
+        n = c.get("TCC_HIT_sum", 0.0) + c.get("TCC_MISS_sum", 0.0)
+        return round(c.get("TCC_HIT_sum", 0.0) / n, 4) if n else None
     if busy:
         res["busy_counters"] = busy
         if busy.get("SQ_BUSY_CU_CYCLES"):
             res["mfma_busy"] = round(busy.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (4.0 * busy["SQ_BUSY_CU_CYCLES"]), 4)
+    if l2:
+        res["l2_counters"] = l2
+        res["l2_hit_rate"] = hit_rate(l2)
+    # the dense-bias kernel of the same short runs (absent for workloads without one)
+    fd, wd, bd, ld = (counter(n, dense_pred) for n in ("fetch", "write", "busy", "l2"))
+    if fd.get("FETCH_SIZE") and "fetch_scale" in res:
+        dres = {"fetch_bytes": int(fd["FETCH_SIZE"] * res["fetch_scale"] * 1024),
+                "write_bytes": int(wd.get("WRITE_SIZE", 0.0) * res["write_scale"] * 1024)}
+        dres["bytes_per_launch"] = dres["fetch_bytes"] + dres["write_bytes"]
+        if bd.get("SQ_BUSY_CU_CYCLES"):
+            dres["mfma_busy"] = round(bd.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (4.0 * bd["SQ_BUSY_CU_CYCLES"]), 4)
+        if ld:
+            dres["l2_counters"] = ld
+            dres["l2_hit_rate"] = hit_rate(ld)
+        if dense_k:
+            dres["trace_avg_us"] = round(dense_k[0][2], 2)
+            dres["hbm_gbs"] = round(dres["bytes_per_launch"] / (dense_k[0][2] * 1e-6) / 1e9, 1)
+        res["dense_bias_kernel"] = dres
     res["counter_runs"] = "3 steps after 1 warm-up, no settle phase (dispatches serialised by the profiler)"
     # shader clock of the counter runs: GRBM_COUNT counts clocks, summed over the XCDs, over
     # the dispatch's duration (start and end timestamps of the same rows)
@@ -661,6 +689,17 @@ def profile_harness(args) -> int:
     if "sclk_mhz_counters" in res:
         lines.append(f"Shader clock in the counter runs: GRBM_COUNT / {N_XCD} XCDs / {res['counter_run_us']} us "
                      f"(the dispatch's own timestamps) = {res['sclk_mhz_counters']:.0f} MHz.")
+    if res.get("l2_hit_rate") is not None:
+        lines.append(f"L2: TCC_HIT_sum {l2.get('TCC_HIT_sum', 0):.4g}, TCC_MISS_sum {l2.get('TCC_MISS_sum', 0):.4g}: "
+                     f"hit rate {100 * res['l2_hit_rate']:.1f}%.")
+    if "dense_bias_kernel" in res:
+        d = res["dense_bias_kernel"]
+        lines += ["", "Dense-bias kernel of the same counter runs (MODE 1, the [.., N, N] bias streamed):"]
+        lines.append(f"FETCH_SIZE -> {d['fetch_bytes'] / 1e6:.1f} MB read, WRITE_SIZE -> {d['write_bytes'] / 1e6:.1f} MB "
+                     f"written per launch" + (f", {d['hbm_gbs']:.0f} GB/s at its traced average" if "hbm_gbs" in d else "")
+                     + (f"; matrix cores busy {100 * d['mfma_busy']:.1f}%" if "mfma_busy" in d else "")
+                     + (f"; L2 hit rate {100 * d['l2_hit_rate']:.1f}%" if d.get("l2_hit_rate") is not None else "")
+                     + ".")
     with open(md, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(json.dumps({"harness": os.path.relpath(harness_file(w, args.jit), ROOT), "summary": os.path.relpath(md, ROOT),
