@@ -127,7 +127,19 @@ BwdWork bwd_work_layout(int B, int H, int N, int R, const int64_t sdphi_q[3], co
   // a factor gradient needs per-(b, h) partials when an axis of size > 1 has stride 0
   auto summed = [&](const int64_t* sd) { return R > 0 && ((sd[0] == 0 && B > 1) || (sd[1] == 0 && H > 1)); };
   const size_t rows = (size_t)B * H * N;
-  BwdWork w{0, SIZE_MAX, SIZE_MAX, up(rows * 4)};
+  BwdWork w{0, SIZE_MAX, SIZE_MAX, up(rows * 4), SIZE_MAX, SIZE_MAX, 0};
+  if (R > 0 && R % 8 != 0) {
+    // padded factors (16-bit) and per-(b, h) padded factor gradients (fp32)
+    w.R8 = (R + 7) / 8 * 8;
+    const size_t fb16 = up(rows * (size_t)w.R8 * 2), fb32 = up(rows * (size_t)w.R8 * 4);
+    w.phq_off = w.bytes;
+    w.phk_off = w.phq_off + fb16;
+    w.pq_off = w.phk_off + fb16;
+    w.pk_off = w.pq_off + fb32;
+    w.bytes = w.pk_off + fb32;
+    if (rows == 0) w.bytes = 0;
+    return w;
+  }
   if (summed(sdphi_q)) {
     w.pq_off = w.bytes;
     w.bytes += up(rows * (size_t)R * 4);
@@ -467,7 +479,7 @@ fb_status attn_bwd_lowrank_impl(const fb_attn_args* a, const void* phi_q, const 
   if (a->dt != FB_BF16 && a->dt != FB_F16) FB_FAIL(FB_EUNSUPPORTED, "%s: q/k/v must be bf16 or f16", fn);
   if (a->D != 32 && a->D != 64) FB_FAIL(FB_EUNSUPPORTED, "%s: head dim %d not in {32, 64}", fn, a->D);
   if (R < 0) FB_FAIL(FB_EINVAL, "%s: negative R", fn);
-  if (R > 64 || R % 8 != 0) FB_FAIL(FB_EUNSUPPORTED, "%s: R = %d (need a multiple of 8, at most 64)", fn, R);
+  if (R > 64) FB_FAIL(FB_EUNSUPPORTED, "%s: R = %d (at most 64)", fn, R);
   if (R > 0) {
     if (!known_dtype(phi_dt) || phi_dt == FB_F32 || (a->dt == FB_F16 && phi_dt != FB_F16))
       FB_FAIL(FB_EUNSUPPORTED, "%s: factor dtype does not match the q/k/v dtype", fn);
@@ -522,25 +534,33 @@ fb_status attn_bwd_lowrank_impl(const fb_attn_args* a, const void* phi_q, const 
   p.scale = a->scale;
   p.nblk = (a->N + kBwdRows - 1) / kBwdRows;
   if (p.nblk * (int64_t)a->H * a->B > 0x7fffffffLL) FB_FAIL(FB_EUNSUPPORTED, "%s: grid too large", fn);
-  int RP = 0;
+  int RP = 0, RW = 0;
   if (R > 0) {
     if (!phi_q || !phi_k || !sphi_q || !sphi_k || !g->dphi_q || !g->dphi_k)
       FB_FAIL(FB_EINVAL, "%s: null factor pointer, strides or factor gradient", fn);
     for (int i = 0; i < 3; ++i)
       if (sphi_q[i] < 0 || sphi_k[i] < 0 || g->sdphi_q[i] < 0 || g->sdphi_k[i] < 0)
         FB_FAIL(FB_EINVAL, "%s: negative factor stride", fn);
-    if (!aligned16(phi_q) || !aligned16(phi_k) || !rows_aligned(sphi_q, esize(phi_dt)) ||
-        !rows_aligned(sphi_k, esize(phi_dt)))
+    const bool padded = wl.R8 > 0;   // R not a multiple of 8: padded copies in the workspace
+    if (!padded && (!aligned16(phi_q) || !aligned16(phi_k) || !rows_aligned(sphi_q, esize(phi_dt)) ||
+                    !rows_aligned(sphi_k, esize(phi_dt))))
       FB_FAIL(FB_EUNSUPPORTED, "%s: factor rows must be 16-byte aligned", fn);
+    if (padded && (((uintptr_t)phi_q | (uintptr_t)phi_k) & 1u))
+      FB_FAIL(FB_EINVAL, "%s: factors not aligned to their element size", fn);
     if (a->N > 1 && (sphi_q[2] < R || sphi_k[2] < R || g->sdphi_q[2] < R || g->sdphi_k[2] < R))
       FB_FAIL(FB_EINVAL, "%s: factor row stride < R", fn);
-    if (((uintptr_t)g->dphi_q & 15u) || ((uintptr_t)g->dphi_k & 15u) || g->sdphi_q[2] % 4 || g->sdphi_k[2] % 4 ||
-        g->sdphi_q[1] % 4 || g->sdphi_k[1] % 4 || g->sdphi_q[0] % 4 || g->sdphi_k[0] % 4)
+    if (!padded && (((uintptr_t)g->dphi_q & 15u) || ((uintptr_t)g->dphi_k & 15u) || g->sdphi_q[2] % 4 ||
+                    g->sdphi_k[2] % 4 || g->sdphi_q[1] % 4 || g->sdphi_k[1] % 4 || g->sdphi_q[0] % 4 ||
+                    g->sdphi_k[0] % 4))
       FB_FAIL(FB_EINVAL, "%s: dphi and its strides must be 16-byte aligned", fn);
+    if (padded && (((uintptr_t)g->dphi_q | (uintptr_t)g->dphi_k) & 3u))
+      FB_FAIL(FB_EINVAL, "%s: dphi must be 4-byte aligned", fn);
     if (!strides_fit32(sphi_q, a->N) || !strides_fit32(sphi_k, a->N) || !strides_fit32(g->sdphi_q, a->N) ||
         !strides_fit32(g->sdphi_k, a->N) || !tile_fits32(sphi_q[2], esize(phi_dt)) ||
         !tile_fits32(sphi_k[2], esize(phi_dt)))
       FB_FAIL(FB_EUNSUPPORTED, "%s: factor strides exceed 32 bits", fn);
+    if (padded && (int64_t)a->H * a->N * wl.R8 > 0x7fffffffLL)
+      FB_FAIL(FB_EUNSUPPORTED, "%s: padded per-(b, h) factors exceed 32-bit strides", fn);
     p.phq = phi_q;
     p.phk = phi_k;
     p.dphq = g->dphi_q;
@@ -551,21 +571,37 @@ fb_status attn_bwd_lowrank_impl(const fb_attn_args* a, const void* phi_q, const 
       p.sdpq[i] = (int)g->sdphi_q[i];
       p.sdpk[i] = (int)g->sdphi_k[i];
     }
-    // a gradient summed over batches or heads goes to per-(b, h) partials first
+    RW = padded ? wl.R8 : R;
+    if (padded) {
+      // the factors go to [B][H][N][R8] copies with zero columns past R
+      void* pq = (char*)g->work + wl.phq_off;
+      void* pk = (char*)g->work + wl.phk_off;
+      st = launch_attention_bwd_pad_factor(phi_q, esize(phi_dt), sphi_q, a->B, a->H, a->N, R, wl.R8, pq, stream);
+      if (st == FB_OK)
+        st = launch_attention_bwd_pad_factor(phi_k, esize(phi_dt), sphi_k, a->B, a->H, a->N, R, wl.R8, pk, stream);
+      if (st != FB_OK) return st;
+      p.phq = pq;
+      p.phk = pk;
+      const int sp[3] = {a->H * a->N * wl.R8, a->N * wl.R8, wl.R8};
+      for (int i = 0; i < 3; ++i) p.spq[i] = p.spk[i] = sp[i];
+      p.R = wl.R8;
+    }
+    // a gradient summed over batches or heads, and every factor gradient of a padded run,
+    // goes to per-(b, h) partials first
     if (wl.pq_off != SIZE_MAX) {
       p.dphq = (float*)((char*)g->work + wl.pq_off);
-      p.sdpq[0] = a->H * a->N * R;
-      p.sdpq[1] = a->N * R;
-      p.sdpq[2] = R;
+      p.sdpq[0] = a->H * a->N * RW;
+      p.sdpq[1] = a->N * RW;
+      p.sdpq[2] = RW;
     }
     if (wl.pk_off != SIZE_MAX) {
       p.dphk = (float*)((char*)g->work + wl.pk_off);
-      p.sdpk[0] = a->H * a->N * R;
-      p.sdpk[1] = a->N * R;
-      p.sdpk[2] = R;
+      p.sdpk[0] = a->H * a->N * RW;
+      p.sdpk[1] = a->N * RW;
+      p.sdpk[2] = RW;
     }
     p.flags |= FLAG_PHQ_VEC | FLAG_PHK_VEC;
-    RP = R <= 16 ? 16 : R <= 32 ? 32 : 64;
+    RP = RW <= 16 ? 16 : RW <= 32 ? 32 : 64;
   }
   st = launch_attention_bwd_delta(a->dt, a->o, a->so, g->dout, g->sdo, a->B, a->H, a->N, a->D, delta, stream);
   if (st != FB_OK) return st;
@@ -573,6 +609,11 @@ fb_status attn_bwd_lowrank_impl(const fb_attn_args* a, const void* phi_q, const 
                   : launch_attention_bwd_d64(a->dt, R > 0 ? phi_dt : a->dt, RP, p, stream);
   if (st == FB_EUNSUPPORTED) set_error("%s: no kernel for this dtype / rank combination", fn);
   if (st != FB_OK) return st;
+  if (R > 0 && wl.R8 > 0) {
+    st = launch_attention_bwd_unpad(p.dphq, a->B, a->H, a->N, wl.R8, R, g->dphi_q, g->sdphi_q, stream);
+    if (st == FB_OK) st = launch_attention_bwd_unpad(p.dphk, a->B, a->H, a->N, wl.R8, R, g->dphi_k, g->sdphi_k, stream);
+    return st;
+  }
   if (wl.pq_off != SIZE_MAX)
     st = launch_attention_bwd_reduce(p.dphq, a->B, a->H, a->N, R, g->dphi_q, g->sdphi_q, stream);
   if (st == FB_OK && wl.pk_off != SIZE_MAX)

@@ -62,6 +62,49 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ p
   }
 }
 
+// One thread per 8 output columns of a padded factor row: the row's elements below R (element
+// loads, any alignment), zeros above.
+template <typename T>
+__global__ __launch_bounds__(256) void pad_factor_kernel(const T* __restrict__ phi, int64_t s0, int64_t s1, int64_t s2,
+                                                         int B, int H, int N, int R, int R8, T* __restrict__ out) {
+  typedef T T8 __attribute__((ext_vector_type(8)));
+  const int C8 = R8 / 8;
+  const int64_t total = (int64_t)B * H * N * C8;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
+    const int c0 = (int)(t % C8) * 8;
+    const int64_t row = t / C8;
+    const int n = (int)(row % N);
+    const int64_t bh = row / N;
+    const int h = (int)(bh % H), b = (int)(bh / H);
+    const T* src = phi + b * s0 + h * s1 + n * s2;
+    T8 v;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = c0 + j < R ? src[c0 + j] : (T)0.f;
+    *(T8*)(out + row * R8 + c0) = v;
+  }
+}
+
+// One thread per output element of a padded run's factor gradient: the partials of the (b, h)
+// pairs it gathers, b outer, h inner.
+__global__ __launch_bounds__(256) void unpad_kernel(const float* __restrict__ part, int B, int H, int N, int R8, int R,
+                                                    int Bo, int Ho, float* __restrict__ out, int64_t s0, int64_t s1,
+                                                    int64_t s2) {
+  const int64_t plane = (int64_t)N * R;
+  const int64_t total = (int64_t)Bo * Ho * plane;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t nr = t % plane;
+    const int64_t bh = t / plane;
+    const int ho = (int)(bh % Ho), bo = (int)(bh / Ho);
+    const int n = (int)(nr / R), c = (int)(nr % R);
+    const int b0 = Bo == 1 ? 0 : bo, b1 = Bo == 1 ? B : bo + 1;
+    const int h0 = Ho == 1 ? 0 : ho, h1 = Ho == 1 ? H : ho + 1;
+    float acc = 0.f;
+    for (int b = b0; b < b1; ++b)
+      for (int h = h0; h < h1; ++h) acc += part[(((int64_t)b * H + h) * N + n) * R8 + c];
+    out[bo * s0 + ho * s1 + n * s2 + c] = acc;
+  }
+}
+
 int grid_for(int64_t work) { return (int)std::min<int64_t>((work + 255) / 256, 8192); }
 
 }  // namespace
@@ -100,6 +143,36 @@ fb_status launch_attention_bwd_reduce(const float* part, int B, int H, int N, in
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_error("factor-gradient reduction failed: %s", hipGetErrorString(e));
+    return FB_EHIP;
+  }
+  return FB_OK;
+}
+
+fb_status launch_attention_bwd_pad_factor(const void* phi, int es, const int64_t sphi[3], int B, int H, int N, int R,
+                                          int R8, void* out, hipStream_t s) {
+  const dim3 grid(grid_for((int64_t)B * H * N * (R8 / 8)));
+  if (es == 2)
+    hipLaunchKernelGGL(pad_factor_kernel<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)phi, sphi[0], sphi[1],
+                       sphi[2], B, H, N, R, R8, (uint16_t*)out);
+  else
+    return FB_EUNSUPPORTED;
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("factor padding failed: %s", hipGetErrorString(e));
+    return FB_EHIP;
+  }
+  return FB_OK;
+}
+
+fb_status launch_attention_bwd_unpad(const float* part, int B, int H, int N, int R8, int R, float* out,
+                                     const int64_t sout[3], hipStream_t s) {
+  // an axis of the output with stride 0 has one position and gathers all of that axis
+  const int Bo = sout[0] ? B : 1, Ho = sout[1] ? H : 1;
+  hipLaunchKernelGGL(unpad_kernel, dim3(grid_for((int64_t)Bo * Ho * N * R)), dim3(256), 0, s, part, B, H, N, R8, R, Bo,
+                     Ho, out, sout[0], sout[1], sout[2]);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("factor-gradient unpadding failed: %s", hipGetErrorString(e));
     return FB_EHIP;
   }
   return FB_OK;

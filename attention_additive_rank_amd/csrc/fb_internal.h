@@ -124,9 +124,23 @@ fb_status launch_attention_bwd_delta(fb_dtype dt, const void* o, const int64_t s
 // heads that an axis of out with stride 0 gathers, in (b, h) order.
 fb_status launch_attention_bwd_reduce(const float* part, int B, int H, int N, int R, float* out,
                                       const int64_t sout[3], hipStream_t s);
+// Factors with R not a multiple of 8: phi ([.][.][N][R] with strides sphi, 0 = broadcast, of
+// element size es) -> out [B][H][N][R8] dense, columns R..R8-1 zero.
+fb_status launch_attention_bwd_pad_factor(const void* phi, int es, const int64_t sphi[3], int B, int H, int N, int R,
+                                          int R8, void* out, hipStream_t s);
+// The summed / copied factor gradient of a padded run: out[b'][h'][n][r] (r < R, any 4-byte
+// aligned strides) = sum of part[b][h][n][r] ([B][H][N][R8] dense fp32) over the batches / heads
+// that an axis of out with stride 0 gathers, in (b, h) order.
+fb_status launch_attention_bwd_unpad(const float* part, int B, int H, int N, int R8, int R, float* out,
+                                     const int64_t sout[3], hipStream_t s);
 // Workspace layout of the backward: Delta, then the partial factor gradients that need a sum.
 struct BwdWork {
   size_t delta_off, pq_off, pk_off, bytes;   // pq_off / pk_off = SIZE_MAX: no partial buffer
+  // R not a multiple of 8: the factors are copied into [B][H][N][R8] buffers (zero columns
+  // R..R8-1) at phq_off / phk_off and the kernels' per-(b, h) factor gradients go to
+  // [B][H][N][R8] partials at pq_off / pk_off; R8 = 0 when no padding is needed
+  size_t phq_off, phk_off;
+  int R8;
 };
 BwdWork bwd_work_layout(int B, int H, int N, int R, const int64_t sdphi_q[3], const int64_t sdphi_k[3]);
 

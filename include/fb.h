@@ -392,7 +392,10 @@ typedef struct {
  * fp32 row sums Delta = rowsum(dO * O) ([B][H][N]) and, for each factor gradient that is
  * summed over batches or heads (a 0 stride on an axis of size > 1), one fp32 partial
  * gradient per (b, h) ([B][H][N][R]), which a final pass adds up in a fixed order (no
- * atomics: the sums are deterministic).  Each part starts on a 256-byte boundary.
+ * atomics: the sums are deterministic).  When R is not a multiple of 8 it holds instead
+ * zero-padded copies of both factors ([B][H][N][R8], R8 = R rounded up to 8, in the factor
+ * dtype) and both factor gradients per (b, h) ([B][H][N][R8] fp32).  Each part starts on a
+ * 256-byte boundary.
  * Returns 0 for negative sizes.
  */
 size_t fb_attn_bwd_workspace_bytes(int B, int H, int N, int R, const int64_t sdphi_q[3], const int64_t sdphi_k[3]);
@@ -410,8 +413,12 @@ size_t fb_attn_bwd_workspace_bytes(int B, int H, int N, int R, const int64_t sdp
  *                forward's LSE output, required)
  *   phi_*, R ... the forward's factors (R == 0: plain attention)
  *   g            dO, the outputs and the workspace (see fb_attn_bwd_args)
- * Supported: a->dt FB_BF16 or FB_F16, D in {32, 64}, R <= 64 with R % 8 == 0 and 16-byte
- * aligned factor rows (pad factors with zero columns).  The fused kernels recompute the
+ * Supported: a->dt FB_BF16 or FB_F16, D in {32, 64}, R <= 64.  With R % 8 == 0 the factor
+ * rows and the factor-gradient rows must be 16-byte aligned (FB_EUNSUPPORTED / FB_EINVAL);
+ * otherwise the library first copies the factors into zero-padded [B][H][N][R8] buffers in
+ * the workspace, runs the kernels at width R8 and writes the first R columns of the
+ * gradients (summed where a stride is 0) into dphi_*, which then need only 4-byte alignment
+ * (the factors: element alignment).  The fused kernels recompute the
  * scores tile by tile; Q*s is rounded to dt as in the forward (for the key-major kernel
  * the scale is applied to K, identical when s is a power of two); P and dS are rounded to
  * dt for their MFMA products; accumulation is fp32.  dphi_* of one (b, h) are written by

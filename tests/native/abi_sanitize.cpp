@@ -91,7 +91,10 @@ static void validation() {
   CHECK(fb_attn_bwd_lowrank(&a, FAKE, FAKE, FB_F16, 8, sp, sp, &g, nullptr) == FB_EINVAL);   // no LSE
   b = a;
   b.lse = (float*)FAKE;
-  CHECK(fb_attn_bwd_lowrank(&b, FAKE, FAKE, FB_F16, 12, sp, sp, &g, nullptr) == FB_EUNSUPPORTED);
+  CHECK(fb_attn_bwd_lowrank(&b, FAKE, FAKE, FB_F16, 72, sp, sp, &g, nullptr) == FB_EUNSUPPORTED);   // R > 64
+  CHECK(fb_attn_bwd_lowrank(&b, FAKE, FAKE, FB_F16, 12, sp, sp, &g, nullptr) == FB_EINVAL);   // row stride < R
+  // R = 12: Delta, two padded 16-bit factor copies and two padded fp32 gradient buffers
+  CHECK(fb_attn_bwd_workspace_bytes(2, 3, 100, 12, shared, full) == 2560 + 2 * 19200 + 2 * 38400);
   g.work_bytes = 64;
   CHECK(fb_attn_bwd_lowrank(&b, FAKE, FAKE, FB_F16, 8, sp, sp, &g, nullptr) == FB_EINVAL);
 }

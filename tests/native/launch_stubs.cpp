@@ -42,4 +42,11 @@ fb_status launch_attention_bwd_delta(fb_dtype, const void*, const int64_t[3], co
 fb_status launch_attention_bwd_reduce(const float*, int, int, int, int, float*, const int64_t[3], hipStream_t) {
   return FB_EUNSUPPORTED;
 }
+fb_status launch_attention_bwd_pad_factor(const void*, int, const int64_t[3], int, int, int, int, int, void*,
+                                          hipStream_t) {
+  return FB_EUNSUPPORTED;
+}
+fb_status launch_attention_bwd_unpad(const float*, int, int, int, int, int, float*, const int64_t[3], hipStream_t) {
+  return FB_EUNSUPPORTED;
+}
 }  // namespace fb

@@ -198,7 +198,8 @@ def _bwd(a, R=0, phi_dt=fb.FB_BF16, pq=FAKE, pk=FAKE, s=(0, 0, 64), **gk):
     (dict(D=16, strides=(1024, 1024, 16), lse=FAKE), {}, fb.FB_EUNSUPPORTED),
     (dict(D=128, strides=(8192, 8192, 128), lse=FAKE), {}, fb.FB_EUNSUPPORTED),
     (dict(dt=fb.FB_F32, lse=FAKE), {}, fb.FB_EUNSUPPORTED),
-    (dict(lse=FAKE), dict(R=12), fb.FB_EUNSUPPORTED),           # R not a multiple of 8
+    (dict(lse=FAKE), dict(R=12, pq=FAKE + 1), fb.FB_EINVAL),     # padded factors: element misaligned
+    (dict(lse=FAKE), dict(R=12, dphi_q=FAKE + 2), fb.FB_EINVAL),  # padded gradients: not 4-byte aligned
     (dict(lse=FAKE), dict(R=72), fb.FB_EUNSUPPORTED),
     (dict(lse=FAKE), dict(R=8, phi_dt=fb.FB_F32), fb.FB_EUNSUPPORTED),
     (dict(lse=FAKE), dict(R=8, pq=FAKE + 8), fb.FB_EUNSUPPORTED),   # factor rows not 16-byte aligned
@@ -422,3 +423,19 @@ def test_fp32_head_dim_limit_and_stride_limit():
     assert _lowrank(a) == fb.FB_EUNSUPPORTED
     big = _args(N=64, strides=(1 << 33, 4096, 64))           # batch stride beyond 32 bits
     assert _lowrank(big) == fb.FB_EUNSUPPORTED
+
+
+def test_backward_workspace_with_padded_factors():
+    """R not a multiple of 8: Delta, then two [B][H][N][R8] 16-bit factor copies and two fp32
+    per-(b, h) gradient buffers, each part rounded up to 256 bytes; R a multiple of 8 with
+    per-(b, h) gradient outputs needs Delta only."""
+    up = lambda x: (x + 255) // 256 * 256
+    B, H, N = 2, 3, 100
+    rows = B * H * N
+    full = fb._I64x3(H * N * 12, N * 12, 12)
+    got = fb.load().fb_attn_bwd_workspace_bytes(B, H, N, 12, ctypes.byref(full), ctypes.byref(full))
+    assert got == up(rows * 4) + 2 * up(rows * 16 * 2) + 2 * up(rows * 16 * 4)
+    got6 = fb.load().fb_attn_bwd_workspace_bytes(B, H, N, 6, ctypes.byref(full), ctypes.byref(full))
+    assert got6 == up(rows * 4) + 2 * up(rows * 8 * 2) + 2 * up(rows * 8 * 4)
+    full16 = fb._I64x3(H * N * 16, N * 16, 16)
+    assert fb.load().fb_attn_bwd_workspace_bytes(B, H, N, 16, ctypes.byref(full16), ctypes.byref(full16)) == up(rows * 4)

@@ -510,6 +510,13 @@ BWD = [
     (1, 1, 1000, 64, 64, "shared", "bf16", "f16", True),
     # a per-head factor shared over three batches: gradient summed over the batch axis only
     (3, 2, 150, 64, 16, "head", "bf16", "f16", False),
+    # R not a multiple of 8: the library pads the factors in its workspace (exact ALiBi rank 2,
+    # its split f16 pieces R' = 6, and wider ranks), every factor shape
+    (2, 3, 210, 64, 2, "head", "bf16", "f16", True),
+    (2, 2, 180, 64, 6, "shared", "bf16", "f16", True),
+    (1, 2, 140, 32, 20, "full", "f16", "f16", False),
+    (2, 2, 260, 64, 60, "shared", "bf16", "bf16", False),
+    (3, 1, 100, 32, 3, "head", "bf16", "f16", False),
 ]
 
 
