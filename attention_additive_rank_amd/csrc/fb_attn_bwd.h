@@ -215,8 +215,10 @@ __device__ __forceinline__ void wait_loads_barrier() {
 
 // ---------------------------------------------------------------------------------
 // dK, dV (and dphi_k): one workgroup per 128 keys of one (b, h).
+// Two workgroups per compute unit up to D = 64; at D = 128 one (its B operands and
+// accumulators take up to 256 VGPRs per wavefront).
 template <typename QT, typename PT, int D, int RP, bool CAUSAL>
-__global__ __launch_bounds__(BTH, 2) void attn_bwd_dkv_kernel(BwdParams p) {
+__global__ __launch_bounds__(BTH, D > 64 ? 1 : 2) void attn_bwd_dkv_kernel(BwdParams p) {
   typedef Tile<D, RP, true> T;
   constexpr int QST = D / 16, PST = RP / 16;
   constexpr int MBQ = D / 32, MBP = (RP + 31) / 32;
@@ -455,7 +457,7 @@ __global__ __launch_bounds__(BTH, 2) void attn_bwd_dkv_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------------
 // dQ (and dphi_q): one workgroup per 128 queries of one (b, h).
 template <typename QT, typename PT, int D, int RP, bool CAUSAL>
-__global__ __launch_bounds__(BTH, 2) void attn_bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(BTH, D > 64 ? 1 : 2) void attn_bwd_dq_kernel(BwdParams p) {
   typedef Tile<D, RP, false> T;
   constexpr int QST = D / 16, PST = RP / 16;
   constexpr int MBQ = D / 32, MBP = (RP + 31) / 32;

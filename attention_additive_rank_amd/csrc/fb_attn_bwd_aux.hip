@@ -107,25 +107,31 @@ __global__ __launch_bounds__(256) void unpad_kernel(const float* __restrict__ pa
 
 int grid_for(int64_t work) { return (int)std::min<int64_t>((work + 255) / 256, 8192); }
 
+template <typename T, int TPR>
+void launch_delta(const void* o, const int64_t so[3], const void* dout, const int64_t sdo[3], int B, int H, int N,
+                  float* delta, hipStream_t s) {
+  const dim3 grid(grid_for((int64_t)B * H * N * TPR));
+  hipLaunchKernelGGL((delta_kernel<T, TPR>), grid, dim3(256), 0, s, (const T*)o, so[0], so[1], so[2], (const T*)dout,
+                     sdo[0], sdo[1], sdo[2], B, H, N, delta);
+}
+
+template <typename T>
+void launch_delta_d(int D, const void* o, const int64_t so[3], const void* dout, const int64_t sdo[3], int B, int H,
+                    int N, float* delta, hipStream_t s) {
+  // D in {32, 64, 128} (checked by the caller): D / 8 threads per row
+  if (D == 32) launch_delta<T, 4>(o, so, dout, sdo, B, H, N, delta, s);
+  else if (D == 64) launch_delta<T, 8>(o, so, dout, sdo, B, H, N, delta, s);
+  else launch_delta<T, 16>(o, so, dout, sdo, B, H, N, delta, s);
+}
+
 }  // namespace
 
 fb_status launch_attention_bwd_delta(fb_dtype dt, const void* o, const int64_t so[3], const void* dout,
                                      const int64_t sdo[3], int B, int H, int N, int D, float* delta, hipStream_t s) {
-  const int64_t rows = (int64_t)B * H * N;
-  const int tpr = D / 8;   // D in {32, 64} (checked by the caller)
-  const dim3 grid(grid_for(rows * tpr));
-  if (dt == FB_BF16 && tpr == 8)
-    hipLaunchKernelGGL((delta_kernel<__bf16, 8>), grid, dim3(256), 0, s, (const __bf16*)o, so[0], so[1], so[2],
-                       (const __bf16*)dout, sdo[0], sdo[1], sdo[2], B, H, N, delta);
-  else if (dt == FB_BF16)
-    hipLaunchKernelGGL((delta_kernel<__bf16, 4>), grid, dim3(256), 0, s, (const __bf16*)o, so[0], so[1], so[2],
-                       (const __bf16*)dout, sdo[0], sdo[1], sdo[2], B, H, N, delta);
-  else if (tpr == 8)
-    hipLaunchKernelGGL((delta_kernel<_Float16, 8>), grid, dim3(256), 0, s, (const _Float16*)o, so[0], so[1], so[2],
-                       (const _Float16*)dout, sdo[0], sdo[1], sdo[2], B, H, N, delta);
+  if (dt == FB_BF16)
+    launch_delta_d<__bf16>(D, o, so, dout, sdo, B, H, N, delta, s);
   else
-    hipLaunchKernelGGL((delta_kernel<_Float16, 4>), grid, dim3(256), 0, s, (const _Float16*)o, so[0], so[1], so[2],
-                       (const _Float16*)dout, sdo[0], sdo[1], sdo[2], B, H, N, delta);
+    launch_delta_d<_Float16>(D, o, so, dout, sdo, B, H, N, delta, s);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_error("attention backward preparation failed: %s", hipGetErrorString(e));

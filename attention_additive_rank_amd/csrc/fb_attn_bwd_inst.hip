@@ -1,4 +1,4 @@
-// Backward kernel instances for one head dimension (compiled with -DFB_BWD_D=<32|64>):
+// Backward kernel instances for one head dimension (compiled with -DFB_BWD_D=<32|64|128>):
 // bf16 / f16 operands, factor width RP in {0, 16, 32, 64}, causal or not.
 #include "fb_attn_bwd.h"
 

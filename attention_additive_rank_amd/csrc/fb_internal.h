@@ -113,10 +113,11 @@ struct BwdParams {
 };
 constexpr int kBwdRows = 128;     // rows (keys or queries) per backward workgroup
 
-// Backward kernels (fb_attn_bwd.h): one function per head dim (32 / 64); phi_dt as the
+// Backward kernels (fb_attn_bwd.h): one function per head dim (32 / 64 / 128); phi_dt as the
 // forward; RP in {0, 16, 32, 64}.  FB_EUNSUPPORTED when no instance matches.
 fb_status launch_attention_bwd_d32(fb_dtype dt, fb_dtype phi_dt, int RP, const BwdParams& p, hipStream_t s);
 fb_status launch_attention_bwd_d64(fb_dtype dt, fb_dtype phi_dt, int RP, const BwdParams& p, hipStream_t s);
+fb_status launch_attention_bwd_d128(fb_dtype dt, fb_dtype phi_dt, int RP, const BwdParams& p, hipStream_t s);
 // Delta = rowsum(dO * O) into delta ([B][H][N] fp32).
 fb_status launch_attention_bwd_delta(fb_dtype dt, const void* o, const int64_t so[3], const void* dout,
                                      const int64_t sdo[3], int B, int H, int N, int D, float* delta, hipStream_t s);
