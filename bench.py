@@ -328,14 +328,7 @@ def main():
         del svd_bias
     del scratch
 
-    if args.calib_copy_mib > 0:
-        n = args.calib_copy_mib * (1 << 20) // 4
-        x = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
-        y = torch.empty_like(x)
-        torch.cuda.synchronize()
-        y.copy_(x)
-        torch.cuda.synchronize()
-        del x, y
+    calib_copy(torch, dev, args.calib_copy_mib)
 
     # rocprofv3 counters (the --profile harness), only while they describe this kernel source
     es = 2 if w.dtype != "f32" else 4
@@ -433,6 +426,19 @@ def settle_phase(torch, fn, ms: float):
     return {"steps": n, "ms": round((time.time() - t0) * 1e3, 1)}
 
 
+def calib_copy(torch, dev, mib: int):
+    """One device copy of ``mib`` MiB (the HBM counter calibration of the --profile harness)."""
+    if mib <= 0:
+        return
+    n = mib * (1 << 20) // 4
+    x = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    y.copy_(x)
+    torch.cuda.synchronize()
+    del x, y
+
+
 def bench_backward(args, w, fb, torch, q, k, v, pq_t, pk_t, stage1, out, dev, stream):
     """Backward step: Delta = rowsum(dO * O), zeroed factor gradients, the key-major dK/dV
     kernel and the query-major dQ kernel (fb_attn_bwd_lowrank), after one forward that
@@ -459,6 +465,7 @@ def bench_backward(args, w, fb, torch, q, k, v, pq_t, pk_t, stage1, out, dev, st
     b.record(stream)
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / K
+    calib_copy(torch, dev, args.calib_copy_mib)
     pairs = w.N * (w.N + 1) / 2 if w.causal else float(w.N) ** 2
     Rp = pq_t.shape[-1]
     F = 2.0 * w.B * w.H * pairs * (3 * (w.D + Rp) + 2 * w.D)
@@ -506,16 +513,115 @@ def _run_child(cmd, log, timeout_s):
     return 0
 
 
+def _harness_backward(args, w, tag, out_root, py, trace_cmd, short) -> int:
+    """--profile --backward: the trace and counter passes of the backward step; per kernel
+    (key-major dK/dV, query-major dQ) average time, bytes beyond L2, matrix-core busy fraction."""
+    passes = {"fetch": ["FETCH_SIZE"], "write": ["WRITE_SIZE"],
+              "busy": ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "GRBM_COUNT"]}
+
+    def shown(cmd):
+        return "cd $REPO && TMPDIR=/tmp " + " ".join(("python3" if c == py else c.replace(ROOT + os.sep, ""))
+                                                  for c in cmd)
+    cmds = {"trace": shown(trace_cmd)}
+    hash_file = os.path.join(out_root, "kernel_source_hash")
+    if not args.profile_reparse:
+        with open(hash_file, "w") as f:
+            f.write(kernel_source_hash() + "\n")
+        if _run_child(trace_cmd, os.path.join(out_root, "trace.log"), 300):
+            return 1
+    for name, ctrs in passes.items():
+        cmd = ["rocprofv3", "--pmc"] + ctrs + ["-d", os.path.join(out_root, name), "-o", name,
+                                               "--output-format", "csv", "--"] + short
+        cmds[name] = shown(cmd)
+        if not args.profile_reparse and _run_child(cmd, os.path.join(out_root, f"{name}.log"), 120):
+            return 1
+    stats = _csv_rows(os.path.join(out_root, "trace", "**", "*kernel_stats.csv"))
+    trace = {}
+    for r in stats:
+        nm = r.get("Name") or r.get("KernelName") or ""
+        trace[nm] = (int(float(r.get("Calls") or 0)), float(r.get("AverageNs") or 0) / 1e3,
+                     float(r.get("Percentage") or 0))
+
+    def counter(name, pred, largest=False):
+        vals = {}
+        for r in _csv_rows(os.path.join(out_root, name, "**", "*counter_collection.csv")):
+            kn = r.get("Kernel_Name") or ""
+            if not pred(kn):
+                continue
+            cid, cn = r.get("Correlation_Id") or r.get("Dispatch_Id"), r.get("Counter_Name")
+            vals.setdefault(cn, {}).setdefault(cid, 0.0)
+            vals[cn][cid] += float(r.get("Counter_Value") or 0)
+        if largest:
+            return {c: max(d.values()) for c, d in vals.items() if d}
+        return {c: sum(d.values()) / len(d) for c, d in vals.items() if d}
+    copy = lambda kn: "copyBuffer" in kn
+    fc, wc = counter("fetch", copy, True), counter("write", copy, True)
+    if not fc.get("FETCH_SIZE") or not wc.get("WRITE_SIZE"):
+        print("[harness] no calibration copy in the counter runs", flush=True)
+        return 1
+    fs, ws = 512 * 1024.0 / fc["FETCH_SIZE"], 512 * 1024.0 / wc["WRITE_SIZE"]
+    src_hash = kernel_source_hash()
+    if os.path.exists(hash_file):
+        with open(hash_file) as f:
+            src_hash = f.read().strip() or src_hash
+    res = {"workload": w.name, "entry": "fb_attn_bwd_lowrank", "kernel_source_hash": src_hash, "commands": cmds,
+           "fetch_scale": fs, "write_scale": ws, "kernels": {}}
+    for key in ("attn_bwd_dkv_kernel", "attn_bwd_dq_kernel", "delta_kernel", "reduce_kernel"):
+        pred = lambda kn, key=key: key in kn
+        rows = [(n, t) for n, t in trace.items() if key in n]
+        if not rows:
+            continue
+        nm, (calls, avg, pct) = max(rows, key=lambda x: x[1][0])
+        f_, w_, b_ = counter("fetch", pred), counter("write", pred), counter("busy", pred)
+        k = {"name": nm, "calls": calls, "trace_avg_us": round(avg, 2), "pct_time": round(pct, 1)}
+        if f_.get("FETCH_SIZE") is not None:
+            k["fetch_bytes"] = int(f_["FETCH_SIZE"] * fs * 1024)
+            k["write_bytes"] = int(w_.get("WRITE_SIZE", 0.0) * ws * 1024)
+        if b_.get("SQ_BUSY_CU_CYCLES"):
+            k["mfma_busy"] = round(b_.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (4.0 * b_["SQ_BUSY_CU_CYCLES"]), 4)
+        res["kernels"][key] = k
+    hf = os.path.join(ROOT, "profiles", f"harness_{tag}.json")
+    with open(hf, "w") as f:
+        json.dump(res, f, indent=1)
+    shape = f"b{w.B}h{w.H}n{w.N}d{w.D}r{w.R}"
+    md = os.path.join(ROOT, "profiles", f"attn_bwd_lowrank_{w.name}_{shape}.md")
+    lines = [f"# `fb_attn_bwd_lowrank` on the {w.name} workload (B={w.B} H={w.H} N={w.N} D={w.D} R={w.R}, "
+             f"{w.dtype}; natural-unit factors)", "",
+             f"Written by `python bench.py --profile --backward --workload {w.name} --steps {args.steps} "
+             f"--warmup {args.warmup}` (the rocprofv3 harness in bench.py); raw CSV under gpurun_out/harness/.", "",
+             "Kernel trace (rocprofv3 --kernel-trace --stats) of the timed backward steps:", "", "```",
+             cmds["trace"], "```", "", "Counter passes (3 steps after 1 warm-up, a 512 MiB copy for calibration):",
+             "", "```"] + [cmds[n] for n in passes] + ["```", "",
+             f"Calibration: FETCH_SIZE x{fs:.3f}, WRITE_SIZE x{ws:.3f}.", "",
+             "| kernel | calls | avg us | % time | read beyond L2 MB | written MB | matrix cores busy |",
+             "|---|---|---|---|---|---|---|"]
+    for key, k in res["kernels"].items():
+        lines.append(f"| `{key}` | {k['calls']} | {k['trace_avg_us']:.1f} | {k['pct_time']:.1f} | "
+                     f"{k.get('fetch_bytes', 0) / 1e6:.1f} | {k.get('write_bytes', 0) / 1e6:.1f} | "
+                     f"{100 * k['mfma_busy']:.1f}% |" if "mfma_busy" in k else
+                     f"| `{key}` | {k['calls']} | {k['trace_avg_us']:.1f} | {k['pct_time']:.1f} | "
+                     f"{k.get('fetch_bytes', 0) / 1e6:.1f} | {k.get('write_bytes', 0) / 1e6:.1f} | — |")
+    with open(md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps({"harness": os.path.relpath(hf, ROOT), "summary": os.path.relpath(md, ROOT),
+                      "kernels": {k: v["trace_avg_us"] for k, v in res["kernels"].items()}}), flush=True)
+    return 0
+
+
 def profile_harness(args) -> int:
     import synth
     w = synth.workload(args.workload)
-    out_root = os.path.join(ROOT, "gpurun_out", "harness", w.name + ("_jit" if args.jit else ""))
+    bwd = args.backward
+    tag = w.name + ("_jit" if args.jit else "") + ("_backward" if bwd else "")
+    out_root = os.path.join(ROOT, "gpurun_out", "harness", tag)
     os.makedirs(out_root, exist_ok=True)
     py = sys.executable or "python3"
     bench = os.path.join(ROOT, "bench.py")
     base = [py, bench, "--workload", w.name, "--cpu-budget", "0", "--cold-launches", "0"]
     if args.jit:
         base.append("--jit")
+    if bwd:
+        base.append("--backward")
     # 1. kernel trace of the timed command (steps / warm-up as given)
     trace_cmd = ["rocprofv3", "--kernel-trace", "--stats", "-d", os.path.join(out_root, "trace"), "-o", "trace",
                  "--output-format", "csv", "--"] + base + ["--steps", str(args.steps), "--warmup", str(args.warmup),
@@ -530,6 +636,8 @@ def profile_harness(args) -> int:
     # 512 MiB device copy as the HBM calibration
     # (the dense-bias kernel runs in the same short runs, so its counters come from the same passes)
     short = base + ["--steps", "3", "--warmup", "1", "--settle-ms", "0", "--calib-copy-mib", "512"]
+    if bwd:
+        return _harness_backward(args, w, tag, out_root, py, trace_cmd, short)
     passes = {"fetch": ["FETCH_SIZE"], "write": ["WRITE_SIZE"],
               "busy": ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES",
                        "GRBM_GUI_ACTIVE", "GRBM_COUNT"],
