@@ -477,8 +477,8 @@ fb_status attn_bwd_lowrank_impl(const fb_attn_args* a, const void* phi_q, const 
   if (st != FB_OK) return st;
   if (!g) FB_FAIL(FB_EINVAL, "%s: null gradient arguments", fn);
   if (a->dt != FB_BF16 && a->dt != FB_F16) FB_FAIL(FB_EUNSUPPORTED, "%s: q/k/v must be bf16 or f16", fn);
-  if (a->D != 32 && a->D != 64 && a->D != 128)
-    FB_FAIL(FB_EUNSUPPORTED, "%s: head dim %d not in {32, 64, 128}", fn, a->D);
+  if (a->D != 16 && a->D != 32 && a->D != 64 && a->D != 128)
+    FB_FAIL(FB_EUNSUPPORTED, "%s: head dim %d not in {16, 32, 64, 128}", fn, a->D);
   if (R < 0) FB_FAIL(FB_EINVAL, "%s: negative R", fn);
   if (R > 64) FB_FAIL(FB_EUNSUPPORTED, "%s: R = %d (at most 64)", fn, R);
   if (R > 0) {
@@ -607,7 +607,8 @@ fb_status attn_bwd_lowrank_impl(const fb_attn_args* a, const void* phi_q, const 
   st = launch_attention_bwd_delta(a->dt, a->o, a->so, g->dout, g->sdo, a->B, a->H, a->N, a->D, delta, stream);
   if (st != FB_OK) return st;
   const fb_dtype pdt = R > 0 ? phi_dt : a->dt;
-  st = a->D == 32   ? launch_attention_bwd_d32(a->dt, pdt, RP, p, stream)
+  st = a->D == 16   ? launch_attention_bwd_d16(a->dt, pdt, RP, p, stream)
+       : a->D == 32 ? launch_attention_bwd_d32(a->dt, pdt, RP, p, stream)
        : a->D == 64 ? launch_attention_bwd_d64(a->dt, pdt, RP, p, stream)
                     : launch_attention_bwd_d128(a->dt, pdt, RP, p, stream);
   if (st == FB_EUNSUPPORTED) set_error("%s: no kernel for this dtype / rank combination", fn);

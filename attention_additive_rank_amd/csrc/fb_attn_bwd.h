@@ -153,9 +153,13 @@ __device__ __forceinline__ void dma4_async(const void* src, uint32_t lds) {
 // or past R copies the row's first chunk).  Per tile, Bases holds each region's first-row
 // address (scalar) and a clamp: rows past N read the last row's last chunk (finite
 // stand-ins, masked by the caller), at the cost of one min per load.
-template <int D, int RP, bool LD>
+// DV < D (head dim 16 in the D = 32 layout): chunks of regions X and Y at or past DV copy a
+// chunk of the same row (finite stand-ins that meet zero register operands; the gradient
+// columns they produce are not stored).
+template <int D, int RP, bool LD, int DV = D>
 struct DmaPlan {
   typedef Tile<D, RP, LD> T;
+  static constexpr int VCH = DV / 8;   // chunks of a row that hold data (regions X, Y)
   static_assert(T::NX % BW == 0 && T::NF % BW == 0 && T::NY % BW == 0, "loads per region");
   static constexpr int NI = T::NLOAD / BW;
   static constexpr int region(int i) { return BW * i < T::NX ? 0 : BW * i < T::NX + T::NF ? 1 : 2; }
@@ -171,7 +175,7 @@ struct DmaPlan {
                                        const char* yb, int ys) {
     src[0] = xb; src[1] = fb; src[2] = yb;
     stride2[0] = 2 * xs; stride2[1] = 2 * fs; stride2[2] = 2 * ys;
-    cmax[0] = T::KCH - 1; cmax[1] = npch - 1; cmax[2] = T::KCH - 1;
+    cmax[0] = VCH - 1; cmax[1] = npch - 1; cmax[2] = VCH - 1;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int r = region(i), c0 = cpr(r);
@@ -179,6 +183,7 @@ struct DmaPlan {
       const int row = nr * (64 / c0) + lane / c0;
       int c = (lane % c0) ^ swzb(c0, row);
       if (r == 1 && c >= npch) c = 0;
+      if (r != 1 && c >= VCH) c %= VCH;
       off[i] = (uint32_t)(row * stride2[r] + c * 16);
     }
   }
@@ -217,7 +222,8 @@ __device__ __forceinline__ void wait_loads_barrier() {
 // dK, dV (and dphi_k): one workgroup per 128 keys of one (b, h).
 // Two workgroups per compute unit up to D = 64; at D = 128 one (its B operands and
 // accumulators take up to 256 VGPRs per wavefront).
-template <typename QT, typename PT, int D, int RP, bool CAUSAL>
+// DV: head dims that hold data (DV = 16 runs in the D = 32 layout; see DmaPlan).
+template <typename QT, typename PT, int D, int RP, bool CAUSAL, int DV = D>
 __global__ __launch_bounds__(BTH, D > 64 ? 1 : 2) void attn_bwd_dkv_kernel(BwdParams p) {
   typedef Tile<D, RP, true> T;
   constexpr int QST = D / 16, PST = RP / 16;
@@ -269,8 +275,12 @@ __global__ __launch_bounds__(BTH, D > 64 ? 1 : 2) void attn_bwd_dkv_kernel(BwdPa
   const u32x4 sgn = {0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
 #pragma unroll
   for (int t = 0; t < QST; ++t) {
-    kf[t] = scale_frag<QT>(ld16(Kp + keyc * p.sk[2] + 16 * t + 8 * hf), -p.scale);
-    vf[t] = ld16(Vp + keyc * p.sv[2] + 16 * t + 8 * hf) ^ sgn;
+    // head dims at or past DV: zero operands (their loads read the row's first chunk)
+    const bool ok = 16 * t + 8 * hf < DV;
+    const int c = ok ? 16 * t + 8 * hf : 0;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    kf[t] = ok ? scale_frag<QT>(ld16(Kp + keyc * p.sk[2] + c), -p.scale) : z;
+    vf[t] = (ok ? ld16(Vp + keyc * p.sv[2] + c) : z) ^ sgn;
   }
   if constexpr (RP > 0) {
 #pragma unroll
@@ -291,13 +301,13 @@ __global__ __launch_bounds__(BTH, D > 64 ? 1 : 2) void attn_bwd_dkv_kernel(BwdPa
   // issues the same number of loads per tile (NV: its chunk slots and one 4-byte copy of
   // the tile's L (even wavefronts) or Delta (odd) into the tile), so "at most NV
   // outstanding" means the next tile has landed.
-  DmaPlan<D, RP, true> plan;
+  DmaPlan<D, RP, true, DV> plan;
   plan.init(wave, lane, (const char*)Qp, p.sq[2], (const char*)PQp, p.spq[2], npch, (const char*)Op, p.sdo[2]);
-  constexpr int NI = DmaPlan<D, RP, true>::NI, NV = NI + 1, NI0 = (NI + 1) / 2;
+  constexpr int NI = DmaPlan<D, RP, true, DV>::NI, NV = NI + 1, NI0 = (NI + 1) / 2;
   const float* LDp = (wave & 1) ? Dp : Lp;
   // direct load j of a tile's NV: chunk slots, then the L / Delta copy
   // direct load j of a tile's NV: chunk slots, then the L / Delta copy
-  auto issue_one = [&](int j, const typename DmaPlan<D, RP, true>::Bases& tb, unsigned char* dst, int r0)
+  auto issue_one = [&](int j, const typename DmaPlan<D, RP, true, DV>::Bases& tb, unsigned char* dst, int r0)
       __attribute__((always_inline)) {
     if (j < NI) plan.issue(j, tb, dst, wave);
     else dma4_async(LDp + r0 + min(lane, N - 1 - r0), lds_addr(dst + T::LOFF + 256 * (wave & 1)));
@@ -436,8 +446,10 @@ __global__ __launch_bounds__(BTH, D > 64 ? 1 : 2) void attn_bwd_dkv_kernel(BwdPa
           k4[c] = (QT)(dkT[mb][4 * a + c] * -p.scale);   // dK = dS^T (Q s); dkT holds -dS^T Q
         }
         const int col = 32 * mb + 8 * a + 4 * hf;
-        *(u32x2*)(dVp + col) = __builtin_bit_cast(u32x2, v4);
-        *(u32x2*)(dKp + col) = __builtin_bit_cast(u32x2, k4);
+        if (col < DV) {
+          *(u32x2*)(dVp + col) = __builtin_bit_cast(u32x2, v4);
+          *(u32x2*)(dKp + col) = __builtin_bit_cast(u32x2, k4);
+        }
       }
     if constexpr (RP > 0) {   // this (b, h)'s dphi_k row (its partial when summed): 4 columns a store
       float* g = p.dphk + ((int64_t)bb * p.sdpk[0] + (int64_t)hh * p.sdpk[1] + (int64_t)key * p.sdpk[2]);
@@ -456,7 +468,7 @@ __global__ __launch_bounds__(BTH, D > 64 ? 1 : 2) void attn_bwd_dkv_kernel(BwdPa
 
 // ---------------------------------------------------------------------------------
 // dQ (and dphi_q): one workgroup per 128 queries of one (b, h).
-template <typename QT, typename PT, int D, int RP, bool CAUSAL>
+template <typename QT, typename PT, int D, int RP, bool CAUSAL, int DV = D>
 __global__ __launch_bounds__(BTH, D > 64 ? 1 : 2) void attn_bwd_dq_kernel(BwdParams p) {
   typedef Tile<D, RP, false> T;
   constexpr int QST = D / 16, PST = RP / 16;
@@ -500,8 +512,11 @@ __global__ __launch_bounds__(BTH, D > 64 ? 1 : 2) void attn_bwd_dq_kernel(BwdPar
   u32x4 qf[QST], of[QST], pqf[PST > 0 ? PST : 1];
 #pragma unroll
   for (int t = 0; t < QST; ++t) {
-    qf[t] = scale_frag<QT>(ld16(Qp + qc * p.sq[2] + 16 * t + 8 * hf), p.scale);
-    of[t] = ld16(Op + qc * p.sdo[2] + 16 * t + 8 * hf);
+    const bool ok = 16 * t + 8 * hf < DV;   // head dims at or past DV: zero operands
+    const int c = ok ? 16 * t + 8 * hf : 0;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    qf[t] = ok ? scale_frag<QT>(ld16(Qp + qc * p.sq[2] + c), p.scale) : z;
+    of[t] = ok ? ld16(Op + qc * p.sdo[2] + c) : z;
   }
   if constexpr (RP > 0) {
 #pragma unroll
@@ -521,9 +536,9 @@ __global__ __launch_bounds__(BTH, D > 64 ? 1 : 2) void attn_bwd_dq_kernel(BwdPar
   const int nkt = (kend + TR - 1) / TR;
   // three tile buffers: tile kt + 2 streams in while tile kt is computed (NI loads per
   // wavefront and tile, so "at most NI outstanding" means the next tile has landed)
-  DmaPlan<D, RP, false> plan;
+  DmaPlan<D, RP, false, DV> plan;
   plan.init(wave, lane, (const char*)Kp, p.sk[2], (const char*)PKp, p.spk[2], npch, (const char*)Vp, p.sv[2]);
-  constexpr int NI = DmaPlan<D, RP, false>::NI;
+  constexpr int NI = DmaPlan<D, RP, false, DV>::NI;
 
   constexpr int NS = 2 * QST + PST;   // S^T (X) and dP^T (Y) alternating, then S^T (F)
   constexpr int NCU = MBQ + MBP;      // gradient MFMAs per k-step u: dQ^T, dphi_q^T
@@ -633,7 +648,7 @@ __global__ __launch_bounds__(BTH, D > 64 ? 1 : 2) void attn_bwd_dq_kernel(BwdPar
         T4 q4;
 #pragma unroll
         for (int c = 0; c < 4; ++c) q4[c] = (QT)(dqT[mb][4 * a + c] * p.scale);
-        *(u32x2*)(dQp + 32 * mb + 8 * a + 4 * hf) = __builtin_bit_cast(u32x2, q4);
+        if (32 * mb + 8 * a + 4 * hf < DV) *(u32x2*)(dQp + 32 * mb + 8 * a + 4 * hf) = __builtin_bit_cast(u32x2, q4);
       }
     if constexpr (RP > 0) {   // this (b, h)'s dphi_q row (its partial when summed): 4 columns a store
       float* g = p.dphq + ((int64_t)bb * p.sdpq[0] + (int64_t)hh * p.sdpq[1] + (int64_t)qrow * p.sdpq[2]);

@@ -118,8 +118,9 @@ void launch_delta(const void* o, const int64_t so[3], const void* dout, const in
 template <typename T>
 void launch_delta_d(int D, const void* o, const int64_t so[3], const void* dout, const int64_t sdo[3], int B, int H,
                     int N, float* delta, hipStream_t s) {
-  // D in {32, 64, 128} (checked by the caller): D / 8 threads per row
-  if (D == 32) launch_delta<T, 4>(o, so, dout, sdo, B, H, N, delta, s);
+  // D in {16, 32, 64, 128} (checked by the caller): D / 8 threads per row
+  if (D == 16) launch_delta<T, 2>(o, so, dout, sdo, B, H, N, delta, s);
+  else if (D == 32) launch_delta<T, 4>(o, so, dout, sdo, B, H, N, delta, s);
   else if (D == 64) launch_delta<T, 8>(o, so, dout, sdo, B, H, N, delta, s);
   else launch_delta<T, 16>(o, so, dout, sdo, B, H, N, delta, s);
 }

@@ -1,4 +1,4 @@
-// Backward kernel instances for one head dimension (compiled with -DFB_BWD_D=<32|64|128>):
+// Backward kernel instances for one head dimension (compiled with -DFB_BWD_D=<16|32|64|128>):
 // bf16 / f16 operands, factor width RP in {0, 16, 32, 64}, causal or not.
 #include "fb_attn_bwd.h"
 
@@ -9,11 +9,16 @@
 namespace fb {
 namespace attnb {
 
+// head dim 16 runs in the head-dim-32 layout with the columns past 16 as zero operands
+constexpr int KD = FB_BWD_D < 32 ? 32 : FB_BWD_D;
+
 template <typename QT, typename PT, int RP, bool CAUSAL>
 static fb_status launch2(const BwdParams& p, hipStream_t s) {
   const int64_t grid = (int64_t)p.nblk * p.H * p.B;
-  hipLaunchKernelGGL((attn_bwd_dkv_kernel<QT, PT, FB_BWD_D, RP, CAUSAL>), dim3((unsigned)grid), dim3(BTH), 0, s, p);
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<QT, PT, FB_BWD_D, RP, CAUSAL>), dim3((unsigned)grid), dim3(BTH), 0, s, p);
+  hipLaunchKernelGGL((attn_bwd_dkv_kernel<QT, PT, KD, RP, CAUSAL, FB_BWD_D>), dim3((unsigned)grid), dim3(BTH), 0, s,
+                     p);
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<QT, PT, KD, RP, CAUSAL, FB_BWD_D>), dim3((unsigned)grid), dim3(BTH), 0, s,
+                     p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_error("attention backward launch failed: %s", hipGetErrorString(e));

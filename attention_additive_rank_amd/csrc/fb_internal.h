@@ -113,8 +113,9 @@ struct BwdParams {
 };
 constexpr int kBwdRows = 128;     // rows (keys or queries) per backward workgroup
 
-// Backward kernels (fb_attn_bwd.h): one function per head dim (32 / 64 / 128); phi_dt as the
+// Backward kernels (fb_attn_bwd.h): one function per head dim (16 / 32 / 64 / 128); phi_dt as the
 // forward; RP in {0, 16, 32, 64}.  FB_EUNSUPPORTED when no instance matches.
+fb_status launch_attention_bwd_d16(fb_dtype dt, fb_dtype phi_dt, int RP, const BwdParams& p, hipStream_t s);
 fb_status launch_attention_bwd_d32(fb_dtype dt, fb_dtype phi_dt, int RP, const BwdParams& p, hipStream_t s);
 fb_status launch_attention_bwd_d64(fb_dtype dt, fb_dtype phi_dt, int RP, const BwdParams& p, hipStream_t s);
 fb_status launch_attention_bwd_d128(fb_dtype dt, fb_dtype phi_dt, int RP, const BwdParams& p, hipStream_t s);

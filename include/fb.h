@@ -413,7 +413,7 @@ size_t fb_attn_bwd_workspace_bytes(int B, int H, int N, int R, const int64_t sdp
  *                forward's LSE output, required)
  *   phi_*, R ... the forward's factors (R == 0: plain attention)
  *   g            dO, the outputs and the workspace (see fb_attn_bwd_args)
- * Supported: a->dt FB_BF16 or FB_F16, D in {32, 64, 128}, R <= 64.  With R % 8 == 0 the factor
+ * Supported: a->dt FB_BF16 or FB_F16, D in {16, 32, 64, 128}, R <= 64.  With R % 8 == 0 the factor
  * rows and the factor-gradient rows must be 16-byte aligned (FB_EUNSUPPORTED / FB_EINVAL);
  * otherwise the library first copies the factors into zero-padded [B][H][N][R8] buffers in
  * the workspace, runs the kernels at width R8 and writes the first R columns of the

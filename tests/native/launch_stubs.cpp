@@ -33,6 +33,7 @@ fb_status launch_mulbias_expand(fb_dtype, fb_dtype, const void*, const int64_t[3
                                 int, int, int, int, float, void*, void*, hipStream_t) {
   return FB_EUNSUPPORTED;
 }
+fb_status launch_attention_bwd_d16(fb_dtype, fb_dtype, int, const BwdParams&, hipStream_t) { return FB_EUNSUPPORTED; }
 fb_status launch_attention_bwd_d32(fb_dtype, fb_dtype, int, const BwdParams&, hipStream_t) { return FB_EUNSUPPORTED; }
 fb_status launch_attention_bwd_d64(fb_dtype, fb_dtype, int, const BwdParams&, hipStream_t) { return FB_EUNSUPPORTED; }
 fb_status launch_attention_bwd_d128(fb_dtype, fb_dtype, int, const BwdParams&, hipStream_t) { return FB_EUNSUPPORTED; }

@@ -517,6 +517,10 @@ BWD = [
     (1, 2, 140, 32, 20, "full", "f16", "f16", False),
     (2, 2, 260, 64, 60, "shared", "bf16", "bf16", False),
     (3, 1, 100, 32, 3, "head", "bf16", "f16", False),
+    # head dim 16 (run in the head-dim-32 layout with zero operands past 16)
+    (2, 2, 230, 16, 8, "head", "bf16", "f16", False),
+    (1, 3, 140, 16, 0, None, "f16", "f16", True),
+    (2, 1, 100, 16, 6, "shared", "bf16", "f16", True),
     # head dim 128 (one workgroup per compute unit)
     (2, 2, 200, 128, 0, None, "bf16", "bf16", False),
     (1, 2, 260, 128, 64, "shared", "bf16", "f16", True),

@@ -112,6 +112,8 @@ BWD = [
     # (B, H, N, D, R, factor shape, dtype, causal)
     (2, 2, 203, 64, 16, "shared", "bf16", True),
     (1, 3, 150, 32, 8, "head", "f16", False),
+    (2, 2, 170, 16, 6, "head", "bf16", True),      # head dim 16, padded rank
+    (1, 2, 90, 128, 16, "shared", "bf16", False),  # head dim 128
 ]
 
 
