@@ -760,6 +760,9 @@ MULTI = [
     ("lowrank", 30, 10, 130, 32, 0, "bf16"),
     ("sandwich", 20, 8, 512, 32, 32, "bf16"),
     ("alibi", 33, 8, 260, 32, 0, "bf16"),
+    # one key tile per item (every step switches items), per-batch factors
+    ("lowrank_log2", 300, 2, 40, 32, 8, "bf16"),
+    ("lowrank_batch", 130, 4, 70, 16, 16, "f16"),
 ]
 
 
@@ -775,9 +778,10 @@ def test_multi_item_workgroups(fb, entry, B, H, N, D, R, dt):
     q, k, v = (synth.round_to(r.standard_normal((B, H, N, D)) * 0.5, dt) for _ in range(3))
     qd, kd, vd = (to_dev(x, dt) for x in (q, k, v))
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda:0")
-    if entry in ("lowrank", "lowrank_log2"):
-        pq = synth.round_to(r.standard_normal((H, N, R)) * 0.5, "f16") if R else None
-        pk = synth.round_to(r.standard_normal((H, N, R)) * 0.5, "f16") if R else None
+    if entry in ("lowrank", "lowrank_log2", "lowrank_batch"):
+        fshape = (B, H, N, R) if entry == "lowrank_batch" else (H, N, R)
+        pq = synth.round_to(r.standard_normal(fshape) * 0.5, "f16") if R else None
+        pk = synth.round_to(r.standard_normal(fshape) * 0.5, "f16") if R else None
         run = fb.fb_attn_fwd_lowrank_log2 if entry == "lowrank_log2" else fb.fb_attn_fwd_lowrank
         o = run(qd, kd, vd, to_dev(pq, "f16") if R else None, to_dev(pk, "f16") if R else None, lse=lse)
         bias = None
