@@ -7,18 +7,23 @@
 // Reviewer UJUf, Q2: concatenate the factor functions with queries and keys,
 // then run FlashAttention).  MODE 1 (dense bias, the baseline): the contraction
 // is Q*s K^T and a bias tile is read from HBM for every (query, key) tile pair,
-// the quadratic IO of the abstract and Fig. 1(c).
+// the quadratic IO of the abstract and Fig. 1(c).  MODE 2 and MODE 4 form the ALiBi and
+// Sandwich factor columns inside the kernel; MODE 3 is MODE 0 with the scores in exp2 units.
 //
 // Work decomposition
 //   * One workgroup = 8 wavefronts = 256 query rows of one (batch, head); each
 //     wavefront owns 32 query rows for the whole key loop.  Waves w and w+4 run
 //     on the same SIMD, so the two groups {0..3} and {4..7} pair up per SIMD.
-//   * Ping-pong schedule: per key tile each wavefront has a matrix phase
-//     (S(t+1) = K'(t+1) Q'^T and O += V(t)^T P(t)^T on the MFMA units) and a
-//     vector phase (online softmax of S(t+1)); the two groups run opposite
-//     phases between workgroup barriers, so on every SIMD one wave keeps the
-//     matrix core busy while the other does exp2/max/sum on the VALU.
-//   * Key tiles of 64 keys are double-buffered in LDS: K' rows (K then phi_k,
+//   * Per key tile each wavefront has a matrix phase (S(t+1) = K'(t+1) Q'^T and
+//     O += V(t)^T P(t)^T on the MFMA units) and a vector phase (online softmax of
+//     S(t+1)).  With loader wavefronts there is one workgroup barrier per tile:
+//     group 0 runs matrix then softmax, group 1 softmax (at raised priority) then
+//     matrix, so on every SIMD one wave's MFMAs overlap the other's softmax.
+//     Without them the two groups run opposite phases between per-phase barriers.
+//   * Non-causal kernels with narrow Q' can take several (b, h, query block) work
+//     items per workgroup, one key-tile stream running across them.
+//   * Key tiles of 64 keys are double-buffered in LDS (three stages with loader
+//     wavefronts): K' rows (K then phi_k,
 //     zero-padded to RP columns) and V rows, each region row-major with a
 //     per-row XOR swizzle of its 16-byte chunks (conflict-free MFMA operand
 //     reads, whole rows per copy).  Tiles arrive by direct global->LDS loads
@@ -30,9 +35,9 @@
 //     them.  Rows past N are not loaded and are masked in the scores.
 //   * V stays row-major in LDS; the A operand of O^T = V^T P^T comes from
 //     64-bit transpose reads (ds_read_b64_tr_b16), four keys per read.
-//   * The softmax row sum (16-bit operands) is one more MFMA per P V k-step with
-//     an all-ones A row, so it costs matrix-core cycles instead of VALU adds and
-//     is rescaled together with O.
+//   * The softmax row sum (16-bit low-rank operands; not in exp2 units at RP 64)
+//     is one more MFMA per P V k-step with an all-ones A row, so it costs
+//     matrix-core cycles instead of VALU adds and is rescaled together with O.
 //   * Scores are computed transposed, S^T = K' Q'^T, with 32x32 MFMAs
 //     (32x32x16 bf16/f16, 32x32x2 fp32).  With that orientation every lane owns
 //     ONE query (lane % 32) and 16 keys per 32-key block, so the row max / row
@@ -304,9 +309,9 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   static_assert((KCH & (KCH - 1)) == 0 && (PCH & (PCH - 1)) == 0 && (VCH & (VCH - 1)) == 0 && VCH >= 4,
                 "tile rows must be a power-of-two number of chunks");
 
-  // Four LDS objects, with the key loop unrolled by two: every access names its buffer
-  // statically, so the compiler can tell that a direct load in flight never writes the
-  // buffer being read, and does not wait for it.
+  // Two stages of K' and V tiles (three with loader wavefronts), the key loop unrolled by the
+  // stage count: every access names its buffer statically, so the compiler can tell that a
+  // direct load in flight never writes the buffer being read, and does not wait for it.
   __shared__ __attribute__((aligned(16))) unsigned char sK0[SK_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char sK1[SK_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char sV0[SV_BYTES];
@@ -1194,12 +1199,13 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
     }
   };
 
-  // ---- ping-pong: per SIMD, one wavefront multiplies while the other does softmax ----
+  // ---- the key loop: per SIMD, one wavefront multiplies while the other does softmax ----
   // Every wavefront runs the same sequence  MFMA(t) | softmax(t+1) | MFMA(t+1) | ...  with
-  // MFMA(t) = {S(t+1) = K'(t+1) Q'^T, O += V(t)^T P(t)}, one phase per barrier; group 1
-  // starts one phase late, so on each SIMD the two wavefronts are always in opposite
-  // phases.  (One code path for both groups: branching on the group around the
-  // accumulators makes the compiler copy them at every join.)
+  // MFMA(t) = {S(t+1) = K'(t+1) Q'^T, O += V(t)^T P(t)}.  With loader wavefronts: one
+  // barrier per tile (see step).  Without: one phase per barrier, group 1 starting one phase
+  // late, so on each SIMD the two wavefronts are always in opposite phases.  (One code path
+  // for both groups: branching on the group around the accumulators makes the compiler copy
+  // them at every join.)
   // Without loader wavefronts the tile copies go out from the softmax phases, which read
   // nothing from LDS (the compiler cannot order LDS reads after an outstanding direct load
   // by the counter, and would wait for all of them), split between the groups: group 0,
