@@ -101,7 +101,7 @@ def load():
             fn.restype = ctypes.c_int
             fn.argtypes = [ctypes.POINTER(_AttnArgs), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                            ctypes.POINTER(_I64x3), ctypes.POINTER(_I64x3), ctypes.c_void_p]
-        for fn in (lib.fb_attn_bwd_lowrank, lib.fb_attn_bwd_lowrank_noalloc):
+        for fn in (lib.fb_attn_bwd_lowrank, lib.fb_attn_bwd_lowrank_log2, lib.fb_attn_bwd_lowrank_noalloc):
             fn.restype = ctypes.c_int
             fn.argtypes = [ctypes.POINTER(_AttnArgs), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                            ctypes.POINTER(_I64x3), ctypes.POINTER(_I64x3), ctypes.POINTER(_BwdArgs), ctypes.c_void_p]
@@ -446,14 +446,16 @@ def fb_mulbias_expand(q, k, phi_q, phi_k, *, scale: Optional[float] = None, work
 
 def fb_attn_bwd_lowrank(q, k, v, out, lse, dout, phi_q=None, phi_k=None, *, causal: bool = False,
                         scale: Optional[float] = None, dq=None, dk=None, dv=None, dphi_q=None, dphi_k=None,
-                        stream=None, noalloc: bool = False):
+                        stream=None, noalloc: bool = False, log2: bool = False):
     """Gradients of fb_attn_fwd_lowrank's output for the upstream gradient ``dout``.
 
     ``out`` and ``lse`` are the forward's output and LSE (float32 ``[B, H, N]``).  Returns
     ``(dq, dk, dv, dphi_q, dphi_k)``; the factor gradients are float32 with the factors'
     own shapes (summed over the axes a factor is broadcast on), None for R = 0.
     ``noalloc``: call fb_attn_bwd_lowrank_noalloc, whose workspace is the library's device
-    scratch (with every output passed in, this wrapper then allocates nothing either)."""
+    scratch (with every output passed in, this wrapper then allocates nothing either).
+    ``log2``: the factors are fb_attn_fwd_lowrank_log2's (phi_q in exp2 units; the gradients
+    are with respect to them): fb_attn_bwd_lowrank_log2."""
     torch = _torch()
     B, H, N, D = q.shape
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
@@ -485,11 +487,13 @@ def fb_attn_bwd_lowrank(q, k, v, out, lse, dout, phi_q=None, phi_k=None, *, caus
         g.dphi_q, g.dphi_k, g.sdphi_q, g.sdphi_k = dpq.data_ptr(), dpk.data_ptr(), gsq, gsk
     work = None
     if noalloc:
+        if log2:
+            raise ValueError("the no-alloc backward takes natural-unit factors")
         entry = load().fb_attn_bwd_lowrank_noalloc
         g.work, g.work_bytes = None, 0
     else:
         # workspace (Delta and per-(b, h) partials of summed factor gradients), 256-byte aligned
-        entry = load().fb_attn_bwd_lowrank
+        entry = load().fb_attn_bwd_lowrank_log2 if log2 else load().fb_attn_bwd_lowrank
         nbytes = int(load().fb_attn_bwd_workspace_bytes(B, H, N, R, ctypes.byref(g.sdphi_q), ctypes.byref(g.sdphi_k)))
         work = torch.empty(nbytes + 256, dtype=torch.uint8, device=q.device)
         g.work = (work.data_ptr() + 255) // 256 * 256

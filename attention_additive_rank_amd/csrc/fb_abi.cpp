@@ -467,12 +467,19 @@ fb_status fb_attn_bwd_lowrank(const fb_attn_args* a, const void* phi_q, const vo
                               hipStream_t stream) {
   return fb::attn_bwd_lowrank_impl(a, phi_q, phi_k, phi_dt, R, sphi_q, sphi_k, g, stream, "fb_attn_bwd_lowrank");
 }
+
+fb_status fb_attn_bwd_lowrank_log2(const fb_attn_args* a, const void* phi_q, const void* phi_k, fb_dtype phi_dt,
+                                   int R, const int64_t sphi_q[3], const int64_t sphi_k[3],
+                                   const fb_attn_bwd_args* g, hipStream_t stream) {
+  return fb::attn_bwd_lowrank_impl(a, phi_q, phi_k, phi_dt, R, sphi_q, sphi_k, g, stream, "fb_attn_bwd_lowrank_log2",
+                                   true);
+}
 }  // extern "C"
 
 namespace fb {
 fb_status attn_bwd_lowrank_impl(const fb_attn_args* a, const void* phi_q, const void* phi_k, fb_dtype phi_dt, int R,
                                 const int64_t sphi_q[3], const int64_t sphi_k[3], const fb_attn_bwd_args* g,
-                                hipStream_t stream, const char* fn) {
+                                hipStream_t stream, const char* fn, bool log2) {
   fb_status st = check_common(a, fn);
   if (st != FB_OK) return st;
   if (!g) FB_FAIL(FB_EINVAL, "%s: null gradient arguments", fn);
@@ -528,7 +535,7 @@ fb_status attn_bwd_lowrank_impl(const fb_attn_args* a, const void* phi_q, const 
     p.sdv[i] = (int)g->sdv[i];
   }
   p.R = R;
-  p.flags = a->causal ? FLAG_CAUSAL : 0;
+  p.flags = (a->causal ? FLAG_CAUSAL : 0) | (log2 && R > 0 ? FLAG_LOG2 : 0);
   p.B = a->B;
   p.H = a->H;
   p.N = a->N;

@@ -222,8 +222,11 @@ __device__ __forceinline__ void wait_loads_barrier() {
 // dK, dV (and dphi_k): one workgroup per 128 keys of one (b, h).
 // Two workgroups per compute unit up to D = 64; at D = 128 one (its B operands and
 // accumulators take up to 256 VGPRs per wavefront).
-// DV: head dims that hold data (DV = 16 runs in the D = 32 layout; see DmaPlan).
-template <typename QT, typename PT, int D, int RP, bool CAUSAL, int DV = D>
+// DV: head dims that hold data (DV = 16 runs in the D = 32 layout; see DmaPlan).  LOG2: phi_q
+// in exp2 units (phi_q log2(e), as fb_attn_fwd_lowrank_log2 takes it): the scores are formed
+// in exp2 units (K s log2(e) here, Q s log2(e) in the dQ kernel, L log2(e)), dS stays in
+// natural units, and the factor gradients are those of the given factors (ln 2 dS phi).
+template <typename QT, typename PT, int D, int RP, bool CAUSAL, int DV = D, bool LOG2 = false>
 __global__ __launch_bounds__(BTH, D > 64 ? 1 : 2) void attn_bwd_dkv_kernel(BwdParams p) {
   typedef Tile<D, RP, true> T;
   constexpr int QST = D / 16, PST = RP / 16;
@@ -279,7 +282,7 @@ __global__ __launch_bounds__(BTH, D > 64 ? 1 : 2) void attn_bwd_dkv_kernel(BwdPa
     const bool ok = 16 * t + 8 * hf < DV;
     const int c = ok ? 16 * t + 8 * hf : 0;
     const u32x4 z = {0u, 0u, 0u, 0u};
-    kf[t] = ok ? scale_frag<QT>(ld16(Kp + keyc * p.sk[2] + c), -p.scale) : z;
+    kf[t] = ok ? scale_frag<QT>(ld16(Kp + keyc * p.sk[2] + c), LOG2 ? -p.scale * LOG2E : -p.scale) : z;
     vf[t] = (ok ? ld16(Vp + keyc * p.sv[2] + c) : z) ^ sgn;
   }
   if constexpr (RP > 0) {
@@ -347,7 +350,7 @@ __global__ __launch_bounds__(BTH, D > 64 ? 1 : 2) void attn_bwd_dkv_kernel(BwdPa
         const f32x4 L4 = lq[g], D4 = dq[g];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          s[4 * g + c] = L4[c];
+          s[4 * g + c] = LOG2 ? L4[c] * LOG2E : L4[c];
           dp[4 * g + c] = D4[c];
         }
       }
@@ -382,7 +385,7 @@ __global__ __launch_bounds__(BTH, D > 64 ? 1 : 2) void attn_bwd_dkv_kernel(BwdPa
       float pv[16], dsv[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        pv[i] = __builtin_amdgcn_exp2f(s[i] * -LOG2E);
+        pv[i] = __builtin_amdgcn_exp2f(LOG2 ? -s[i] : s[i] * -LOG2E);
         dsv[i] = pv[i] * dp[i];
       }
       u32x4 pb[2], dsb[2], dsp[2];
@@ -458,8 +461,9 @@ __global__ __launch_bounds__(BTH, D > 64 ? 1 : 2) void attn_bwd_dkv_kernel(BwdPa
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           const int col = 32 * mb + 8 * a + 4 * hf;
-          const f32x4 v = {-dkT[MBQ + mb][4 * a], -dkT[MBQ + mb][4 * a + 1], -dkT[MBQ + mb][4 * a + 2],
-                           -dkT[MBQ + mb][4 * a + 3]};
+          const float f = LOG2 ? -LN2 : -1.f;   // dphi_k = dS^T phi_q (ln 2 dS^T phi_q with LOG2)
+          const f32x4 v = {f * dkT[MBQ + mb][4 * a], f * dkT[MBQ + mb][4 * a + 1], f * dkT[MBQ + mb][4 * a + 2],
+                           f * dkT[MBQ + mb][4 * a + 3]};
           if (col < p.R) *(f32x4*)(g + col) = v;
         }
     }
@@ -468,7 +472,7 @@ __global__ __launch_bounds__(BTH, D > 64 ? 1 : 2) void attn_bwd_dkv_kernel(BwdPa
 
 // ---------------------------------------------------------------------------------
 // dQ (and dphi_q): one workgroup per 128 queries of one (b, h).
-template <typename QT, typename PT, int D, int RP, bool CAUSAL, int DV = D>
+template <typename QT, typename PT, int D, int RP, bool CAUSAL, int DV = D, bool LOG2 = false>
 __global__ __launch_bounds__(BTH, D > 64 ? 1 : 2) void attn_bwd_dq_kernel(BwdParams p) {
   typedef Tile<D, RP, false> T;
   constexpr int QST = D / 16, PST = RP / 16;
@@ -515,7 +519,7 @@ __global__ __launch_bounds__(BTH, D > 64 ? 1 : 2) void attn_bwd_dq_kernel(BwdPar
     const bool ok = 16 * t + 8 * hf < DV;   // head dims at or past DV: zero operands
     const int c = ok ? 16 * t + 8 * hf : 0;
     const u32x4 z = {0u, 0u, 0u, 0u};
-    qf[t] = ok ? scale_frag<QT>(ld16(Qp + qc * p.sq[2] + c), p.scale) : z;
+    qf[t] = ok ? scale_frag<QT>(ld16(Qp + qc * p.sq[2] + c), LOG2 ? p.scale * LOG2E : p.scale) : z;
     of[t] = ok ? ld16(Op + qc * p.sdo[2] + c) : z;
   }
   if constexpr (RP > 0) {
@@ -595,7 +599,8 @@ __global__ __launch_bounds__(BTH, D > 64 ? 1 : 2) void attn_bwd_dq_kernel(BwdPar
       }
       float dsv[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) dsv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], LOG2E, -L2q)) * (dp[i] - Dq);
+      for (int i = 0; i < 16; ++i)
+        dsv[i] = __builtin_amdgcn_exp2f(LOG2 ? s[i] - L2q : __builtin_fmaf(s[i], LOG2E, -L2q)) * (dp[i] - Dq);
       u32x4 dsb[2], dsp[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -657,8 +662,9 @@ __global__ __launch_bounds__(BTH, D > 64 ? 1 : 2) void attn_bwd_dq_kernel(BwdPar
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           const int col = 32 * mb + 8 * a + 4 * hf;
-          const f32x4 v = {dqT[MBQ + mb][4 * a], dqT[MBQ + mb][4 * a + 1], dqT[MBQ + mb][4 * a + 2],
-                           dqT[MBQ + mb][4 * a + 3]};
+          const float f = LOG2 ? LN2 : 1.f;   // dphi_q = dS phi_k (ln 2 dS phi_k with LOG2)
+          const f32x4 v = {f * dqT[MBQ + mb][4 * a], f * dqT[MBQ + mb][4 * a + 1], f * dqT[MBQ + mb][4 * a + 2],
+                           f * dqT[MBQ + mb][4 * a + 3]};
           if (col < p.R) *(f32x4*)(g + col) = v;
         }
     }

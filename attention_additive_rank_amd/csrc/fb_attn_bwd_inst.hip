@@ -12,19 +12,27 @@ namespace attnb {
 // head dim 16 runs in the head-dim-32 layout with the columns past 16 as zero operands
 constexpr int KD = FB_BWD_D < 32 ? 32 : FB_BWD_D;
 
-template <typename QT, typename PT, int RP, bool CAUSAL>
-static fb_status launch2(const BwdParams& p, hipStream_t s) {
+template <typename QT, typename PT, int RP, bool CAUSAL, bool LOG2>
+static fb_status launch3(const BwdParams& p, hipStream_t s) {
   const int64_t grid = (int64_t)p.nblk * p.H * p.B;
-  hipLaunchKernelGGL((attn_bwd_dkv_kernel<QT, PT, KD, RP, CAUSAL, FB_BWD_D>), dim3((unsigned)grid), dim3(BTH), 0, s,
-                     p);
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<QT, PT, KD, RP, CAUSAL, FB_BWD_D>), dim3((unsigned)grid), dim3(BTH), 0, s,
-                     p);
+  hipLaunchKernelGGL((attn_bwd_dkv_kernel<QT, PT, KD, RP, CAUSAL, FB_BWD_D, LOG2>), dim3((unsigned)grid), dim3(BTH), 0,
+                     s, p);
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<QT, PT, KD, RP, CAUSAL, FB_BWD_D, LOG2>), dim3((unsigned)grid), dim3(BTH), 0,
+                     s, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_error("attention backward launch failed: %s", hipGetErrorString(e));
     return FB_EHIP;
   }
   return FB_OK;
+}
+
+// phi_q in exp2 units (FLAG_LOG2) only with factors
+template <typename QT, typename PT, int RP, bool CAUSAL>
+static fb_status launch2(const BwdParams& p, hipStream_t s) {
+  if constexpr (RP > 0)
+    if (p.flags & FLAG_LOG2) return launch3<QT, PT, RP, CAUSAL, true>(p, s);
+  return launch3<QT, PT, RP, CAUSAL, false>(p, s);
 }
 
 template <typename QT, typename PT, int RP>

@@ -52,6 +52,7 @@ constexpr int FLAG_CAUSAL = 1;
 constexpr int FLAG_PHQ_VEC = 2;   // phi_q rows 16-byte aligned -> vector loads
 constexpr int FLAG_PHK_VEC = 4;   // phi_k rows 16-byte aligned -> vector loads
 constexpr int FLAG_BIAS_VEC = 8;  // bias rows 16-byte aligned -> vector loads
+constexpr int FLAG_LOG2 = 16;     // backward: phi_q in exp2 units
 
 // Launch one fused attention forward; one function per head dim (16/32/64/128) and Q/K/V
 // element type.  mode 0: low-rank factors padded to RP columns (0 = plain attention);
@@ -153,6 +154,6 @@ void set_error(const char* fmt, ...);
 // bwd_work_layout(...).bytes bytes.
 fb_status attn_bwd_lowrank_impl(const fb_attn_args* a, const void* phi_q, const void* phi_k, fb_dtype phi_dt, int R,
                                 const int64_t sphi_q[3], const int64_t sphi_k[3], const fb_attn_bwd_args* g,
-                                hipStream_t stream, const char* fn);
+                                hipStream_t stream, const char* fn, bool log2 = false);
 
 }  // namespace fb

@@ -144,6 +144,8 @@ def main():
                          "no factor step")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (fb_attn_bwd_lowrank) of the workload instead")
+    ap.add_argument("--bwd-log2", action="store_true",
+                    help="with --backward: factors in exp2 units, fb_attn_fwd_lowrank_log2 / fb_attn_bwd_lowrank_log2")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one device copy of this many MiB (HBM counter calibration)")
     ap.add_argument("--profile", action="store_true",
@@ -447,12 +449,15 @@ def bench_backward(args, w, fb, torch, q, k, v, pq_t, pk_t, stage1, out, dev, st
     more (the dQ kernel), which is not counted."""
     import numpy as np
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
-    stage1(False)                   # the factors, as the forward step makes them, in natural units
-    fb.fb_attn_fwd_lowrank(q, k, v, pq_t, pk_t, causal=w.causal, out=out, lse=lse)
+    lg = args.bwd_log2
+    stage1(lg)                      # the factors, as the forward step makes them
+    fwd = fb.fb_attn_fwd_lowrank_log2 if lg else fb.fb_attn_fwd_lowrank
+    fwd(q, k, v, pq_t, pk_t, causal=w.causal, out=out, lse=lse)
     g = np.random.default_rng(w.seed + 7).standard_normal(q.shape) * 0.5
     dout = torch.from_numpy(g).to(q.dtype).to(dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    bstep = lambda: fb.fb_attn_bwd_lowrank(q, k, v, out, lse, dout, pq_t, pk_t, causal=w.causal, dq=dq, dk=dk, dv=dv)
+    bstep = lambda: fb.fb_attn_bwd_lowrank(q, k, v, out, lse, dout, pq_t, pk_t, causal=w.causal, dq=dq, dk=dk, dv=dv,
+                                           log2=lg)
     settle = settle_phase(torch, bstep, args.settle_ms)
     for _ in range(args.warmup):
         bstep()
@@ -476,7 +481,8 @@ def bench_backward(args, w, fb, torch, q, k, v, pq_t, pk_t, stage1, out, dev, st
                       "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
                       "data": "synthetic",
                       "config": {"workload": w.name + "_backward", "B": w.B, "H": w.H, "N": w.N, "D": w.D,
-                                 "R_columns": Rp, "causal": w.causal, "flops_per_step": F},
+                                 "R_columns": Rp, "causal": w.causal, "flops_per_step": F,
+                                 "factor_units": "exp2 (phi_q log2(e))" if lg else "natural"},
                       "settle": settle,
                       "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": peak, "unit": "TFLOP/s",
                                    "frac": round(tf / peak, 4), "traffic": None,

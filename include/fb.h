@@ -432,6 +432,20 @@ fb_status fb_attn_bwd_lowrank(const fb_attn_args* a, const void* phi_q, const vo
                               const int64_t sphi_q[3], const int64_t sphi_k[3], const fb_attn_bwd_args* g,
                               hipStream_t stream);
 
+/*
+ * fb_attn_bwd_lowrank_log2 -- the gradients of fb_attn_fwd_lowrank_log2's output:
+ *   O = softmax(s Q K^T + ln(2) phi_q phi_k^T) V,   phi_q in exp2 units,
+ * with respect to Q, K, V and the factors as given (dphi_q is the gradient with respect to
+ * the exp2-unit phi_q: ln(2) dS phi_k; dphi_k = ln(2) dS^T phi_q).  The fused kernels form the
+ * scores in exp2 units, as the forward does (K s log2(e) in the key-major kernel, Q s log2(e)
+ * in the query-major one, L log2(e)); dS = P (dP - Delta) is in natural units.  a->lse is the
+ * forward's natural-log LSE.  Arguments, workspace (fb_attn_bwd_workspace_bytes), support and
+ * errors as fb_attn_bwd_lowrank; R == 0 is identical to fb_attn_bwd_lowrank.
+ */
+fb_status fb_attn_bwd_lowrank_log2(const fb_attn_args* a, const void* phi_q, const void* phi_k, fb_dtype phi_dt,
+                                   int R, const int64_t sphi_q[3], const int64_t sphi_k[3],
+                                   const fb_attn_bwd_args* g, hipStream_t stream);
+
 /* Size of the device scratch array behind fb_attn_bwd_lowrank_noalloc (64 MiB per GPU). */
 #define FB_BWD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 

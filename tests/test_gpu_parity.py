@@ -797,3 +797,41 @@ def test_multi_item_workgroups(fb, entry, B, H, N, D, R, dt):
     ro, rl = oracle.attention(q, k, v, bias=bias)
     assert_close(to_np(o), ro, dt, f"multi-item {entry}")
     np.testing.assert_allclose(lse.cpu().double().numpy(), rl, rtol=0, atol=2e-2)
+
+
+# ------------------------------------------------ backward in exp2 units ----
+BWD_LOG2 = [
+    # (B, H, N, D, R, factor shape, dtype, causal)
+    (2, 2, 230, 64, 64, "shared", "bf16", False),
+    (1, 3, 190, 32, 16, "head", "bf16", True),
+    (2, 2, 150, 64, 6, "full", "f16", True),
+    (2, 1, 130, 16, 8, "head", "bf16", False),
+]
+
+
+@pytest.mark.parametrize("B,H,N,D,R,fs,dt,causal", BWD_LOG2, ids=[f"bwdlog2-{i}" for i in range(len(BWD_LOG2))])
+def test_backward_log2_units(fb, B, H, N, D, R, fs, dt, causal):
+    """fb_attn_bwd_lowrank_log2 on fb_attn_fwd_lowrank_log2's output: dQ, dK, dV and the
+    gradients with respect to the exp2-unit phi_q and phi_k, against the oracle's chain rule for
+    the bias ln(2) phi_q phi_k^T (d/d phi_q = ln(2) db phi_k, d/d phi_k = db^T ln(2) phi_q)."""
+    import torch
+    r = np.random.default_rng(1600 + N + R + D)
+    q, k, v, do = (synth.round_to(r.standard_normal((B, H, N, D)) * 0.5, dt) for _ in range(4))
+    shape = {"shared": (N, R), "head": (H, N, R), "full": (B, H, N, R)}[fs]
+    pq2 = synth.round_to(r.standard_normal(shape) * 0.6, "f16")   # exp2 units
+    pk = synth.round_to(r.standard_normal(shape) * 0.4, "f16")
+    qd, kd, vd, dod = (to_dev(x, dt) for x in (q, k, v, do))
+    pqd, pkd = to_dev(pq2, "f16"), to_dev(pk, "f16")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda:0")
+    o = fb.fb_attn_fwd_lowrank_log2(qd, kd, vd, pqd, pkd, causal=causal, lse=lse)
+    dq, dk, dv, gpq, gpk = fb.fb_attn_bwd_lowrank(qd, kd, vd, o, lse, dod, pqd, pkd, causal=causal, log2=True)
+    torch.cuda.synchronize()
+    ln2 = np.log(2.0)
+    rq, rk, rv, db = oracle.attention_backward(q, k, v, do, bias=ln2 * oracle.lowrank_bias(pq2, pk), causal=causal)
+    for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        assert_grad_close(to_np(got), ref, f"{name} exp2 units R={R} D={D}")
+    full_q = np.broadcast_to(pq2, (B, H, N, R))
+    full_k = np.broadcast_to(pk, (B, H, N, R))
+    rgq_nat, rgk = oracle.lowrank_factor_grads(db, ln2 * full_q, full_k)
+    assert_grad_close(gpq.cpu().double().numpy(), _sum_to(ln2 * rgq_nat, shape), f"dphi_q (exp2 units) R={R}")
+    assert_grad_close(gpk.cpu().double().numpy(), _sum_to(rgk, shape), f"dphi_k R={R}")
