@@ -35,9 +35,9 @@
 //     them.  Rows past N are not loaded and are masked in the scores.
 //   * V stays row-major in LDS; the A operand of O^T = V^T P^T comes from
 //     64-bit transpose reads (ds_read_b64_tr_b16), four keys per read.
-//   * The softmax row sum (16-bit low-rank operands; not in exp2 units at RP 64)
-//     is one more MFMA per P V k-step with an all-ones A row, so it costs
-//     matrix-core cycles instead of VALU adds and is rescaled together with O.
+//   * The softmax row sum (16-bit low-rank operands) is one more, 16x16x32 MFMA
+//     per P V k-step with a ones / zeros A operand, so it costs matrix-core
+//     cycles instead of VALU adds and is rescaled together with O.
 //   * Scores are computed transposed, S^T = K' Q'^T, with 32x32 MFMAs
 //     (32x32x16 bf16/f16, 32x32x2 fp32).  With that orientation every lane owns
 //     ONE query (lane % 32) and 16 keys per 32-key block, so the row max / row
@@ -115,6 +115,21 @@ template <> struct Mma<f16_t> {
 template <> struct Mma<float> {
   static __device__ __forceinline__ f32x16 run(float a, float b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+};
+// 16x16x32 MFMA (lane l: A row / B column l % 16, k elements 8 (l / 16) .. + 7; D column
+// l % 16, rows 4 (l / 16) .. + 3)
+template <typename T> struct Mma16;
+template <> struct Mma16<bf16_t> {
+  static __device__ __forceinline__ f32x4 run(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+  }
+};
+template <> struct Mma16<f16_t> {
+  static __device__ __forceinline__ f32x4 run(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                  0, 0, 0);
   }
 };
 
@@ -779,20 +794,25 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   float m_run = -INFINITY;
   float l_run = 0.f;      // row sum (vector-unit path)
   float M2 = 0.f;                 // FOLD: running max in exp2 units
-  // Low-rank mode, 16-bit: the row sum of P rides on the matrix core as one more MFMA per
-  // k-step, with an A operand whose row 0 is all ones (lane 0 of each half) and rows 1..31
-  // zero: row 0 of lacc (register 0 of the lanes of half 0) is then sum_k P[k][query], and
-  // the rescaling of O scales it too.  This takes 32 adds per tile off the vector unit.
-  // (Dense-bias mode keeps the adds: its bias registers leave no room for lacc.  In exp2
-  // units at rank 64, where the score chain is longest, the extra MFMAs measured slower
-  // than the adds, so that case keeps them too.)
-  constexpr bool MROW = KW > 1 && MODE != 1 && (!FOLD || RP < 64);
-  // FOLD: every score chain starts from -M2 in all 16 registers.  Without MROW a copy of
-  // that vector is kept (minit); with MROW its registers hold lacc instead and the vector is
-  // written into the accumulator when the chain starts.
+  // Low-rank mode, 16-bit: the row sum of P rides on the matrix core as one 16x16x32 MFMA
+  // per P V k-step (32 keys of P's B-operand registers read as 16 columns x 32 k), lacc +=
+  // A P: lane l of the B operand holds query row l % 32 (keys of lane half l / 32), i.e.
+  // column l % 16 and k group l / 16 there; A is 1 where the k group's parity equals the
+  // parity of the row's quad ((row / 4) % 2), 0 elsewhere, so D rows 4g..4g+3 of column c,
+  // which lane 16 g + c holds, sum the k groups of g's parity: query row 16 (g % 2) + c,
+  // the lane's own row (l % 32).  Every register of lacc thus holds the lane's row sum in
+  // both halves, and the rescaling of O scales it with the lane's own factor.  This takes
+  // 36 adds per tile off the vector unit for 8 registers (lacc, A) and 4 MFMAs per tile, each
+  // half the size of a P V MFMA.  (Dense-bias mode keeps the adds: its bias registers leave
+  // no room.)
+  constexpr bool MROW = KW > 1 && MODE != 1;
+  // FOLD: every score chain starts from -M2 in all 16 registers: at RP 64 a copy of that
+  // vector is kept (minit), otherwise it is written into the accumulator when the chain
+  // starts (registers for the longer chains' operands).
+  constexpr bool MINIT = FOLD && RP >= 64;
   f32x16 minit = f32x16{};
   auto chain_init = [&]() __attribute__((always_inline)) {
-    if constexpr (FOLD && !MROW) {
+    if constexpr (MINIT) {
       return minit;
     } else {
       f32x16 c = f32x16{};
@@ -803,9 +823,9 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
       return c;
     }
   };
-  f32x16 lacc = f32x16{};
+  f32x4 lacc = f32x4{};
   const uint32_t one2 = __is_same(QT, bf16_t) ? 0x3F803F80u : 0x3C003C00u;   // two 1.0 values of QT
-  const u32x4 ones = ln == 0 ? u32x4{one2, one2, one2, one2} : u32x4{0u, 0u, 0u, 0u};
+  const u32x4 ones = (((lane >> 2) ^ (lane >> 4)) & 1) == 0 ? u32x4{one2, one2, one2, one2} : u32x4{0u, 0u, 0u, 0u};
 
   // dense bias of this lane's row, keys kb + 32*kb2 + 16*hf + [0, 16), loaded one tile ahead
   constexpr int BES = MODE == 1 ? (int)sizeof(BT) : 2;
@@ -942,7 +962,7 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
         for (int u = 0; u < 2; ++u) {
 #pragma unroll
           for (int db = 0; db < DB; ++db) oacc[db] = Mma<QT>::run(vread_tr(sVt, kb2, u, db), pfrag[kb2 * 2 + u], oacc[db]);
-          if constexpr (MROW) lacc = Mma<QT>::run(ones, pfrag[kb2 * 2 + u], lacc);
+          if constexpr (MROW) lacc = Mma16<QT>::run(ones, pfrag[kb2 * 2 + u], lacc);
         }
       }
     }
@@ -981,7 +1001,7 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
         if (g < NPV) {
 #pragma unroll
           for (int db = 0; db < DB; ++db) oacc[db] = Mma<QT>::run(opnd[g][db], pfrag[g], oacc[db]);
-          if constexpr (MROW) lacc = Mma<QT>::run(ones, pfrag[g], lacc);
+          if constexpr (MROW) lacc = Mma16<QT>::run(ones, pfrag[g], lacc);
         } else {
           const int t = g - NPV;
 #pragma unroll
@@ -1060,7 +1080,7 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
         M2 += d;
 #pragma unroll
         for (int kb2 = 0; kb2 < NKB; ++kb2) sacc[kb2] -= d;
-        if constexpr (!MROW) {
+        if constexpr (MINIT) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) minit[r] = -M2;
         }
@@ -1140,8 +1160,8 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   // ---- one item's epilogue: O = O / l, LSE = m + ln l ------------------------------
   auto store_item = [&]() __attribute__((always_inline)) {
     // register r of lane half hf in head-dim block db holds head dim 32 db + 8 (r / 4) + 4 hf + r % 4
-    // (register 0 of lacc is row 0 in half 0 and row 4, all zeros, in half 1)
-    const float l_tot = halves_sum(MROW ? lacc[0] : l_run);
+    // (every register of lacc holds the lane's row sum, in both halves)
+    const float l_tot = MROW ? lacc[0] : halves_sum(l_run);
     if (qvalid) {
       const float inv = 1.f / l_tot;
       QT* orow = Op + qrow * p.so[2];
@@ -1192,7 +1212,7 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
       Op = (QT*)p.o + ((int64_t)bb * p.so[0] + (int64_t)hh * p.so[1]);
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
-      lacc = f32x16{};
+      lacc = f32x4{};
       l_run = 0.f;
       m_run = -INFINITY;
       if (cur + 1 < item0 + nitems) prefetch_q(cur + 1);
