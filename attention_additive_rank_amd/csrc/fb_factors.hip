@@ -9,11 +9,15 @@
 //   phi_q = phi_k = phi, so phi phi^T = b by cos(a-b) = cos a cos b + sin a sin b.
 // All values are computed in fp64 and rounded once (round to nearest even) into
 // the output type; the optional split writes each value as a sum of pieces.
+#include <cmath>
+
 #include "fb_internal.h"
 
 namespace fb {
 namespace {
 
+// ALiBi: the caller's slopes (use_host set), or none; Sandwich: the frequencies w_1..w_{C/2}
+// from the host's fp64 pow (use_host set when C / 2 <= kMaxSlopes), else computed here.
 struct Slopes {
   double m[kMaxSlopes];
 };
@@ -26,8 +30,8 @@ __device__ __forceinline__ double round_prec(double x, int prec, int emin) {
   frexp(x, &e);              // x = f * 2^e, 0.5 <= |f| < 1
   int ex = e - 1;            // exponent of the leading bit
   if (ex < emin) ex = emin;  // subnormal range: fixed quantum
-  const double q = ldexp(1.0, ex - prec + 1);
-  return rint(x / q) * q;
+  // quantum q = 2^(ex - prec + 1); scaling by 1 / q (a power of two) is exact
+  return rint(x * ldexp(1.0, prec - 1 - ex)) * ldexp(1.0, ex - prec + 1);
 }
 
 template <typename T> struct Fmt;
@@ -56,8 +60,8 @@ __device__ __forceinline__ double alibi_slope(const Slopes& s, int use_host, int
   return use_host ? s.m[h] : exp2(-8.0 * (double)(h + 1) / (double)H);
 }
 
-__device__ __forceinline__ double sandwich_freq(int k, int C) {  // k = 1..C/2
-  return pow(10000.0, -2.0 * (double)k / (double)C);
+__device__ __forceinline__ double sandwich_freq(const Slopes& s, int use_host, int k, int C) {  // k = 1..C/2
+  return use_host ? s.m[k - 1] : pow(10000.0, -2.0 * (double)k / (double)C);
 }
 
 // pair index -> (a, b) pieces, ordered (0,0), (0,1), (1,0), (0,2), (1,1), (2,0)
@@ -96,7 +100,7 @@ __global__ void make_factors_kernel(fb_bias_kind kind, int H, int N, int C, Slop
         fk[1] = -m;
       } else {
         double sn, cs;
-        sincos((double)n * sandwich_freq(g + 1, C), &sn, &cs);
+        sincos((double)n * sandwich_freq(slopes, use_host, g + 1, C), &sn, &cs);
         fq[0] = fk[0] = cs;
         fq[1] = fk[1] = sn;
       }
@@ -138,16 +142,24 @@ __global__ void make_dense_bias_kernel(fb_bias_kind kind, int H, int N, int C, S
     } else {
       v = 0.0;
       const double d = (double)(i - j);
-      for (int k = 1; k <= C / 2; ++k) v += cos(d * sandwich_freq(k, C));
+      for (int k = 1; k <= C / 2; ++k) v += cos(d * sandwich_freq(slopes, use_host, k, C));
     }
     bias[h * head_stride + (int64_t)i * row_stride + j] = exact_to<T>(rn<T>(v));
   }
 }
 
-Slopes pack_slopes(const double* host, int H) {
+// The kernel argument for `kind`; use_host says whether it holds the values (ALiBi: the
+// caller's slopes, if any; Sandwich: the C / 2 frequencies, if they fit).
+Slopes pack_slopes(fb_bias_kind kind, const double* host, int H, int C, int& use_host) {
   Slopes s{};
-  if (host)
+  use_host = 0;
+  if (kind == FB_ALIBI && host) {
     for (int h = 0; h < H; ++h) s.m[h] = host[h];
+    use_host = 1;
+  } else if (kind == FB_SANDWICH && C / 2 <= kMaxSlopes) {
+    for (int k = 1; k <= C / 2; ++k) s.m[k - 1] = std::pow(10000.0, -2.0 * k / C);
+    use_host = 1;
+  }
   return s;
 }
 
@@ -161,8 +173,8 @@ int grid_for(int64_t total) {
 fb_status launch_make_factors(fb_bias_kind kind, int H, int N, int C, const double* slopes_host,
                               fb_dtype out_dt, int split, void* phq, void* phk, int R_pad, int R_nat,
                               double qscale, hipStream_t stream) {
-  const Slopes s = pack_slopes(slopes_host, H);
-  const int use_host = slopes_host != nullptr;
+  int use_host;
+  const Slopes s = pack_slopes(kind, slopes_host, H, C, use_host);
   const int split_pairs = split * (split + 1) / 2;
   const int grid = grid_for((int64_t)H * N * ((R_pad + 2 * split_pairs - 1) / (2 * split_pairs)));
   switch (out_dt) {
@@ -192,8 +204,8 @@ fb_status launch_make_factors(fb_bias_kind kind, int H, int N, int C, const doub
 fb_status launch_make_dense_bias(fb_bias_kind kind, int H, int N, int C, const double* slopes_host,
                                  fb_dtype out_dt, void* bias, int64_t head_stride, int64_t row_stride,
                                  hipStream_t stream) {
-  const Slopes s = pack_slopes(slopes_host, H);
-  const int use_host = slopes_host != nullptr;
+  int use_host;
+  const Slopes s = pack_slopes(kind, slopes_host, H, C, use_host);
   const int grid = grid_for((int64_t)H * N * N);
   switch (out_dt) {
     case FB_F32:
