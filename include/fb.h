@@ -252,10 +252,9 @@ fb_status fb_attn_fwd_lowrank(const fb_attn_args* a, const void* phi_q, const vo
  * Q2: the factor columns are concatenated with queries and keys); only the unit of
  * phi_q differs.
  * Arguments, alignment and errors as fb_attn_fwd_lowrank, for bf16 / f16 Q/K/V
- * only (FB_EUNSUPPORTED for fp32).  Numerics differ in one rounding, Q s log2(e) is
- * rounded to dt, and for R > 32 (factor columns padded to 64) in one more: the row sum of
- * P is taken in fp32 before P is rounded (for R <= 32 it is taken from the rounded P, as
- * in fb_attn_fwd_lowrank).
+ * only (FB_EUNSUPPORTED for fp32).  Numerics differ in one rounding: Q s log2(e) is
+ * rounded to dt (the row sum of P is taken from the rounded P, as in
+ * fb_attn_fwd_lowrank).
  * R == 0 is plain attention in the same exp2 form.  LSE (when requested) is the
  * natural-log value as for fb_attn_fwd_lowrank; fb_attn_bwd_lowrank takes natural-unit
  * factors (phi_q ln(2) for the factors given here).
