@@ -183,7 +183,9 @@ def _slopes_ptr(slopes):
 def fb_make_factors(kind, H: int, N: int, C: int = 0, slopes=None, dtype=None, split: int = 1,
                     R_pad: Optional[int] = None, phi_q=None, phi_k=None, device="cuda", stream=None):
     """Exact ALiBi / Sandwich factors on the GPU.  Returns ``(phi_q, phi_k, R_used)`` with
-    ``phi_*`` of shape ``[H, N, R_pad]`` (allocated here if not given)."""
+    ``phi_*`` of shape ``[H, N, R_pad]`` (allocated here if not given).  R_pad defaults to
+    R_used rounded up to whole 16-byte rows (zero columns past R_used), the width with
+    which the attention kernels copy phi_k rows straight into on-chip memory."""
     return _make_factors("fb_make_factors", kind, H, N, C, slopes, dtype, split, R_pad, phi_q, phi_k, device, stream)
 
 
@@ -200,7 +202,9 @@ def _make_factors(entry, kind, H, N, C, slopes, dtype, split, R_pad, phi_q, phi_
     dtype = dtype or torch.bfloat16
     used = factor_columns(kind, C, split)
     if phi_q is None or phi_k is None:
-        R_pad = R_pad if R_pad is not None else used
+        if R_pad is None:
+            ce = 16 // torch.empty((), dtype=dtype).element_size()
+            R_pad = (used + ce - 1) // ce * ce
         phi_q = torch.empty((H, N, R_pad), dtype=dtype, device=device)
         phi_k = torch.empty((H, N, R_pad), dtype=dtype, device=device)
     else:
