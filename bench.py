@@ -673,9 +673,14 @@ def profile_harness(args) -> int:
     # the step's attention kernel: the attn_fwd_kernel instance that is not the dense-bias one
     # (template MODE 1 shows as "Li1E" after the head dim and the factor width)
     def mode_of(name):
+        """the MODE template argument, from a (partly) mangled ("...Li<D>ELi<RP>ELi<MODE>E...")
+        or a demangled ("attn_fwd_kernel<QT, PT, D, RP, MODE, ...>") kernel name"""
         try:
-            parts = name.split("attn_fwd_kernel")[1].split("Li")
-            return int(parts[3].split("E")[0])
+            rest = name.split("attn_fwd_kernel")[1]
+            li = rest.split("Li")
+            if len(li) > 3:
+                return int(li[3].split("E")[0])
+            return int(rest[1:].split(",")[4].strip())
         except Exception:
             return -1
     trace_rows = []
