@@ -89,9 +89,11 @@ constexpr float RESCALE_GAP = 8.0f / LOG2E;   // 2^8 in exp2 units, as a natural
 // Kernels whose workgroups take several work items ((b, h, query block) triples) one after
 // another, with one stream of key tiles across them and the next item's query rows loaded
 // while the current item runs: non-causal 16-bit kernels with loader wavefronts (not the
-// dense-bias mode) whose Q' fragments are narrow enough to hold the next item's as well.
+// dense-bias mode) whose Q' fragments are narrow enough to hold the next item's as well
+// (D + RP <= 80; the rest of the item switch spills a few registers there, outside the
+// matrix and softmax phases).
 constexpr bool attn_multi_item(int D, int RP, int MODE, bool loader, bool causal, int es) {
-  return loader && !causal && es == 2 && MODE != 1 && D + RP <= 64;
+  return loader && !causal && es == 2 && MODE != 1 && D + RP <= 80;
 }
 
 template <typename T> struct Elem;

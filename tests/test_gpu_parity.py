@@ -746,7 +746,7 @@ def test_random_sweep_forward_and_backward(fb, B, H, N, D, R, fs, dt, pdt, causa
 
 
 # ------------------------------------------- several work items per workgroup ----
-# Non-causal 16-bit kernels with D + R_pad <= 64 take several (b, h, query block) items per
+# Non-causal 16-bit kernels with D + R_pad <= 80 take several (b, h, query block) items per
 # workgroup when there are more items than compute units: one key-tile stream runs across
 # the items and the next item's query rows load while the current one runs.  These shapes
 # have more items than the 256 compute units of an MI355X, ragged sequence lengths (partial
@@ -763,6 +763,12 @@ MULTI = [
     # one key tile per item (every step switches items), per-batch factors
     ("lowrank_log2", 300, 2, 40, 32, 8, "bf16"),
     ("lowrank_batch", 130, 4, 70, 16, 16, "f16"),
+    # D = 64 with 16 factor columns (D + R_pad = 80)
+    ("lowrank_log2", 36, 8, 300, 64, 16, "bf16"),
+    ("lowrank", 300, 2, 60, 64, 8, "f16"),
+    ("alibi", 33, 8, 260, 64, 0, "bf16"),
+    ("sandwich", 20, 8, 520, 64, 16, "bf16"),
+    ("lowrank_batch", 70, 4, 130, 64, 12, "bf16"),
 ]
 
 
