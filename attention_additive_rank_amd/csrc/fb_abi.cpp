@@ -483,13 +483,16 @@ fb_status attn_bwd_lowrank_impl(const fb_attn_args* a, const void* phi_q, const 
   fb_status st = check_common(a, fn);
   if (st != FB_OK) return st;
   if (!g) FB_FAIL(FB_EINVAL, "%s: null gradient arguments", fn);
-  if (a->dt != FB_BF16 && a->dt != FB_F16) FB_FAIL(FB_EUNSUPPORTED, "%s: q/k/v must be bf16 or f16", fn);
+  const bool f32 = a->dt == FB_F32;
+  if (a->dt != FB_BF16 && a->dt != FB_F16 && !f32) FB_FAIL(FB_EUNSUPPORTED, "%s: q/k/v must be bf16, f16 or fp32", fn);
   if (a->D != 16 && a->D != 32 && a->D != 64 && a->D != 128)
     FB_FAIL(FB_EUNSUPPORTED, "%s: head dim %d not in {16, 32, 64, 128}", fn, a->D);
+  if (f32 && a->D > 64) FB_FAIL(FB_EUNSUPPORTED, "%s: fp32 q/k/v with head dims up to 64", fn);
+  if (f32 && log2) FB_FAIL(FB_EUNSUPPORTED, "%s: exp2-unit factors need bf16 or f16 q/k/v", fn);
   if (R < 0) FB_FAIL(FB_EINVAL, "%s: negative R", fn);
   if (R > 64) FB_FAIL(FB_EUNSUPPORTED, "%s: R = %d (at most 64)", fn, R);
   if (R > 0) {
-    if (!known_dtype(phi_dt) || phi_dt == FB_F32 || (a->dt == FB_F16 && phi_dt != FB_F16))
+    if (!known_dtype(phi_dt) || (f32 ? phi_dt != FB_F32 : phi_dt == FB_F32) || (a->dt == FB_F16 && phi_dt != FB_F16))
       FB_FAIL(FB_EUNSUPPORTED, "%s: factor dtype does not match the q/k/v dtype", fn);
   }
   if ((int64_t)a->B * a->H * a->N == 0) return FB_OK;
@@ -549,11 +552,14 @@ fb_status attn_bwd_lowrank_impl(const fb_attn_args* a, const void* phi_q, const 
     for (int i = 0; i < 3; ++i)
       if (sphi_q[i] < 0 || sphi_k[i] < 0 || g->sdphi_q[i] < 0 || g->sdphi_k[i] < 0)
         FB_FAIL(FB_EINVAL, "%s: negative factor stride", fn);
-    const bool padded = wl.R8 > 0;   // R not a multiple of 8: padded copies in the workspace
-    if (!padded && (!aligned16(phi_q) || !aligned16(phi_k) || !rows_aligned(sphi_q, esize(phi_dt)) ||
-                    !rows_aligned(sphi_k, esize(phi_dt))))
+    // R not a multiple of 8: 16-bit factors are copied (zero-padded) into the workspace, and
+    // the factor gradients go through [B][H][N][R8] partials; the fp32 kernels read the
+    // factors in place, element by element
+    const bool padded = wl.R8 > 0;
+    if (!f32 && !padded && (!aligned16(phi_q) || !aligned16(phi_k) || !rows_aligned(sphi_q, esize(phi_dt)) ||
+                            !rows_aligned(sphi_k, esize(phi_dt))))
       FB_FAIL(FB_EUNSUPPORTED, "%s: factor rows must be 16-byte aligned", fn);
-    if (padded && (((uintptr_t)phi_q | (uintptr_t)phi_k) & 1u))
+    if ((padded || f32) && (((uintptr_t)phi_q | (uintptr_t)phi_k) & (uintptr_t)(esize(phi_dt) - 1)))
       FB_FAIL(FB_EINVAL, "%s: factors not aligned to their element size", fn);
     if (a->N > 1 && (sphi_q[2] < R || sphi_k[2] < R || g->sdphi_q[2] < R || g->sdphi_k[2] < R))
       FB_FAIL(FB_EINVAL, "%s: factor row stride < R", fn);
@@ -580,7 +586,7 @@ fb_status attn_bwd_lowrank_impl(const fb_attn_args* a, const void* phi_q, const 
       p.sdpk[i] = (int)g->sdphi_k[i];
     }
     RW = padded ? wl.R8 : R;
-    if (padded) {
+    if (padded && !f32) {
       // the factors go to [B][H][N][R8] copies with zero columns past R
       void* pq = (char*)g->work + wl.phq_off;
       void* pk = (char*)g->work + wl.phk_off;
@@ -611,10 +617,12 @@ fb_status attn_bwd_lowrank_impl(const fb_attn_args* a, const void* phi_q, const 
     p.flags |= FLAG_PHQ_VEC | FLAG_PHK_VEC;
     RP = RW <= 16 ? 16 : RW <= 32 ? 32 : 64;
   }
-  st = launch_attention_bwd_delta(a->dt, a->o, a->so, g->dout, g->sdo, a->B, a->H, a->N, a->D, delta, stream);
+  st = f32 ? launch_attention_bwd_delta_f32(a->o, a->so, g->dout, g->sdo, a->B, a->H, a->N, a->D, delta, stream)
+          : launch_attention_bwd_delta(a->dt, a->o, a->so, g->dout, g->sdo, a->B, a->H, a->N, a->D, delta, stream);
   if (st != FB_OK) return st;
   const fb_dtype pdt = R > 0 ? phi_dt : a->dt;
-  st = a->D == 16   ? launch_attention_bwd_d16(a->dt, pdt, RP, p, stream)
+  st = f32              ? launch_attention_bwd_f32(p, a->D, stream)
+       : a->D == 16   ? launch_attention_bwd_d16(a->dt, pdt, RP, p, stream)
        : a->D == 32 ? launch_attention_bwd_d32(a->dt, pdt, RP, p, stream)
        : a->D == 64 ? launch_attention_bwd_d64(a->dt, pdt, RP, p, stream)
                     : launch_attention_bwd_d128(a->dt, pdt, RP, p, stream);

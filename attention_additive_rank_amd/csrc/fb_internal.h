@@ -136,6 +136,11 @@ fb_status launch_attention_bwd_pad_factor(const void* phi, int es, const int64_t
 // that an axis of out with stride 0 gathers, in (b, h) order.
 fb_status launch_attention_bwd_unpad(const float* part, int B, int H, int N, int R8, int R, float* out,
                                      const int64_t sout[3], hipStream_t s);
+// fp32 Q/K/V and factors (fb_attn_bwd_f32.hip): Delta, then the dK/dV and dQ kernels (head
+// dims 16 / 32 / 64, any R up to 64, factors read in place with their strides).
+fb_status launch_attention_bwd_delta_f32(const void* o, const int64_t so[3], const void* dout, const int64_t sdo[3],
+                                         int B, int H, int N, int D, float* delta, hipStream_t s);
+fb_status launch_attention_bwd_f32(const BwdParams& p, int D, hipStream_t s);
 // Workspace layout of the backward: Delta, then the partial factor gradients that need a sum.
 struct BwdWork {
   size_t delta_off, pq_off, pk_off, bytes;   // pq_off / pk_off = SIZE_MAX: no partial buffer

@@ -412,12 +412,14 @@ size_t fb_attn_bwd_workspace_bytes(int B, int H, int N, int R, const int64_t sdp
  *                forward's LSE output, required)
  *   phi_*, R ... the forward's factors (R == 0: plain attention)
  *   g            dO, the outputs and the workspace (see fb_attn_bwd_args)
- * Supported: a->dt FB_BF16 or FB_F16, D in {16, 32, 64, 128}, R <= 64.  With R % 8 == 0 the factor
- * rows and the factor-gradient rows must be 16-byte aligned (FB_EUNSUPPORTED / FB_EINVAL);
- * otherwise the library first copies the factors into zero-padded [B][H][N][R8] buffers in
- * the workspace, runs the kernels at width R8 and writes the first R columns of the
- * gradients (summed where a stride is 0) into dphi_*, which then need only 4-byte alignment
- * (the factors: element alignment).  The fused kernels recompute the
+ * Supported: a->dt FB_BF16 or FB_F16, D in {16, 32, 64, 128}, R <= 64; or a->dt FB_F32 with
+ * FB_F32 factors, D in {16, 32, 64}, R <= 64 (fp32 matrix-core kernels that read the factors
+ * in place with their strides, element-aligned; fp32 throughout).  16-bit, R % 8 == 0: the
+ * factor rows and the factor-gradient rows must be 16-byte aligned (FB_EUNSUPPORTED /
+ * FB_EINVAL); otherwise the library first copies the factors into zero-padded [B][H][N][R8]
+ * buffers in the workspace, runs the kernels at width R8 and writes the first R columns of
+ * the gradients (summed where a stride is 0) into dphi_*, which then need only 4-byte
+ * alignment (the factors: element alignment).  The fused kernels recompute the
  * scores tile by tile; Q*s is rounded to dt as in the forward (for the key-major kernel
  * the scale is applied to K, identical when s is a power of two); P and dS are rounded to
  * dt for their MFMA products; accumulation is fp32.  dphi_* of one (b, h) are written by

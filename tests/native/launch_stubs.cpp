@@ -48,6 +48,11 @@ fb_status launch_attention_bwd_pad_factor(const void*, int, const int64_t[3], in
                                           hipStream_t) {
   return FB_EUNSUPPORTED;
 }
+fb_status launch_attention_bwd_delta_f32(const void*, const int64_t[3], const void*, const int64_t[3], int, int, int, int,
+                                         float*, hipStream_t) {
+  return FB_EUNSUPPORTED;
+}
+fb_status launch_attention_bwd_f32(const BwdParams&, int, hipStream_t) { return FB_EUNSUPPORTED; }
 fb_status launch_attention_bwd_unpad(const float*, int, int, int, int, int, float*, const int64_t[3], hipStream_t) {
   return FB_EUNSUPPORTED;
 }

@@ -196,7 +196,11 @@ def _bwd(a, R=0, phi_dt=fb.FB_BF16, pq=FAKE, pk=FAKE, s=(0, 0, 64), **gk):
 
 @pytest.mark.parametrize("kw,bkw,code", [
     (dict(D=8, strides=(1024, 1024, 8), lse=FAKE), {}, fb.FB_EUNSUPPORTED),   # head dim 8: no kernel
-    (dict(dt=fb.FB_F32, lse=FAKE), {}, fb.FB_EUNSUPPORTED),
+    (dict(dt=fb.FB_F32, D=128, strides=(8192, 8192, 128), lse=FAKE), {}, fb.FB_EUNSUPPORTED),   # fp32: D <= 64
+    (dict(dt=fb.FB_F32, D=32, strides=(2048, 2048, 32), lse=FAKE), dict(R=8, phi_dt=fb.FB_BF16),
+     fb.FB_EUNSUPPORTED),                                                         # fp32 q/k/v, bf16 factors
+    (dict(dt=fb.FB_F32, D=32, strides=(2048, 2048, 32), lse=FAKE), dict(R=8, phi_dt=fb.FB_F32, pq=FAKE + 2),
+     fb.FB_EINVAL),                                                               # fp32 factors: element misaligned
     (dict(lse=FAKE), dict(R=12, pq=FAKE + 1), fb.FB_EINVAL),     # padded factors: element misaligned
     (dict(lse=FAKE), dict(R=12, dphi_q=FAKE + 2), fb.FB_EINVAL),  # padded gradients: not 4-byte aligned
     (dict(lse=FAKE), dict(R=72), fb.FB_EUNSUPPORTED),
@@ -218,6 +222,22 @@ def _bwd(a, R=0, phi_dt=fb.FB_BF16, pq=FAKE, pk=FAKE, s=(0, 0, 64), **gk):
 def test_backward_validation(kw, bkw, code):
     assert _bwd(_args(**kw), **bkw) == code
     assert fb.fb_last_error() != ""
+
+
+def test_backward_log2_needs_16bit():
+    """exp2-unit factors are a 16-bit path (as in the forward): fp32 q/k/v is refused."""
+    a = _args(dt=fb.FB_F32, D=32, strides=(2048, 2048, 32), lse=FAKE)
+    g = fb._BwdArgs()
+    st = (a.H * a.N * a.D, a.N * a.D, a.D)
+    g.dout = g.dq = g.dk = g.dv = g.dphi_q = g.dphi_k = FAKE
+    for n in ("sdo", "sdq", "sdk", "sdv"):
+        setattr(g, n, fb._I64x3(*st))
+    g.sdphi_q = g.sdphi_k = fb._I64x3(0, 0, 8)
+    g.work, g.work_bytes = FAKE, 1 << 40
+    sp = fb._I64x3(0, 0, 8)
+    assert fb.load().fb_attn_bwd_lowrank_log2(ctypes.byref(a), FAKE, FAKE, fb.FB_F32, 8, ctypes.byref(sp),
+                                              ctypes.byref(sp), ctypes.byref(g), None) == fb.FB_EUNSUPPORTED
+    assert "bf16 or f16" in fb.fb_last_error()
 
 
 def _bwd_noalloc(a, R=0, **gk):

@@ -560,6 +560,90 @@ def test_backward_parity(fb, B, H, N, D, R, fs, dt, pdt, causal):
         assert_grad_close(gpk.cpu().double().numpy(), _sum_to(rgk, shape), f"dphi_k R={R}")
 
 
+# fp32 Q/K/V and factors: the fp32 matrix-core kernels (any R up to 64, factors read in place).
+# Their arithmetic is fp32 throughout (products, accumulation, exp2 of the recomputed scores
+# against the fp32 LSE), so the bar is that of fp32 rounding over contractions of a few
+# hundred terms: relative L2 <= 2e-5 and max-abs <= 2e-4 of the largest reference entry.
+BWD_F32 = [
+    # (B, H, N, D, R, factor shape, causal); the tiny ALiBi configuration first (B1 H2 N128 D32
+    # with the exact ALiBi factors, rank 2 padded to 4 columns)
+    (1, 2, 128, 32, "alibi", "head", False),
+    (2, 3, 150, 64, 5, "full", True),
+    (1, 2, 200, 16, 0, None, False),
+    (2, 2, 100, 32, 16, "shared", True),
+    (1, 1, 70, 64, 32, "head", False),
+    (3, 2, 90, 16, 7, "head", True),
+]
+F32_GRAD_TOL = (2e-5, 2e-4)
+
+
+def _assert_f32_grad(got, ref, what):
+    assert np.all(np.isfinite(got)), f"{what}: non-finite gradient"
+    ma, rl = errors(got, ref)
+    scale = max(float(np.abs(ref).max()), 1e-30)
+    say(f"  {what}: rel-L2 {rl:.3e}, max-abs/max|ref| {ma / scale:.3e}")
+    assert rl <= F32_GRAD_TOL[0] and ma / scale <= F32_GRAD_TOL[1], f"{what}: rel-L2 {rl:.3e}, max-abs {ma:.3e}"
+
+
+@pytest.mark.parametrize("B,H,N,D,R,fs,causal", BWD_F32, ids=[f"bwdf32-{i}" for i in range(len(BWD_F32))])
+def test_backward_fp32(fb, B, H, N, D, R, fs, causal):
+    """fp32 backward on the fp32 forward's own output and LSE: dQ, dK, dV and the factor
+    gradients against the oracle's chain rule (fp64)."""
+    import torch
+    r = np.random.default_rng(900 + N + D)
+    q, k, v, do = (r.standard_normal((B, H, N, D)).astype(np.float32).astype(np.float64) * 0.5 for _ in range(4))
+    if R == "alibi":
+        pqd, pkd, _ = fb.fb_make_factors("alibi", H, N, dtype=torch.float32)
+        pq, pk = to_np(pqd), to_np(pkd)
+        R, shape = pq.shape[-1], pq.shape
+    else:
+        shape = {"shared": (N, R), "head": (H, N, R), "full": (B, H, N, R)}.get(fs)
+        pq = r.standard_normal(shape).astype(np.float32).astype(np.float64) * 0.4 if R else None
+        pk = r.standard_normal(shape).astype(np.float32).astype(np.float64) * 0.4 if R else None
+        pqd = to_dev(pq, "f32") if R else None
+        pkd = to_dev(pk, "f32") if R else None
+    say(f"fp32 backward B={B} H={H} N={N} D={D} R={R} {fs} causal={causal}")
+    qd, kd, vd, dod = (to_dev(x, "f32") for x in (q, k, v, do))
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda:0")
+    o = fb.fb_attn_fwd_lowrank(qd, kd, vd, pqd, pkd, causal=causal, lse=lse)
+    dq, dk, dv, gpq, gpk = fb.fb_attn_bwd_lowrank(qd, kd, vd, o, lse, dod, pqd, pkd, causal=causal)
+    torch.cuda.synchronize()
+    bias = oracle.lowrank_bias(pq, pk) if R else None
+    rq, rk, rv, db = oracle.attention_backward(q, k, v, do, bias=bias, causal=causal)
+    for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        _assert_f32_grad(to_np(got), ref, f"{name} fp32 R={R} D={D}")
+    if R:
+        full_q = np.broadcast_to(pq, (B, H, N, R)) if pq.ndim < 4 else pq
+        full_k = np.broadcast_to(pk, (B, H, N, R)) if pk.ndim < 4 else pk
+        rgq, rgk = oracle.lowrank_factor_grads(db, full_q, full_k)
+        _assert_f32_grad(gpq.cpu().double().numpy(), _sum_to(rgq, shape), f"dphi_q fp32 R={R}")
+        _assert_f32_grad(gpk.cpu().double().numpy(), _sum_to(rgk, shape), f"dphi_k fp32 R={R}")
+
+
+def test_backward_fp32_rank64(fb):
+    """Rank 64 with fp32 factors (the fp32 forward stops at rank 32): the backward given the
+    oracle's forward output and LSE, rounded to fp32, against the oracle's gradients."""
+    import torch
+    B, H, N, D, R = 1, 2, 150, 64, 64
+    r = np.random.default_rng(990)
+    q, k, v, do = (r.standard_normal((B, H, N, D)).astype(np.float32).astype(np.float64) * 0.5 for _ in range(4))
+    pq, pk = (r.standard_normal((N, R)).astype(np.float32).astype(np.float64) * 0.3 for _ in range(2))
+    bias = oracle.lowrank_bias(pq, pk)
+    ro, rl = oracle.attention(q, k, v, bias=bias, causal=True)
+    o32 = ro.astype(np.float32).astype(np.float64)
+    qd, kd, vd, dod, od = (to_dev(x, "f32") for x in (q, k, v, do, o32))
+    lse = torch.from_numpy(rl.astype(np.float32)).to("cuda:0")
+    dq, dk, dv, gpq, gpk = fb.fb_attn_bwd_lowrank(qd, kd, vd, od, lse, dod, to_dev(pq, "f32"), to_dev(pk, "f32"),
+                                                  causal=True)
+    torch.cuda.synchronize()
+    rq, rk, rv, db = oracle.attention_backward(q, k, v, do, bias=bias, causal=True)
+    for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        _assert_f32_grad(to_np(got), ref, f"{name} fp32 R=64")
+    rgq, rgk = oracle.lowrank_factor_grads(db, np.broadcast_to(pq, (B, H, N, R)), np.broadcast_to(pk, (B, H, N, R)))
+    _assert_f32_grad(gpq.cpu().double().numpy(), _sum_to(rgq, (N, R)), "dphi_q fp32 R=64")
+    _assert_f32_grad(gpk.cpu().double().numpy(), _sum_to(rgk, (N, R)), "dphi_k fp32 R=64")
+
+
 def test_backward_full_size_sampled(fb):
     """The Sandwich workload at full size (B4 H8 N4096 D64, R = 64 f16 factors shared by all
     (b, h)) in the benchmark's launch, the backward alone: every gradient element of two
