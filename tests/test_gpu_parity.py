@@ -829,6 +829,52 @@ def test_random_sweep_forward_and_backward(fb, B, H, N, D, R, fs, dt, pdt, causa
         assert_grad_close(gpk.cpu().double().numpy(), _sum_to(rgk, shape), "dphi_k")
 
 
+def _sweep_configs_f32(n=8, seed=20260300):
+    """The same for fp32 Q/K/V and factors (head dims 16-64; the fp32 forward takes ranks up
+    to 32)."""
+    r = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        D = int(r.choice([16, 32, 64]))
+        R = int(r.choice([0, 3, 8, 16, 32]))
+        N = int(r.integers(1, 330))
+        B, H = int(r.integers(1, 4)), int(r.integers(1, 4))
+        fs = str(r.choice(["shared", "head", "full"]))
+        out.append((B, H, N, D, R, fs, bool(r.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("B,H,N,D,R,fs,causal", _sweep_configs_f32(), ids=[f"sweepf32-{i}" for i in range(8)])
+def test_random_sweep_fp32(fb, B, H, N, D, R, fs, causal):
+    """fp32 forward output and LSE, then all gradients, against the oracle (fp32 bars)."""
+    import torch
+    r = np.random.default_rng(950 + B * 1000 + H * 100 + N + R)
+    q, k, v, do = (r.standard_normal((B, H, N, D)).astype(np.float32).astype(np.float64) * 0.5 for _ in range(4))
+    shape = {"shared": (N, R), "head": (H, N, R), "full": (B, H, N, R)}[fs]
+    pq = r.standard_normal(shape).astype(np.float32).astype(np.float64) * 0.4 if R else None
+    pk = r.standard_normal(shape).astype(np.float32).astype(np.float64) * 0.4 if R else None
+    qd, kd, vd, dod = (to_dev(x, "f32") for x in (q, k, v, do))
+    pqd = to_dev(pq, "f32") if R else None
+    pkd = to_dev(pk, "f32") if R else None
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda:0")
+    o = fb.fb_attn_fwd_lowrank(qd, kd, vd, pqd, pkd, causal=causal, lse=lse)
+    dq, dk, dv, gpq, gpk = fb.fb_attn_bwd_lowrank(qd, kd, vd, o, lse, dod, pqd, pkd, causal=causal)
+    torch.cuda.synchronize()
+    bias = oracle.lowrank_bias(pq, pk) if R else None
+    ro, rl = oracle.attention(q, k, v, bias=bias, causal=causal)
+    assert_close(to_np(o), ro, "f32", f"O fp32 {B}x{H}x{N} D={D} R={R} {fs} causal={causal}")
+    np.testing.assert_allclose(lse.cpu().double().numpy(), rl, rtol=0, atol=1e-4)
+    rq, rk, rv, db = oracle.attention_backward(q, k, v, do, bias=bias, causal=causal)
+    for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        _assert_f32_grad(to_np(got), ref, name)
+    if R:
+        full_q = np.broadcast_to(pq, (B, H, N, R)) if pq.ndim < 4 else pq
+        full_k = np.broadcast_to(pk, (B, H, N, R)) if pk.ndim < 4 else pk
+        rgq, rgk = oracle.lowrank_factor_grads(db, full_q, full_k)
+        _assert_f32_grad(gpq.cpu().double().numpy(), _sum_to(rgq, shape), "dphi_q")
+        _assert_f32_grad(gpk.cpu().double().numpy(), _sum_to(rgk, shape), "dphi_k")
+
+
 # ------------------------------------------- several work items per workgroup ----
 # Non-causal 16-bit kernels with D + R_pad <= 80 take several (b, h, query block) items per
 # workgroup when there are more items than compute units: one key-tile stream runs across
