@@ -2,7 +2,9 @@
 // Q/K/V element type.  Compiled once per (head dim, type) pair with
 // -DFB_ATTN_D=<16|32|64|128> -DFB_ATTN_QT=<0 bf16 | 1 f16 | 2 fp32> so that the
 // instances build in parallel.
-#include "fb_attn_kernel.h"
+#include "fb_attn_resident.h"
+
+#include <cstdlib>
 
 #if !defined(FB_ATTN_D) || !defined(FB_ATTN_QT)
 #error "compile with -DFB_ATTN_D=<head dim> -DFB_ATTN_QT=<0|1|2>"
@@ -11,11 +13,32 @@
 namespace fb {
 namespace attn {
 
+// FB_ATTN_STREAMING=1 in the environment turns the resident-K'/V kernel off (the streaming
+// kernel then takes every launch), for comparisons; read at every launch
+static bool resident_allowed() {
+  const char* e = std::getenv("FB_ATTN_STREAMING");
+  return !(e && e[0] == '1');
+}
+
 template <typename QT, typename PT, int D, int RP, int MODE, typename BT, bool PHI_DMA>
 static fb_status launch_kernel(const AttnParams& p, hipStream_t stream) {
   // loader wavefronts where their register budget (three wavefronts on one SIMD) holds
   constexpr bool LOADER = PHI_DMA && sizeof(QT) == 2 && D <= 64 && RP <= 64 && (MODE != 1 || sizeof(BT) == 2);
   const bool causal = (p.flags & FLAG_CAUSAL) != 0;
+  // short non-causal sequences in exp2 units: the whole K' and V of a (b, h) in LDS, one
+  // workgroup per (b, h), no barrier in the key loop (fb_attn_resident.h)
+  if constexpr (MODE == 3 && sizeof(QT) == 2 && PHI_DMA && D <= 64 && RP <= 32) {
+    if (!causal && p.N <= res_max_keys(D, RP) && resident_allowed()) {
+      const int64_t grid = (int64_t)p.B * p.H;
+      hipLaunchKernelGGL((attn_fwd_res_kernel<QT, PT, D, RP>), dim3((unsigned)grid), dim3(RNT), 0, stream, p);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) {
+        set_error("attention launch failed: %s", hipGetErrorString(e));
+        return FB_EHIP;
+      }
+      return FB_OK;
+    }
+  }
   // work items (b, h, query block); with more items than compute units, kernels that can
   // take several items per workgroup get one workgroup per compute unit (ceil(items / CUs)
   // items each: the same number of item-times as one item per workgroup, without a

@@ -90,5 +90,13 @@ FB_HD constexpr int loader_src_byte(const TileSlot& d, int KCH, int npch) {
   return slot_has_data(d, KCH, npch) ? d.c * 16 : 0;
 }
 
+// The resident-K'/V kernel (fb_attn_resident.h) holds every tile of one (b, h) in LDS: at most
+// 80 KB per workgroup (two workgroups per compute unit).  Bytes of one 64-key tile (K rows, RP
+// factor columns, V rows at least 32 wide), and the tiles / keys that fit.
+constexpr int kResLdsBytes = 80 * 1024;
+FB_HD constexpr int res_tile_bytes(int D, int RP) { return 64 * 2 * (D + RP + (D < 32 ? 32 : D)); }
+FB_HD constexpr int res_max_tiles(int D, int RP) { return kResLdsBytes / res_tile_bytes(D, RP); }
+FB_HD constexpr int res_max_keys(int D, int RP) { return 64 * res_max_tiles(D, RP); }
+
 }  // namespace attn
 }  // namespace fb

@@ -668,13 +668,15 @@ def profile_harness(args) -> int:
                        w.bias == "mulbias_cos", w)
 
     def is_attn(name):
-        return "attn_fwd_kernel" in name
+        return "attn_fwd_kernel" in name or "attn_fwd_res_kernel" in name
 
     # the step's attention kernel: the attn_fwd_kernel instance that is not the dense-bias one
     # (template MODE 1 shows as "Li1E" after the head dim and the factor width)
     def mode_of(name):
         """the MODE template argument, from a (partly) mangled ("...Li<D>ELi<RP>ELi<MODE>E...")
         or a demangled ("attn_fwd_kernel<QT, PT, D, RP, MODE, ...>") kernel name"""
+        if "attn_fwd_res_kernel" in name:
+            return 3          # the resident kernel: low rank in exp2 units only
         try:
             rest = name.split("attn_fwd_kernel")[1]
             li = rest.split("Li")

@@ -54,8 +54,40 @@ static int check(int D, int RP, int R, bool loader) {
   return 0;
 }
 
+// The resident kernel copies every tile of one (b, h): load g of the workgroup is load
+// g mod NDMA of tile g / NDMA, written at tile * (tile bytes) + 1024 (load within the region)
+// + 16 lane.  With the most tiles that fit (the host admits N <= res_max_keys), every write
+// must land inside the K' and V arrays and both must fit the workgroup's LDS.
+static int check_resident(int D, int RP) {
+  const int CE = 8;
+  const int KCH = D / CE, PCH = RP / CE, VCH = (D < 32 ? 32 : D) / CE;
+  const int NDMA = KCH + PCH + VCH;
+  const int SKB = 1024 * (KCH + PCH), SVB = 1024 * VCH;
+  const int T = res_max_tiles(D, RP);
+  if (T < 1 || T * (SKB + SVB) > kResLdsBytes || SKB + SVB != res_tile_bytes(D, RP)) {
+    std::printf("resident D=%d RP=%d: %d tiles of %d bytes do not fit %d\n", D, RP, T, SKB + SVB, kResLdsBytes);
+    return 1;
+  }
+  for (int g = 0; g < T * NDMA; ++g) {
+    const int t = g / NDMA, n = g % NDMA;
+    for (int lane = 0; lane < 64; ++lane) {
+      const bool isv = n >= KCH + PCH;
+      const int off = isv ? t * SVB + (n - KCH - PCH) * 1024 + 16 * lane : t * SKB + n * 1024 + 16 * lane;
+      if (off < 0 || off + 16 > (isv ? T * SVB : T * SKB)) {
+        std::printf("resident D=%d RP=%d: load %d lane %d writes bytes [%d, %d)\n", D, RP, g, lane, off, off + 16);
+        return 1;
+      }
+    }
+  }
+  std::printf("ok resident D=%d RP=%d: %d tiles (%d keys), %d bytes of LDS\n", D, RP, T, res_max_keys(D, RP),
+              T * (SKB + SVB));
+  return 0;
+}
+
 int main() {
   int bad = 0;
+  for (int D : {16, 32, 64})
+    for (int RP : {0, 16, 32}) bad |= check_resident(D, RP);
   const int Ds[] = {16, 32, 64, 128};
   const int RPs[] = {0, 16, 32, 64, 128};
   for (int D : Ds)

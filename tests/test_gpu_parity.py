@@ -935,6 +935,59 @@ def test_multi_item_workgroups(fb, entry, B, H, N, D, R, dt):
     np.testing.assert_allclose(lse.cpu().double().numpy(), rl, rtol=0, atol=2e-2)
 
 
+# ------------------------------------------- whole K' and V resident in LDS ----
+# Non-causal 16-bit launches in exp2 units whose K' and V tiles all fit in 80 KB of LDS run the
+# resident kernel (one workgroup per (b, h), no barrier in the key loop); FB_ATTN_STREAMING=1
+# sends the same launch to the streaming kernel.  Shapes: the largest N of each (D, R_pad)
+# (512 keys at D 32 / R_pad 16, 640 at D 16 / 16, 256 at D 64 / 16, 384 at D 32 / 32, 320 at
+# D 64 / 0), one key, ragged tails, R not a multiple of 16 (zero padding inside the kernel),
+# per-batch factors, bf16 factors, f16 operands, and more (b, h) than compute units.
+RESIDENT = [
+    # (B, H, N, D, R, factor shape, Q/K/V dtype, factor dtype)
+    (3, 4, 512, 32, 16, "head", "bf16", "f16"),
+    (2, 3, 301, 32, 16, "head", "bf16", "f16"),
+    (1, 2, 1, 32, 16, "head", "bf16", "f16"),
+    (2, 2, 64, 16, 8, "batch", "f16", "f16"),
+    (2, 2, 640, 16, 16, "head", "bf16", "f16"),
+    (1, 3, 256, 64, 16, "head", "bf16", "f16"),
+    (2, 2, 320, 64, 0, None, "bf16", "f16"),
+    (2, 2, 384, 32, 24, "batch", "bf16", "f16"),
+    (4, 2, 97, 16, 32, "head", "f16", "f16"),
+    (2, 2, 130, 32, 16, "head", "bf16", "bf16"),
+    (160, 4, 200, 32, 16, "head", "bf16", "f16"),
+]
+
+
+@pytest.mark.parametrize("B,H,N,D,R,fsh,dt,pdt", RESIDENT, ids=[f"res-{i}" for i in range(len(RESIDENT))])
+def test_resident_kernel(fb, B, H, N, D, R, fsh, dt, pdt, monkeypatch):
+    """Every output row and LSE of fb_attn_fwd_lowrank_log2 against the oracle (factors in exp2
+    units, i.e. the oracle's bias is ln 2 phi_q phi_k^T), once through the resident kernel and
+    once through the streaming kernel."""
+    import torch
+    say(f"resident B={B} H={H} N={N} D={D} R={R} {fsh} {dt}/{pdt}")
+    r = np.random.default_rng(2700 + N + D + R)
+    q, k, v = (synth.round_to(r.standard_normal((B, H, N, D)) * 0.5, dt) for _ in range(3))
+    qd, kd, vd = (to_dev(x, dt) for x in (q, k, v))
+    pq = pk = None
+    bias = None
+    if R:
+        fshape = (B, H, N, R) if fsh == "batch" else (H, N, R)
+        pq, pk = (synth.round_to(r.standard_normal(fshape) * 0.5, pdt) for _ in range(2))
+        bias = oracle.lowrank_bias(pq, pk) * np.log(2.0)
+    ro, rl = oracle.attention(q, k, v, bias=bias)
+    for streaming in (False, True):
+        if streaming:
+            monkeypatch.setenv("FB_ATTN_STREAMING", "1")
+        lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda:0")
+        o = fb.fb_attn_fwd_lowrank_log2(qd, kd, vd, to_dev(pq, pdt) if R else None,
+                                        to_dev(pk, pdt) if R else None, lse=lse)
+        torch.cuda.synchronize()
+        what = "streaming" if streaming else "resident"
+        assert_close(to_np(o), ro, dt, f"{what} O")
+        np.testing.assert_allclose(lse.cpu().double().numpy(), rl, rtol=0, atol=2e-2, err_msg=f"{what} LSE")
+    monkeypatch.delenv("FB_ATTN_STREAMING")
+
+
 # ------------------------------------------------ backward in exp2 units ----
 BWD_LOG2 = [
     # (B, H, N, D, R, factor shape, dtype, causal)

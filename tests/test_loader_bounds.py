@@ -2,7 +2,8 @@
 kernel): compiled with the host compiler and run for every 16-bit shape the library
 instantiates.  Every direct load must read inside its source row (K and V rows of D
 elements, phi_k rows of R elements; a V row is narrower than its LDS region when D < 32)
-and every chunk slot of a tile must be written exactly once."""
+and every chunk slot of a tile must be written exactly once; the resident kernel's copies of
+every tile of a (b, h) must land inside its LDS arrays."""
 import os
 import shutil
 import subprocess
@@ -25,3 +26,4 @@ def test_tile_copies_stay_in_their_rows(tmp_path):
     print(r.stdout)
     assert r.returncode == 0, r.stdout
     assert "ok D=16 RP=16 R=8 loader" in r.stdout
+    assert "ok resident D=32 RP=16: 8 tiles (512 keys)" in r.stdout
