@@ -26,8 +26,9 @@ static fb_status launch_kernel(const AttnParams& p, hipStream_t stream) {
   constexpr bool LOADER = PHI_DMA && sizeof(QT) == 2 && D <= 64 && RP <= 64 && (MODE != 1 || sizeof(BT) == 2);
   const bool causal = (p.flags & FLAG_CAUSAL) != 0;
   // short non-causal sequences in exp2 units: the whole K' and V of a (b, h) in LDS, one
-  // workgroup per (b, h), no barrier in the key loop (fb_attn_resident.h)
-  if constexpr (MODE == 3 && sizeof(QT) == 2 && PHI_DMA && D <= 64 && RP <= 32) {
+  // workgroup per (b, h), no barrier in the key loop (fb_attn_resident.h); narrow Q' only
+  // (D + RP <= 48: two query blocks per wavefront and one step's operands fit 256 registers)
+  if constexpr (MODE == 3 && sizeof(QT) == 2 && PHI_DMA && D + RP <= 48) {
     if (!causal && p.N <= res_max_keys(D, RP) && resident_allowed()) {
       const int64_t grid = (int64_t)p.B * p.H;
       hipLaunchKernelGGL((attn_fwd_res_kernel<QT, PT, D, RP>), dim3((unsigned)grid), dim3(RNT), 0, stream, p);

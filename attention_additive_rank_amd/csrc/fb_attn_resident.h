@@ -25,11 +25,12 @@
 //   * Per tile and block: S^T = K' Q'^T on 32x32x16 MFMAs (a factor chain in the factor dtype
 //     into the same fp32 accumulator, every chain started from -M, M the running max in exp2
 //     units), the online softmax with lazy rescaling (M moves only when a tile's max exceeds
-//     it by 2^8), P^T rounded to the input dtype as the B operand of O^T = V^T P^T, and the
+//     it by 2^15), P^T rounded to the input dtype as the B operand of O^T = V^T P^T, and the
 //     row sum of P as one 16x16x32 MFMA per P V k-step.  The softmax's max and rescale (a
 //     uniform branch) run before the interleaved part; the exponentials, conversions and
 //     MFMAs after it form one scheduling region.
-// Only non-causal launches whose key tiles fit (res_max_keys) take this kernel.
+// Only non-causal launches with D + RP <= 48 whose key tiles fit (res_max_keys) take this
+// kernel: wider Q' would not fit two blocks and a step's operands in 256 registers.
 #pragma once
 
 #include <type_traits>
@@ -39,6 +40,13 @@
 namespace fb {
 namespace attn {
 
+// Lazy rescaling headroom in exp2 units: M moves only when a tile's max exceeds it by more than
+// 15, so P <= 2^15 (an f16 P must stay below its 65504 limit).  P is rounded to bf16 / f16
+// with the same relative precision at any magnitude and O, l accumulate in fp32, so the wide
+// headroom costs no accuracy; it makes the rescale (about 50 vector operations for the
+// wavefront) rare also for wide bias ranges, where a 2^8 headroom rescaled in about one key
+// step in seven.
+constexpr float RES_GROW = 15.f;
 constexpr int RNW = 4;                  // wavefronts per workgroup
 constexpr int RNT = RNW * 64;           // threads per workgroup
 // LDS per workgroup and tiles that fit: kResLdsBytes, res_max_tiles (fb_tile_map.h)
@@ -94,23 +102,46 @@ __global__ __launch_bounds__(RNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // written: a row past N copies row N - 1 (its scores are masked, its P is 0), a chunk
   // without data an in-row stand-in (loader_src_byte: it meets zero phi_q columns or feeds
   // head dims >= D only), so everything the MFMAs read is finite.
+  // With four or more tiles the copies go in two halves: tiles [0, th) before the first
+  // barrier, tiles [th, nkt) right after it, waited for at a second barrier in the first
+  // block pair's key loop before any read of tile th (the workgroups of a launch start
+  // together, so their copies would otherwise all wait on HBM at once).
+  const bool split = nkt >= 4;
+  const int th = split ? (nkt + 1) / 2 : nkt;
+  // This wavefront issues loads n = wave + RNW i (< NDMA) of every tile; their per-lane source
+  // rows and bytes are fixed, only the tile's first row moves (and the clamp to row N - 1 in
+  // the last tile).
+  constexpr int LPW = (NDMA + RNW - 1) / RNW;
+  int lrow[LPW], lbyte[LPW];
   {
     const int npch = RP > 0 ? p.R / CE : 0;
-    for (int g = wave; g < nkt * NDMA; g += RNW) {
-      const int t = g / NDMA;
-      const int n = g - t * NDMA;
-      const TileSlot d = tile_slot(n, lane, KCH, PCH, VCH);
-      const int row = min(t * BN + d.row, N - 1);
-      const int cb = loader_src_byte(d, KCH, npch);
-      if (n < KCH) {
-        dma16((const char*)(Kp + row * p.sk[2]) + cb, sK + t * SKB + n * 1024);
-      } else if (RP > 0 && n < KCH + PCH) {
-        dma16((const char*)(PKp + row * p.spk[2]) + cb, sK + t * SKB + n * 1024);
-      } else {
-        dma16((const char*)(Vp + row * p.sv[2]) + cb, sV + t * SVB + (n - KCH - PCH) * 1024);
-      }
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const TileSlot d = tile_slot(min(wave + RNW * i, NDMA - 1), lane, KCH, PCH, VCH);
+      lrow[i] = d.row;
+      lbyte[i] = loader_src_byte(d, KCH, npch);
     }
   }
+  auto copy_tiles = [&](int t0, int t1) __attribute__((always_inline)) {
+    for (int t = t0; t < t1; ++t) {
+      const int kb = t * BN;
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int n = wave + RNW * i;
+        if (n < NDMA) {
+          const int region = n < KCH ? 0 : n < KCH + PCH ? 1 : 2;
+          const int stride = region == 0 ? p.sk[2] : region == 1 ? p.spk[2] : p.sv[2];
+          const char* base = region == 0 ? (const char*)(Kp + (int64_t)kb * p.sk[2])
+                           : region == 1 ? (const char*)(PKp + (int64_t)kb * p.spk[2])
+                                         : (const char*)(Vp + (int64_t)kb * p.sv[2]);
+          unsigned char* dst = region == 2 ? sV + t * SVB + (n - KCH - PCH) * 1024 : sK + t * SKB + n * 1024;
+          const int row = kb + BN > N ? min(lrow[i], N - 1 - kb) : lrow[i];
+          dma16(base + (row * stride * 2 + lbyte[i]), dst);
+        }
+      }
+    }
+  };
+  copy_tiles(0, th);
 
   // ---- per-block state ------------------------------------------------------------
   struct Blk {
@@ -119,6 +150,7 @@ __global__ __launch_bounds__(RNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     f32x16 o[DB];
     f32x4 l;                // row sum of P (matrix core), the lane's own row in every register
     float m;                // running max in exp2 units
+    f32x16 mi;              // -m in every register: the score chains' starting accumulator
     u32x4 qf[QSTEPS];       // Q' fragments (B operand of S^T = K' Q'^T)
     u32x4 pf[PSTEPS > 0 ? PSTEPS : 1];
   };
@@ -147,6 +179,13 @@ __global__ __launch_bounds__(RNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   load_frags(B, row_of(a0 + RNW));
   __builtin_amdgcn_s_waitcnt(0);   // this wavefront's tile copies have landed
   __syncthreads();                 // ... and everyone else's
+  copy_tiles(th, nkt);             // the second half, waited for at the split barrier
+  bool split_pending = split;
+  auto split_barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    split_pending = false;
+  };
 
   // ---- LDS operand addresses (tile-relative; the streaming kernel's maps) ------------
   // Score operand of k-step t, key block kb2: key row 32 kb2 + inv_perm_row(ln), logical
@@ -187,17 +226,16 @@ __global__ __launch_bounds__(RNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // output row's quad, so every register of l holds the lane's own row (l % 32) sum.
   const uint32_t one2 = __is_same(QT, bf16_t) ? 0x3F803F80u : 0x3C003C00u;   // two 1.0 values of QT
   const u32x4 ones = (((lane >> 2) ^ (lane >> 4)) & 1) == 0 ? u32x4{one2, one2, one2, one2} : u32x4{0u, 0u, 0u, 0u};
-  auto chain_init = [&](float m) __attribute__((always_inline)) {
-    f32x16 c;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) c[r] = -m;
-    return c;
-  };
   auto reset = [&](Blk& b) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) b.o[db] = f32x16{};
     b.l = f32x4{};
     b.m = 0.f;
+  };
+  auto set_m = [&](Blk& b, float m) __attribute__((always_inline)) {
+    b.m = m;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) b.mi[r] = -m;
   };
 
   // S^T = K'(0) Q'^T of a block's first tile (chains start from 0: M is not set yet)
@@ -214,12 +252,15 @@ __global__ __launch_bounds__(RNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int kb2 = 0; kb2 < NKB; ++kb2) b.s[kb2] = Mma<PT>::run(kread(sK, true, t, kb2), b.pf[t], b.s[kb2]);
   };
   // The matrix work of block x in one key step: O += V(t)^T P(t)^T (with the row sum), then
-  // (with_qk) S(t+1) = K'(t+1) Q'^T; LDS operands read one group ahead (group = the MFMAs of
-  // one k-step).
+  // (with_qk) S(t+1) = K'(t+1) Q'^T, every score chain starting from the block's -M vector;
+  // LDS operands read one group ahead (group = the MFMAs of one k-step: DB P V MFMAs and a
+  // row-sum MFMA, or NKB score MFMAs).  (The two blocks read the same operands; reading them
+  // once for both needs 40 more registers, which the -M vectors use to better effect: the
+  // vector unit, not the LDS, bounds this kernel.)
+  constexpr int NPV = NKB * 2;
+  constexpr int NQK = QSTEPS + PSTEPS;
   auto mma = [&](Blk& x, const unsigned char* sKn, const unsigned char* sVt, auto with_qk) __attribute__((always_inline)) {
-    constexpr bool WITH_QK = decltype(with_qk)::value;
-    constexpr int NPV = NKB * 2;
-    constexpr int NG = NPV + (WITH_QK ? QSTEPS + PSTEPS : 0);
+    constexpr int NG = NPV + (decltype(with_qk)::value ? NQK : 0);
     u32x4 opnd[NG][NKB > DB ? NKB : DB];
     auto issue = [&](int g) __attribute__((always_inline)) {
       if (g < NPV) {
@@ -236,10 +277,6 @@ __global__ __launch_bounds__(RNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       if (g + 1 < NG) issue(g + 1);
-      if (g == NPV) {
-#pragma unroll
-        for (int kb2 = 0; kb2 < NKB; ++kb2) x.s[kb2] = chain_init(x.m);
-      }
       if (g < NPV) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) x.o[db] = Mma<QT>::run(opnd[g][db], x.pr[g], x.o[db]);
@@ -247,16 +284,17 @@ __global__ __launch_bounds__(RNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       } else {
         const int t = g - NPV;
 #pragma unroll
-        for (int kb2 = 0; kb2 < NKB; ++kb2)
-          x.s[kb2] = t < QSTEPS ? Mma<QT>::run(opnd[g][kb2], x.qf[t], x.s[kb2])
-                                : Mma<PT>::run(opnd[g][kb2], x.pf[t - QSTEPS], x.s[kb2]);
+        for (int kb2 = 0; kb2 < NKB; ++kb2) {
+          const f32x16 c = t == 0 ? x.mi : x.s[kb2];
+          x.s[kb2] = t < QSTEPS ? Mma<QT>::run(opnd[g][kb2], x.qf[t], c) : Mma<PT>::run(opnd[g][kb2], x.pf[t - QSTEPS], c);
+        }
       }
     }
   };
   // First part of the softmax of tile t (scores S log2(e) - M in y.s): keys past N masked, the
   // row max; the first tile sets M to its max (key 0 is always visible), later tiles move it
-  // when they exceed it by 8, rescaling O and the row sum.  (A uniform branch: it stays
-  // outside the interleaved region.)
+  // when they exceed it by RES_GROW, rescaling O and the row sum.  (A uniform branch: it
+  // stays outside the interleaved region.)
   auto rowmax = [&](Blk& y, int t, auto may_mask) __attribute__((always_inline)) {
     const int kb = t * BN;
     if (decltype(may_mask)::value && kb + BN > N) {
@@ -277,7 +315,7 @@ __global__ __launch_bounds__(RNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, y.s[kb2][r]);
     mx = halves_max(mx);
     const bool first = t == 0;
-    const bool grow = first || mx > 8.f;
+    const bool grow = first || mx > RES_GROW;
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
       const float d = grow ? mx : 0.f;
       if (!first) {
@@ -286,7 +324,7 @@ __global__ __launch_bounds__(RNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int db = 0; db < DB; ++db) y.o[db] *= alpha;
         y.l *= alpha;
       }
-      y.m += d;
+      set_m(y, y.m + d);
 #pragma unroll
       for (int kb2 = 0; kb2 < NKB; ++kb2) y.s[kb2] -= d;
     }
@@ -362,7 +400,12 @@ __global__ __launch_bounds__(RNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     qk0(B);
     expo(A);
     int t = 0;
-    for (; t + 2 < nkt; ++t) step(t, NOMASK);
+    for (; t + 2 < nkt; ++t) {
+      // step t reads tile t + 1 (K') and t (V); tile th first at step th - 1 >= 1, inside this
+      // loop since th <= nkt - 2; every wavefront with a block pair gets here in its first one
+      if (split_pending && t == th - 1) split_barrier();
+      step(t, NOMASK);
+    }
     if (t + 1 < nkt) step(t++, MASK);
     {
       const unsigned char* vt = sV + t * SVB;
@@ -379,6 +422,8 @@ __global__ __launch_bounds__(RNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     store(A, a0);
     store(B, a0 + RNW);
   }
+  // a wavefront without a block pair (short N) still takes its part in the split barrier
+  if (split_pending) split_barrier();
 }
 
 }  // namespace attn

@@ -34,6 +34,7 @@ import csv
 import glob
 import hashlib
 import json
+import re
 import os
 import subprocess
 import sys
@@ -46,6 +47,7 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # MI355X dense mat
 PEAK_HBM_GBS = 8000.0
 N_XCD = 8
 KERNEL_SOURCES = ["attention_additive_rank_amd/csrc/fb_attn_kernel.h",
+                  "attention_additive_rank_amd/csrc/fb_attn_resident.h",
                   "attention_additive_rank_amd/csrc/fb_tile_map.h",
                   "attention_additive_rank_amd/csrc/fb_attn_inst.hip"]
 WORKLOAD_CHOICES = ["sandwich", "gpt2_alibi_causal", "mulbias_cos", "vision_svd", "pairformer_svd",
@@ -342,6 +344,7 @@ def main():
     else:
         alg_bytes = algorithmic_bytes(w, es, phi_es, fH * w.N)
     counters = None
+    kernel_label = f"fused attention kernel ({entry_name(use_log2, jit, mul, w)})"
     hf = harness_file(w, jit)
     if os.path.exists(hf):
         with open(hf) as f:
@@ -355,6 +358,11 @@ def main():
             counters["hbm_gbs"] = round(hr["bytes_per_launch"] / (kern_ms * 1e-3) / 1e9, 1) \
                 if hr.get("bytes_per_launch") else None
             counters["source"] = os.path.relpath(hf, ROOT)
+            if hr.get("kernel"):
+                # the kernel that ran, from the trace: its name up to the template arguments
+                m = re.search(r"attn_fwd_(res_)?kernel", hr["kernel"])
+                if m:
+                    kernel_label = f"{m.group(0)} ({entry_name(use_log2, jit, mul, w)})"
 
     cpu = None
     if args.cpu_budget > 0:
@@ -399,7 +407,7 @@ def main():
                      "traffic": counters["bytes_per_launch"] if counters else None,
                      "algorithmic_bytes": alg_bytes,
                      "timing": "average of the timed launches (HIP events on the launch stream)",
-                     "kernel": f"attn_fwd_kernel ({entry_name(use_log2, jit, mul, w)})"},
+                     "kernel": kernel_label},
         "counters": counters,
         "cpu_baseline": cpu,
     }

@@ -259,10 +259,10 @@ fb_status fb_attn_fwd_lowrank(const fb_attn_args* a, const void* phi_q, const vo
  * natural-log value as for fb_attn_fwd_lowrank; fb_attn_bwd_lowrank takes natural-unit
  * factors (phi_q ln(2) for the factors given here).
  * Kernel choice (results to the same bars either way): a non-causal launch with
- * D <= 64, R rounded up to 16 at most 32 and N at most the keys whose K' and V tiles
- * fit in 80 KB of LDS (512 for D = 32 with R <= 16; 640, 256 and 384 for D = 16, 64
- * with R <= 16 and D = 32 with R <= 32) runs one workgroup per (b, h) with all its
- * tiles resident in LDS; every other launch streams the tiles.  The environment
+ * D = 16 and R <= 32, or D = 32 and R <= 16, and N at most the keys whose K' and V
+ * tiles fit in 80 KB of LDS (D = 32: 512 keys with R <= 16, 640 with R = 0; D = 16:
+ * 512, 640 and 832 keys with R <= 32, R <= 16 and R = 0) runs one workgroup per
+ * (b, h) with all its tiles resident in LDS; every other launch streams the tiles.  The environment
  * variable FB_ATTN_STREAMING=1 (read at each call) selects the streaming kernel
  * for every launch.
  */

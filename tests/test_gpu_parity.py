@@ -936,12 +936,13 @@ def test_multi_item_workgroups(fb, entry, B, H, N, D, R, dt):
 
 
 # ------------------------------------------- whole K' and V resident in LDS ----
-# Non-causal 16-bit launches in exp2 units whose K' and V tiles all fit in 80 KB of LDS run the
-# resident kernel (one workgroup per (b, h), no barrier in the key loop); FB_ATTN_STREAMING=1
-# sends the same launch to the streaming kernel.  Shapes: the largest N of each (D, R_pad)
-# (512 keys at D 32 / R_pad 16, 640 at D 16 / 16, 256 at D 64 / 16, 384 at D 32 / 32, 320 at
-# D 64 / 0), one key, ragged tails, R not a multiple of 16 (zero padding inside the kernel),
-# per-batch factors, bf16 factors, f16 operands, and more (b, h) than compute units.
+# Non-causal 16-bit launches in exp2 units with D + R_pad <= 48 whose K' and V tiles all fit
+# in 80 KB of LDS run the resident kernel (one workgroup per (b, h), no barrier in the key
+# loop); FB_ATTN_STREAMING=1 sends the same launch to the streaming kernel.  Shapes: the
+# largest N of each (D, R_pad) (512 keys at D 32 / R_pad 16, 640 at D 32 / 0 and D 16 / 16,
+# 512 at D 16 / 32, 832 at D 16 / 0), one key, ragged tails, R not a multiple of 16 (zero
+# padding inside the kernel), per-batch factors, bf16 factors, f16 operands, more (b, h) than
+# compute units, and two shapes just outside (D 64; D 32 with R_pad 32) that stream.
 RESIDENT = [
     # (B, H, N, D, R, factor shape, Q/K/V dtype, factor dtype)
     (3, 4, 512, 32, 16, "head", "bf16", "f16"),
@@ -949,12 +950,18 @@ RESIDENT = [
     (1, 2, 1, 32, 16, "head", "bf16", "f16"),
     (2, 2, 64, 16, 8, "batch", "f16", "f16"),
     (2, 2, 640, 16, 16, "head", "bf16", "f16"),
-    (1, 3, 256, 64, 16, "head", "bf16", "f16"),
-    (2, 2, 320, 64, 0, None, "bf16", "f16"),
-    (2, 2, 384, 32, 24, "batch", "bf16", "f16"),
+    (2, 2, 512, 16, 24, "batch", "bf16", "f16"),
+    (2, 3, 640, 32, 0, None, "bf16", "f16"),
+    (1, 2, 832, 16, 0, None, "f16", "f16"),
     (4, 2, 97, 16, 32, "head", "f16", "f16"),
     (2, 2, 130, 32, 16, "head", "bf16", "bf16"),
     (160, 4, 200, 32, 16, "head", "bf16", "f16"),
+    (1, 3, 256, 64, 16, "head", "bf16", "f16"),
+    (2, 2, 384, 32, 24, "batch", "bf16", "f16"),
+    # wide, fast-moving scores (factor entries of scale 2.5: bias spread of about 25 in
+    # exp2 units, running maxima that jump by more than the lazy-rescale headroom)
+    (4, 2, 512, 32, 16, "wide", "bf16", "f16"),
+    (2, 2, 512, 16, 32, "wide", "f16", "f16"),
 ]
 
 
@@ -972,7 +979,8 @@ def test_resident_kernel(fb, B, H, N, D, R, fsh, dt, pdt, monkeypatch):
     bias = None
     if R:
         fshape = (B, H, N, R) if fsh == "batch" else (H, N, R)
-        pq, pk = (synth.round_to(r.standard_normal(fshape) * 0.5, pdt) for _ in range(2))
+        fs = 2.5 if fsh == "wide" else 0.5
+        pq, pk = (synth.round_to(r.standard_normal(fshape) * fs, pdt) for _ in range(2))
         bias = oracle.lowrank_bias(pq, pk) * np.log(2.0)
     ro, rl = oracle.attention(q, k, v, bias=bias)
     for streaming in (False, True):
