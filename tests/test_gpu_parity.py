@@ -996,6 +996,54 @@ def test_resident_kernel(fb, B, H, N, D, R, fsh, dt, pdt, monkeypatch):
     monkeypatch.delenv("FB_ATTN_STREAMING")
 
 
+def _resident_sweep(n=12, seed=20261204):
+    """Random shapes the resident kernel takes (non-causal, D + R_pad <= 48, N up to the keys
+    that fit), drawn once from a fixed seed: ragged N, every factor layout, both Q/K/V dtypes,
+    factor scales from narrow to wide score ranges."""
+    r = np.random.default_rng(seed)
+    maxkeys = {(16, 0): 832, (16, 16): 640, (16, 32): 512, (32, 0): 640, (32, 16): 512}
+    out = []
+    for i in range(n):
+        D = int(r.choice([16, 32]))
+        R = int(r.choice([0, 8, 16] + ([24, 32] if D == 16 else [])))
+        rp = 0 if R == 0 else 16 * ((R + 15) // 16)
+        N = int(r.integers(1, maxkeys[(D, rp)] + 1))
+        B, H = int(r.integers(1, 5)), int(r.integers(1, 4))
+        fsh = str(r.choice(["head", "batch"]))
+        dt = str(r.choice(["bf16", "f16"]))
+        pdt = "f16" if dt == "f16" else str(r.choice(["bf16", "f16"]))
+        out.append((B, H, N, D, R, fsh, dt, pdt, float(r.choice([0.25, 0.5, 1.5, 2.5]))))
+    return out
+
+
+@pytest.mark.parametrize("B,H,N,D,R,fsh,dt,pdt,fs", _resident_sweep(), ids=[f"res-sweep-{i}" for i in range(12)])
+def test_resident_random_sweep(fb, B, H, N, D, R, fsh, dt, pdt, fs, monkeypatch):
+    """Every output row and LSE of fb_attn_fwd_lowrank_log2 on seeded random resident-kernel
+    shapes, through the resident and the streaming kernel, against the oracle."""
+    import torch
+    say(f"resident sweep B={B} H={H} N={N} D={D} R={R} {fsh} {dt}/{pdt} scale {fs}")
+    r = np.random.default_rng(3100 + N + 7 * D + R)
+    q, k, v = (synth.round_to(r.standard_normal((B, H, N, D)) * 0.5, dt) for _ in range(3))
+    qd, kd, vd = (to_dev(x, dt) for x in (q, k, v))
+    pq = pk = bias = None
+    if R:
+        fshape = (B, H, N, R) if fsh == "batch" else (H, N, R)
+        pq, pk = (synth.round_to(r.standard_normal(fshape) * fs, pdt) for _ in range(2))
+        bias = oracle.lowrank_bias(pq, pk) * np.log(2.0)
+    ro, rl = oracle.attention(q, k, v, bias=bias)
+    for streaming in (False, True):
+        if streaming:
+            monkeypatch.setenv("FB_ATTN_STREAMING", "1")
+        lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda:0")
+        o = fb.fb_attn_fwd_lowrank_log2(qd, kd, vd, to_dev(pq, pdt) if R else None,
+                                        to_dev(pk, pdt) if R else None, lse=lse)
+        torch.cuda.synchronize()
+        what = "streaming" if streaming else "resident"
+        assert_close(to_np(o), ro, dt, f"{what} O")
+        np.testing.assert_allclose(lse.cpu().double().numpy(), rl, rtol=0, atol=2e-2, err_msg=f"{what} LSE")
+    monkeypatch.delenv("FB_ATTN_STREAMING")
+
+
 # ------------------------------------------------ backward in exp2 units ----
 BWD_LOG2 = [
     # (B, H, N, D, R, factor shape, dtype, causal)
