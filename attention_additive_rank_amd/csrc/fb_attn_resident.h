@@ -8,10 +8,12 @@
 // kernel in fb_attn_kernel.h is the schedule:
 //   * One workgroup = 4 wavefronts (one per SIMD) = one (b, h).  It copies every 64-key tile
 //     of K' and V into LDS once (direct global->LDS loads, the streaming kernel's tile layout
-//     and slot map), waits for them at its only barrier, and each wavefront then runs its
-//     query blocks of 32 rows over all key tiles with no further synchronisation.  On short
-//     sequences the streaming kernel spends much of each tile waiting at its barrier for the
-//     slowest of its wavefronts (8 key tiles per item there, a barrier per tile).
+//     and slot map) and each wavefront runs its query blocks of 32 rows over all key tiles
+//     with at most two barriers in all: one after the copies (after the first half of them
+//     with four or more tiles) and, with four or more tiles, one in the first block pair's
+//     key loop before the second half is read.  On short sequences the streaming kernel
+//     spends much of each tile waiting at its barrier for the slowest of its wavefronts
+//     (8 key tiles per item there, a barrier per tile).
 //   * Two workgroups share a compute unit (at most 80 KB of LDS each): one's copies and
 //     set-up run under the other's key loop.
 //   * Each wavefront carries TWO query blocks, A and B, half a key step apart, so its matrix
@@ -30,7 +32,7 @@
 //     uniform branch) run before the interleaved part; the exponentials, conversions and
 //     MFMAs after it form one scheduling region.
 // Only non-causal launches with D + RP <= 48 whose key tiles fit (res_max_keys) take this
-// kernel: wider Q' would not fit two blocks and a step's operands in 256 registers.
+// kernel: with wider Q' the state of two blocks spills out of 256 registers.
 #pragma once
 
 #include <type_traits>
@@ -97,9 +99,8 @@ __global__ __launch_bounds__(RNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 
   // ---- every key tile into LDS ------------------------------------------------------
-  // Load g of the workgroup is load n = g mod NDMA of tile g / NDMA (tile_slot: K region,
-  // then phi_k, then V; lane l fills chunk slot l of the load's 1 KB).  Every slot is
-  // written: a row past N copies row N - 1 (its scores are masked, its P is 0), a chunk
+  // A tile takes NDMA loads of 1 KB, load n filling slots of the K region, then phi_k, then V
+  // (tile_slot; lane l fills chunk slot l of the load's 1 KB).  Every slot is written: a row past N copies row N - 1 (its scores are masked, its P is 0), a chunk
   // without data an in-row stand-in (loader_src_byte: it meets zero phi_q columns or feeds
   // head dims >= D only), so everything the MFMAs read is finite.
   // With four or more tiles the copies go in two halves: tiles [0, th) before the first
