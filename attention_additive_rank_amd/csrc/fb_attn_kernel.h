@@ -808,10 +808,12 @@ __global__ __launch_bounds__(LOADER ? NT + NLW * 64 : NT, 1) void attn_fwd_kerne
   // half the size of a P V MFMA.  (Dense-bias mode keeps the adds: its bias registers leave
   // no room.)
   constexpr bool MROW = KW > 1 && MODE != 1;
-  // FOLD: every score chain starts from -M2 in all 16 registers: at RP 64 a copy of that
-  // vector is kept (minit), otherwise it is written into the accumulator when the chain
-  // starts (registers for the longer chains' operands).
-  constexpr bool MINIT = FOLD && RP >= 64;
+  // FOLD: every score chain starts from -M2 in all 16 registers, kept as a copy (minit,
+  // rewritten only when M2 moves) instead of 16 moves into the accumulator when each chain
+  // starts: the softmax phase is the longer one on narrow heads and in the causal kernel.
+  // Multi-item instances with D + RP > 48 write it into the accumulator instead: with the
+  // next item's fragments the copy does not fit in their registers.
+  constexpr bool MINIT = FOLD && !(MULTI && D + RP > 48);
   f32x16 minit = f32x16{};
   auto chain_init = [&]() __attribute__((always_inline)) {
     if constexpr (MINIT) {
