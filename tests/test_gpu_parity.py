@@ -358,6 +358,32 @@ def test_strided_inputs_and_broadcast_factors(fb):
     assert_close(to_np(out), ro, "bf16", "strided + broadcast")
 
 
+def test_resident_strided_inputs_and_broadcast_factors(fb, monkeypatch):
+    """The resident kernel's copies and stores on strided views: Q/K/V as permuted views into one
+    packed buffer, a permuted output view, factors broadcast over batch and heads, LSE too;
+    compared with the oracle through both kernels."""
+    import torch
+    r = np.random.default_rng(8)
+    B, H, N, D, R = 3, 2, 300, 32, 16
+    big = to_dev(synth.round_to(r.standard_normal((B, N, H, 3 * D + 8)) * 0.5, "bf16"), "bf16")
+    qd, kd, vd = (big[..., i * D:(i + 1) * D].permute(0, 2, 1, 3) for i in range(3))
+    pq = synth.round_to(r.standard_normal((N, R)) * 0.6, "f16")
+    pk = synth.round_to(r.standard_normal((N, R)) * 0.6, "f16")
+    qn, kn, vn = (to_np(x) for x in (qd, kd, vd))
+    ro, rl = oracle.attention(qn, kn, vn, bias=oracle.lowrank_bias(pq, pk) * np.log(2.0))
+    for streaming in (False, True):
+        if streaming:
+            monkeypatch.setenv("FB_ATTN_STREAMING", "1")
+        out = torch.empty((B, N, H, D), dtype=torch.bfloat16, device="cuda:0").permute(0, 2, 1, 3)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda:0")
+        fb.fb_attn_fwd_lowrank_log2(qd, kd, vd, to_dev(pq, "f16"), to_dev(pk, "f16"), out=out, lse=lse)
+        torch.cuda.synchronize()
+        what = "streaming" if streaming else "resident"
+        assert_close(to_np(out), ro, "bf16", f"{what} strided + broadcast")
+        np.testing.assert_allclose(lse.cpu().double().numpy(), rl, rtol=0, atol=2e-2, err_msg=f"{what} LSE")
+    monkeypatch.delenv("FB_ATTN_STREAMING")
+
+
 def test_unaligned_factor_rows(fb):
     """Factor rows that are not 16-byte aligned take the element-wise load path."""
     import torch
