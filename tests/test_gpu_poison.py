@@ -59,6 +59,9 @@ FWD = [
     ("lowrank", 1, 2, 190, 32, "f32", True),
     ("lowrank_log2", 2, 2, 301, 64, "f16", True),
     ("lowrank_log2", 1, 3, 129, 16, "bf16", False),
+    # factor rows of whole 16-byte chunks: these take the resident-K'/V kernel
+    ("lowrank_log2_res", 2, 3, 301, 32, "bf16", False),
+    ("lowrank_log2_res", 3, 1, 129, 16, "f16", False),
     ("densebias", 1, 2, 333, 64, "bf16", False),
     ("densebias", 2, 1, 200, 32, "f16", True),
     ("alibi", 2, 3, 275, 64, "bf16", True),
@@ -77,8 +80,11 @@ def test_forward_writes_every_output_and_nothing_more(fb, entry, B, H, N, D, dt,
     lse = Guarded((B, H, N), torch.float32)
     say(f"poisoned outputs: {entry} B={B} H={H} N={N} D={D} {dt} causal={causal}")
     kw = dict(causal=causal, out=o.view, lse=lse.view)
-    R = 3 if entry == "mulbias" else 6          # mulbias: (R - 1) D <= 128
+    # mulbias: (R - 1) D <= 128; the resident kernel needs R a multiple of 8 with D + R <= 48
+    R = 3 if entry == "mulbias" else (48 - D if entry == "lowrank_log2_res" else 6)
     pdt = "f32" if dt == "f32" else "f16"
+    if entry == "lowrank_log2_res":
+        entry = "lowrank_log2"
     if entry in ("lowrank", "lowrank_log2", "mulbias"):
         pq = synth.round_to(r.standard_normal((H, N, R)) * 0.5, pdt)
         pk = synth.round_to(r.standard_normal((H, N, R)) * 0.5, pdt)
